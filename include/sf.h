@@ -1,0 +1,305 @@
+/*
+ * sf.h -- C ABI of the layer-sliding fine-tuning step for MI355X (gfx950).
+ *
+ * The method: "An Efficient Heterogeneous Co-Design for Fine-Tuning on a
+ * Single GPU" (SlideFormer), as summarised on gist.science (de/es/fr).  The
+ * device holds only a small window of decoder layers; each layer's weights
+ * stream in from pinned host memory, its gradients stream out to host memory
+ * and a host-side Adam updates it while the device moves on to the next layer
+ * (de §2A "Leichtgewichtige asynchrone Engine", es §2A "Arquitectura de
+ * Deslizamiento de Capas", fr §2A).  Device memory is a fixed queue of
+ * pre-allocated cache units, each sized for exactly one layer's parameters and
+ * gradients (de §2B, es §2B "Cola de Cache GPU Pre-asignada", fr §2B).
+ *
+ * Conventions for every entry point:
+ *   - Return value: sf_status; 0 = SF_OK, negative = error.  No C++
+ *     exception crosses the ABI.  sf_last_error() returns a thread-local
+ *     message describing the last failure on the calling thread.
+ *   - Ownership: the caller owns every device buffer and every pinned host
+ *     buffer passed in; the library borrows raw pointers and never frees
+ *     them.  The library owns only the objects its *_create calls make
+ *     (contexts, engines, their side streams, events and host threads) and
+ *     releases them in the matching *_destroy.
+ *   - No entry point allocates device memory.  Buffers are carved out of
+ *     caller-provided regions whose sizes come from sf_layer_layout().
+ *   - Arguments are validated before any device work is enqueued; a
+ *     validation failure leaves every buffer untouched.
+ *   - Streams are passed as sf_stream (a hipStream_t); NULL is the default
+ *     stream.  Device work is enqueued asynchronously on that stream unless
+ *     the entry point says otherwise.
+ *   - Device pointers must be 16-byte aligned.  Row-major layouts throughout.
+ *   - Storage dtype: SF_F32 (everything fp32) or SF_BF16 (parameters and
+ *     activations bf16, accumulation and statistics fp32).  Weight gradients
+ *     are always fp32.
+ */
+#ifndef SF_H
+#define SF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sf_status;
+enum {
+  SF_OK = 0,
+  SF_ERR_ARG = -1,          /* bad argument (NULL, size, inconsistent shape) */
+  SF_ERR_UNSUPPORTED = -2,  /* shape outside what the kernels implement     */
+  SF_ERR_ALIGN = -3,        /* pointer not 16-byte aligned                   */
+  SF_ERR_NOT_PINNED = -4,   /* host pointer is not page-locked host memory   */
+  SF_ERR_POOL = -5,         /* caller-provided region too small              */
+  SF_ERR_HIP = -6,          /* a HIP runtime call failed                     */
+  SF_ERR_STATE = -7,        /* object is in a sticky error state             */
+  SF_ERR_NO_DEVICE = -8     /* no usable gfx950 device                       */
+};
+
+typedef enum { SF_F32 = 0, SF_BF16 = 1 } sf_dtype;
+
+typedef void* sf_stream; /* hipStream_t */
+
+/*
+ * Shape of one Llama-style decoder block and its batch.  The pages name the
+ * Llama, Qwen and Mistral families (de §5, es §3) and the fused RoPE,
+ * RMSNorm and SwiGLU ops (de §2C, es §2C, fr §2C); the block is:
+ *   xn = RMSNorm(x; g1); q,k,v = xn Wq^T, xn Wk^T, xn Wv^T; q',k' = RoPE;
+ *   A = causal softmax(q'k'^T/sqrt(d)) v (GQA: query head h reads KV head
+ *   floor(h*n_kv/n_h)); h = x + A Wo^T; hn = RMSNorm(h; g2);
+ *   a = silu(hn Wg^T) * (hn Wu^T); y = h + a Wd^T.
+ * Supported: head_dim in {64, 128}; n_heads % n_kv_heads == 0; hidden, ffn
+ * and vocab multiples of 8; batch, seq >= 1.  rope_base > 0, rms_eps >= 0.
+ */
+typedef struct {
+  int32_t hidden, n_heads, n_kv_heads, head_dim, ffn;
+  int32_t vocab;      /* 0 = no embedding / LM head                        */
+  int32_t batch, seq; /* tokens T = batch * seq                             */
+  float rms_eps;      /* 1e-6 for the Llama family                          */
+  float rope_base;    /* 10000                                              */
+  int32_t dtype;      /* sf_dtype                                           */
+} sf_shape;
+
+/* Tensor order inside one layer's flat parameter (and gradient) buffer. */
+enum { SF_WQ = 0, SF_WK, SF_WV, SF_WO, SF_WG, SF_WU, SF_WD, SF_G1, SF_G2, SF_NTENSORS };
+
+/*
+ * Byte layout of one layer.  Parameters use the storage dtype; gradients are
+ * fp32 with the same tensor order.  W tensors are [out, in] row-major.
+ * Wq, Wk, Wv are adjacent with no padding (one [(n_h+2 n_kv) d, H] matrix);
+ * Wg, Wu likewise (one [2F, H] matrix); other tensors start 256-B aligned.
+ */
+typedef struct {
+  size_t off[SF_NTENSORS], bytes[SF_NTENSORS];           /* parameters */
+  size_t grad_off[SF_NTENSORS], grad_bytes_t[SF_NTENSORS]; /* fp32 grads */
+  size_t n_params;        /* parameter count of one layer                      */
+  size_t param_bytes;     /* size of the flat parameter buffer                 */
+  size_t grad_bytes;      /* size of the flat fp32 gradient buffer             */
+  size_t saved_bytes;     /* per-layer activations kept from fwd for bwd       */
+  size_t workspace_bytes; /* per-context device workspace                      */
+  size_t head_workspace_bytes; /* extra workspace of sf_head_fwd_bwd for the
+                                  chunk size given to sf_layer_layout           */
+} sf_layout;
+
+/*
+ * Sizes of every region for `shape`.  head_chunk_rows is the LCE chunk
+ * (rows of logits per block, >= 1; ignored when vocab == 0).  Host-only:
+ * touches no device.
+ */
+sf_status sf_layer_layout(const sf_shape* shape, int32_t head_chunk_rows, sf_layout* out);
+
+typedef struct sf_ctx sf_ctx;
+
+/*
+ * Create a context for `shape` on the current HIP device.  d_workspace must
+ * hold layout.workspace_bytes (+ head_workspace_bytes when the head is used);
+ * the context keeps the pointer and carves bwd temporaries and the RoPE
+ * tables out of it (the tables are uploaded here, synchronously).  The
+ * region must stay alive and untouched by the caller until sf_ctx_destroy.
+ * Returns SF_ERR_NO_DEVICE when no gfx950 device is current.
+ */
+sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_workspace,
+                        size_t workspace_bytes, sf_ctx** out);
+sf_status sf_ctx_destroy(sf_ctx* ctx);
+
+/*
+ * Forward of one decoder block (the steps above).
+ *   d_w     : flat parameters, sf_layout.param_bytes, storage dtype.
+ *   d_x     : [T, H] layer input, storage dtype.
+ *   d_y     : [T, H] layer output, storage dtype (may not alias d_x).
+ *   d_saved : sf_layout.saved_bytes; receives the activations bwd needs.
+ * Enqueued on `stream`; no host synchronisation.
+ */
+sf_status sf_layer_fwd(sf_ctx* ctx, const void* d_w, const void* d_x, void* d_y, void* d_saved,
+                       sf_stream stream);
+
+/*
+ * Backward of one decoder block.
+ *   d_x     : the same layer input given to sf_layer_fwd (RMSNorm-1 bwd).
+ *   d_saved : as filled by sf_layer_fwd with the same d_w and d_x.
+ *   d_dy    : [T, H] upstream gradient, storage dtype.
+ *   d_dx    : [T, H] input gradient, storage dtype (may alias d_dy).
+ *   d_dw    : fp32 gradients in layout order (sf_layout.grad_off), overwritten
+ *             (not accumulated).  Deterministic: no floating-point atomics.
+ * Uses the context workspace for temporaries; calls on one context must be
+ * serialised on one stream.
+ */
+sf_status sf_layer_bwd(sf_ctx* ctx, const void* d_w, const void* d_x, const void* d_saved,
+                       const void* d_dy, void* d_dx, float* d_dw, sf_stream stream);
+
+/*
+ * Fused LinearCrossEntropy head (de §2C "Fused LinearCrossEntropy",
+ * es §2C, fr §2C): final RMSNorm with gain d_gf [H], logits = hf W_lm^T in
+ * blocks of head_chunk_rows rows (the full [T, V] logits never exist),
+ * next-token cross-entropy averaged over batch*(seq-1) positions (target of
+ * position s is ids[b, s+1]), and its backward.
+ *   d_wlm  : [V, H] storage dtype;  d_x : [T, H] last block output;
+ *   d_ids  : [T] int32 token ids in [0, V) (checked on the device: an id
+ *            outside the range makes the loss NaN);
+ *   d_loss : one fp32 (device);  d_dx : [T, H] storage dtype;
+ *   d_dgf  : [H] fp32;  d_dwlm : [V, H] fp32.  All outputs overwritten.
+ */
+sf_status sf_head_fwd_bwd(sf_ctx* ctx, const void* d_gf, const void* d_wlm, const void* d_x,
+                          const int32_t* d_ids, float* d_loss, void* d_dx, float* d_dgf,
+                          float* d_dwlm, sf_stream stream);
+
+/* x0[t] = E[ids[t]] for t < T.  E [V, H] storage dtype, x0 [T, H]. */
+sf_status sf_embed_fwd(sf_ctx* ctx, const void* d_E, const int32_t* d_ids, void* d_x0, sf_stream stream);
+
+/* dE[v] = sum over t with ids[t] == v of dx0[t], fp32 [V, H], overwritten,
+ * summed in increasing t (deterministic). */
+sf_status sf_embed_bwd(sf_ctx* ctx, const void* d_dx0, const int32_t* d_ids, float* d_dE,
+                       sf_stream stream);
+
+/*
+ * Host Adam over n fp32 elements (es §2A: the CPU updates layer L_i with
+ * host-resident optimizer states; es §2B: states are flattened host
+ * tensors; de/es/fr §2B: shared buffers do the FP32 -> BF16 conversion).
+ *   m <- b1 m + (1-b1) g ; v <- b2 v + (1-b2) g^2 ;
+ *   p <- p - lr (m/(1-b1^step)) / (sqrt(v/(1-b2^step)) + eps)
+ * p_bf16 (optional, may be NULL) receives round-to-nearest-even bf16 of the
+ * new p.  step >= 1.  Runs synchronously on n_threads host threads
+ * (n_threads <= 0: one per available core).  Host pointers, any memory.
+ */
+sf_status sf_adam_host(float* p, float* m, float* v, const float* g, uint16_t* p_bf16, size_t n,
+                       int64_t step, float lr, float b1, float b2, float eps, int32_t n_threads);
+
+/* ------------------------------------------------------------------ engine */
+
+typedef struct sf_engine sf_engine;
+
+enum {
+  SF_ENGINE_ADAM = 1,  /* run host Adam on every streamed-out gradient          */
+  SF_ENGINE_HEAD = 2   /* ids in; embedding + fused LinearCrossEntropy head    */
+};
+
+/*
+ * Engine configuration.  All pointers are borrowed and must outlive the
+ * engine.
+ *   d_pool/pool_bytes : device region (256-B aligned) for min(window,
+ *       n_layers) cache units; unit u holds one layer's parameters (storage
+ *       dtype, param_bytes rounded up to 256) followed by its fp32 gradients
+ *       (grad_bytes rounded up to 256).  Layer l always uses unit l % window.
+ *   d_act/act_bytes   : device region (256-B aligned) of at least
+ *       sf_engine_act_bytes(): the n_layers + 1 layer inputs/outputs [T, H],
+ *       the n_layers saved activation sets, one [T, H] gradient buffer and
+ *       the device loss.
+ *   h_params[l]       : pinned host, layer l flat parameters in the
+ *       parameter layout (storage dtype).  Streamed to the device twice per
+ *       step (forward and backward) except for the last `window` layers,
+ *       which stay resident across the forward/backward turnaround.  With
+ *       SF_ENGINE_ADAM the updated parameters are written back here.
+ *   h_master/h_m/h_v[l]: host fp32 master weights and Adam moments of
+ *       layer l in the fp32 gradient layout (grad_off / grad_bytes_t); any
+ *       host memory.  Required with SF_ENGINE_ADAM.  For SF_F32 storage
+ *       h_master[l] may equal h_params[l].
+ *   h_grad_slots[k]   : n_grad_slots pinned fp32 buffers of grad_bytes,
+ *       shared by every layer in turn (de/es/fr §2B shared CPU buffers).
+ *   compute_stream    : the stream kernels run on (the caller's).
+ *   SF_ENGINE_HEAD: d_E [V, H], d_gf [H], d_wlm [V, H] device, storage
+ *       dtype, resident; d_head_grads device fp32 [dE | dgf | dWlm] of
+ *       2 V H + H floats; h_head_grads pinned fp32, same shape; with
+ *       SF_ENGINE_ADAM also h_head_params (pinned, storage dtype, [E | gf |
+ *       Wlm]) and fp32 h_head_master/m/v of the same shape.  The updated
+ *       head parameters are copied back to d_E/d_gf/d_wlm before the step
+ *       returns.
+ */
+typedef struct {
+  int32_t n_layers;
+  int32_t window;          /* >= 2 */
+  int32_t n_grad_slots;    /* >= 2 */
+  int32_t flags;
+  int32_t adam_threads;    /* <= 0: one per available core */
+  float lr, b1, b2, eps;
+  void* d_pool;
+  size_t pool_bytes;
+  void* d_act;
+  size_t act_bytes;
+  void** h_params;
+  float** h_master;
+  float** h_m;
+  float** h_v;
+  float** h_grad_slots;
+  sf_stream compute_stream;
+  void* d_E;
+  void* d_gf;
+  void* d_wlm;
+  float* d_head_grads;
+  void* h_head_params;
+  float* h_head_master;
+  float* h_head_m;
+  float* h_head_v;
+  float* h_head_grads;
+} sf_engine_cfg;
+
+/* Per-step measurements (host wall clock and device events). */
+typedef struct {
+  double wall_ms;          /* sf_slide_step entry to return                   */
+  double compute_ms;       /* union of compute-stream busy intervals          */
+  double copy_ms;          /* union of H2D and D2H busy intervals             */
+  double h2d_ms, d2h_ms;   /* per-direction busy time                          */
+  double overlap_pct;      /* 100 (compute + copy - span) / min(compute, copy) */
+  double span_ms;          /* first device event to last                       */
+  double adam_ms;          /* sum of host Adam job durations                   */
+  double h2d_bytes, d2h_bytes;
+  double h2d_gbps, d2h_gbps;
+  float loss;
+} sf_step_stats;
+
+/* Device bytes the engine needs in d_act for `shape` and n_layers. */
+sf_status sf_engine_act_bytes(const sf_shape* shape, int32_t n_layers, size_t* out);
+
+sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** out);
+
+/*
+ * One training iteration (de §2A, es §2A, fr §2A): forward through every
+ * layer with the next layer's parameters prefetched into a free cache unit,
+ * the head (with SF_ENGINE_HEAD), then backward in reverse order; each
+ * layer's fp32 gradients stream to a shared host slot and, with
+ * SF_ENGINE_ADAM, are applied by host Adam threads while the device runs the
+ * next layer's backward.  Adam of layer i uses this iteration's gradients
+ * (no staleness), so the step equals plain synchronous training.
+ *   d_in  : [T] int32 ids (SF_ENGINE_HEAD) or [T, H] layer-0 input.
+ *   d_dy  : [T, H] upstream gradient of the last layer (no head), else NULL.
+ *   h_loss: receives the loss (SF_ENGINE_HEAD), may be NULL.
+ * Returns after the iteration's device work and Adam jobs are complete.
+ * A HIP failure moves the engine to a sticky error state (SF_ERR_STATE on
+ * later calls).
+ */
+sf_status sf_slide_step(sf_engine* eng, const void* d_in, const void* d_dy, float* h_loss,
+                        sf_step_stats* stats);
+
+/* Device pointer of layer l's input activation from the last step (l = 0..
+ * n_layers; l = n_layers is the last layer's output), and of the input
+ * gradient of layer 0 after the last step.  For tests and inspection. */
+sf_status sf_engine_layer_input(sf_engine* eng, int32_t layer, void** d_x);
+sf_status sf_engine_dx0(sf_engine* eng, void** d_dx0);
+
+sf_status sf_engine_destroy(sf_engine* eng);
+
+const char* sf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SF_H */

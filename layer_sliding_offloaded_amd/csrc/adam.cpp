@@ -1,0 +1,105 @@
+// Host-side Adam over flat fp32 arrays with a fused fp32 -> bf16 copy.
+//
+// The pages put the optimizer on the CPU: while the device runs the backward
+// of L_{i-1}, host threads update L_i with optimizer states that live in
+// host memory as flattened tensors, and shared buffers carry the FP32 ->
+// BF16 conversion (es §2A "Actualizacion Asincrona", es §2B, de §2B, fr §2B).
+// One pass reads g, p, m, v and writes p, m, v and the bf16 copy (about 30
+// bytes per parameter of host DRAM traffic), so the loop is written to
+// vectorise (AVX2/FMA) and is split across threads in cache-sized chunks.
+#include "adam.h"
+
+#include <algorithm>
+#include <cmath>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+
+namespace sf {
+
+namespace {
+
+inline uint16_t f32_to_bf16(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, 4);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return static_cast<uint16_t>(b >> 16);
+}
+
+}  // namespace
+
+AdamCoef adam_coef(int64_t step, float lr, float b1, float b2, float eps) {
+  AdamCoef c;
+  c.b1 = b1;
+  c.b2 = b2;
+  c.one_b1 = 1.0f - b1;
+  c.one_b2 = 1.0f - b2;
+  c.inv_bc1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(b1), static_cast<double>(step))));
+  c.inv_bc2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(b2), static_cast<double>(step))));
+  c.lr = lr;
+  c.eps = eps;
+  return c;
+}
+
+void adam_range(float* __restrict p, float* __restrict m, float* __restrict v, const float* __restrict g,
+                uint16_t* __restrict pb, size_t n, const AdamCoef& c) {
+  const float b1 = c.b1, b2 = c.b2, o1 = c.one_b1, o2 = c.one_b2;
+  const float ib1 = c.inv_bc1, ib2 = c.inv_bc2, lr = c.lr, eps = c.eps;
+  if (pb) {
+#pragma GCC ivdep
+    for (size_t i = 0; i < n; ++i) {
+      const float gi = g[i];
+      const float mi = b1 * m[i] + o1 * gi;
+      const float vi = b2 * v[i] + o2 * gi * gi;
+      m[i] = mi;
+      v[i] = vi;
+      const float pi = p[i] - lr * (mi * ib1) / (std::sqrt(vi * ib2) + eps);
+      p[i] = pi;
+      pb[i] = f32_to_bf16(pi);
+    }
+  } else {
+#pragma GCC ivdep
+    for (size_t i = 0; i < n; ++i) {
+      const float gi = g[i];
+      const float mi = b1 * m[i] + o1 * gi;
+      const float vi = b2 * v[i] + o2 * gi * gi;
+      m[i] = mi;
+      v[i] = vi;
+      p[i] = p[i] - lr * (mi * ib1) / (std::sqrt(vi * ib2) + eps);
+    }
+  }
+}
+
+int default_threads() {
+  const unsigned n = std::thread::hardware_concurrency();
+  return n == 0 ? 1 : static_cast<int>(std::min(n, 64u));
+}
+
+}  // namespace sf
+
+using namespace sf;
+
+extern "C" sf_status sf_adam_host(float* p, float* m, float* v, const float* g, uint16_t* p_bf16, size_t n,
+                                  int64_t step, float lr, float b1, float b2, float eps, int32_t n_threads) {
+  if (n == 0) return SF_OK;
+  if (!p || !m || !v || !g) return fail(SF_ERR_ARG, "NULL array");
+  if (step < 1) return fail(SF_ERR_ARG, "step must be >= 1");
+  const AdamCoef c = adam_coef(step, lr, b1, b2, eps);
+  int nt = n_threads > 0 ? n_threads : default_threads();
+  const size_t min_chunk = 1 << 16;
+  nt = static_cast<int>(std::max<size_t>(1, std::min<size_t>(nt, (n + min_chunk - 1) / min_chunk)));
+  if (nt == 1) {
+    adam_range(p, m, v, g, p_bf16, n, c);
+    return SF_OK;
+  }
+  std::vector<std::thread> th;
+  const size_t per = (n + nt - 1) / nt;
+  for (int t = 0; t < nt; ++t) {
+    const size_t b = t * per, e = std::min(n, b + per);
+    if (b >= e) break;
+    th.emplace_back([=, &c] { adam_range(p + b, m + b, v + b, g + b, p_bf16 ? p_bf16 + b : nullptr, e - b, c); });
+  }
+  for (auto& x : th) x.join();
+  return SF_OK;
+}

@@ -1,0 +1,502 @@
+// C ABI: shape validation, buffer layouts, contexts, and the kernel
+// sequences of one decoder block's forward and backward and of the fused
+// LinearCrossEntropy head.
+//
+// The block (a Llama-family decoder layer; the pages name Llama, Qwen and
+// Mistral -- de §5, es §3 -- and the fused RoPE / RMSNorm / SwiGLU /
+// LinearCrossEntropy kernels -- de §2C, es §2C, fr §2C):
+//   xn = RMSNorm(x; g1); [q|k|v] = xn Wqkv^T, RoPE on q and k;
+//   A = causal attention; h = x + A Wo^T; hn = RMSNorm(h; g2);
+//   G, U = hn Wg^T, hn Wu^T; a = silu(G) U; y = h + a Wd^T.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "attention.h"
+#include "gemm.h"
+#include "internal.h"
+#include "rowops.h"
+
+namespace sf {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+sf_status fail(sf_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+sf_status check_shape(const sf_shape* s, Dims* out) {
+  if (!s) return fail(SF_ERR_ARG, "shape is NULL");
+  if (s->dtype != SF_F32 && s->dtype != SF_BF16) return fail(SF_ERR_ARG, "dtype %d is not SF_F32/SF_BF16", s->dtype);
+  if (s->hidden <= 0 || s->n_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 || s->ffn <= 0 ||
+      s->batch <= 0 || s->seq <= 0 || s->vocab < 0)
+    return fail(SF_ERR_ARG, "non-positive size in shape");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SF_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", s->head_dim);
+  if (s->n_heads % s->n_kv_heads != 0)
+    return fail(SF_ERR_UNSUPPORTED, "n_heads %d not a multiple of n_kv_heads %d", s->n_heads, s->n_kv_heads);
+  if (s->hidden % 8 || s->ffn % 8 || s->vocab % 8)
+    return fail(SF_ERR_UNSUPPORTED, "hidden, ffn and vocab must be multiples of 8");
+  if (!(s->rms_eps >= 0.f) || !(s->rope_base > 0.f)) return fail(SF_ERR_ARG, "rms_eps must be >= 0, rope_base > 0");
+  const int64_t T = static_cast<int64_t>(s->batch) * s->seq;
+  if (T > (1 << 30) || static_cast<int64_t>(s->hidden) * 4 > (1 << 30))
+    return fail(SF_ERR_UNSUPPORTED, "sizes exceed 32-bit row indexing");
+  Dims d;
+  d.H = s->hidden; d.nh = s->n_heads; d.nkv = s->n_kv_heads; d.d = s->head_dim; d.F = s->ffn;
+  d.V = s->vocab; d.B = s->batch; d.S = s->seq; d.T = T;
+  d.Nq = d.nh * d.d; d.Nkv = d.nkv * d.d; d.Nqkv = d.Nq + 2 * d.Nkv;
+  d.dtype = s->dtype; d.e = s->dtype == SF_BF16 ? 2 : 4;
+  d.eps = s->rms_eps; d.rope_base = s->rope_base;
+  if (out) *out = d;
+  return SF_OK;
+}
+
+// Tensor order Wq Wk Wv | Wo | Wg Wu | Wd | g1 | g2; '|' = 256-B boundary.
+void param_layout(const Dims& d, size_t elem, size_t* off, size_t* bytes, size_t* total) {
+  const size_t H = d.H, F = d.F;
+  bytes[SF_WQ] = d.Nq * H * elem;
+  bytes[SF_WK] = d.Nkv * H * elem;
+  bytes[SF_WV] = d.Nkv * H * elem;
+  bytes[SF_WO] = H * d.Nq * elem;
+  bytes[SF_WG] = F * H * elem;
+  bytes[SF_WU] = F * H * elem;
+  bytes[SF_WD] = H * F * elem;
+  bytes[SF_G1] = H * elem;
+  bytes[SF_G2] = H * elem;
+  off[SF_WQ] = 0;
+  off[SF_WK] = off[SF_WQ] + bytes[SF_WQ];
+  off[SF_WV] = off[SF_WK] + bytes[SF_WK];
+  off[SF_WO] = align256(off[SF_WV] + bytes[SF_WV]);
+  off[SF_WG] = align256(off[SF_WO] + bytes[SF_WO]);
+  off[SF_WU] = off[SF_WG] + bytes[SF_WG];
+  off[SF_WD] = align256(off[SF_WU] + bytes[SF_WU]);
+  off[SF_G1] = align256(off[SF_WD] + bytes[SF_WD]);
+  off[SF_G2] = align256(off[SF_G1] + bytes[SF_G1]);
+  *total = align256(off[SF_G2] + bytes[SF_G2]);
+}
+
+SavedLayout saved_layout(const Dims& d) {
+  SavedLayout s;
+  const size_t T = d.T, e = d.e;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t r = o; o = align256(o + bytes); return r; };
+  s.xn = take(T * d.H * e);
+  s.r1 = take(T * 4);
+  s.qkv = take(T * d.Nqkv * e);
+  s.O = take(T * d.Nq * e);
+  s.lse = take(static_cast<size_t>(d.B) * d.nh * d.S * 4);
+  s.h = take(T * d.H * e);
+  s.hn = take(T * d.H * e);
+  s.r2 = take(T * 4);
+  s.G = take(T * d.F * e);
+  s.U = take(T * d.F * e);
+  s.a = take(T * d.F * e);
+  s.total = o;
+  return s;
+}
+
+WorkLayout work_layout(const Dims& d, int head_chunk_rows) {
+  WorkLayout w;
+  const size_t T = d.T, e = d.e;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t r = o; o = align256(o + bytes); return r; };
+  w.rope_cos = take(static_cast<size_t>(d.S) * (d.d / 2) * 4);
+  w.rope_sin = take(static_cast<size_t>(d.S) * (d.d / 2) * 4);
+  w.dGU = take(T * 2 * d.F * e);
+  w.dhn = take(T * d.H * e);
+  w.dh = take(T * d.H * e);
+  w.dA = take(T * d.Nq * e);
+  w.dsum = take(static_cast<size_t>(d.B) * d.nh * d.S * 4);
+  w.dqkv = take(T * d.Nqkv * e);
+  w.dxn = take(T * d.H * e);
+  w.gain_partial = take(static_cast<size_t>(kGainChunks) * d.H * 4);
+  w.total = o;
+  if (d.V > 0) {
+    const size_t R = static_cast<size_t>(head_chunk_rows > 0 ? head_chunk_rows : 1);
+    w.hf = take(T * d.H * e);
+    w.rf = take(T * 4);
+    w.dhf = take(T * d.H * e);
+    w.logits = take(R * d.V * 4);
+    w.dlogits = take(R * d.V * e);
+    w.loss_rows = take(T * 4);
+  } else {
+    w.hf = w.rf = w.dhf = w.logits = w.dlogits = w.loss_rows = 0;
+  }
+  w.head_total = o - w.total;
+  return w;
+}
+
+namespace {
+
+sf_status check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (!p) return fail(SF_ERR_ARG, "NULL buffer pointer");
+    if (!aligned16(p)) return fail(SF_ERR_ALIGN, "buffer %p is not 16-byte aligned", p);
+  }
+  return SF_OK;
+}
+
+sf_status check_ctx(const sf_ctx* c) {
+  if (!c) return fail(SF_ERR_ARG, "ctx is NULL");
+  return SF_OK;
+}
+
+inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+inline const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
+
+}  // namespace
+
+}  // namespace sf
+
+using namespace sf;
+
+extern "C" {
+
+const char* sf_last_error(void) { return sf::g_last_error.c_str(); }
+
+sf_status sf_layer_layout(const sf_shape* shape, int32_t head_chunk_rows, sf_layout* out) {
+  Dims d;
+  sf_status st = check_shape(shape, &d);
+  if (st) return st;
+  if (!out) return fail(SF_ERR_ARG, "out is NULL");
+  if (d.V > 0 && head_chunk_rows <= 0) return fail(SF_ERR_ARG, "head_chunk_rows must be >= 1");
+  sf_layout L;
+  std::memset(&L, 0, sizeof L);
+  param_layout(d, d.e, L.off, L.bytes, &L.param_bytes);
+  param_layout(d, 4, L.grad_off, L.grad_bytes_t, &L.grad_bytes);
+  L.n_params = static_cast<size_t>(d.Nqkv) * d.H + static_cast<size_t>(d.H) * d.Nq +
+               3 * static_cast<size_t>(d.F) * d.H + 2 * static_cast<size_t>(d.H);
+  L.saved_bytes = saved_layout(d).total;
+  const WorkLayout w = work_layout(d, head_chunk_rows);
+  L.workspace_bytes = w.total;
+  L.head_workspace_bytes = w.head_total;
+  *out = L;
+  return SF_OK;
+}
+
+sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_workspace, size_t workspace_bytes,
+                        sf_ctx** out) {
+  Dims d;
+  sf_status st = check_shape(shape, &d);
+  if (st) return st;
+  if (!out) return fail(SF_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  sf_layout L;
+  st = sf_layer_layout(shape, head_chunk_rows, &L);
+  if (st) return st;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(SF_ERR_NO_DEVICE, "no HIP device");
+  int dev = 0;
+  SF_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  SF_HIP(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(SF_ERR_NO_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  const size_t need = L.workspace_bytes + (d.V > 0 ? L.head_workspace_bytes : 0);
+  if (!d_workspace) return fail(SF_ERR_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(d_workspace) & 255u) return fail(SF_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(SF_ERR_POOL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  sf_ctx* c = new sf_ctx();
+  c->dims = d;
+  c->layout = L;
+  c->saved = saved_layout(d);
+  c->work = work_layout(d, head_chunk_rows);
+  c->head_chunk_rows = head_chunk_rows;
+  c->ws = static_cast<char*>(d_workspace);
+  c->ws_bytes = workspace_bytes;
+  c->device = dev;
+  // RoPE tables: phi[s, i] = s * base^(-2i/d), evaluated in double, stored fp32.
+  const int half = d.d / 2;
+  std::vector<float> cs(static_cast<size_t>(d.S) * half), sn(cs.size());
+  for (int s = 0; s < d.S; ++s)
+    for (int i = 0; i < half; ++i) {
+      const double w = std::pow(static_cast<double>(d.rope_base), -2.0 * i / d.d);
+      const double phi = s * w;
+      cs[static_cast<size_t>(s) * half + i] = static_cast<float>(std::cos(phi));
+      sn[static_cast<size_t>(s) * half + i] = static_cast<float>(std::sin(phi));
+    }
+  hipError_t e1 = hipMemcpy(c->ws + c->work.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice);
+  hipError_t e2 = hipMemcpy(c->ws + c->work.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
+  if (e1 != hipSuccess || e2 != hipSuccess) {
+    delete c;
+    return fail(SF_ERR_HIP, "uploading RoPE tables failed: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  }
+  *out = c;
+  return SF_OK;
+}
+
+sf_status sf_ctx_destroy(sf_ctx* ctx) {
+  delete ctx;
+  return SF_OK;
+}
+
+sf_status sf_layer_fwd(sf_ctx* c, const void* d_w, const void* d_x, void* d_y, void* d_saved, sf_stream stream) {
+  if (sf_status st = check_ctx(c)) return st;
+  if (sf_status st = check_ptrs({d_w, d_x, d_y, d_saved})) return st;
+  if (d_x == d_y) return fail(SF_ERR_ARG, "d_y may not alias d_x");
+  const Dims& d = c->dims;
+  const sf_layout& L = c->layout;
+  const SavedLayout& sv = c->saved;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = static_cast<int>(d.T);
+  char* ws = c->ws;
+
+  void* xn = at(d_saved, sv.xn);
+  float* r1 = reinterpret_cast<float*>(at(d_saved, sv.r1));
+  void* qkv = at(d_saved, sv.qkv);
+  void* O = at(d_saved, sv.O);
+  float* lse = reinterpret_cast<float*>(at(d_saved, sv.lse));
+  void* h = at(d_saved, sv.h);
+  void* hn = at(d_saved, sv.hn);
+  float* r2 = reinterpret_cast<float*>(at(d_saved, sv.r2));
+  void* G = at(d_saved, sv.G);
+  void* U = at(d_saved, sv.U);
+  void* a = at(d_saved, sv.a);
+
+  SF_HIP(rmsnorm_fwd(d.dtype, d_x, at(d_w, L.off[SF_G1]), xn, r1, T, d.H, d.eps, s));
+
+  GemmArgs g;
+  g.A = xn; g.lda = d.H;
+  g.B = at(d_w, L.off[SF_WQ]); g.ldb = d.H;
+  g.C = qkv; g.ldc = d.Nqkv;
+  g.M = T; g.N = d.Nqkv; g.K = d.H;
+  g.rope_cos = reinterpret_cast<const float*>(ws + c->work.rope_cos);
+  g.rope_sin = reinterpret_cast<const float*>(ws + c->work.rope_sin);
+  g.seq = d.S; g.head_dim = d.d; g.rope_cols = d.Nq + d.Nkv;
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Rope, g, s));
+
+  AttnArgs at_;
+  at_.qkv = qkv; at_.ld_qkv = d.Nqkv;
+  at_.out = O; at_.ld_out = d.Nq;
+  at_.lse = lse;
+  at_.batch = d.B; at_.seq = d.S; at_.n_heads = d.nh; at_.n_kv = d.nkv; at_.head_dim = d.d;
+  at_.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d)));
+  SF_HIP(attention_fwd(d.dtype, at_, s));
+
+  g = GemmArgs();
+  g.A = O; g.lda = d.Nq;
+  g.B = at(d_w, L.off[SF_WO]); g.ldb = d.Nq;
+  g.C = h; g.ldc = d.H; g.R = d_x; g.ldr = d.H;
+  g.M = T; g.N = d.H; g.K = d.Nq;
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Resid, g, s));
+
+  SF_HIP(rmsnorm_fwd(d.dtype, h, at(d_w, L.off[SF_G2]), hn, r2, T, d.H, d.eps, s));
+
+  g = GemmArgs();
+  g.A = hn; g.lda = d.H;
+  g.B = at(d_w, L.off[SF_WG]); g.ldb = d.H;
+  g.C = G; g.C2 = U; g.C3 = a; g.ldc = d.F;
+  g.M = T; g.N = 2 * d.F; g.K = d.H; g.ffn = d.F;
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::SwigluFwd, g, s));
+
+  g = GemmArgs();
+  g.A = a; g.lda = d.F;
+  g.B = at(d_w, L.off[SF_WD]); g.ldb = d.F;
+  g.C = d_y; g.ldc = d.H; g.R = h; g.ldr = d.H;
+  g.M = T; g.N = d.H; g.K = d.F;
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Resid, g, s));
+  return SF_OK;
+}
+
+sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy,
+                       void* d_dx, float* d_dw, sf_stream stream) {
+  if (sf_status st = check_ctx(c)) return st;
+  if (sf_status st = check_ptrs({d_w, d_x, d_saved, d_dy, d_dx, d_dw})) return st;
+  const Dims& d = c->dims;
+  const sf_layout& L = c->layout;
+  const SavedLayout& sv = c->saved;
+  const WorkLayout& wl = c->work;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = static_cast<int>(d.T);
+  char* ws = c->ws;
+  char* dw = reinterpret_cast<char*>(d_dw);
+
+  const void* xn = at(d_saved, sv.xn);
+  const float* r1 = reinterpret_cast<const float*>(at(d_saved, sv.r1));
+  const void* qkv = at(d_saved, sv.qkv);
+  const void* O = at(d_saved, sv.O);
+  const float* lse = reinterpret_cast<const float*>(at(d_saved, sv.lse));
+  const void* h = at(d_saved, sv.h);
+  const void* hn = at(d_saved, sv.hn);
+  const float* r2 = reinterpret_cast<const float*>(at(d_saved, sv.r2));
+  const void* G = at(d_saved, sv.G);
+  const void* U = at(d_saved, sv.U);
+  const void* a = at(d_saved, sv.a);
+  char* dGU = ws + wl.dGU;
+  void* dhn = ws + wl.dhn;
+  void* dh = ws + wl.dh;
+  void* dA = ws + wl.dA;
+  float* dsum = reinterpret_cast<float*>(ws + wl.dsum);
+  void* dqkv = ws + wl.dqkv;
+  void* dxn = ws + wl.dxn;
+  float* partial = reinterpret_cast<float*>(ws + wl.gain_partial);
+
+  // down projection: da = dy Wd fused with SwiGLU backward -> [dG | dU]
+  GemmArgs g;
+  g.A = d_dy; g.lda = d.H;
+  g.B = at(d_w, L.off[SF_WD]); g.ldb = d.F;
+  g.C = dGU; g.C2 = dGU + static_cast<size_t>(d.F) * d.e; g.ldc = 2 * d.F;
+  g.R = G; g.R2 = U; g.ldr = d.F;
+  g.M = T; g.N = d.F; g.K = d.H;
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::SwigluBwd, g, s));
+  // dWd = dy^T a
+  g = GemmArgs();
+  g.A = d_dy; g.lda = d.H;
+  g.B = a; g.ldb = d.F;
+  g.C = dw + L.grad_off[SF_WD]; g.ldc = d.F;
+  g.M = d.H; g.N = d.F; g.K = T;
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  // dhn = [dG | dU] [Wg; Wu]
+  g = GemmArgs();
+  g.A = dGU; g.lda = 2 * d.F;
+  g.B = at(d_w, L.off[SF_WG]); g.ldb = d.H;
+  g.C = dhn; g.ldc = d.H;
+  g.M = T; g.N = d.H; g.K = 2 * d.F;
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+  // [dWg; dWu] = [dG | dU]^T hn
+  g = GemmArgs();
+  g.A = dGU; g.lda = 2 * d.F;
+  g.B = hn; g.ldb = d.H;
+  g.C = dw + L.grad_off[SF_WG]; g.ldc = d.H;
+  g.M = 2 * d.F; g.N = d.H; g.K = T;
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  // RMSNorm-2 backward (+ residual dy) -> dh, dg2
+  SF_HIP(rmsnorm_bwd(d.dtype, dhn, h, r2, at(d_w, L.off[SF_G2]), d_dy, dh, partial, kGainChunks,
+                     reinterpret_cast<float*>(dw + L.grad_off[SF_G2]), T, d.H, s));
+  // dA = dh Wo
+  g = GemmArgs();
+  g.A = dh; g.lda = d.H;
+  g.B = at(d_w, L.off[SF_WO]); g.ldb = d.Nq;
+  g.C = dA; g.ldc = d.Nq;
+  g.M = T; g.N = d.Nq; g.K = d.H;
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+  // dWo = dh^T A
+  g = GemmArgs();
+  g.A = dh; g.lda = d.H;
+  g.B = O; g.ldb = d.Nq;
+  g.C = dw + L.grad_off[SF_WO]; g.ldc = d.Nq;
+  g.M = d.H; g.N = d.Nq; g.K = T;
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  // attention backward (+ inverse RoPE) -> [dq | dk | dv]
+  AttnArgs at_;
+  at_.qkv = qkv; at_.ld_qkv = d.Nqkv;
+  at_.out = const_cast<void*>(O); at_.ld_out = d.Nq;
+  at_.dout = dA; at_.ld_dout = d.Nq;
+  at_.dqkv = dqkv; at_.ld_dqkv = d.Nqkv;
+  at_.lse = const_cast<float*>(lse); at_.dsum = dsum;
+  at_.rope_cos = reinterpret_cast<const float*>(ws + wl.rope_cos);
+  at_.rope_sin = reinterpret_cast<const float*>(ws + wl.rope_sin);
+  at_.batch = d.B; at_.seq = d.S; at_.n_heads = d.nh; at_.n_kv = d.nkv; at_.head_dim = d.d;
+  at_.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d)));
+  SF_HIP(attention_bwd(d.dtype, at_, s));
+  // dxn = [dq | dk | dv] Wqkv
+  g = GemmArgs();
+  g.A = dqkv; g.lda = d.Nqkv;
+  g.B = at(d_w, L.off[SF_WQ]); g.ldb = d.H;
+  g.C = dxn; g.ldc = d.H;
+  g.M = T; g.N = d.H; g.K = d.Nqkv;
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+  // dWqkv = [dq | dk | dv]^T xn
+  g = GemmArgs();
+  g.A = dqkv; g.lda = d.Nqkv;
+  g.B = xn; g.ldb = d.H;
+  g.C = dw + L.grad_off[SF_WQ]; g.ldc = d.H;
+  g.M = d.Nqkv; g.N = d.H; g.K = T;
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  // RMSNorm-1 backward (+ residual dh) -> dx, dg1
+  SF_HIP(rmsnorm_bwd(d.dtype, dxn, d_x, r1, at(d_w, L.off[SF_G1]), dh, d_dx, partial, kGainChunks,
+                     reinterpret_cast<float*>(dw + L.grad_off[SF_G1]), T, d.H, s));
+  return SF_OK;
+}
+
+sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
+                          float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream) {
+  if (sf_status st = check_ctx(c)) return st;
+  if (sf_status st = check_ptrs({d_gf, d_wlm, d_x, d_ids, d_dx, d_dgf, d_dwlm})) return st;
+  if (!d_loss) return fail(SF_ERR_ARG, "d_loss is NULL");
+  const Dims& d = c->dims;
+  if (d.V <= 0) return fail(SF_ERR_ARG, "context was created with vocab = 0");
+  if (d.S < 2) return fail(SF_ERR_ARG, "next-token loss needs seq >= 2");
+  const WorkLayout& wl = c->work;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = static_cast<int>(d.T);
+  char* ws = c->ws;
+  void* hf = ws + wl.hf;
+  float* rf = reinterpret_cast<float*>(ws + wl.rf);
+  char* dhf = ws + wl.dhf;
+  float* logits = reinterpret_cast<float*>(ws + wl.logits);
+  void* dlogits = ws + wl.dlogits;
+  float* loss_rows = reinterpret_cast<float*>(ws + wl.loss_rows);
+  float* partial = reinterpret_cast<float*>(ws + wl.gain_partial);
+  const float inv_n = 1.0f / (static_cast<float>(d.B) * static_cast<float>(d.S - 1));
+
+  SF_HIP(rmsnorm_fwd(d.dtype, d_x, d_gf, hf, rf, T, d.H, d.eps, s));
+  const int R = c->head_chunk_rows;
+  for (int r0 = 0; r0 < T; r0 += R) {
+    const int rows = std::min(R, T - r0);
+    const char* hfc = static_cast<const char*>(hf) + static_cast<size_t>(r0) * d.H * d.e;
+    GemmArgs g;
+    g.A = hfc; g.lda = d.H;
+    g.B = d_wlm; g.ldb = d.H;
+    g.C = logits; g.ldc = d.V;
+    g.M = rows; g.N = d.V; g.K = d.H;
+    SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::StoreF32, g, s));
+    SF_HIP(ce_rows(d.dtype, logits, d_ids, dlogits, loss_rows, r0, rows, d.V, d.S, inv_n, s));
+    g = GemmArgs();
+    g.A = dlogits; g.lda = d.V;
+    g.B = d_wlm; g.ldb = d.H;
+    g.C = dhf + static_cast<size_t>(r0) * d.H * d.e; g.ldc = d.H;
+    g.M = rows; g.N = d.H; g.K = d.V;
+    SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+    g = GemmArgs();
+    g.A = dlogits; g.lda = d.V;
+    g.B = hfc; g.ldb = d.H;
+    g.C = d_dwlm; g.ldc = d.H;
+    g.M = d.V; g.N = d.H; g.K = rows;
+    SF_HIP(gemm(d.dtype, GemmLayout::TN, r0 == 0 ? Epi::StoreF32 : Epi::AccF32, g, s));
+  }
+  SF_HIP(loss_reduce(loss_rows, d_loss, T, inv_n, s));
+  SF_HIP(rmsnorm_bwd(d.dtype, dhf, d_x, rf, d_gf, nullptr, d_dx, partial, kGainChunks, d_dgf, T, d.H, s));
+  return SF_OK;
+}
+
+sf_status sf_embed_fwd(sf_ctx* c, const void* d_E, const int32_t* d_ids, void* d_x0, sf_stream stream) {
+  if (sf_status st = check_ctx(c)) return st;
+  if (sf_status st = check_ptrs({d_E, d_ids, d_x0})) return st;
+  const Dims& d = c->dims;
+  if (d.V <= 0) return fail(SF_ERR_ARG, "context was created with vocab = 0");
+  SF_HIP(embed_fwd(d.dtype, d_E, d_ids, d_x0, static_cast<int>(d.T), d.H, d.V, static_cast<hipStream_t>(stream)));
+  return SF_OK;
+}
+
+sf_status sf_embed_bwd(sf_ctx* c, const void* d_dx0, const int32_t* d_ids, float* d_dE, sf_stream stream) {
+  if (sf_status st = check_ctx(c)) return st;
+  if (sf_status st = check_ptrs({d_dx0, d_ids, d_dE})) return st;
+  const Dims& d = c->dims;
+  if (d.V <= 0) return fail(SF_ERR_ARG, "context was created with vocab = 0");
+  SF_HIP(embed_bwd(d.dtype, d_dx0, d_ids, d_dE, static_cast<int>(d.T), d.H, d.V, static_cast<hipStream_t>(stream)));
+  return SF_OK;
+}
+
+}  // extern "C"

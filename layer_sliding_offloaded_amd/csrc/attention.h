@@ -1,0 +1,29 @@
+// Host interface of the causal flash-attention kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sf {
+
+struct AttnArgs {
+  const void* qkv = nullptr;  // [T, ld_qkv]: q' | k' | v  (storage dtype)
+  int64_t ld_qkv = 0;
+  void* out = nullptr;        // A = [T, ld_out], head h at column h d
+  int64_t ld_out = 0;
+  const void* dout = nullptr; // dA, same layout as out (backward)
+  int64_t ld_dout = 0;
+  void* dqkv = nullptr;       // [T, ld_dqkv]: dq | dk | dv (backward output)
+  int64_t ld_dqkv = 0;
+  float* lse = nullptr;       // [B, n_heads, S] base-2 log-sum-exp of scaled scores
+  float* dsum = nullptr;      // [B, n_heads, S] rowsum(dA * A)   (backward scratch)
+  const float* rope_cos = nullptr;  // [S, d/2] (backward: inverse rotation)
+  const float* rope_sin = nullptr;
+  int batch = 0, seq = 0, n_heads = 0, n_kv = 0, head_dim = 0;
+  float scale = 0.f;          // 1 / sqrt(d)
+};
+
+hipError_t attention_fwd(int dtype, const AttnArgs& a, hipStream_t s);
+hipError_t attention_bwd(int dtype, const AttnArgs& a, hipStream_t s);
+
+}  // namespace sf

@@ -1,0 +1,665 @@
+// The layer-sliding engine: one training iteration over L decoder layers
+// with only `window` layers' parameters and gradients resident on the device.
+//
+// What the pages describe (de §2A "Leichtgewichtige asynchrone Engine",
+// es §2A "Arquitectura de Deslizamiento de Capas", fr §2A; de/es/fr §2B):
+//  - the device holds a small active window of layers, the rest live in host
+//    memory; a layer is the unit of transfer and update;
+//  - a fixed queue of pre-allocated device cache units, each sized for one
+//    layer's parameters and gradients (fixed footprint, no reallocation);
+//  - in the backward, layer L_i's gradients go to host memory asynchronously
+//    and host threads run Adam on L_i while the device computes L_{i-1} and
+//    the parameters of L_{i-2} are prefetched;
+//  - a thread-based design with dedicated streams and CPU threads;
+//  - gradient buffers on the host are shared by all layers.
+//
+// Realisation here.  Three HIP streams: compute (the caller's), H2D and D2H
+// (both at default priority), ordered only through events, so host-link
+// copies in both directions overlap kernels.  Unit u = layer mod window;
+// each unit has separate "parameters free" and "gradients free" events, so a
+// unit's parameter slot can be refilled for L_{i-window+1} as soon as the
+// backward of L_i is done while its gradient slot is still draining.  A
+// dispatcher thread waits for each layer's D2H copy and runs Adam on a worker
+// pool, then releases the shared host gradient slot.  Adam of layer i uses
+// this iteration's gradients and only affects the next iteration, so the
+// result equals plain synchronous training.
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <condition_variable>
+#include <deque>
+#include <cstring>
+#include <functional>
+#include <memory>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "adam.h"
+#include "internal.h"
+
+namespace sf {
+
+namespace {
+
+// A fixed pool of worker threads running index-parallel loops.
+class Pool {
+ public:
+  explicit Pool(int n) {
+    for (int i = 0; i < n; ++i) th_.emplace_back([this] { loop(); });
+  }
+  ~Pool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (auto& t : th_) t.join();
+  }
+  // Run fn(0 .. n-1) on the pool and the calling thread; returns when done.
+  void run(size_t n, const std::function<void(size_t)>& fn) {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      fn_ = &fn;
+      n_ = n;
+      next_.store(0);
+      done_ = 0;
+      ++gen_;
+    }
+    cv_.notify_all();
+    work();
+    std::unique_lock<std::mutex> lk(mu_);
+    cv_done_.wait(lk, [&] { return done_ == n_; });
+    fn_ = nullptr;
+  }
+
+ private:
+  void work() {
+    for (;;) {
+      const size_t i = next_.fetch_add(1);
+      if (i >= n_) break;
+      (*fn_)(i);
+      std::lock_guard<std::mutex> lk(mu_);
+      if (++done_ == n_) cv_done_.notify_all();
+    }
+  }
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+        if (!fn_) continue;
+      }
+      work();
+    }
+  }
+  std::vector<std::thread> th_;
+  std::mutex mu_;
+  std::condition_variable cv_, cv_done_;
+  const std::function<void(size_t)>* fn_ = nullptr;
+  size_t n_ = 0, done_ = 0;
+  std::atomic<size_t> next_{0};
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
+
+struct Job {
+  int layer;  // -1 = embedding + head
+  int slot;   // host gradient slot (-1 for the head)
+  hipEvent_t ready;
+};
+
+struct Interval {
+  hipEvent_t a, b;
+  int kind;  // 0 compute, 1 H2D, 2 D2H
+  double bytes;
+};
+
+double now_ms() {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+bool is_pinned(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return a.type == hipMemoryTypeHost;
+}
+
+}  // namespace
+
+}  // namespace sf
+
+using namespace sf;
+
+struct sf_engine {
+  sf_ctx* ctx = nullptr;
+  sf_engine_cfg cfg{};
+  Dims d;
+  sf_layout L{};
+  int nl = 0, W = 0;
+  size_t unit_bytes = 0, x_bytes = 0, head_elems = 0;
+  hipStream_t s_comp = nullptr, s_h2d = nullptr, s_d2h = nullptr;
+  std::vector<char*> uparam, ugrad, x, saved;
+  char* dbuf = nullptr;
+  float* d_loss = nullptr;
+  std::vector<hipEvent_t> ev_param_ready, ev_param_free, ev_grad_ready, ev_grad_free;
+  std::vector<hipEvent_t> tev;
+  size_t tev_used = 0;
+  std::vector<Interval> iv;
+  int64_t step = 0;
+  bool failed = false;
+  // Adam machinery
+  std::unique_ptr<Pool> pool;
+  std::thread dispatcher;
+  std::mutex mu;
+  std::condition_variable cv;
+  std::deque<Job> jobs;
+  std::vector<bool> slot_free;
+  int next_slot = 0;
+  int pending = 0;
+  bool stop = false;
+  bool adam_error = false;
+  AdamCoef coef{};
+  double adam_ms = 0;
+};
+
+namespace sf {
+namespace {
+
+hipEvent_t timing_event(sf_engine* e) {
+  if (e->tev_used >= e->tev.size()) {
+    hipEvent_t ev;
+    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    e->tev.push_back(ev);
+  }
+  return e->tev[e->tev_used++];
+}
+
+// Adam over one segment list: (fp32 offset in master/m/v/grad, count,
+// element offset of the storage-dtype copy).
+struct Seg {
+  size_t off, n, out_off;
+};
+
+void run_adam(sf_engine* e, float* p, float* m, float* v, const float* g, void* out, bool out_is_master,
+              const std::vector<Seg>& segs) {
+  constexpr size_t kChunk = 1 << 18;
+  std::vector<Seg> tasks;
+  for (const Seg& s : segs)
+    for (size_t b = 0; b < s.n; b += kChunk) tasks.push_back({s.off + b, std::min(kChunk, s.n - b), s.out_off + b});
+  const bool bf = e->d.dtype == SF_BF16;
+  const AdamCoef c = e->coef;
+  e->pool->run(tasks.size(), [&](size_t i) {
+    const Seg& t = tasks[i];
+    if (bf) {
+      adam_range(p + t.off, m + t.off, v + t.off, g + t.off, static_cast<uint16_t*>(out) + t.out_off, t.n, c);
+    } else {
+      adam_range(p + t.off, m + t.off, v + t.off, g + t.off, nullptr, t.n, c);
+      if (!out_is_master) std::memcpy(static_cast<float*>(out) + t.out_off, p + t.off, t.n * 4);
+    }
+  });
+}
+
+void dispatcher_loop(sf_engine* e) {
+  (void)hipSetDevice(e->ctx->device);
+  for (;;) {
+    Job j;
+    {
+      std::unique_lock<std::mutex> lk(e->mu);
+      e->cv.wait(lk, [&] { return e->stop || !e->jobs.empty(); });
+      if (e->jobs.empty()) return;  // stop requested and nothing left
+      j = e->jobs.front();
+      e->jobs.pop_front();
+    }
+    const bool ok = hipEventSynchronize(j.ready) == hipSuccess;
+    const double t0 = now_ms();
+    if (ok) {
+      const sf_engine_cfg& c = e->cfg;
+      if (j.layer >= 0) {
+        std::vector<Seg> segs;
+        for (int t = 0; t < SF_NTENSORS; ++t)
+          segs.push_back({e->L.grad_off[t] / 4, e->L.grad_bytes_t[t] / 4, e->L.off[t] / e->d.e});
+        run_adam(e, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot],
+                 c.h_params[j.layer], c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), segs);
+      } else {
+        run_adam(e, c.h_head_master, c.h_head_m, c.h_head_v, c.h_head_grads, c.h_head_params,
+                 c.h_head_params == static_cast<void*>(c.h_head_master), {{0, e->head_elems, 0}});
+      }
+    }
+    const double dt = now_ms() - t0;
+    std::lock_guard<std::mutex> lk(e->mu);
+    if (!ok) e->adam_error = true;
+    e->adam_ms += dt;
+    if (j.slot >= 0) e->slot_free[j.slot] = true;
+    --e->pending;
+    e->cv.notify_all();
+  }
+}
+
+sf_status record_interval(sf_engine* e, hipEvent_t a, hipEvent_t b, int kind, double bytes) {
+  if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
+  e->iv.push_back({a, b, kind, bytes});
+  return SF_OK;
+}
+
+// H2D of layer j's parameters into unit j % W.
+sf_status prefetch(sf_engine* e, int j) {
+  const int u = j % e->W;
+  SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_param_free[u], 0));
+  hipEvent_t a = timing_event(e), b = timing_event(e);
+  if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
+  SF_HIP(hipEventRecord(a, e->s_h2d));
+  SF_HIP(hipMemcpyAsync(e->uparam[u], e->cfg.h_params[j], e->L.param_bytes, hipMemcpyHostToDevice, e->s_h2d));
+  SF_HIP(hipEventRecord(b, e->s_h2d));
+  SF_HIP(hipEventRecord(e->ev_param_ready[u], e->s_h2d));
+  return record_interval(e, a, b, 1, static_cast<double>(e->L.param_bytes));
+}
+
+double union_ms(std::vector<std::pair<double, double>> v) {
+  std::sort(v.begin(), v.end());
+  double tot = 0, cs = -1e300, ce = -1e300;
+  for (auto& p : v) {
+    if (p.first > ce) {
+      if (ce > cs) tot += ce - cs;
+      cs = p.first;
+      ce = p.second;
+    } else {
+      ce = std::max(ce, p.second);
+    }
+  }
+  if (ce > cs) tot += ce - cs;
+  return tot;
+}
+
+sf_status fill_stats(sf_engine* e, hipEvent_t ev0, sf_step_stats* st) {
+  std::vector<std::pair<double, double>> comp, copy, h2d, d2h;
+  double lo = 1e300, hi = -1e300, hb = 0, db = 0;
+  for (const Interval& x : e->iv) {
+    float a = 0, b = 0;
+    SF_HIP(hipEventElapsedTime(&a, ev0, x.a));
+    SF_HIP(hipEventElapsedTime(&b, ev0, x.b));
+    lo = std::min(lo, static_cast<double>(a));
+    hi = std::max(hi, static_cast<double>(b));
+    if (x.kind == 0) comp.push_back({a, b});
+    else copy.push_back({a, b});
+    if (x.kind == 1) { h2d.push_back({a, b}); hb += x.bytes; }
+    if (x.kind == 2) { d2h.push_back({a, b}); db += x.bytes; }
+  }
+  st->compute_ms = union_ms(comp);
+  st->copy_ms = union_ms(copy);
+  st->h2d_ms = union_ms(h2d);
+  st->d2h_ms = union_ms(d2h);
+  st->span_ms = hi > lo ? hi - lo : 0;
+  const double mn = std::min(st->compute_ms, st->copy_ms);
+  st->overlap_pct = mn > 0 ? 100.0 * (st->compute_ms + st->copy_ms - st->span_ms) / mn : 0.0;
+  st->h2d_bytes = hb;
+  st->d2h_bytes = db;
+  st->h2d_gbps = st->h2d_ms > 0 ? hb / (st->h2d_ms * 1e6) : 0;
+  st->d2h_gbps = st->d2h_ms > 0 ? db / (st->d2h_ms * 1e6) : 0;
+  return SF_OK;
+}
+
+sf_status wait_slot(sf_engine* e, int* slot) {
+  std::unique_lock<std::mutex> lk(e->mu);
+  const int k = e->next_slot;
+  e->next_slot = (k + 1) % e->cfg.n_grad_slots;
+  e->cv.wait(lk, [&] { return e->slot_free[k]; });
+  if (e->cfg.flags & SF_ENGINE_ADAM) e->slot_free[k] = false;
+  *slot = k;
+  return SF_OK;
+}
+
+void push_job(sf_engine* e, const Job& j) {
+  std::lock_guard<std::mutex> lk(e->mu);
+  e->jobs.push_back(j);
+  ++e->pending;
+  e->cv.notify_all();
+}
+
+void drain(sf_engine* e) {
+  std::unique_lock<std::mutex> lk(e->mu);
+  e->cv.wait(lk, [&] { return e->pending == 0; });
+}
+
+sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_stats* st) {
+  const Dims& d = e->d;
+  const sf_engine_cfg& c = e->cfg;
+  const bool head = (c.flags & SF_ENGINE_HEAD) != 0;
+  const bool adam = (c.flags & SF_ENGINE_ADAM) != 0;
+  const int nl = e->nl, W = e->W;
+  sf_ctx* ctx = e->ctx;
+  e->tev_used = 0;
+  e->iv.clear();
+  e->step += 1;
+  e->coef = adam_coef(e->step, c.lr, c.b1, c.b2, c.eps);
+  {
+    std::lock_guard<std::mutex> lk(e->mu);
+    e->adam_ms = 0;
+  }
+
+  hipEvent_t ev0 = timing_event(e);
+  if (!ev0) return fail(SF_ERR_HIP, "event pool exhausted");
+  SF_HIP(hipEventRecord(ev0, e->s_comp));
+  // The copy streams start after everything the caller queued before this call.
+  SF_HIP(hipStreamWaitEvent(e->s_h2d, ev0, 0));
+  SF_HIP(hipStreamWaitEvent(e->s_d2h, ev0, 0));
+
+  auto comp_begin = [&](hipEvent_t* a) -> sf_status {
+    *a = timing_event(e);
+    if (!*a) return fail(SF_ERR_HIP, "event pool exhausted");
+    SF_HIP(hipEventRecord(*a, e->s_comp));
+    return SF_OK;
+  };
+  auto comp_end = [&](hipEvent_t a) -> sf_status {
+    hipEvent_t b = timing_event(e);
+    if (!b) return fail(SF_ERR_HIP, "event pool exhausted");
+    SF_HIP(hipEventRecord(b, e->s_comp));
+    return record_interval(e, a, b, 0, 0);
+  };
+  sf_status rc;
+  hipEvent_t a;
+
+  std::vector<const void*> xin(nl + 1);
+  const int32_t* ids = static_cast<const int32_t*>(d_in);
+  if (head) {
+    if ((rc = comp_begin(&a))) return rc;
+    if ((rc = sf_embed_fwd(ctx, c.d_E, ids, e->x[0], e->s_comp))) return rc;
+    if ((rc = comp_end(a))) return rc;
+    xin[0] = e->x[0];
+  } else {
+    xin[0] = d_in;
+  }
+  for (int i = 1; i <= nl; ++i) xin[i] = e->x[i];
+
+  // ---------------- forward: layer i in unit i % W, prefetch i + 1
+  if ((rc = prefetch(e, 0))) return rc;
+  for (int i = 0; i < nl; ++i) {
+    if (i + 1 < nl && (rc = prefetch(e, i + 1))) return rc;
+    const int u = i % W;
+    SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
+    if ((rc = comp_begin(&a))) return rc;
+    if ((rc = sf_layer_fwd(ctx, e->uparam[u], xin[i], e->x[i + 1], e->saved[i], e->s_comp))) return rc;
+    if ((rc = comp_end(a))) return rc;
+    SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
+  }
+
+  // ---------------- head: loss, dx_L, dg_f, dW_lm
+  const void* dy = d_dy;
+  float* hg = c.d_head_grads;
+  const size_t VH = static_cast<size_t>(d.V) * d.H;
+  if (head) {
+    if ((rc = comp_begin(&a))) return rc;
+    if ((rc = sf_head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
+                              e->s_comp)))
+      return rc;
+    if ((rc = comp_end(a))) return rc;
+    hipEvent_t ready = timing_event(e), b0 = timing_event(e), b1 = timing_event(e);
+    if (!ready || !b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
+    SF_HIP(hipEventRecord(ready, e->s_comp));
+    SF_HIP(hipStreamWaitEvent(e->s_d2h, ready, 0));
+    SF_HIP(hipEventRecord(b0, e->s_d2h));
+    SF_HIP(hipMemcpyAsync(c.h_head_grads + VH, hg + VH, (VH + d.H) * 4, hipMemcpyDeviceToHost, e->s_d2h));
+    SF_HIP(hipEventRecord(b1, e->s_d2h));
+    if ((rc = record_interval(e, b0, b1, 2, static_cast<double>((VH + d.H) * 4)))) return rc;
+    dy = e->dbuf;
+  }
+
+  // ---------------- backward: layer i in unit i % W, prefetch i - W + 1
+  for (int i = nl - 1; i >= 0; --i) {
+    const int u = i % W;
+    const int j = i - W + 1;
+    if (j >= 0 && j < nl - W && (rc = prefetch(e, j))) return rc;
+    SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
+    SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_grad_free[u], 0));
+    if ((rc = comp_begin(&a))) return rc;
+    if ((rc = sf_layer_bwd(ctx, e->uparam[u], xin[i], e->saved[i], dy, e->dbuf,
+                           reinterpret_cast<float*>(e->ugrad[u]), e->s_comp)))
+      return rc;
+    if ((rc = comp_end(a))) return rc;
+    dy = e->dbuf;
+    SF_HIP(hipEventRecord(e->ev_grad_ready[u], e->s_comp));
+    SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
+    int k = 0;
+    if ((rc = wait_slot(e, &k))) return rc;
+    hipEvent_t b0 = timing_event(e), b1 = timing_event(e);
+    if (!b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
+    SF_HIP(hipStreamWaitEvent(e->s_d2h, e->ev_grad_ready[u], 0));
+    SF_HIP(hipEventRecord(b0, e->s_d2h));
+    SF_HIP(hipMemcpyAsync(c.h_grad_slots[k], e->ugrad[u], e->L.grad_bytes, hipMemcpyDeviceToHost, e->s_d2h));
+    SF_HIP(hipEventRecord(b1, e->s_d2h));
+    SF_HIP(hipEventRecord(e->ev_grad_free[u], e->s_d2h));
+    if ((rc = record_interval(e, b0, b1, 2, static_cast<double>(e->L.grad_bytes)))) return rc;
+    if (adam) push_job(e, Job{i, k, b1});
+  }
+
+  // ---------------- embedding backward
+  if (head) {
+    if ((rc = comp_begin(&a))) return rc;
+    if ((rc = sf_embed_bwd(ctx, e->dbuf, ids, hg, e->s_comp))) return rc;
+    if ((rc = comp_end(a))) return rc;
+    hipEvent_t ready = timing_event(e), b0 = timing_event(e), b1 = timing_event(e);
+    if (!ready || !b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
+    SF_HIP(hipEventRecord(ready, e->s_comp));
+    SF_HIP(hipStreamWaitEvent(e->s_d2h, ready, 0));
+    SF_HIP(hipEventRecord(b0, e->s_d2h));
+    SF_HIP(hipMemcpyAsync(c.h_head_grads, hg, VH * 4, hipMemcpyDeviceToHost, e->s_d2h));
+    SF_HIP(hipEventRecord(b1, e->s_d2h));
+    if ((rc = record_interval(e, b0, b1, 2, static_cast<double>(VH * 4)))) return rc;
+    if (adam) push_job(e, Job{-1, -1, b1});
+  }
+
+  SF_HIP(hipStreamSynchronize(e->s_comp));
+  SF_HIP(hipStreamSynchronize(e->s_h2d));
+  SF_HIP(hipStreamSynchronize(e->s_d2h));
+  drain(e);
+  if (e->adam_error) return fail(SF_ERR_HIP, "a gradient copy failed before Adam");
+
+  // updated embedding / head parameters back to the device for the next step
+  if (head && adam) {
+    const char* hp = static_cast<const char*>(c.h_head_params);
+    hipEvent_t b0 = timing_event(e), b1 = timing_event(e);
+    if (!b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
+    SF_HIP(hipEventRecord(b0, e->s_h2d));
+    SF_HIP(hipMemcpyAsync(c.d_E, hp, VH * d.e, hipMemcpyHostToDevice, e->s_h2d));
+    SF_HIP(hipMemcpyAsync(c.d_gf, hp + VH * d.e, d.H * d.e, hipMemcpyHostToDevice, e->s_h2d));
+    SF_HIP(hipMemcpyAsync(c.d_wlm, hp + (VH + d.H) * d.e, VH * d.e, hipMemcpyHostToDevice, e->s_h2d));
+    SF_HIP(hipEventRecord(b1, e->s_h2d));
+    if ((rc = record_interval(e, b0, b1, 1, static_cast<double>((2 * VH + d.H) * d.e)))) return rc;
+    SF_HIP(hipStreamSynchronize(e->s_h2d));
+  }
+  if (st) {
+    if ((rc = fill_stats(e, ev0, st))) return rc;
+    std::lock_guard<std::mutex> lk(e->mu);
+    st->adam_ms = e->adam_ms;
+  }
+  return SF_OK;
+}
+
+}  // namespace
+}  // namespace sf
+
+extern "C" {
+
+sf_status sf_engine_act_bytes(const sf_shape* shape, int32_t n_layers, size_t* out) {
+  Dims d;
+  if (sf_status st = check_shape(shape, &d)) return st;
+  if (n_layers < 1 || !out) return fail(SF_ERR_ARG, "n_layers must be >= 1 and out non-NULL");
+  const size_t xb = align256(static_cast<size_t>(d.T) * d.H * d.e);
+  *out = (n_layers + 1) * xb + n_layers * saved_layout(d).total + xb + 256;
+  return SF_OK;
+}
+
+sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** out) {
+  if (!ctx || !cfg || !out) return fail(SF_ERR_ARG, "NULL argument");
+  *out = nullptr;
+  const sf_engine_cfg& c = *cfg;
+  const Dims& d = ctx->dims;
+  const bool head = (c.flags & SF_ENGINE_HEAD) != 0;
+  const bool adam = (c.flags & SF_ENGINE_ADAM) != 0;
+  if (c.n_layers < 1) return fail(SF_ERR_ARG, "n_layers must be >= 1");
+  if (c.window < 2) return fail(SF_ERR_ARG, "window must be >= 2");
+  if (c.n_grad_slots < 2) return fail(SF_ERR_ARG, "n_grad_slots must be >= 2");
+  if (head && d.V <= 0) return fail(SF_ERR_ARG, "SF_ENGINE_HEAD needs a context with vocab > 0");
+  if (!c.d_pool || !c.d_act || !c.h_params || !c.h_grad_slots || !c.compute_stream)
+    return fail(SF_ERR_ARG, "d_pool, d_act, h_params, h_grad_slots and compute_stream are required");
+  if ((reinterpret_cast<uintptr_t>(c.d_pool) | reinterpret_cast<uintptr_t>(c.d_act)) & 255u)
+    return fail(SF_ERR_ALIGN, "d_pool and d_act must be 256-byte aligned");
+  const sf_layout& L = ctx->layout;
+  const int W = std::min(c.window, c.n_layers);
+  const size_t unit = align256(L.param_bytes) + align256(L.grad_bytes);
+  if (c.pool_bytes < static_cast<size_t>(W) * unit)
+    return fail(SF_ERR_POOL, "pool has %zu bytes, %d units need %zu", c.pool_bytes, W, W * unit);
+  sf_shape shp{};
+  shp.hidden = d.H; shp.n_heads = d.nh; shp.n_kv_heads = d.nkv; shp.head_dim = d.d; shp.ffn = d.F;
+  shp.vocab = d.V; shp.batch = d.B; shp.seq = d.S; shp.rms_eps = d.eps; shp.rope_base = d.rope_base;
+  shp.dtype = d.dtype;
+  size_t act = 0;
+  if (sf_status st = sf_engine_act_bytes(&shp, c.n_layers, &act)) return st;
+  if (c.act_bytes < act) return fail(SF_ERR_POOL, "activation region has %zu bytes, needs %zu", c.act_bytes, act);
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (!c.h_params[l]) return fail(SF_ERR_ARG, "h_params[%d] is NULL", l);
+    if (!is_pinned(c.h_params[l])) return fail(SF_ERR_NOT_PINNED, "h_params[%d] is not pinned host memory", l);
+    if (adam && (!c.h_master || !c.h_m || !c.h_v || !c.h_master[l] || !c.h_m[l] || !c.h_v[l]))
+      return fail(SF_ERR_ARG, "SF_ENGINE_ADAM needs h_master/h_m/h_v for layer %d", l);
+  }
+  for (int k = 0; k < c.n_grad_slots; ++k)
+    if (!c.h_grad_slots[k] || !is_pinned(c.h_grad_slots[k]))
+      return fail(SF_ERR_NOT_PINNED, "h_grad_slots[%d] is not pinned host memory", k);
+  if (head) {
+    if (!c.d_E || !c.d_gf || !c.d_wlm || !c.d_head_grads || !c.h_head_grads)
+      return fail(SF_ERR_ARG, "SF_ENGINE_HEAD needs d_E, d_gf, d_wlm, d_head_grads, h_head_grads");
+    if (!is_pinned(c.h_head_grads)) return fail(SF_ERR_NOT_PINNED, "h_head_grads is not pinned");
+    if (adam) {
+      if (!c.h_head_params || !c.h_head_master || !c.h_head_m || !c.h_head_v)
+        return fail(SF_ERR_ARG, "SF_ENGINE_HEAD with ADAM needs h_head_params/master/m/v");
+      if (!is_pinned(c.h_head_params)) return fail(SF_ERR_NOT_PINNED, "h_head_params is not pinned");
+    }
+  }
+
+  sf_engine* e = new sf_engine();
+  e->ctx = ctx;
+  e->cfg = c;
+  e->d = d;
+  e->L = L;
+  e->nl = c.n_layers;
+  e->W = W;
+  e->unit_bytes = unit;
+  e->x_bytes = align256(static_cast<size_t>(d.T) * d.H * d.e);
+  e->head_elems = head ? 2 * static_cast<size_t>(d.V) * d.H + d.H : 0;
+  e->s_comp = static_cast<hipStream_t>(c.compute_stream);
+  auto cleanup = [&](sf_status st) {
+    sf_engine_destroy(e);
+    return st;
+  };
+  if (hipStreamCreateWithFlags(&e->s_h2d, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&e->s_d2h, hipStreamNonBlocking) != hipSuccess)
+    return cleanup(fail(SF_ERR_HIP, "stream creation failed"));
+  char* pool = static_cast<char*>(c.d_pool);
+  for (int u = 0; u < W; ++u) {
+    e->uparam.push_back(pool + u * unit);
+    e->ugrad.push_back(pool + u * unit + align256(L.param_bytes));
+  }
+  char* act_p = static_cast<char*>(c.d_act);
+  const size_t sb = ctx->saved.total;
+  for (int i = 0; i <= e->nl; ++i) e->x.push_back(act_p + i * e->x_bytes);
+  act_p += (e->nl + 1) * e->x_bytes;
+  for (int i = 0; i < e->nl; ++i) e->saved.push_back(act_p + i * sb);
+  act_p += e->nl * sb;
+  e->dbuf = act_p;
+  e->d_loss = reinterpret_cast<float*>(act_p + e->x_bytes);
+  auto mk = [&](std::vector<hipEvent_t>& v) {
+    for (int u = 0; u < W; ++u) {
+      hipEvent_t ev;
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return false;
+      v.push_back(ev);
+    }
+    return true;
+  };
+  if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_ready) || !mk(e->ev_grad_free))
+    return cleanup(fail(SF_ERR_HIP, "event creation failed"));
+  for (int i = 0; i < 8 * e->nl + 32; ++i) {
+    hipEvent_t ev;
+    if (hipEventCreate(&ev) != hipSuccess) return cleanup(fail(SF_ERR_HIP, "event creation failed"));
+    e->tev.push_back(ev);
+  }
+  e->slot_free.assign(c.n_grad_slots, true);
+  const int nt = c.adam_threads > 0 ? c.adam_threads : default_threads();
+  e->pool.reset(new Pool(std::max(0, nt - 1)));
+  e->dispatcher = std::thread(dispatcher_loop, e);
+  *out = e;
+  return SF_OK;
+}
+
+sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float* h_loss, sf_step_stats* stats) {
+  if (!e) return fail(SF_ERR_ARG, "engine is NULL");
+  if (e->failed) return fail(SF_ERR_STATE, "engine is in an error state after an earlier failure");
+  const bool head = (e->cfg.flags & SF_ENGINE_HEAD) != 0;
+  if (!d_in || (!head && !d_dy)) return fail(SF_ERR_ARG, "d_in (and d_dy without a head) are required");
+  if (!aligned16(d_in) || (d_dy && !aligned16(d_dy))) return fail(SF_ERR_ALIGN, "inputs must be 16-byte aligned");
+  const double t0 = now_ms();
+  sf_status rc = step_impl(e, d_in, d_dy, stats);
+  if (rc != SF_OK) {
+    // Leave no work in flight: finish the streams and any queued Adam jobs.
+    const std::string msg = sf_last_error();
+    (void)hipStreamSynchronize(e->s_comp);
+    (void)hipStreamSynchronize(e->s_h2d);
+    (void)hipStreamSynchronize(e->s_d2h);
+    drain(e);
+    e->failed = true;
+    return fail(rc, "%s", msg.c_str());
+  }
+  float loss = 0.f;
+  if (head) {
+    if (hipMemcpy(&loss, e->d_loss, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+      e->failed = true;
+      return fail(SF_ERR_HIP, "loss copy failed");
+    }
+    if (h_loss) *h_loss = loss;
+  }
+  if (stats) {
+    stats->wall_ms = now_ms() - t0;
+    stats->loss = loss;
+  }
+  return SF_OK;
+}
+
+sf_status sf_engine_layer_input(sf_engine* e, int32_t layer, void** d_x) {
+  if (!e || !d_x || layer < 0 || layer > e->nl) return fail(SF_ERR_ARG, "bad argument");
+  *d_x = e->x[layer];
+  return SF_OK;
+}
+
+sf_status sf_engine_dx0(sf_engine* e, void** d_dx0) {
+  if (!e || !d_dx0) return fail(SF_ERR_ARG, "bad argument");
+  *d_dx0 = e->dbuf;
+  return SF_OK;
+}
+
+sf_status sf_engine_destroy(sf_engine* e) {
+  if (!e) return SF_OK;
+  if (e->dispatcher.joinable()) {
+    {
+      std::lock_guard<std::mutex> lk(e->mu);
+      e->stop = true;
+    }
+    e->cv.notify_all();
+    e->dispatcher.join();
+  }
+  e->pool.reset();
+  if (e->s_h2d) (void)hipStreamSynchronize(e->s_h2d);
+  if (e->s_d2h) (void)hipStreamSynchronize(e->s_d2h);
+  for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_ready, &e->ev_grad_free, &e->tev})
+    for (hipEvent_t ev : *v) (void)hipEventDestroy(ev);
+  if (e->s_h2d) (void)hipStreamDestroy(e->s_h2d);
+  if (e->s_d2h) (void)hipStreamDestroy(e->s_d2h);
+  delete e;
+  return SF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,415 @@
+// MFMA GEMM for gfx950 with LDS-staged, double-buffered tiles.
+//
+// Every dense projection of the decoder block and of the LM head goes
+// through this kernel: the forward products y = x W^T (NT), the input
+// gradients dX = dY W (NN) and the weight gradients dW = dY^T X (TN).  Fused
+// epilogues carry the elementwise steps that follow a product (RoPE on q/k,
+// SwiGLU forward and backward, the residual add, fp32 gradient stores), so
+// those tensors make one trip through HBM instead of three.
+//
+// Tile scheme.  A block computes a BM x BN output tile with NW = (BM/WM) *
+// (BN/WN) waves, each owning a WM x WN sub-tile built from 16x16 MFMA
+// fragments.  Per k-stage the block stages BM x 128 B of A and BN x 128 B of
+// B in LDS, always as [row][k] with 16 B of padding per row (row stride
+// 144 B: the 8 lanes of each 128-bit LDS access phase then hit distinct
+// banks).  Operands that are k-contiguous in HBM are copied as 16-byte
+// vectors; operands that are row-contiguous (the transposed side of NN/TN)
+// are read as 8x8 (bf16) or 4x4 (fp32) blocks and transposed in registers
+// before the LDS write, so the MFMA side never sees a strided read.
+// Global loads for stage k+1 are issued before the MFMAs of stage k and
+// written to the other LDS buffer after them: one barrier per stage.
+//
+// Output fragments are computed transposed (MFMA A-operand = B tile) so each
+// lane ends with 4 consecutive output columns of one row: 8-byte (bf16) or
+// 16-byte (fp32) stores, and the partner columns that RoPE (i, i + d/2) and
+// SwiGLU (gate j, up j) need sit in the same lane.
+#include "common.h"
+#include "gemm.h"
+
+namespace sf {
+
+namespace {
+
+constexpr int kStageBytes = 128;  // k-bytes per LDS stage row
+
+// Map a tile-local B row (= output column slot) to the global B row, or -1.
+// Pair epilogues permute the slots so that slot q and q + WN/2 of a wave are
+// partners; otherwise the map is the identity.
+template <Epi E, int WN>
+struct ColMap {
+  __device__ __forceinline__ static int brow(int r, int n0, const GemmArgs& g, int BN) {
+    if constexpr (E == Epi::Rope) {
+      const int wn = r / WN, q = r % WN, half = WN / 2;
+      const int p = wn * half + (q % half);
+      const int hd2 = g.head_dim / 2;
+      const int col = n0 + (p / hd2) * g.head_dim + (p % hd2) + (q >= half ? hd2 : 0);
+      return col < g.N ? col : -1;
+    } else if constexpr (E == Epi::SwigluFwd) {
+      const int wn = r / WN, q = r % WN, half = WN / 2;
+      const int f = n0 / 2 + wn * half + (q % half);
+      if (f >= g.ffn) return -1;
+      return q >= half ? g.ffn + f : f;
+    } else {
+      const int col = n0 + r;
+      return col < g.N ? col : -1;
+    }
+  }
+};
+
+template <typename T, int ROWS, int NT, bool KC>
+struct Loader {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int KG = kStageBytes / 16;  // 16-byte k-groups per row = 8
+  static constexpr int BKE = kStageBytes / sizeof(T);
+  static constexpr int ROW = BKE + VE;
+  // k-contiguous: one 16-byte vector per (row, k-group)
+  static constexpr int NVEC_K = (ROWS * KG + NT - 1) / NT;
+  // row-contiguous: blocks of 4 k-rows x VE columns, transposed on the way
+  // into LDS (4 k-values per LDS row segment: 8 B bf16, 16 B fp32)
+  static constexpr int KB = 4;
+  static constexpr int KGT = BKE / KB;
+  static constexpr int NBLK = (ROWS / VE) * KGT;
+  static constexpr int NB_T = (NBLK + NT - 1) / NT;
+  static constexpr int NREG = KC ? NVEC_K : NB_T * KB;
+  uint4 reg[NREG];
+
+  // src: element (row, k) at src[row * ld + k] (KC) or src[k * ld + row] (!KC).
+  // rowmap(r) gives the global row of tile row r, or -1.
+  template <typename RowMap>
+  __device__ __forceinline__ void load(const T* __restrict__ src, int64_t ld, int k0, int K,
+                                       int tid, RowMap rowmap) {
+    if constexpr (KC) {
+#pragma unroll
+      for (int j = 0; j < NVEC_K; ++j) {
+        const int i = tid + j * NT;
+        const int r = i / KG, c = i % KG;
+        const int kk = k0 + c * VE;
+        const int gr = (i < ROWS * KG) ? rowmap(r) : -1;
+        if (gr >= 0 && kk < K)
+          reg[j] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(gr) * ld + kk);
+        else
+          reg[j] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB_T; ++j) {
+        const int i = tid + j * NT;
+        const int kg = i % KGT, mg = i / KGT;
+        const int gc = (i < NBLK) ? rowmap(mg * VE) : -1;
+#pragma unroll
+        for (int r = 0; r < KB; ++r) {
+          const int kk = k0 + kg * KB + r;
+          if (gc >= 0 && kk < K)
+            reg[j * KB + r] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(kk) * ld + gc);
+          else
+            reg[j * KB + r] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(T* lds, int tid) {
+    if constexpr (KC) {
+#pragma unroll
+      for (int j = 0; j < NVEC_K; ++j) {
+        const int i = tid + j * NT;
+        if (ROWS * KG % NT == 0 || i < ROWS * KG) {
+          const int r = i / KG, c = i % KG;
+          *reinterpret_cast<uint4*>(lds + r * ROW + c * VE) = reg[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB_T; ++j) {
+        const int i = tid + j * NT;
+        if (NBLK % NT == 0 || i < NBLK) {
+          const int kg = i % KGT, mg = i / KGT;
+          const uint4* v = &reg[j * KB];
+          if constexpr (sizeof(T) == 2) {
+            // 4 rows x 8 bf16 -> 8 columns x 4 bf16
+            const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w}, {v[1].x, v[1].y, v[1].z, v[1].w},
+                                      {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w}};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const int d = c >> 1;
+              const uint32_t lo = (c & 1) ? ((w[0][d] >> 16) | (w[1][d] & 0xFFFF0000u))
+                                          : ((w[0][d] & 0xFFFFu) | (w[1][d] << 16));
+              const uint32_t hi = (c & 1) ? ((w[2][d] >> 16) | (w[3][d] & 0xFFFF0000u))
+                                          : ((w[2][d] & 0xFFFFu) | (w[3][d] << 16));
+              *reinterpret_cast<uint2*>(lds + (mg * VE + c) * ROW + kg * KB) = make_uint2(lo, hi);
+            }
+          } else {
+            uint4 t[4];
+            transpose4x4_b32(v, t);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              *reinterpret_cast<uint4*>(lds + (mg * VE + c) * ROW + kg * KB) = t[c];
+          }
+        }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_kernel(const GemmArgs g, int ntm, int ntn) {
+  constexpr bool AKC = (LAY != GemmLayout::TN);
+  constexpr bool BKC = (LAY == GemmLayout::NT);
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int NT = NW * 64;
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int BKE = kStageBytes / sizeof(T);
+  constexpr int ROW = BKE + VE;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int WGM = BM / WM;
+  static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
+
+  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * ROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wm = w % WGM, wn = w / WGM;
+
+  // Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
+  // contiguous range of tiles, then walk that range in groups of 8 tile-rows
+  // so the A rows and B columns a group shares stay in that XCD's L2.
+  const int ntiles = ntm * ntn;
+  int t = blockIdx.x;
+  if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+  constexpr int GM = 8;
+  const int group = t / (GM * ntn);
+  const int first_m = group * GM;
+  const int gsize = min(ntm - first_m, GM);
+  const int tm = first_m + (t % (GM * ntn)) % gsize;
+  const int tn = (t % (GM * ntn)) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const T* __restrict__ A = static_cast<const T*>(g.A);
+  const T* __restrict__ B = static_cast<const T*>(g.B);
+
+  Loader<T, BM, NT, AKC> la;
+  Loader<T, BN, NT, BKC> lb;
+  auto amap = [&](int r) { const int m = m0 + r; return m < g.M ? m : -1; };
+  auto bmap = [&](int r) { return ColMap<E, WN>::brow(r, n0, g, BN); };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (g.K + BKE - 1) / BKE;
+  la.load(A, g.lda, 0, g.K, tid, amap);
+  lb.load(B, g.ldb, 0, g.K, tid, bmap);
+  la.store(smem[0], tid);
+  lb.store(smem[0] + BM * ROW, tid);
+  __syncthreads();
+
+  const int lr = lane % 16, lg = lane / 16;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      la.load(A, g.lda, (kt + 1) * BKE, g.K, tid, amap);
+      lb.load(B, g.ldb, (kt + 1) * BKE, g.K, tid, bmap);
+    }
+    const T* As = smem[buf];
+    const T* Bs = smem[buf] + BM * ROW;
+#pragma unroll
+    for (int s = 0; s < BKE / (4 * VE); ++s) {
+      const int koff = s * 4 * VE + lg * VE;
+      uint4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(As + (wm * WM + i * 16 + lr) * ROW + koff);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(Bs + (wn * WN + j * 16 + lr) * ROW + koff);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[j], af[i]);
+    }
+    if (kt + 1 < nk) {
+      la.store(smem[buf ^ 1], tid);
+      lb.store(smem[buf ^ 1] + BM * ROW, tid);
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------ epilogue
+  // lane holds C[m][c .. c+3] with m = row lr of fragment i, c = 4*lg of
+  // fragment j (tile-local slot numbering, mapped through ColMap).
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WM + i * 16 + lr;
+    if (m >= g.M) continue;
+    if constexpr (E == Epi::Rope || E == Epi::SwigluFwd) {
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+        const int slot = wn * WN + j * 16 + lg * 4;
+        const int c1 = ColMap<E, WN>::brow(slot, n0, g, BN);
+        if (c1 < 0) continue;
+        const f32x4 a1 = acc[i][j], a2 = acc[i][j + FN / 2];
+        float o1[4], o2[4];
+        if constexpr (E == Epi::Rope) {
+          const int c2 = c1 + g.head_dim / 2;
+          T* C = static_cast<T*>(g.C);
+          if (c1 < g.rope_cols) {
+            const int pos = m % g.seq;
+            const int fi = c1 % g.head_dim;  // < head_dim / 2
+            const float* cs = g.rope_cos + static_cast<int64_t>(pos) * (g.head_dim / 2) + fi;
+            const float* sn = g.rope_sin + static_cast<int64_t>(pos) * (g.head_dim / 2) + fi;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              o1[v] = a1[v] * cs[v] - a2[v] * sn[v];
+              o2[v] = a2[v] * cs[v] + a1[v] * sn[v];
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) { o1[v] = a1[v]; o2[v] = a2[v]; }
+          }
+          store4<T>(C + static_cast<int64_t>(m) * g.ldc + c1, o1);
+          store4<T>(C + static_cast<int64_t>(m) * g.ldc + c2, o2);
+        } else {
+          const int f = c1;  // gate row index == output column
+          float o3[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            o1[v] = a1[v];
+            o2[v] = a2[v];
+            o3[v] = silu_f(a1[v]) * a2[v];
+          }
+          const int64_t off = static_cast<int64_t>(m) * g.ldc + f;
+          store4<T>(static_cast<T*>(g.C) + off, o1);
+          store4<T>(static_cast<T*>(g.C2) + off, o2);
+          store4<T>(static_cast<T*>(g.C3) + off, o3);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WN + j * 16 + lg * 4;
+        if (n >= g.N) continue;
+        const f32x4 a = acc[i][j];
+        float o[4] = {a[0], a[1], a[2], a[3]};
+        const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
+        if constexpr (E == Epi::Store) {
+          store4<T>(static_cast<T*>(g.C) + off, o);
+        } else if constexpr (E == Epi::StoreF32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(g.C) + off) = make_float4(o[0], o[1], o[2], o[3]);
+        } else if constexpr (E == Epi::AccF32) {
+          float4* p = reinterpret_cast<float4*>(static_cast<float*>(g.C) + off);
+          float4 c = *p;
+          *p = make_float4(c.x + o[0], c.y + o[1], c.z + o[2], c.w + o[3]);
+        } else if constexpr (E == Epi::Resid) {
+          float r[4];
+          load4<T>(static_cast<const T*>(g.R) + static_cast<int64_t>(m) * g.ldr + n, r);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] += r[v];
+          store4<T>(static_cast<T*>(g.C) + off, o);
+        } else if constexpr (E == Epi::SwigluBwd) {
+          float G[4], U[4], dG[4], dU[4];
+          const int64_t roff = static_cast<int64_t>(m) * g.ldr + n;
+          load4<T>(static_cast<const T*>(g.R) + roff, G);
+          load4<T>(static_cast<const T*>(g.R2) + roff, U);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float sg = 1.0f / (1.0f + __expf(-G[v]));
+            dG[v] = o[v] * U[v] * sg * (1.0f + G[v] * (1.0f - sg));
+            dU[v] = o[v] * G[v] * sg;
+          }
+          store4<T>(static_cast<T*>(g.C) + off, dG);
+          store4<T>(static_cast<T*>(g.C2) + off, dU);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
+hipError_t launch(const GemmArgs& g, hipStream_t s) {
+  const int ntm = (g.M + BM - 1) / BM;
+  const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
+  const int ntn = (ncols + BN - 1) / BN;
+  if (ntm == 0 || ntn == 0) return hipSuccess;
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn), dim3(NT), 0, s, g, ntm, ntn);
+  return hipGetLastError();
+}
+
+// Tile configurations: 0 = 256x256 (8 waves of 128x64), 1 = 128x128 (4 waves of 64x64).
+template <typename T, GemmLayout LAY, Epi E>
+hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s) {
+  if (gemm_tile_config(g.M, (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N) == 0)
+    return launch<T, 256, 256, 128, 64, LAY, E>(g, s);
+  return launch<T, 128, 128, 64, 64, LAY, E>(g, s);
+}
+
+template <typename T>
+hipError_t dispatch(GemmLayout lay, Epi epi, const GemmArgs& g, hipStream_t s) {
+  switch (lay) {
+    case GemmLayout::NT:
+      switch (epi) {
+        case Epi::Store: return dispatch_tiles<T, GemmLayout::NT, Epi::Store>(g, s);
+        case Epi::StoreF32: return dispatch_tiles<T, GemmLayout::NT, Epi::StoreF32>(g, s);
+        case Epi::Resid: return dispatch_tiles<T, GemmLayout::NT, Epi::Resid>(g, s);
+        case Epi::Rope: return dispatch_tiles<T, GemmLayout::NT, Epi::Rope>(g, s);
+        case Epi::SwigluFwd: return dispatch_tiles<T, GemmLayout::NT, Epi::SwigluFwd>(g, s);
+        default: break;
+      }
+      break;
+    case GemmLayout::NN:
+      switch (epi) {
+        case Epi::Store: return dispatch_tiles<T, GemmLayout::NN, Epi::Store>(g, s);
+        case Epi::SwigluBwd: return dispatch_tiles<T, GemmLayout::NN, Epi::SwigluBwd>(g, s);
+        default: break;
+      }
+      break;
+    case GemmLayout::TN:
+      switch (epi) {
+        case Epi::StoreF32: return dispatch_tiles<T, GemmLayout::TN, Epi::StoreF32>(g, s);
+        case Epi::AccF32: return dispatch_tiles<T, GemmLayout::TN, Epi::AccF32>(g, s);
+        default: break;
+      }
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int gemm_tile_config(int M, int N) {
+  const long big = static_cast<long>((M + 255) / 256) * ((N + 255) / 256);
+  return big >= 256 ? 0 : 1;
+}
+
+hipError_t gemm(int dtype, GemmLayout layout, Epi epi, const GemmArgs& g, hipStream_t stream) {
+  if (dtype == 1) return dispatch<bf16>(layout, epi, g, stream);
+  return dispatch<float>(layout, epi, g, stream);
+}
+
+}  // namespace sf

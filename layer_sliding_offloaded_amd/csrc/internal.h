@@ -1,0 +1,66 @@
+// Internal host-side definitions shared by the C-ABI implementation files.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/sf.h"
+
+namespace sf {
+
+// Thread-local last-error message behind sf_last_error().
+void set_error(const char* fmt, ...);
+sf_status fail(sf_status code, const char* fmt, ...);
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Dims {
+  int H = 0, nh = 0, nkv = 0, d = 0, F = 0, V = 0, B = 0, S = 0;
+  int64_t T = 0;
+  int Nq = 0, Nkv = 0, Nqkv = 0;
+  int dtype = 0;
+  size_t e = 4;  // storage element bytes
+  float eps = 0, rope_base = 0;
+};
+
+// Offsets of the activations a layer's forward keeps for its backward.
+struct SavedLayout {
+  size_t xn, r1, qkv, O, lse, h, hn, r2, G, U, a, total;
+};
+// Offsets of the per-context workspace.
+struct WorkLayout {
+  size_t rope_cos, rope_sin, dGU, dhn, dh, dA, dsum, dqkv, dxn, gain_partial, total;
+  // head (appended when vocab > 0)
+  size_t hf, rf, dhf, logits, dlogits, loss_rows, head_total;
+};
+
+sf_status check_shape(const sf_shape* s, Dims* out);
+void param_layout(const Dims& d, size_t elem, size_t* off, size_t* bytes, size_t* total);
+SavedLayout saved_layout(const Dims& d);
+WorkLayout work_layout(const Dims& d, int head_chunk_rows);
+
+}  // namespace sf
+
+struct sf_ctx {
+  sf::Dims dims;
+  sf_layout layout;
+  sf::SavedLayout saved;
+  sf::WorkLayout work;
+  int head_chunk_rows = 0;
+  char* ws = nullptr;  // caller-provided device workspace
+  size_t ws_bytes = 0;
+  int device = 0;
+};
+
+#define SF_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return sf::fail(SF_ERR_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_), \
+                      __FILE__, __LINE__);                                            \
+  } while (0)

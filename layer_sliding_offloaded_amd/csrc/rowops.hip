@@ -1,0 +1,373 @@
+// Row-wise kernels: RMSNorm forward/backward, gain-gradient reduction,
+// embedding gather/scatter, cross-entropy rows and the loss reduction.
+//
+// All are HBM-bound.  A wavefront owns one row and walks it in 16-byte
+// vectors (64 lanes x 16 B = 1 KiB per step, fully coalesced); row
+// statistics are reduced with cross-lane shuffles.  Column reductions over
+// tokens (gain gradients, the loss) go through fixed-order partial sums, never
+// floating-point atomics, so results are bitwise reproducible.
+#include <math.h>
+
+#include "common.h"
+#include "rowops.h"
+
+namespace sf {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* p, float* f) {
+  Elem<T>::unpack(*reinterpret_cast<const uint4*>(p), f);
+}
+template <typename T>
+__device__ __forceinline__ void store_vec(T* p, const float* f) {
+  *reinterpret_cast<uint4*>(p) = Elem<T>::pack(f);
+}
+
+// RMSNorm forward: r = (mean x^2 + eps)^-1/2, y = x r g.
+template <typename T>
+__global__ void __launch_bounds__(256)
+rmsnorm_fwd_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict__ y,
+                   float* __restrict__ r, int rows, int H, float eps) {
+  constexpr int VE = 16 / sizeof(T);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const T* xr = x + static_cast<int64_t>(row) * H;
+  float ss = 0.f;
+  for (int c = lane * VE; c < H; c += 64 * VE) {
+    float f[VE];
+    load_vec<T>(xr + c, f);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ss += f[e] * f[e];
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.0f / sqrtf(ss / H + eps);
+  if (lane == 0) r[row] = rr;
+  T* yr = y + static_cast<int64_t>(row) * H;
+  for (int c = lane * VE; c < H; c += 64 * VE) {
+    float f[VE], gg[VE];
+    load_vec<T>(xr + c, f);
+    load_vec<T>(g + c, gg);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) f[e] = f[e] * rr * gg[e];
+    store_vec<T>(yr + c, f);
+  }
+}
+
+// RMSNorm backward (input part): n = xin r, dn = dout g,
+// dx = resid + r (dn - n mean(dn n)).  resid may be null (treated as 0).
+template <typename T>
+__global__ void __launch_bounds__(256)
+rmsnorm_bwd_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const float* __restrict__ r,
+                   const T* __restrict__ g, const T* __restrict__ resid, T* __restrict__ dx, int rows,
+                   int H) {
+  constexpr int VE = 16 / sizeof(T);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t base = static_cast<int64_t>(row) * H;
+  const float rr = r[row];
+  float dot = 0.f;
+  for (int c = lane * VE; c < H; c += 64 * VE) {
+    float d[VE], xv[VE], gg[VE];
+    load_vec<T>(dout + base + c, d);
+    load_vec<T>(xin + base + c, xv);
+    load_vec<T>(g + c, gg);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) dot += d[e] * gg[e] * xv[e];
+  }
+  dot = wave_sum(dot);
+  const float proj = dot * rr / H;  // mean(dn * n)
+  for (int c = lane * VE; c < H; c += 64 * VE) {
+    float d[VE], xv[VE], gg[VE], o[VE];
+    load_vec<T>(dout + base + c, d);
+    load_vec<T>(xin + base + c, xv);
+    load_vec<T>(g + c, gg);
+    if (resid) load_vec<T>(resid + base + c, o);
+    else
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[e] += rr * (d[e] * gg[e] - xv[e] * rr * proj);
+    store_vec<T>(dx + base + c, o);
+  }
+}
+
+// Gain gradient, stage 1: partial[chunk][j] = sum over the chunk's rows of
+// dout[t, j] * xin[t, j] * r[t].  Thread owns VE adjacent columns.
+template <typename T>
+__global__ void __launch_bounds__(256)
+gain_partial_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const float* __restrict__ r,
+                    float* __restrict__ partial, int rows, int H, int rows_per_chunk) {
+  constexpr int VE = 16 / sizeof(T);
+  const int col = (blockIdx.x * 256 + threadIdx.x) * VE;
+  const int chunk = blockIdx.y;
+  if (col >= H) return;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  const int t0 = chunk * rows_per_chunk, t1 = min(rows, t0 + rows_per_chunk);
+  for (int t = t0; t < t1; ++t) {
+    float d[VE], xv[VE];
+    const int64_t base = static_cast<int64_t>(t) * H + col;
+    load_vec<T>(dout + base, d);
+    load_vec<T>(xin + base, xv);
+    const float rr = r[t];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] += d[e] * xv[e] * rr;
+  }
+  float* p = partial + static_cast<int64_t>(chunk) * H + col;
+#pragma unroll
+  for (int e = 0; e < VE; e += 4) *reinterpret_cast<float4*>(p + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+}
+
+// Gain gradient, stage 2: dg[j] = sum over chunks (in order) of partial.
+__global__ void __launch_bounds__(256)
+gain_reduce_kernel(const float* __restrict__ partial, float* __restrict__ dg, int nchunks, int H) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= H) return;
+  float s = 0.f;
+  for (int c = 0; c < nchunks; ++c) s += partial[static_cast<int64_t>(c) * H + j];
+  dg[j] = s;
+}
+
+// x0[t] = E[ids[t]]; an id outside [0, V) yields a NaN row.
+template <typename T>
+__global__ void __launch_bounds__(256)
+embed_fwd_kernel(const T* __restrict__ E, const int32_t* __restrict__ ids, T* __restrict__ x0, int rows,
+                 int H, int V) {
+  constexpr int VE = 16 / sizeof(T);
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= rows) return;
+  const int id = ids[t];
+  T* out = x0 + static_cast<int64_t>(t) * H;
+  if (id < 0 || id >= V) {
+    float f[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) f[e] = __builtin_nanf("");
+    for (int c = lane * VE; c < H; c += 64 * VE) store_vec<T>(out + c, f);
+    return;
+  }
+  const T* src = E + static_cast<int64_t>(id) * H;
+  for (int c = lane * VE; c < H; c += 64 * VE)
+    *reinterpret_cast<uint4*>(out + c) = *reinterpret_cast<const uint4*>(src + c);
+}
+
+__global__ void __launch_bounds__(256)
+fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v, v, v, v);
+  } else {
+    for (int64_t k = i; k < n; ++k) p[k] = v;
+  }
+}
+
+// dE[id] = sum over t with ids[t] == id of dx0[t], in increasing t.  The
+// wave of token t does the work only if t is the first occurrence of its id;
+// it then walks the later tokens with a ballot per 64 ids.
+template <typename T>
+__global__ void __launch_bounds__(256)
+embed_bwd_kernel(const T* __restrict__ dx0, const int32_t* __restrict__ ids, float* __restrict__ dE,
+                 int rows, int H, int V) {
+  constexpr int VE = 16 / sizeof(T);
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= rows) return;
+  const int id = ids[t];
+  if (id < 0 || id >= V) return;
+  // first occurrence?
+  bool earlier = false;
+  for (int base = 0; base < t && !earlier; base += 64) {
+    const int u = base + lane;
+    const bool hit = (u < t) && ids[u] == id;
+    earlier = __ballot(hit) != 0;
+  }
+  if (earlier) return;
+  float* out = dE + static_cast<int64_t>(id) * H;
+  for (int c0 = 0; c0 < H; c0 += 64 * VE) {
+    const int c = c0 + lane * VE;
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+    for (int base = t; base < rows; base += 64) {
+      const int u = base + lane;
+      unsigned long long m = __ballot(u < rows && ids[u] == id);
+      while (m) {
+        const int k = __ffsll(static_cast<long long>(m)) - 1;
+        m &= m - 1;
+        if (c < H) {
+          float f[VE];
+          load_vec<T>(dx0 + static_cast<int64_t>(base + k) * H + c, f);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[e] += f[e];
+        }
+      }
+    }
+    if (c < H)
+#pragma unroll
+      for (int e = 0; e < VE; e += 4)
+        *reinterpret_cast<float4*>(out + c + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  }
+}
+
+// Cross-entropy rows of one LCE chunk.  logits [R, V] fp32 for tokens
+// t0 .. t0+R-1.  Token t (position s = t mod S) targets ids[t + 1] unless
+// s = S - 1.  Writes dlogits = (softmax - onehot) / N (storage dtype) and the
+// per-token loss lse - logit[target] (0 when there is no target).
+template <typename T>
+__global__ void __launch_bounds__(256)
+ce_rows_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids, T* __restrict__ dlogits,
+               float* __restrict__ loss_rows, int t0, int R, int V, int S, float inv_n) {
+  __shared__ float red[8];
+  const int r = blockIdx.x;
+  const int t = t0 + r;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* lr = logits + static_cast<int64_t>(r) * V;
+  T* dr = dlogits + static_cast<int64_t>(r) * V;
+  const bool has_target = (t % S) != S - 1;
+  if (!has_target) {
+    for (int v = tid; v < V; v += 256) Elem<T>::store(dr, v, 0.f);
+    if (tid == 0) loss_rows[t] = 0.f;
+    return;
+  }
+  const int tgt = ids[t + 1];
+  // pass 1: max and sum of exp (online)
+  float m = -INFINITY, s = 0.f;
+  for (int v = tid; v < V; v += 256) {
+    const float x = lr[v];
+    if (x > m) { s = s * __expf(m - x) + 1.f; m = x; }
+    else s += __expf(x - m);
+  }
+  float mw = wave_max(m);
+  s = s * __expf(m - mw);
+  s = wave_sum(s);
+  if (lane == 0) { red[w] = mw; red[4 + w] = s; }
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) M = fmaxf(M, red[i]);
+  float Ssum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Ssum += red[4 + i] * __expf(red[i] - M);
+  const float lse = M + __logf(Ssum);
+  const bool ok = tgt >= 0 && tgt < V;
+  if (tid == 0) loss_rows[t] = ok ? (lse - lr[tgt]) : __builtin_nanf("");
+  for (int v = tid; v < V; v += 256) {
+    float p = __expf(lr[v] - lse);
+    if (v == tgt) p -= 1.f;
+    Elem<T>::store(dr, v, ok ? p * inv_n : __builtin_nanf(""));
+  }
+}
+
+// loss = (sum over t of loss_rows[t]) * inv_n, one block, fixed order.
+__global__ void __launch_bounds__(256)
+loss_reduce_kernel(const float* __restrict__ loss_rows, float* __restrict__ loss, int rows, float inv_n) {
+  __shared__ float part[256];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < rows; i += 256) s += loss_rows[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = part[0] * inv_n;
+}
+
+}  // namespace
+
+#define SF_DISPATCH(dtype, KERNEL, grid, block, stream, ...)                                          \
+  do {                                                                                                \
+    if ((dtype) == 1) hipLaunchKernelGGL(KERNEL<bf16>, grid, block, 0, stream, __VA_ARGS__);          \
+    else hipLaunchKernelGGL(KERNEL<float>, grid, block, 0, stream, __VA_ARGS__);                      \
+  } while (0)
+
+hipError_t rmsnorm_fwd(int dtype, const void* x, const void* g, void* y, float* r, int rows, int H,
+                       float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s,
+                       static_cast<const bf16*>(x), static_cast<const bf16*>(g), static_cast<bf16*>(y), r, rows, H, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s,
+                       static_cast<const float*>(x), static_cast<const float*>(g), static_cast<float*>(y), r, rows, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd(int dtype, const void* dout, const void* xin, const float* r, const void* g,
+                       const void* resid, void* dx, float* partial, int nchunks, float* dg, int rows, int H,
+                       hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int VE = dtype == 1 ? 8 : 4;
+  const int rpc = (rows + nchunks - 1) / nchunks;
+  const dim3 pg((H / VE + 255) / 256, nchunks);
+  if (dtype == 1) {
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s,
+                       static_cast<const bf16*>(dout), static_cast<const bf16*>(xin), r, static_cast<const bf16*>(g),
+                       static_cast<const bf16*>(resid), static_cast<bf16*>(dx), rows, H);
+    hipLaunchKernelGGL(gain_partial_kernel<bf16>, pg, dim3(256), 0, s, static_cast<const bf16*>(dout),
+                       static_cast<const bf16*>(xin), r, partial, rows, H, rpc);
+  } else {
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s,
+                       static_cast<const float*>(dout), static_cast<const float*>(xin), r, static_cast<const float*>(g),
+                       static_cast<const float*>(resid), static_cast<float*>(dx), rows, H);
+    hipLaunchKernelGGL(gain_partial_kernel<float>, pg, dim3(256), 0, s, static_cast<const float*>(dout),
+                       static_cast<const float*>(xin), r, partial, rows, H, rpc);
+  }
+  hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + 255) / 256), dim3(256), 0, s, partial, dg, nchunks, H);
+  return hipGetLastError();
+}
+
+hipError_t embed_fwd(int dtype, const void* E, const int32_t* ids, void* x0, int rows, int H, int V,
+                     hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_fwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const bf16*>(E),
+                       ids, static_cast<bf16*>(x0), rows, H, V);
+  else
+    hipLaunchKernelGGL(embed_fwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const float*>(E),
+                       ids, static_cast<float*>(x0), rows, H, V);
+  return hipGetLastError();
+}
+
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n / 4 + 255) / 256 + 1;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t embed_bwd(int dtype, const void* dx0, const int32_t* ids, float* dE, int rows, int H, int V,
+                     hipStream_t s) {
+  hipError_t e = fill_f32(dE, static_cast<int64_t>(V) * H, 0.f, s);
+  if (e != hipSuccess || rows <= 0) return e;
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_bwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const bf16*>(dx0),
+                       ids, dE, rows, H, V);
+  else
+    hipLaunchKernelGGL(embed_bwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const float*>(dx0),
+                       ids, dE, rows, H, V);
+  return hipGetLastError();
+}
+
+hipError_t ce_rows(int dtype, const float* logits, const int32_t* ids, void* dlogits, float* loss_rows, int t0,
+                   int R, int V, int S, float inv_n, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(R), dim3(256), 0, s, logits, ids, static_cast<bf16*>(dlogits),
+                       loss_rows, t0, R, V, S, inv_n);
+  else
+    hipLaunchKernelGGL(ce_rows_kernel<float>, dim3(R), dim3(256), 0, s, logits, ids, static_cast<float*>(dlogits),
+                       loss_rows, t0, R, V, S, inv_n);
+  return hipGetLastError();
+}
+
+hipError_t loss_reduce(const float* loss_rows, float* loss, int rows, float inv_n, hipStream_t s) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, loss_rows, loss, rows, inv_n);
+  return hipGetLastError();
+}
+
+}  // namespace sf

@@ -1,0 +1,202 @@
+"""Host-side plumbing around the C ABI: torch device/pinned buffers, flat
+parameter packing, and small helpers that drive one layer, the head or the
+sliding engine.  No arithmetic of the training step happens here.
+"""
+
+import numpy as np
+import torch
+
+from . import sf
+
+TENSORS = sf.TENSOR_NAMES
+
+
+def shape_from(w, batch=None, seq=None):
+    """sf_shape for a workload-like object (fields of seeded_inputs.Workload)."""
+    return sf.make_shape(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn, w.vocab,
+                         batch if batch is not None else w.batch, seq if seq is not None else w.seq,
+                         w.eps, w.rope_base, sf.SF_BF16 if w.dtype == "bf16" else sf.SF_F32)
+
+
+def storage_dtype(w):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def device_bytes(n, device="cuda"):
+    """Uninitialised device buffer of n bytes (torch allocations are >= 256-B aligned)."""
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+
+
+def pinned_bytes(n):
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, pin_memory=True)
+
+
+def to_storage_tensor(a, w):
+    """float32 numpy array (storage-representable values) -> torch tensor of the storage dtype (CPU)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(storage_dtype(w))
+
+
+def pack_params(layout, params, w, out=None):
+    """Place each tensor at its layout offset in a flat byte buffer (CPU uint8 tensor)."""
+    buf = out if out is not None else torch.zeros(layout.param_bytes, dtype=torch.uint8)
+    for i, name in enumerate(TENSORS):
+        t = to_storage_tensor(params[name], w).reshape(-1)
+        nb = t.numel() * t.element_size()
+        assert nb == layout.bytes[i], (name, nb, layout.bytes[i])
+        buf[layout.off[i]:layout.off[i] + nb].copy_(t.view(torch.uint8))
+    return buf
+
+
+def master_from_params(layout, params):
+    """fp32 master weights in the gradient layout (the host Adam layout)."""
+    m = np.zeros(layout.grad_bytes // 4, dtype=np.float32)
+    for i, name in enumerate(TENSORS):
+        o = layout.grad_off[i] // 4
+        a = np.asarray(params[name], dtype=np.float32).reshape(-1)
+        m[o:o + a.size] = a
+    return m
+
+
+def unpack_grads(layout, flat, shapes):
+    """fp32 flat gradient buffer (numpy, grad layout) -> dict name -> array."""
+    out = {}
+    for i, name in enumerate(TENSORS):
+        o = layout.grad_off[i] // 4
+        n = layout.grad_bytes_t[i] // 4
+        out[name] = flat[o:o + n].reshape(shapes[name])
+    return out
+
+
+def unpack_params(layout, flat_bytes, shapes, w):
+    """Storage-dtype flat parameter buffer (CPU uint8 tensor) -> dict of float32 arrays."""
+    out = {}
+    dt = storage_dtype(w)
+    es = 2 if w.dtype == "bf16" else 4
+    for i, name in enumerate(TENSORS):
+        o, nb = layout.off[i], layout.bytes[i]
+        t = flat_bytes[o:o + nb].view(dt).to(torch.float32)
+        out[name] = t.numpy().reshape(shapes[name])
+    return out
+
+
+def stream_handle(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Context:
+    """An sf_ctx plus the device workspace it borrows."""
+
+    def __init__(self, w, head_chunk_rows=2048, batch=None, seq=None):
+        self.w = w
+        self.shape = shape_from(w, batch, seq)
+        self.chunk = head_chunk_rows
+        self.layout = sf.sf_layer_layout(self.shape, head_chunk_rows)
+        n = self.layout.workspace_bytes + (self.layout.head_workspace_bytes if w.vocab else 0)
+        self.ws = device_bytes(n)
+        self.ctx = sf.sf_ctx_create(self.shape, head_chunk_rows, self.ws.data_ptr(), self.ws.numel())
+
+    def close(self):
+        if self.ctx:
+            sf.sf_ctx_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Engine:
+    """An sf_engine with every buffer it borrows: the device unit pool and
+    activation region, pinned host parameters and gradient slots, host fp32
+    master weights and Adam moments, and (with a head) the resident
+    embedding / LM-head tensors.
+
+    layers: list of per-layer parameter dicts (float32 storage values).
+    head: None or dict with E [V, H], gf [H], Wlm [V, H] (float32 storage values).
+    """
+
+    def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
+                 adam_threads=0, adam_hp=None, stream=None):
+        import ctypes
+        hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
+        self.w = w
+        self.nl = len(layers)
+        self.ctx = Context(w, chunk)
+        L = self.ctx.layout
+        self.layout = L
+        shape = self.ctx.shape
+        W = min(window, self.nl)
+        unit = (L.param_bytes + 255) // 256 * 256 + (L.grad_bytes + 255) // 256 * 256
+        self.pool = device_bytes(W * unit)
+        act = sf.sf_engine_act_bytes(shape, self.nl)
+        self.act = device_bytes(act)
+        self.h_params = [pack_params(L, p, w, pinned_bytes(L.param_bytes)) for p in layers]
+        self.h_master = [master_from_params(L, p) for p in layers]
+        self.h_m = [np.zeros_like(m) for m in self.h_master]
+        self.h_v = [np.zeros_like(m) for m in self.h_master]
+        self.h_slots = [pinned_bytes(L.grad_bytes) for _ in range(n_grad_slots)]
+        self._arrays = []
+
+        def parr(ptrs):
+            a = sf.pointer_array(ptrs)
+            self._arrays.append(a)
+            return ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+
+        flags = (sf.SF_ENGINE_ADAM if adam else 0) | (sf.SF_ENGINE_HEAD if head is not None else 0)
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        cfg = sf.SfEngineCfg()
+        cfg.n_layers, cfg.window, cfg.n_grad_slots, cfg.flags = self.nl, window, n_grad_slots, flags
+        cfg.adam_threads = adam_threads
+        cfg.lr, cfg.b1, cfg.b2, cfg.eps = hp["lr"], hp["b1"], hp["b2"], hp["eps"]
+        cfg.d_pool, cfg.pool_bytes = self.pool.data_ptr(), self.pool.numel()
+        cfg.d_act, cfg.act_bytes = self.act.data_ptr(), self.act.numel()
+        cfg.h_params = parr([t.data_ptr() for t in self.h_params])
+        cfg.h_master = parr([m.ctypes.data for m in self.h_master])
+        cfg.h_m = parr([m.ctypes.data for m in self.h_m])
+        cfg.h_v = parr([m.ctypes.data for m in self.h_v])
+        cfg.h_grad_slots = parr([t.data_ptr() for t in self.h_slots])
+        cfg.compute_stream = self.stream.cuda_stream
+        if head is not None:
+            V, H = w.vocab, w.hidden
+            dt = storage_dtype(w)
+            self.d_E = to_storage_tensor(head["E"], w).cuda()
+            self.d_gf = to_storage_tensor(head["gf"], w).cuda()
+            self.d_wlm = to_storage_tensor(head["Wlm"], w).cuda()
+            self.d_head_grads = torch.empty(2 * V * H + H, dtype=torch.float32, device="cuda")
+            self.h_head_grads = torch.empty(2 * V * H + H, dtype=torch.float32, pin_memory=True)
+            flat = np.concatenate([head["E"].reshape(-1), head["gf"].reshape(-1), head["Wlm"].reshape(-1)])
+            self.h_head_params = torch.empty(flat.size, dtype=dt, pin_memory=True)
+            self.h_head_params.copy_(to_storage_tensor(flat, w))
+            self.h_head_master = flat.astype(np.float32).copy()
+            self.h_head_m = np.zeros_like(self.h_head_master)
+            self.h_head_v = np.zeros_like(self.h_head_master)
+            cfg.d_E, cfg.d_gf, cfg.d_wlm = self.d_E.data_ptr(), self.d_gf.data_ptr(), self.d_wlm.data_ptr()
+            cfg.d_head_grads = self.d_head_grads.data_ptr()
+            cfg.h_head_params = self.h_head_params.data_ptr()
+            cfg.h_head_master = self.h_head_master.ctypes.data
+            cfg.h_head_m = self.h_head_m.ctypes.data
+            cfg.h_head_v = self.h_head_v.ctypes.data
+            cfg.h_head_grads = self.h_head_grads.data_ptr()
+        self.cfg = cfg
+        torch.cuda.synchronize()
+        self.eng = sf.sf_engine_create(self.ctx.ctx, cfg)
+
+    def step(self, d_in, d_dy=None):
+        """d_in: device int32 ids [T] (head) or storage-dtype x [T, H]; returns (loss, stats dict)."""
+        loss, st = sf.sf_slide_step(self.eng, d_in.data_ptr(), None if d_dy is None else d_dy.data_ptr())
+        return loss, st.as_dict()
+
+    def close(self):
+        if getattr(self, "eng", None):
+            sf.sf_engine_destroy(self.eng)
+            self.eng = None
+        self.ctx.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

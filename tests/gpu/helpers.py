@@ -1,0 +1,85 @@
+"""Shared plumbing of the GPU parity tests (all calls go through the C ABI)."""
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import seeded_inputs as si
+from layer_sliding_offloaded_amd import runtime as rt
+from layer_sliding_offloaded_amd import sf
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
+
+
+def oracle_shape(w):
+    return oracle.LayerShape(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn, w.batch, w.seq, w.eps,
+                             w.rope_base)
+
+
+def f64(d):
+    return {k: np.asarray(v, dtype=np.float64) for k, v in d.items()}
+
+
+class LayerRun:
+    """One decoder layer's forward and backward through sf_layer_fwd / sf_layer_bwd."""
+
+    def __init__(self, w, params, x, dy):
+        self.w = w
+        self.c = rt.Context(w)
+        L = self.c.layout
+        self.L = L
+        self.dw = rt.pack_params(L, params, w).cuda()
+        self.x = rt.to_storage_tensor(x, w).cuda()
+        self.dy = rt.to_storage_tensor(dy, w).cuda()
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        self.saved = rt.device_bytes(L.saved_bytes)
+        self.grads = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+        self.shapes = {k: v.shape for k, v in params.items()}
+
+    def fwd(self):
+        sf.sf_layer_fwd(self.c.ctx, self.dw.data_ptr(), self.x.data_ptr(), self.y.data_ptr(),
+                        self.saved.data_ptr(), rt.stream_handle())
+
+    def bwd(self):
+        sf.sf_layer_bwd(self.c.ctx, self.dw.data_ptr(), self.x.data_ptr(), self.saved.data_ptr(),
+                        self.dy.data_ptr(), self.dx.data_ptr(), self.grads.data_ptr(), rt.stream_handle())
+
+    def results(self):
+        torch.cuda.synchronize()
+        y = self.y.float().cpu().numpy()
+        dx = self.dx.float().cpu().numpy()
+        g = rt.unpack_grads(self.L, self.grads.cpu().numpy(), self.shapes)
+        return y, dx, g
+
+    def close(self):
+        self.c.close()
+
+
+def layer_errors(w, p, x, dy, y, dx, g):
+    """rel-L2 of every output against the oracle (y - x and dx - dy deltas too)."""
+    sh = oracle_shape(w)
+    yo, cache = oracle.layer_fwd(f64(p), x.astype(np.float64), sh)
+    dxo, go = oracle.layer_bwd(f64(p), cache, dy.astype(np.float64), sh)
+    errs = {"y": rel(y, yo), "y-x": rel(y - x, yo - x), "dx": rel(dx, dxo), "dx-dy": rel(dx - dy, dxo - dy)}
+    for k in go:
+        errs["d" + k] = rel(g[k], go[k])
+    return errs
+
+
+def make_layer_case(w, seed_layer=0, gains="random"):
+    p = si.layer_params(w, seed_layer, gains=gains)
+    x = si.layer_input(w)
+    dy = si.upstream_grad(w)
+    return p, x, dy

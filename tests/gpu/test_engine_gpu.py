@@ -1,0 +1,184 @@
+"""The sliding engine: one training iteration with a window of resident layers
+must equal the plain resident computation bitwise (deterministic kernels,
+Adam on this iteration's gradients), and match the oracle's stack step."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from layer_sliding_offloaded_amd import runtime as rt
+from layer_sliding_offloaded_amd import sf
+from tests.gpu.helpers import f64, oracle_shape, rel, say
+
+pytestmark = pytest.mark.gpu
+
+STACK = si.WORKLOADS["layer-h256-fp32"].with_(dtype="bf16", vocab=1000, batch=2, seq=128, n_layers=4)
+
+
+def make_stack(w, n_layers):
+    layers = [si.layer_params(w, l, gains="random") for l in range(n_layers)]
+    head = dict(E=si.embedding(w), gf=si.final_gain(w, gains="random"), Wlm=si.lm_head(w))
+    return layers, head
+
+
+def manual_step(w, layers, head, ids, chunk, t, hp, masters, moments, head_state):
+    """Resident reference: every layer's weights on the device, the same kernels
+    through sf_layer_fwd / sf_head_fwd_bwd / sf_layer_bwd / sf_embed_bwd, then
+    sf_adam_host on each tensor.  Updates masters/moments/head_state in place
+    and returns (loss, new layer params (bf16 values), new head params)."""
+    c = rt.Context(w, chunk)
+    L = c.layout
+    s = rt.stream_handle()
+    dws = [rt.pack_params(L, p, w).cuda() for p in layers]
+    dt = rt.storage_dtype(w)
+    d_E = rt.to_storage_tensor(head["E"], w).cuda()
+    d_gf = rt.to_storage_tensor(head["gf"], w).cuda()
+    d_wlm = rt.to_storage_tensor(head["Wlm"], w).cuda()
+    d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
+    xs = [torch.empty(w.tokens, w.hidden, dtype=dt, device="cuda") for _ in range(len(layers) + 1)]
+    saved = [rt.device_bytes(L.saved_bytes) for _ in layers]
+    sf.sf_embed_fwd(c.ctx, d_E.data_ptr(), d_ids.data_ptr(), xs[0].data_ptr(), s)
+    for i in range(len(layers)):
+        sf.sf_layer_fwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), xs[i + 1].data_ptr(), saved[i].data_ptr(), s)
+    V, H = w.vocab, w.hidden
+    hg = torch.empty(2 * V * H + H, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    dbuf = torch.empty_like(xs[0])
+    sf.sf_head_fwd_bwd(c.ctx, d_gf.data_ptr(), d_wlm.data_ptr(), xs[-1].data_ptr(), d_ids.data_ptr(), loss.data_ptr(),
+                       dbuf.data_ptr(), hg[V * H:].data_ptr(), hg[V * H + H:].data_ptr(), s)
+    grads = []
+    for i in reversed(range(len(layers))):
+        g = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+        sf.sf_layer_bwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), saved[i].data_ptr(), dbuf.data_ptr(),
+                        dbuf.data_ptr(), g.data_ptr(), s)
+        grads.insert(0, g)
+    sf.sf_embed_bwd(c.ctx, dbuf.data_ptr(), d_ids.data_ptr(), hg.data_ptr(), s)
+    torch.cuda.synchronize()
+    new_layers = []
+    for i in range(len(layers)):
+        g = grads[i].cpu().numpy()
+        pm, (mm, vm) = masters[i], moments[i]
+        out = np.zeros(L.param_bytes // 2, dtype=np.uint16)
+        for k in range(9):
+            o, n, po = L.grad_off[k] // 4, L.grad_bytes_t[k] // 4, L.off[k] // 2
+            sf.sf_adam_host(pm[o:].ctypes.data, mm[o:].ctypes.data, vm[o:].ctypes.data, g[o:].ctypes.data,
+                            out[po:].ctypes.data, n, t, hp["lr"], hp["b1"], hp["b2"], hp["eps"], 2)
+        new_layers.append(out)
+    hgn = hg.cpu().numpy()
+    hm, hmm, hvm = head_state
+    hout = np.zeros(hm.size, dtype=np.uint16)
+    sf.sf_adam_host(hm.ctypes.data, hmm.ctypes.data, hvm.ctypes.data, hgn.ctypes.data, hout.ctypes.data, hm.size, t,
+                    hp["lr"], hp["b1"], hp["b2"], hp["eps"], 2)
+    lv = loss.item()
+    c.close()
+    return lv, new_layers, hout, grads, hgn
+
+
+@pytest.mark.parametrize("window,slots,n_layers", [(2, 2, 4), (3, 3, 5), (2, 2, 1)])
+def test_engine_matches_resident_bitwise(window, slots, n_layers):
+    w = STACK.with_(n_layers=n_layers)
+    say("engine", window, slots, n_layers, w)
+    layers, head = make_stack(w, n_layers)
+    ids = si.token_ids(w)
+    hp = si.ADAM
+    eng = rt.Engine(w, layers, head, window=window, n_grad_slots=slots, adam=True, chunk=96, adam_hp=hp)
+    L = eng.layout
+    masters = [rt.master_from_params(L, p) for p in layers]
+    moments = [(np.zeros_like(m), np.zeros_like(m)) for m in masters]
+    flat = np.concatenate([head["E"].reshape(-1), head["gf"].reshape(-1), head["Wlm"].reshape(-1)]).astype(np.float32)
+    head_state = (flat.copy(), np.zeros_like(flat), np.zeros_like(flat))
+    d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
+    cur_layers, cur_head = layers, head
+    for t in (1, 2):
+        loss_e, st = eng.step(d_ids)
+        say("step", t, "loss", loss_e, {k: round(v, 3) for k, v in st.items()})
+        loss_m, new_layers, hout, _, _ = manual_step(w, cur_layers, cur_head, ids, 96, t, hp, masters, moments,
+                                                     head_state)
+        assert loss_e == loss_m
+        for i in range(n_layers):
+            assert np.array_equal(eng.h_master[i], masters[i]), (t, i)
+            assert np.array_equal(eng.h_params[i].numpy().view(np.uint16), new_layers[i]), (t, i)
+        assert np.array_equal(eng.h_head_master, head_state[0])
+        assert np.array_equal(eng.h_head_params.view(torch.int16).numpy().view(np.uint16), hout)
+        # next step's inputs for the manual path: the bf16 copies Adam wrote
+        shapes = {k: v.shape for k, v in layers[0].items()}
+        cur_layers = [rt.unpack_params(L, torch.from_numpy(nl.view(np.uint8)), shapes, w) for nl in new_layers]
+        hf = si.bf16_bits_to_f32(hout)
+        VH = w.vocab * w.hidden
+        cur_head = dict(E=hf[:VH].reshape(w.vocab, w.hidden), gf=hf[VH:VH + w.hidden],
+                        Wlm=hf[VH + w.hidden:].reshape(w.vocab, w.hidden))
+        assert st["overlap_pct"] >= 0.0 and st["h2d_bytes"] > 0 and st["d2h_bytes"] > 0
+    eng.close()
+
+
+def test_engine_step_matches_oracle():
+    w = STACK
+    say("engine-vs-oracle", w)
+    layers, head = make_stack(w, w.n_layers)
+    ids = si.token_ids(w)
+    hp = si.ADAM
+    eng = rt.Engine(w, layers, head, window=2, n_grad_slots=2, adam=True, chunk=128, adam_hp=hp)
+    loss, _ = eng.step(torch.from_numpy(ids.reshape(-1)).cuda())
+    sh = oracle_shape(w)
+    lo, lg, dE, dgf, dWlm = oracle.stack_step([f64(p) for p in layers], head["E"].astype(np.float64),
+                                              head["gf"].astype(np.float64), head["Wlm"].astype(np.float64), ids, sh)
+    assert abs(loss - lo) / lo <= 2e-2
+    L = eng.layout
+    errs = {}
+    for i, p in enumerate(layers):
+        w0 = rt.master_from_params(L, p).astype(np.float64)
+        st = {k: (np.zeros_like(v, dtype=np.float64), np.zeros_like(v, dtype=np.float64)) for k, v in p.items()}
+        w1 = oracle.model.adam_all(f64(p), lg[i], st, 1, hp["lr"], hp["b1"], hp["b2"], hp["eps"])
+        refd = np.zeros_like(w0)
+        for k, name in enumerate(sf.TENSOR_NAMES):
+            o, n = L.grad_off[k] // 4, L.grad_bytes_t[k] // 4
+            refd[o:o + n] = (w1[name] - f64(p)[name]).reshape(-1)
+        got = eng.h_master[i].astype(np.float64)
+        errs[f"w{i}"] = rel(got, w0 + refd)
+        errs[f"dw{i}"] = rel(got - w0, refd)  # reported: the step itself
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        if k.startswith("w"):
+            assert v <= 1e-3, (k, v)
+    eng.close()
+
+
+def test_engine_without_head_or_adam():
+    w = STACK.with_(vocab=0, n_layers=3)
+    say("engine-no-head", w)
+    layers = [si.layer_params(w, l, gains="random") for l in range(3)]
+    x = si.layer_input(w)
+    dy = si.upstream_grad(w)
+    eng = rt.Engine(w, layers, None, window=2, n_grad_slots=2, adam=False)
+    d_x = rt.to_storage_tensor(x, w).cuda()
+    d_dy = rt.to_storage_tensor(dy, w).cuda()
+    loss, st = eng.step(d_x, d_dy)
+    torch.cuda.synchronize()
+    # reference through the per-layer ABI
+    c = rt.Context(w)
+    L = c.layout
+    s = rt.stream_handle()
+    dws = [rt.pack_params(L, p, w).cuda() for p in layers]
+    xs = [d_x] + [torch.empty_like(d_x) for _ in layers]
+    saved = [rt.device_bytes(L.saved_bytes) for _ in layers]
+    for i in range(3):
+        sf.sf_layer_fwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), xs[i + 1].data_ptr(), saved[i].data_ptr(), s)
+    d = d_dy.clone()
+    g = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+    for i in reversed(range(3)):
+        sf.sf_layer_bwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), saved[i].data_ptr(), d.data_ptr(), d.data_ptr(),
+                        g.data_ptr(), s)
+    # the engine's activation region is eng.act: locate the two outputs in it
+    base = eng.act.data_ptr()
+    n = w.tokens * w.hidden * 2
+    oy = sf.sf_engine_layer_input(eng.eng, 3) - base
+    od = sf.sf_engine_dx0(eng.eng) - base
+    yL = eng.act[oy:oy + n].view(torch.bfloat16).reshape(d_x.shape)
+    dx0 = eng.act[od:od + n].view(torch.bfloat16).reshape(d_x.shape)
+    assert torch.equal(yL, xs[3])
+    assert torch.equal(dx0, d)
+    assert st["h2d_bytes"] == (2 * 3 - 2) * L.param_bytes  # the last window of layers is reused
+    c.close()
+    eng.close()

@@ -1,0 +1,84 @@
+"""Parity of the fused LinearCrossEntropy head and the embedding against the
+oracle, chunk invariance, and deterministic embedding scatter."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from layer_sliding_offloaded_amd import runtime as rt
+from layer_sliding_offloaded_amd import sf
+from tests.gpu.helpers import rel, say
+
+pytestmark = pytest.mark.gpu
+
+BASE = si.WORKLOADS["layer-h256-fp32"].with_(vocab=1000, batch=2, seq=96)
+
+
+def run_head(w, chunk, gf, Wlm, x, ids):
+    c = rt.Context(w, head_chunk_rows=chunk)
+    d_gf = rt.to_storage_tensor(gf, w).cuda()
+    d_wlm = rt.to_storage_tensor(Wlm, w).cuda()
+    d_x = rt.to_storage_tensor(x, w).cuda()
+    d_ids = torch.from_numpy(ids.reshape(-1).astype(np.int32)).cuda()
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    dx = torch.empty_like(d_x)
+    dgf = torch.empty(w.hidden, dtype=torch.float32, device="cuda")
+    dwlm = torch.empty(w.vocab, w.hidden, dtype=torch.float32, device="cuda")
+    sf.sf_head_fwd_bwd(c.ctx, d_gf.data_ptr(), d_wlm.data_ptr(), d_x.data_ptr(), d_ids.data_ptr(), loss.data_ptr(),
+                       dx.data_ptr(), dgf.data_ptr(), dwlm.data_ptr(), rt.stream_handle())
+    torch.cuda.synchronize()
+    out = (loss.item(), dx.float().cpu().numpy(), dgf.cpu().numpy(), dwlm.cpu().numpy())
+    c.close()
+    return out
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-4), ("bf16", 2e-2)])
+@pytest.mark.parametrize("chunk", [192, 64, 50])
+def test_head_parity(dtype, tol, chunk):
+    w = BASE.with_(dtype=dtype)
+    say("head", dtype, "chunk", chunk, w)
+    gf = si.final_gain(w, gains="random")
+    Wlm = si.lm_head(w)
+    x = si.layer_input(w)
+    ids = si.token_ids(w)
+    loss, dx, dgf, dwlm = run_head(w, chunk, gf, Wlm, x, ids)
+    lo, dxo, dgfo, dwo = oracle.head_fwd_bwd(gf.astype(np.float64), Wlm.astype(np.float64), x.astype(np.float64),
+                                             ids, w.eps)
+    errs = {"loss": abs(loss - lo) / abs(lo), "dx": rel(dx, dxo), "dgf": rel(dgf, dgfo), "dWlm": rel(dwlm, dwo)}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(v <= tol for v in errs.values()), errs
+
+
+def test_head_zero_weight_loss_is_ln_v():
+    w = BASE.with_(dtype="bf16", vocab=32000, seq=64)
+    say("head-zero-weight", w)
+    loss, dx, dgf, _ = run_head(w, 64, np.ones(w.hidden, np.float32), np.zeros((w.vocab, w.hidden), np.float32),
+                                si.layer_input(w), si.token_ids(w))
+    assert abs(loss - np.log(32000.0)) <= 1e-5 * np.log(32000.0)
+    assert np.all(dx == 0) and np.all(dgf == 0)
+
+
+def test_embedding_gather_and_scatter():
+    w = BASE.with_(dtype="bf16", vocab=64, batch=4, seq=96)
+    say("embedding", w)
+    c = rt.Context(w, head_chunk_rows=64)
+    E = si.embedding(w)
+    ids = si.token_ids(w)  # 384 ids over 64 rows: many repeats
+    d_E = rt.to_storage_tensor(E, w).cuda()
+    d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
+    x0 = torch.empty(w.tokens, w.hidden, dtype=torch.bfloat16, device="cuda")
+    sf.sf_embed_fwd(c.ctx, d_E.data_ptr(), d_ids.data_ptr(), x0.data_ptr(), rt.stream_handle())
+    g = si.upstream_grad(w).reshape(w.tokens, w.hidden)
+    d_g = rt.to_storage_tensor(g, w).cuda()
+    dE1 = torch.empty(w.vocab, w.hidden, dtype=torch.float32, device="cuda")
+    dE2 = torch.empty_like(dE1)
+    sf.sf_embed_bwd(c.ctx, d_g.data_ptr(), d_ids.data_ptr(), dE1.data_ptr(), rt.stream_handle())
+    sf.sf_embed_bwd(c.ctx, d_g.data_ptr(), d_ids.data_ptr(), dE2.data_ptr(), rt.stream_handle())
+    torch.cuda.synchronize()
+    assert np.array_equal(x0.float().cpu().numpy(), E[ids.reshape(-1)])
+    ref = oracle.embed_bwd(g.astype(np.float64), ids.reshape(-1), w.vocab)
+    assert rel(dE1.cpu().numpy(), ref) <= 1e-6
+    assert torch.equal(dE1, dE2)
+    c.close()
