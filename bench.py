@@ -1,0 +1,249 @@
+"""Benchmark of the layer-sliding training step on one MI355X.
+
+One "step" is one sf_slide_step over a batch of synthetic tokens: forward
+through every layer with the next layer's bf16 weights streamed in from
+pinned host memory, the fused LinearCrossEntropy head, the backward in
+reverse order with each layer's fp32 gradients streamed out, and host Adam
+on every layer (window of 2 layers resident).  The default workload is the
+4-layer stack with hidden 1024, 16 heads x 64, ffn 2816, vocab 32000,
+batch 4 x seq 512.
+
+Printed (one JSON line): tokens/s per layer fwd+bwd of the sliding step
+(value), MFMA utilisation of the resident layer kernels, copy/compute
+overlap of the sliding engine, the roofline of the dominant kernel (timed
+live with HIP events), and the fp64 oracle's CPU throughput on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
+PEAK_HBM_GBPS = 8000.0
+
+
+def layer_flops(w):
+    """Algorithmic FLOPs of one layer forward + backward: 6 T P_lin + 6 B n_h S^2 d (causal half)."""
+    T = w.tokens
+    p_lin = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim * w.hidden + w.hidden * w.n_heads * w.head_dim \
+        + 3 * w.ffn * w.hidden
+    attn = 6.0 * w.batch * w.n_heads * w.seq * w.seq * w.head_dim  # (2 fwd + 4 bwd) x 2 x S^2 d / 2
+    return 6.0 * T * p_lin + attn
+
+
+def layer_gemms(w):
+    """The 12 GEMMs of one layer's forward + backward: (name, layout, M, N, K)."""
+    T, H, F = w.tokens, w.hidden, w.ffn
+    Nq = w.n_heads * w.head_dim
+    Nqkv = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim
+    return [
+        ("qkv_fwd", 0, T, Nqkv, H), ("o_fwd", 0, T, H, Nq), ("gu_fwd", 0, T, 2 * F, H), ("down_fwd", 0, T, H, F),
+        ("down_dx", 1, T, F, H), ("down_dw", 2, H, F, T), ("gu_dx", 1, T, H, 2 * F), ("gu_dw", 2, 2 * F, H, T),
+        ("o_dx", 1, T, Nq, H), ("o_dw", 2, H, Nq, T), ("qkv_dx", 1, T, H, Nqkv), ("qkv_dw", 2, Nqkv, H, T),
+    ]
+
+
+def time_gemms(w, sf, torch, reps=20):
+    """Average duration (ms) of each layer GEMM, launched alone on the current stream."""
+    dt = sf.SF_BF16 if w.dtype == "bf16" else sf.SF_F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    s = torch.cuda.current_stream()
+    out = {}
+    for name, lay, M, N, K in layer_gemms(w):
+        a_shape = (K, M) if lay == 2 else (M, K)
+        b_shape = (N, K) if lay == 0 else (K, N)
+        A = torch.randn(a_shape, device="cuda").to(tdt)
+        B = torch.randn(b_shape, device="cuda").to(tdt)
+        C = torch.empty((M, N), device="cuda", dtype=torch.float32 if lay == 2 else tdt)
+        f32out = 1 if lay == 2 else 0
+        call = lambda: sf.sf_gemm(dt, lay, f32out, M, N, K, A.data_ptr(), a_shape[1], B.data_ptr(), b_shape[1],
+                                  C.data_ptr(), N, s.cuda_stream)
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            call()
+        e1.record(s)
+        torch.cuda.synchronize()
+        out[name] = dict(layout=lay, M=M, N=N, K=K, ms=e0.elapsed_time(e1) / reps)
+        del A, B, C
+    return out
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The fp64 oracle, as it stands, on one layer fwd+bwd of a bounded slice
+    (batch 1) of the workload, repeated until about target_s of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import seeded_inputs as si
+
+    ws = w.with_(batch=1)
+    p = {k: v.astype(np.float64) for k, v in si.layer_params(ws, 0).items()}
+    x = si.layer_input(ws).astype(np.float64)
+    dy = si.upstream_grad(ws).astype(np.float64)
+    sh = oracle.LayerShape(ws.hidden, ws.n_heads, ws.n_kv_heads, ws.head_dim, ws.ffn, ws.batch, ws.seq, ws.eps,
+                           ws.rope_base)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        y, cache = oracle.layer_fwd(p, x, sh)
+        oracle.layer_bwd(p, cache, dy, sh)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or n >= 50:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(n * ws.tokens / el, 2), "unit": "tokens/s per layer (fwd+bwd)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} x one layer fwd+bwd, fp64 numpy, batch 1 x seq {ws.seq}, hidden {ws.hidden} "
+                      f"({el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stack4-h1024-bf16")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--adam-threads", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the layer-sliding step is a "
+              "single-GPU method and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import seeded_inputs as si
+    from layer_sliding_offloaded_amd import runtime as rt
+    from layer_sliding_offloaded_amd import sf
+
+    sf.load()
+    torch.cuda.set_device(0)
+    w = si.WORKLOADS[args.workload]
+    if args.layers:
+        w = w.with_(n_layers=args.layers)
+    print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+
+    layers = [si.layer_params(w, l) for l in range(w.n_layers)]
+    head = None
+    if w.vocab:
+        head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
+    eng = rt.Engine(w, layers, head, window=w.window, n_grad_slots=2, adam=True, chunk=2048,
+                    adam_threads=args.adam_threads)
+    if head is not None:
+        d_in = torch.from_numpy(si.token_ids(w).reshape(-1)).cuda()
+        d_dy = None
+    else:
+        d_in = rt.to_storage_tensor(si.layer_input(w), w).cuda()
+        d_dy = rt.to_storage_tensor(si.upstream_grad(w), w).cuda()
+    for i in range(args.warmup):
+        loss, st = eng.step(d_in, d_dy)
+        print(f"[bench] warmup {i} loss {loss:.4f} wall {st['wall_ms']:.2f} ms", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    stats = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        loss, st = eng.step(d_in, d_dy)
+        stats.append(st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1000.0 * elapsed / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, loss {loss:.4f}", file=sys.stderr, flush=True)
+    med = {k: float(np.median([s[k] for s in stats])) for k in stats[0]}
+    eng.close()
+    del eng
+
+    # resident layer kernels: one layer fwd + bwd with weights in HBM
+    p = layers[0]
+    c = rt.Context(w, 2048)
+    L = c.layout
+    dw = rt.pack_params(L, p, w).cuda()
+    x = rt.to_storage_tensor(si.layer_input(w), w).cuda()
+    dy = rt.to_storage_tensor(si.upstream_grad(w), w).cuda()
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    saved = rt.device_bytes(L.saved_bytes)
+    g = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def layer_step():
+        sf.sf_layer_fwd(c.ctx, dw.data_ptr(), x.data_ptr(), y.data_ptr(), saved.data_ptr(), s.cuda_stream)
+        sf.sf_layer_bwd(c.ctx, dw.data_ptr(), x.data_ptr(), saved.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                        g.data_ptr(), s.cuda_stream)
+
+    for _ in range(3):
+        layer_step()
+    reps = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        layer_step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / reps
+    fl = layer_flops(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    layer_tflops = fl / (layer_ms * 1e-3) / 1e12
+    c.close()
+    del dw, x, dy, y, dx, saved, g
+
+    # dominant kernel: the layer GEMM with the longest launch, timed alone
+    gem = time_gemms(w, sf, torch)
+    dom_name = max(gem, key=lambda k: gem[k]["ms"])
+    dom = gem[dom_name]
+    dom_flops = 2.0 * dom["M"] * dom["N"] * dom["K"]
+    achieved = dom_flops / (dom["ms"] * 1e-3) / 1e12
+    print(f"[bench] layer fwd+bwd {layer_ms:.3f} ms ({layer_tflops:.1f} TFLOP/s); GEMMs: "
+          + ", ".join(f"{k} {v['ms']:.3f}ms" for k, v in gem.items()), file=sys.stderr, flush=True)
+
+    T = w.tokens
+    value = T * w.n_layers / (ms_step * 1e-3)
+    out = {
+        "metric": "train tokens/s per layer fwd+bwd (bf16) at 1 GPU; MFMA util %; copy overlap %",
+        "value": round(value, 1),
+        "unit": "tokens/s per layer (fwd+bwd)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_layers": w.n_layers, "window": w.window, "batch": w.batch,
+                   "seq": w.seq, "hidden": w.hidden, "heads": w.n_heads, "kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab, "adam": "host fp32",
+                   "parallelism": "none (1 GPU)"},
+        "mfma_util_pct": round(100.0 * layer_tflops / peak, 2),
+        "kernel_tokens_per_s_per_layer": round(T / (layer_ms * 1e-3), 1),
+        "layer_fwd_bwd_ms": round(layer_ms, 4),
+        "overlap_pct": round(med["overlap_pct"], 2),
+        "engine": {k: round(v, 4) for k, v in med.items()},
+        "gemm_ms": {k: round(v["ms"], 5) for k, v in gem.items()},
+        "roofline": {"bound": "mfma", "kernel": f"gemm {dom_name} ({['NT', 'NN', 'TN'][dom['layout']]}, "
+                                                f"M={dom['M']} N={dom['N']} K={dom['K']})",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -162,6 +162,21 @@ sf_status sf_head_fwd_bwd(sf_ctx* ctx, const void* d_gf, const void* d_wlm, cons
                           const int32_t* d_ids, float* d_loss, void* d_dx, float* d_dgf,
                           float* d_dwlm, sf_stream stream);
 
+/*
+ * One dense projection with the block's MFMA GEMM -- the primitive behind
+ * every projection above (exposed for measurement and testing):
+ *   layout 0 (NT): C[M, N] = A[M, K] B[N, K]^T   (forward  y = x W^T)
+ *   layout 1 (NN): C[M, N] = A[M, K] B[K, N]     (input gradient dX = dY W)
+ *   layout 2 (TN): C[M, N] = A[K, M]^T B[K, N]   (weight gradient dW = dY^T X)
+ * A, B: storage dtype `dtype`, row-major with leading dimensions lda, ldb
+ * (elements).  C: fp32 when out_f32 != 0, else the storage dtype, leading
+ * dimension ldc; overwritten.  The contiguous dimension of every operand
+ * (and N) must be a multiple of 8; M, N, K >= 0 otherwise arbitrary.
+ */
+sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K,
+                  const void* d_A, int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc,
+                  sf_stream stream);
+
 /* x0[t] = E[ids[t]] for t < T.  E [V, H] storage dtype, x0 [T, H]. */
 sf_status sf_embed_fwd(sf_ctx* ctx, const void* d_E, const int32_t* d_ids, void* d_x0, sf_stream stream);
 
@@ -214,7 +229,7 @@ enum {
  *       h_master[l] may equal h_params[l].
  *   h_grad_slots[k]   : n_grad_slots pinned fp32 buffers of grad_bytes,
  *       shared by every layer in turn (de/es/fr §2B shared CPU buffers).
- *   compute_stream    : the stream kernels run on (the caller's).
+ *   compute_stream    : the stream kernels run on (NULL = default stream).
  *   SF_ENGINE_HEAD: d_E [V, H], d_gf [H], d_wlm [V, H] device, storage
  *       dtype, resident; d_head_grads device fp32 [dE | dgf | dWlm] of
  *       2 V H + H floats; h_head_grads pinned fp32, same shape; with
@@ -257,8 +272,11 @@ typedef struct {
   double compute_ms;       /* union of compute-stream busy intervals          */
   double copy_ms;          /* union of H2D and D2H busy intervals             */
   double h2d_ms, d2h_ms;   /* per-direction busy time                          */
-  double overlap_pct;      /* 100 (compute + copy - span) / min(compute, copy) */
-  double span_ms;          /* first device event to last                       */
+  double overlap_pct;      /* 100 |compute n copy| / min(compute, copy): the
+                              share of the shorter activity hidden under the
+                              other (|compute n copy| = compute + copy - busy) */
+  double busy_ms;          /* union of compute and copy intervals              */
+  double span_ms;          /* first device event to last; span - busy = idle   */
   double adam_ms;          /* sum of host Adam job durations                   */
   double h2d_bytes, d2h_bytes;
   double h2d_gbps, d2h_gbps;

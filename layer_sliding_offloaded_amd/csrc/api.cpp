@@ -481,6 +481,29 @@ sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const 
   return SF_OK;
 }
 
+sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* d_A,
+                  int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc, sf_stream stream) {
+  if (dtype != SF_F32 && dtype != SF_BF16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
+  if (layout < 0 || layout > 2) return fail(SF_ERR_ARG, "bad layout %d", layout);
+  if (M < 0 || N < 0 || K < 0) return fail(SF_ERR_ARG, "negative size");
+  if (M == 0 || N == 0) return SF_OK;
+  if (sf_status st = check_ptrs({d_A, d_B, d_C})) return st;
+  // contiguous dimensions of A, B, C and N itself in multiples of 8 elements
+  const int64_t a_contig = layout == 2 ? M : K;
+  const int64_t b_contig = layout == 0 ? K : N;
+  if (a_contig % 8 || b_contig % 8 || N % 8 || lda % 8 || ldb % 8 || ldc % 8)
+    return fail(SF_ERR_UNSUPPORTED, "contiguous dimensions and leading dimensions must be multiples of 8");
+  if (lda < a_contig || ldb < b_contig || ldc < N) return fail(SF_ERR_ARG, "leading dimension too small");
+  GemmArgs g;
+  g.A = d_A; g.lda = lda;
+  g.B = d_B; g.ldb = ldb;
+  g.C = d_C; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K;
+  SF_HIP(gemm(dtype, static_cast<GemmLayout>(layout), out_f32 ? Epi::StoreF32 : Epi::Store, g,
+              static_cast<hipStream_t>(stream)));
+  return SF_OK;
+}
+
 sf_status sf_embed_fwd(sf_ctx* c, const void* d_E, const int32_t* d_ids, void* d_x0, sf_stream stream) {
   if (sf_status st = check_ctx(c)) return st;
   if (sf_status st = check_ptrs({d_E, d_ids, d_x0})) return st;

@@ -296,8 +296,13 @@ sf_status fill_stats(sf_engine* e, hipEvent_t ev0, sf_step_stats* st) {
   st->h2d_ms = union_ms(h2d);
   st->d2h_ms = union_ms(d2h);
   st->span_ms = hi > lo ? hi - lo : 0;
+  std::vector<std::pair<double, double>> all(comp);
+  all.insert(all.end(), copy.begin(), copy.end());
+  st->busy_ms = union_ms(all);
+  // time both a kernel and a copy are in flight = comp + copy - (comp U copy)
+  const double both = st->compute_ms + st->copy_ms - st->busy_ms;
   const double mn = std::min(st->compute_ms, st->copy_ms);
-  st->overlap_pct = mn > 0 ? 100.0 * (st->compute_ms + st->copy_ms - st->span_ms) / mn : 0.0;
+  st->overlap_pct = mn > 0 ? 100.0 * both / mn : 0.0;
   st->h2d_bytes = hb;
   st->d2h_bytes = db;
   st->h2d_gbps = st->h2d_ms > 0 ? hb / (st->h2d_ms * 1e6) : 0;
@@ -506,8 +511,8 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   if (c.window < 2) return fail(SF_ERR_ARG, "window must be >= 2");
   if (c.n_grad_slots < 2) return fail(SF_ERR_ARG, "n_grad_slots must be >= 2");
   if (head && d.V <= 0) return fail(SF_ERR_ARG, "SF_ENGINE_HEAD needs a context with vocab > 0");
-  if (!c.d_pool || !c.d_act || !c.h_params || !c.h_grad_slots || !c.compute_stream)
-    return fail(SF_ERR_ARG, "d_pool, d_act, h_params, h_grad_slots and compute_stream are required");
+  if (!c.d_pool || !c.d_act || !c.h_params || !c.h_grad_slots)
+    return fail(SF_ERR_ARG, "d_pool, d_act, h_params and h_grad_slots are required");
   if ((reinterpret_cast<uintptr_t>(c.d_pool) | reinterpret_cast<uintptr_t>(c.d_act)) & 255u)
     return fail(SF_ERR_ALIGN, "d_pool and d_act must be 256-byte aligned");
   const sf_layout& L = ctx->layout;

@@ -385,12 +385,14 @@ hipError_t dispatch(GemmLayout lay, Epi epi, const GemmArgs& g, hipStream_t s) {
     case GemmLayout::NN:
       switch (epi) {
         case Epi::Store: return dispatch_tiles<T, GemmLayout::NN, Epi::Store>(g, s);
+        case Epi::StoreF32: return dispatch_tiles<T, GemmLayout::NN, Epi::StoreF32>(g, s);
         case Epi::SwigluBwd: return dispatch_tiles<T, GemmLayout::NN, Epi::SwigluBwd>(g, s);
         default: break;
       }
       break;
     case GemmLayout::TN:
       switch (epi) {
+        case Epi::Store: return dispatch_tiles<T, GemmLayout::TN, Epi::Store>(g, s);
         case Epi::StoreF32: return dispatch_tiles<T, GemmLayout::TN, Epi::StoreF32>(g, s);
         case Epi::AccF32: return dispatch_tiles<T, GemmLayout::TN, Epi::AccF32>(g, s);
         default: break;

@@ -66,7 +66,7 @@ class SfEngineCfg(ctypes.Structure):
 class SfStepStats(ctypes.Structure):
     _fields_ = [("wall_ms", ctypes.c_double), ("compute_ms", ctypes.c_double), ("copy_ms", ctypes.c_double),
                 ("h2d_ms", ctypes.c_double), ("d2h_ms", ctypes.c_double), ("overlap_pct", ctypes.c_double),
-                ("span_ms", ctypes.c_double), ("adam_ms", ctypes.c_double), ("h2d_bytes", ctypes.c_double),
+                ("busy_ms", ctypes.c_double), ("span_ms", ctypes.c_double), ("adam_ms", ctypes.c_double), ("h2d_bytes", ctypes.c_double),
                 ("d2h_bytes", ctypes.c_double), ("h2d_gbps", ctypes.c_double), ("d2h_gbps", ctypes.c_double),
                 ("loss", ctypes.c_float)]
 
@@ -82,7 +82,7 @@ class SfError(RuntimeError):
 
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
-    "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_engine_act_bytes", "sf_engine_create", "sf_slide_step",
+    "sf_gemm", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_engine_act_bytes", "sf_engine_create", "sf_slide_step",
     "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_destroy", "sf_last_error",
 )
 
@@ -105,6 +105,7 @@ def load():
         "sf_layer_fwd": [P, P, P, P, P, P],
         "sf_layer_bwd": [P, P, P, P, P, P, P, P],
         "sf_head_fwd_bwd": [P, P, P, P, P, P, P, P, P, P],
+        "sf_gemm": [i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int64, P],
         "sf_embed_fwd": [P, P, P, P, P],
         "sf_embed_bwd": [P, P, P, P, P],
         "sf_adam_host": [P, P, P, P, P, _size_t, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
@@ -167,6 +168,10 @@ def sf_layer_bwd(ctx, d_w, d_x, d_saved, d_dy, d_dx, d_dw, stream):
 
 def sf_head_fwd_bwd(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream):
     _check(load().sf_head_fwd_bwd(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream))
+
+
+def sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream):
+    _check(load().sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream))
 
 
 def sf_embed_fwd(ctx, d_E, d_ids, d_x0, stream):

@@ -119,16 +119,18 @@ def layer_params(w, layer, gains="one"):
     return out
 
 
-def layer_input(w, seed=1):
-    """x ~ N(0, 1), shape [B, S, H]."""
+def layer_input(w, seed=1, scale=1.0):
+    """x ~ N(0, scale^2), shape [B, S, H] (scale 1 for every workload)."""
     rng = np.random.default_rng([seed])
-    return to_storage(rng.standard_normal((w.batch, w.seq, w.hidden), dtype=np.float32), w.dtype)
+    x = rng.standard_normal((w.batch, w.seq, w.hidden), dtype=np.float32)
+    return to_storage(x * np.float32(scale) if scale != 1.0 else x, w.dtype)
 
 
-def upstream_grad(w, seed=2):
-    """dy ~ N(0, 1), shape [B, S, H]."""
+def upstream_grad(w, seed=2, scale=1.0):
+    """dy ~ N(0, scale^2), shape [B, S, H] (scale 1 for every workload)."""
     rng = np.random.default_rng([seed])
-    return to_storage(rng.standard_normal((w.batch, w.seq, w.hidden), dtype=np.float32), w.dtype)
+    g = rng.standard_normal((w.batch, w.seq, w.hidden), dtype=np.float32)
+    return to_storage(g * np.float32(scale) if scale != 1.0 else g, w.dtype)
 
 
 def token_ids(w, seed=3):

@@ -1,0 +1,48 @@
+"""Parity of the MFMA GEMM (sf_gemm) in its three operand layouts against a
+float64 matmul of the same stored operands, at sizes spanning several tiles
+with ragged tails in every dimension."""
+
+import numpy as np
+import pytest
+import torch
+
+from layer_sliding_offloaded_amd import runtime as rt
+from layer_sliding_offloaded_amd import sf
+from tests.gpu.helpers import rel, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(128, 256, 64), (200, 688, 256), (1000, 520, 1376), (37, 8, 8), (4096, 1024, 520), (300, 3072, 2048)]
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2], ids=["NT", "NN", "TN"])
+@pytest.mark.parametrize("dtype", [sf.SF_F32, sf.SF_BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_parity(layout, dtype, M, N, K):
+    if layout == 2 and M % 8:
+        pytest.skip("TN needs M % 8 == 0 (M is A's contiguous dimension)")
+    if layout == 0 and K % 8 or layout == 1 and K % 8:
+        pytest.skip("A's contiguous dimension K must be a multiple of 8")
+    say("gemm", layout, dtype, M, N, K)
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    tdt = torch.bfloat16 if dtype == sf.SF_BF16 else torch.float32
+    a_shape = (K, M) if layout == 2 else (M, K)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A = torch.from_numpy(rng.standard_normal(a_shape, dtype=np.float32)).to(tdt)
+    B = torch.from_numpy(rng.standard_normal(b_shape, dtype=np.float32)).to(tdt)
+    a64 = A.double().numpy()
+    b64 = B.double().numpy()
+    ref = (a64.T if layout == 2 else a64) @ (b64.T if layout == 0 else b64)
+    dA, dB = A.cuda(), B.cuda()
+    out = {}
+    for out_f32 in (1, 0):
+        C = torch.full((M, N), float("nan"), dtype=torch.float32 if out_f32 else tdt, device="cuda")
+        sf.sf_gemm(dtype, layout, out_f32, M, N, K, dA.data_ptr(), a_shape[1], dB.data_ptr(), b_shape[1],
+                   C.data_ptr(), N, rt.stream_handle())
+        torch.cuda.synchronize()
+        out[out_f32] = C.double().cpu().numpy()
+    tol = 1e-5 if dtype == sf.SF_F32 else 1e-5
+    assert rel(out[1], ref) <= tol
+    # storage-dtype output: one rounding of the fp32 result
+    tol_s = 1e-6 if dtype == sf.SF_F32 else 4e-3
+    assert rel(out[0], ref) <= tol_s

@@ -109,7 +109,8 @@ def test_engine_matches_resident_bitwise(window, slots, n_layers):
         VH = w.vocab * w.hidden
         cur_head = dict(E=hf[:VH].reshape(w.vocab, w.hidden), gf=hf[VH:VH + w.hidden],
                         Wlm=hf[VH + w.hidden:].reshape(w.vocab, w.hidden))
-        assert st["overlap_pct"] >= 0.0 and st["h2d_bytes"] > 0 and st["d2h_bytes"] > 0
+        assert 0.0 <= st["overlap_pct"] <= 100.0 + 1e-6 and st["h2d_bytes"] > 0 and st["d2h_bytes"] > 0
+        assert st["busy_ms"] <= st["span_ms"] + 1e-3
     eng.close()
 
 
