@@ -198,13 +198,27 @@ sf_status sf_embed_bwd(sf_ctx* ctx, const void* d_dx0, const int32_t* d_ids, flo
 sf_status sf_adam_host(float* p, float* m, float* v, const float* g, uint16_t* p_bf16, size_t n,
                        int64_t step, float lr, float b1, float b2, float eps, int32_t n_threads);
 
+/*
+ * The same Adam step on the device for tensors that stay resident in HBM
+ * (the embedding and LM head): d_p (fp32 master), d_m, d_v updated in place
+ * from d_g, n elements; d_out receives the storage-dtype copy of the new
+ * parameters (dtype SF_BF16: round to nearest even; SF_F32: a copy; may be
+ * NULL).  Every operation is rounded exactly as in sf_adam_host, so the two
+ * agree bit for bit.  Enqueued on `stream`.
+ */
+sf_status sf_adam_device(int32_t dtype, float* d_p, float* d_m, float* d_v, const float* d_g, void* d_out, size_t n,
+                         int64_t step, float lr, float b1, float b2, float eps, sf_stream stream);
+
 /* ------------------------------------------------------------------ engine */
 
 typedef struct sf_engine sf_engine;
 
 enum {
-  SF_ENGINE_ADAM = 1,  /* run host Adam on every streamed-out gradient          */
-  SF_ENGINE_HEAD = 2   /* ids in; embedding + fused LinearCrossEntropy head    */
+  SF_ENGINE_ADAM = 1,           /* run host Adam on every streamed-out gradient  */
+  SF_ENGINE_HEAD = 2,           /* ids in; embedding + fused LinearCrossEntropy */
+  SF_ENGINE_HEAD_HOST_ADAM = 4  /* update the resident embedding / LM head on the
+                                   host too (gradients out, parameters back in)
+                                   instead of with sf_adam_device in HBM        */
 };
 
 /*
@@ -232,10 +246,14 @@ enum {
  *   compute_stream    : the stream kernels run on (NULL = default stream).
  *   SF_ENGINE_HEAD: d_E [V, H], d_gf [H], d_wlm [V, H] device, storage
  *       dtype, resident; d_head_grads device fp32 [dE | dgf | dWlm] of
- *       2 V H + H floats; h_head_grads pinned fp32, same shape; with
- *       SF_ENGINE_ADAM also h_head_params (pinned, storage dtype, [E | gf |
- *       Wlm]) and fp32 h_head_master/m/v of the same shape.  The updated
- *       head parameters are copied back to d_E/d_gf/d_wlm before the step
+ *       2 V H + H floats.  With SF_ENGINE_ADAM the resident tensors are
+ *       updated in place by default on the device from d_head_state (device
+ *       fp32 [master | m | v], each 2 V H + H floats in [E | gf | Wlm]
+ *       order).  With SF_ENGINE_HEAD_HOST_ADAM instead: h_head_grads (pinned
+ *       fp32, 2 V H + H), h_head_params (pinned, storage dtype [E | gf |
+ *       Wlm]) and fp32 host h_head_master/m/v; the LM-head gradients leave
+ *       after the head, the embedding gradient leaves as its nonzero rows,
+ *       and the updated parameters are uploaded back before the step
  *       returns.
  */
 typedef struct {
@@ -264,6 +282,7 @@ typedef struct {
   float* h_head_m;
   float* h_head_v;
   float* h_head_grads;
+  float* d_head_state;
 } sf_engine_cfg;
 
 /* Per-step measurements (host wall clock and device events). */

@@ -24,7 +24,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
-HOST_EXTRA = {"adam.cpp": ["-mavx2", "-mfma", "-fno-math-errno"]}
+# -ffp-contract=off: host Adam rounds every operation exactly like the device kernel
+HOST_EXTRA = {"adam.cpp": ["-mavx2", "-mfma", "-fno-math-errno", "-ffp-contract=off"]}
 
 
 def _run(cmd):

@@ -9,6 +9,8 @@
 // vectorise (AVX2/FMA) and is split across threads in cache-sized chunks.
 #include "adam.h"
 
+#include <sched.h>
+
 #include <algorithm>
 #include <cmath>
 #include <thread>
@@ -72,8 +74,13 @@ void adam_range(float* __restrict p, float* __restrict m, float* __restrict v, c
 }
 
 int default_threads() {
-  const unsigned n = std::thread::hardware_concurrency();
-  return n == 0 ? 1 : static_cast<int>(std::min(n, 64u));
+  // the cores this process may run on (a container's share), not the machine's
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  int n = 0;
+  if (sched_getaffinity(0, sizeof set, &set) == 0) n = CPU_COUNT(&set);
+  if (n <= 0) n = static_cast<int>(std::thread::hardware_concurrency());
+  return std::max(1, std::min(n, 64));
 }
 
 }  // namespace sf

@@ -15,6 +15,7 @@
 #include <cstring>
 #include <vector>
 
+#include "adam.h"
 #include "attention.h"
 #include "gemm.h"
 #include "internal.h"
@@ -501,6 +502,21 @@ sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int
   g.M = M; g.N = N; g.K = K;
   SF_HIP(gemm(dtype, static_cast<GemmLayout>(layout), out_f32 ? Epi::StoreF32 : Epi::Store, g,
               static_cast<hipStream_t>(stream)));
+  return SF_OK;
+}
+
+sf_status sf_adam_device(int32_t dtype, float* d_p, float* d_m, float* d_v, const float* d_g, void* d_out, size_t n,
+                         int64_t step, float lr, float b1, float b2, float eps, sf_stream stream) {
+  if (dtype != SF_F32 && dtype != SF_BF16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
+  if (n == 0) return SF_OK;
+  if (!d_p || !d_m || !d_v || !d_g) return fail(SF_ERR_ARG, "NULL array");
+  if (step < 1) return fail(SF_ERR_ARG, "step must be >= 1");
+  const AdamCoef c = adam_coef(step, lr, b1, b2, eps);
+  // without a storage copy the kernel writes the copy over the master (same value)
+  void* out = d_out ? d_out : (dtype == SF_F32 ? static_cast<void*>(d_p) : nullptr);
+  if (!out) return fail(SF_ERR_ARG, "bf16 storage copy needs d_out");
+  SF_HIP(adam_device(dtype, d_p, d_m, d_v, d_g, out, static_cast<int64_t>(n), c.b1, c.b2, c.one_b1, c.one_b2,
+                     c.inv_bc1, c.inv_bc2, c.lr, c.eps, static_cast<hipStream_t>(stream)));
   return SF_OK;
 }
 

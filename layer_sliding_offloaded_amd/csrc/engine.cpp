@@ -13,30 +13,40 @@
 //  - a thread-based design with dedicated streams and CPU threads;
 //  - gradient buffers on the host are shared by all layers.
 //
-// Realisation here.  Three HIP streams: compute (the caller's), H2D and D2H
-// (both at default priority), ordered only through events, so host-link
-// copies in both directions overlap kernels.  Unit u = layer mod window;
-// each unit has separate "parameters free" and "gradients free" events, so a
-// unit's parameter slot can be refilled for L_{i-window+1} as soon as the
-// backward of L_i is done while its gradient slot is still draining.  A
-// dispatcher thread waits for each layer's D2H copy and runs Adam on a worker
-// pool, then releases the shared host gradient slot.  Adam of layer i uses
-// this iteration's gradients and only affects the next iteration, so the
-// result equals plain synchronous training.
+// Realisation here.  HIP streams: compute (the caller's), H2D (layer
+// prefetch), D2H (gradients) and a head-upload stream, all at default
+// priority and ordered only through events, so host-link copies in both
+// directions overlap kernels.  Unit u = layer mod window; each unit has
+// separate "parameters free" and "gradients free" events, so a unit's
+// parameter slot can be refilled for L_{i-window+1} as soon as the backward
+// of L_i is done while its gradient slot is still draining.  A dispatcher
+// thread waits for each gradient copy and runs Adam on a worker pool, then
+// releases the shared host gradient slot.  Adam of layer i uses this
+// iteration's gradients and only affects the next iteration, so the result
+// equals plain synchronous training.
+//
+// Embedding and LM head (resident in HBM, updated by host Adam like a
+// layer): the LM-head and final-norm gradients leave right after the head
+// and are applied (and their parameters uploaded again) while the layer
+// backward runs; the embedding gradient leaves sparse -- only the rows of
+// ids present in the batch are nonzero -- and its dense Adam (every row:
+// moments decay) is pipelined with the upload of the updated rows.
 #include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <condition_variable>
-#include <deque>
 #include <cstring>
+#include <deque>
 #include <functional>
 #include <memory>
 #include <mutex>
+#include <string>
 #include <thread>
 #include <vector>
 
 #include "adam.h"
 #include "internal.h"
+#include "rowops.h"
 
 namespace sf {
 
@@ -58,6 +68,7 @@ class Pool {
   }
   // Run fn(0 .. n-1) on the pool and the calling thread; returns when done.
   void run(size_t n, const std::function<void(size_t)>& fn) {
+    if (n == 0) return;
     {
       std::lock_guard<std::mutex> lk(mu_);
       fn_ = &fn;
@@ -106,9 +117,12 @@ class Pool {
   bool stop_ = false;
 };
 
+enum JobKind { kLayer = 0, kHeadLm = 1, kEmbed = 2 };
+
 struct Job {
-  int layer;  // -1 = embedding + head
-  int slot;   // host gradient slot (-1 for the head)
+  int kind;
+  int layer;  // kLayer
+  int slot;   // host gradient slot (kLayer)
   hipEvent_t ready;
 };
 
@@ -131,6 +145,22 @@ bool is_pinned(const void* p) {
   return a.type == hipMemoryTypeHost;
 }
 
+// Sparse embedding-gradient block inside the first V*H floats of the head
+// gradient region: [count | pad | ids (T) | pad | rows (T x H) | scratch (2T)],
+// offsets in 4-byte words.
+struct SparseLayout {
+  size_t ids, rows, scratch, copy_words, total;
+};
+SparseLayout sparse_layout(int64_t T, int H) {
+  SparseLayout s;
+  s.ids = 64;
+  s.rows = (s.ids + T + 63) / 64 * 64;
+  s.scratch = s.rows + static_cast<size_t>(T) * H;
+  s.copy_words = s.scratch;
+  s.total = s.scratch + 2 * static_cast<size_t>(T);
+  return s;
+}
+
 }  // namespace
 
 }  // namespace sf
@@ -143,17 +173,23 @@ struct sf_engine {
   Dims d;
   sf_layout L{};
   int nl = 0, W = 0;
-  size_t unit_bytes = 0, x_bytes = 0, head_elems = 0;
-  hipStream_t s_comp = nullptr, s_h2d = nullptr, s_d2h = nullptr;
+  size_t unit_bytes = 0, x_bytes = 0;
+  hipStream_t s_comp = nullptr, s_h2d = nullptr, s_d2h = nullptr, s_head = nullptr;
   std::vector<char*> uparam, ugrad, x, saved;
   char* dbuf = nullptr;
   float* d_loss = nullptr;
-  std::vector<hipEvent_t> ev_param_ready, ev_param_free, ev_grad_ready, ev_grad_free;
+  std::vector<hipEvent_t> ev_param_ready, ev_param_free, ev_grad_free;
+  // timing events and intervals (shared with the dispatcher thread)
+  std::mutex tmu;
   std::vector<hipEvent_t> tev;
   size_t tev_used = 0;
   std::vector<Interval> iv;
   int64_t step = 0;
   bool failed = false;
+  // embedding sparse gradients
+  SparseLayout sp{};
+  std::vector<int32_t> slot_of_row;
+  std::vector<float> zero_row;
   // Adam machinery
   std::unique_ptr<Pool> pool;
   std::thread dispatcher;
@@ -164,7 +200,7 @@ struct sf_engine {
   int next_slot = 0;
   int pending = 0;
   bool stop = false;
-  bool adam_error = false;
+  std::string job_error;
   AdamCoef coef{};
   double adam_ms = 0;
 };
@@ -173,6 +209,7 @@ namespace sf {
 namespace {
 
 hipEvent_t timing_event(sf_engine* e) {
+  std::lock_guard<std::mutex> lk(e->tmu);
   if (e->tev_used >= e->tev.size()) {
     hipEvent_t ev;
     if (hipEventCreate(&ev) != hipSuccess) return nullptr;
@@ -181,8 +218,25 @@ hipEvent_t timing_event(sf_engine* e) {
   return e->tev[e->tev_used++];
 }
 
-// Adam over one segment list: (fp32 offset in master/m/v/grad, count,
-// element offset of the storage-dtype copy).
+sf_status record_interval(sf_engine* e, hipEvent_t a, hipEvent_t b, int kind, double bytes) {
+  if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
+  std::lock_guard<std::mutex> lk(e->tmu);
+  e->iv.push_back({a, b, kind, bytes});
+  return SF_OK;
+}
+
+// One H2D copy on stream s with a timed interval.
+sf_status timed_h2d(sf_engine* e, void* dst, const void* src, size_t bytes, hipStream_t s) {
+  hipEvent_t a = timing_event(e), b = timing_event(e);
+  if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
+  SF_HIP(hipEventRecord(a, s));
+  SF_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s));
+  SF_HIP(hipEventRecord(b, s));
+  return record_interval(e, a, b, 1, static_cast<double>(bytes));
+}
+
+// Adam over segments (fp32 offset in master/m/v/grad, count, element offset
+// of the storage-dtype copy), chunked across the pool.
 struct Seg {
   size_t off, n, out_off;
 };
@@ -206,6 +260,79 @@ void run_adam(sf_engine* e, float* p, float* m, float* v, const float* g, void* 
   });
 }
 
+// Embedding: dense Adam over every row (rows without a gradient this step
+// take g = 0, exactly as a dense zero gradient would), in groups of rows;
+// each group's updated storage-dtype rows are uploaded on the head stream
+// while the next group is updated.
+sf_status run_embed_adam(sf_engine* e) {
+  const sf_engine_cfg& c = e->cfg;
+  const int H = e->d.H, V = e->d.V;
+  const float* hg = c.h_head_grads;
+  const int32_t count = reinterpret_cast<const int32_t*>(hg)[0];
+  const int32_t* ids = reinterpret_cast<const int32_t*>(hg) + e->sp.ids;
+  const float* rows = hg + e->sp.rows;
+  if (count < 0 || count > e->d.T) return fail(SF_ERR_HIP, "corrupt sparse embedding gradient count %d", count);
+  for (int s = 0; s < count; ++s) {
+    const int id = ids[s];
+    if (id < 0 || id >= V) return fail(SF_ERR_HIP, "corrupt sparse embedding gradient id %d", id);
+    e->slot_of_row[id] = s;
+  }
+  const bool bf = e->d.dtype == SF_BF16;
+  const bool out_is_master = c.h_head_params == static_cast<void*>(c.h_head_master);
+  const AdamCoef cf = e->coef;
+  const int rows_per_task = std::max(1, (1 << 17) / H);
+  const int groups = 8;
+  const int rows_per_group = (V + groups - 1) / groups;
+  sf_status rc = SF_OK;
+  for (int g0 = 0; g0 < V && rc == SF_OK; g0 += rows_per_group) {
+    const int g1 = std::min(V, g0 + rows_per_group);
+    const size_t ntask = (g1 - g0 + rows_per_task - 1) / rows_per_task;
+    e->pool->run(ntask, [&](size_t ti) {
+      const int r0 = g0 + static_cast<int>(ti) * rows_per_task, r1 = std::min(g1, r0 + rows_per_task);
+      for (int r = r0; r < r1; ++r) {
+        const int s = e->slot_of_row[r];
+        const float* gr = s >= 0 ? rows + static_cast<size_t>(s) * H : e->zero_row.data();
+        const size_t o = static_cast<size_t>(r) * H;
+        if (bf) {
+          adam_range(c.h_head_master + o, c.h_head_m + o, c.h_head_v + o, gr,
+                     static_cast<uint16_t*>(c.h_head_params) + o, H, cf);
+        } else {
+          adam_range(c.h_head_master + o, c.h_head_m + o, c.h_head_v + o, gr, nullptr, H, cf);
+          if (!out_is_master) std::memcpy(static_cast<float*>(c.h_head_params) + o, c.h_head_master + o, H * 4);
+        }
+      }
+    });
+    const size_t off = static_cast<size_t>(g0) * H * e->d.e;
+    rc = timed_h2d(e, static_cast<char*>(c.d_E) + off, static_cast<const char*>(c.h_head_params) + off,
+                   static_cast<size_t>(g1 - g0) * H * e->d.e, e->s_head);
+  }
+  for (int s = 0; s < count; ++s) e->slot_of_row[ids[s]] = -1;
+  return rc;
+}
+
+sf_status run_job(sf_engine* e, const Job& j) {
+  const sf_engine_cfg& c = e->cfg;
+  const size_t VH = static_cast<size_t>(e->d.V) * e->d.H;
+  if (j.kind == kLayer) {
+    std::vector<Seg> segs;
+    for (int t = 0; t < SF_NTENSORS; ++t)
+      segs.push_back({e->L.grad_off[t] / 4, e->L.grad_bytes_t[t] / 4, e->L.off[t] / e->d.e});
+    run_adam(e, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot], c.h_params[j.layer],
+             c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), segs);
+    return SF_OK;
+  }
+  if (j.kind == kHeadLm) {
+    // final-norm gain and LM head: [VH, VH + H) and [VH + H, 2 VH + H)
+    run_adam(e, c.h_head_master, c.h_head_m, c.h_head_v, c.h_head_grads, c.h_head_params,
+             c.h_head_params == static_cast<void*>(c.h_head_master), {{VH, VH + e->d.H, VH}});
+    const char* hp = static_cast<const char*>(c.h_head_params);
+    sf_status rc = timed_h2d(e, c.d_gf, hp + VH * e->d.e, e->d.H * e->d.e, e->s_head);
+    if (rc) return rc;
+    return timed_h2d(e, c.d_wlm, hp + (VH + e->d.H) * e->d.e, VH * e->d.e, e->s_head);
+  }
+  return run_embed_adam(e);
+}
+
 void dispatcher_loop(sf_engine* e) {
   (void)hipSetDevice(e->ctx->device);
   for (;;) {
@@ -217,48 +344,32 @@ void dispatcher_loop(sf_engine* e) {
       j = e->jobs.front();
       e->jobs.pop_front();
     }
-    const bool ok = hipEventSynchronize(j.ready) == hipSuccess;
+    std::string err;
+    const hipError_t he = hipEventSynchronize(j.ready);
     const double t0 = now_ms();
-    if (ok) {
-      const sf_engine_cfg& c = e->cfg;
-      if (j.layer >= 0) {
-        std::vector<Seg> segs;
-        for (int t = 0; t < SF_NTENSORS; ++t)
-          segs.push_back({e->L.grad_off[t] / 4, e->L.grad_bytes_t[t] / 4, e->L.off[t] / e->d.e});
-        run_adam(e, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot],
-                 c.h_params[j.layer], c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), segs);
-      } else {
-        run_adam(e, c.h_head_master, c.h_head_m, c.h_head_v, c.h_head_grads, c.h_head_params,
-                 c.h_head_params == static_cast<void*>(c.h_head_master), {{0, e->head_elems, 0}});
-      }
+    if (he != hipSuccess) {
+      err = std::string("gradient copy failed: ") + hipGetErrorString(he);
+    } else {
+      const sf_status rc = run_job(e, j);
+      if (rc != SF_OK) err = sf_last_error();
     }
     const double dt = now_ms() - t0;
     std::lock_guard<std::mutex> lk(e->mu);
-    if (!ok) e->adam_error = true;
+    if (!err.empty() && e->job_error.empty()) e->job_error = err;
     e->adam_ms += dt;
-    if (j.slot >= 0) e->slot_free[j.slot] = true;
+    if (j.kind == kLayer) e->slot_free[j.slot] = true;
     --e->pending;
     e->cv.notify_all();
   }
-}
-
-sf_status record_interval(sf_engine* e, hipEvent_t a, hipEvent_t b, int kind, double bytes) {
-  if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
-  e->iv.push_back({a, b, kind, bytes});
-  return SF_OK;
 }
 
 // H2D of layer j's parameters into unit j % W.
 sf_status prefetch(sf_engine* e, int j) {
   const int u = j % e->W;
   SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_param_free[u], 0));
-  hipEvent_t a = timing_event(e), b = timing_event(e);
-  if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
-  SF_HIP(hipEventRecord(a, e->s_h2d));
-  SF_HIP(hipMemcpyAsync(e->uparam[u], e->cfg.h_params[j], e->L.param_bytes, hipMemcpyHostToDevice, e->s_h2d));
-  SF_HIP(hipEventRecord(b, e->s_h2d));
+  if (sf_status rc = timed_h2d(e, e->uparam[u], e->cfg.h_params[j], e->L.param_bytes, e->s_h2d)) return rc;
   SF_HIP(hipEventRecord(e->ev_param_ready[u], e->s_h2d));
-  return record_interval(e, a, b, 1, static_cast<double>(e->L.param_bytes));
+  return SF_OK;
 }
 
 double union_ms(std::vector<std::pair<double, double>> v) {
@@ -332,28 +443,47 @@ void drain(sf_engine* e) {
   e->cv.wait(lk, [&] { return e->pending == 0; });
 }
 
+// D2H copy on the gradient stream after `after` (an event on the compute
+// stream); returns the copy's end event in *done.
+sf_status timed_d2h(sf_engine* e, void* dst, const void* src, size_t bytes, hipEvent_t after, hipEvent_t* done) {
+  hipEvent_t b0 = timing_event(e), b1 = timing_event(e);
+  if (!b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
+  SF_HIP(hipStreamWaitEvent(e->s_d2h, after, 0));
+  SF_HIP(hipEventRecord(b0, e->s_d2h));
+  SF_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, e->s_d2h));
+  SF_HIP(hipEventRecord(b1, e->s_d2h));
+  *done = b1;
+  return record_interval(e, b0, b1, 2, static_cast<double>(bytes));
+}
+
 sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_stats* st) {
   const Dims& d = e->d;
   const sf_engine_cfg& c = e->cfg;
   const bool head = (c.flags & SF_ENGINE_HEAD) != 0;
   const bool adam = (c.flags & SF_ENGINE_ADAM) != 0;
+  const bool head_host = (c.flags & SF_ENGINE_HEAD_HOST_ADAM) != 0;
   const int nl = e->nl, W = e->W;
   sf_ctx* ctx = e->ctx;
-  e->tev_used = 0;
-  e->iv.clear();
+  {
+    std::lock_guard<std::mutex> lk(e->tmu);
+    e->tev_used = 0;
+    e->iv.clear();
+  }
   e->step += 1;
   e->coef = adam_coef(e->step, c.lr, c.b1, c.b2, c.eps);
   {
     std::lock_guard<std::mutex> lk(e->mu);
     e->adam_ms = 0;
+    e->job_error.clear();
   }
 
   hipEvent_t ev0 = timing_event(e);
   if (!ev0) return fail(SF_ERR_HIP, "event pool exhausted");
   SF_HIP(hipEventRecord(ev0, e->s_comp));
-  // The copy streams start after everything the caller queued before this call.
+  // The side streams start after everything the caller queued before this call.
   SF_HIP(hipStreamWaitEvent(e->s_h2d, ev0, 0));
   SF_HIP(hipStreamWaitEvent(e->s_d2h, ev0, 0));
+  SF_HIP(hipStreamWaitEvent(e->s_head, ev0, 0));
 
   auto comp_begin = [&](hipEvent_t* a) -> sf_status {
     *a = timing_event(e);
@@ -361,21 +491,22 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     SF_HIP(hipEventRecord(*a, e->s_comp));
     return SF_OK;
   };
-  auto comp_end = [&](hipEvent_t a) -> sf_status {
+  auto comp_end = [&](hipEvent_t a, hipEvent_t* b_out) -> sf_status {
     hipEvent_t b = timing_event(e);
     if (!b) return fail(SF_ERR_HIP, "event pool exhausted");
     SF_HIP(hipEventRecord(b, e->s_comp));
+    if (b_out) *b_out = b;
     return record_interval(e, a, b, 0, 0);
   };
   sf_status rc;
-  hipEvent_t a;
+  hipEvent_t a, b;
 
   std::vector<const void*> xin(nl + 1);
   const int32_t* ids = static_cast<const int32_t*>(d_in);
   if (head) {
     if ((rc = comp_begin(&a))) return rc;
     if ((rc = sf_embed_fwd(ctx, c.d_E, ids, e->x[0], e->s_comp))) return rc;
-    if ((rc = comp_end(a))) return rc;
+    if ((rc = comp_end(a, nullptr))) return rc;
     xin[0] = e->x[0];
   } else {
     xin[0] = d_in;
@@ -390,28 +521,42 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
     if ((rc = comp_begin(&a))) return rc;
     if ((rc = sf_layer_fwd(ctx, e->uparam[u], xin[i], e->x[i + 1], e->saved[i], e->s_comp))) return rc;
-    if ((rc = comp_end(a))) return rc;
+    if ((rc = comp_end(a, nullptr))) return rc;
     SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
   }
 
-  // ---------------- head: loss, dx_L, dg_f, dW_lm
+  // ---------------- head: loss, dx_L, dg_f, dW_lm; their Adam starts now
   const void* dy = d_dy;
   float* hg = c.d_head_grads;
   const size_t VH = static_cast<size_t>(d.V) * d.H;
+  // device Adam of a resident head tensor: master/m/v at element offset `off`
+  // of d_head_state's three regions, gradient at the same offset of hg
+  const size_t NH = 2 * VH + d.H;
+  auto dev_adam = [&](size_t off, size_t n, void* out) -> sf_status {
+    float* st = c.d_head_state;
+    const AdamCoef& k = e->coef;
+    SF_HIP(adam_device(d.dtype, st + off, st + NH + off, st + 2 * NH + off, hg + off, out, static_cast<int64_t>(n),
+                       k.b1, k.b2, k.one_b1, k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, e->s_comp));
+    return SF_OK;
+  };
   if (head) {
     if ((rc = comp_begin(&a))) return rc;
     if ((rc = sf_head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
                               e->s_comp)))
       return rc;
-    if ((rc = comp_end(a))) return rc;
-    hipEvent_t ready = timing_event(e), b0 = timing_event(e), b1 = timing_event(e);
-    if (!ready || !b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
-    SF_HIP(hipEventRecord(ready, e->s_comp));
-    SF_HIP(hipStreamWaitEvent(e->s_d2h, ready, 0));
-    SF_HIP(hipEventRecord(b0, e->s_d2h));
-    SF_HIP(hipMemcpyAsync(c.h_head_grads + VH, hg + VH, (VH + d.H) * 4, hipMemcpyDeviceToHost, e->s_d2h));
-    SF_HIP(hipEventRecord(b1, e->s_d2h));
-    if ((rc = record_interval(e, b0, b1, 2, static_cast<double>((VH + d.H) * 4)))) return rc;
+    if (adam && !head_host) {
+      if ((rc = dev_adam(VH, d.H, c.d_gf)) || (rc = dev_adam(VH + d.H, VH, c.d_wlm))) return rc;
+    }
+    if ((rc = comp_end(a, &b))) return rc;
+    if (head_host) {
+      hipEvent_t done;
+      if ((rc = timed_d2h(e, c.h_head_grads + VH, hg + VH, (VH + d.H) * 4, b, &done))) return rc;
+      if (adam) {
+        // the head-upload stream may overwrite d_gf / d_wlm only after the head read them
+        SF_HIP(hipStreamWaitEvent(e->s_head, b, 0));
+        push_job(e, Job{kHeadLm, -1, -1, done});
+      }
+    }
     dy = e->dbuf;
   }
 
@@ -426,57 +571,48 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if ((rc = sf_layer_bwd(ctx, e->uparam[u], xin[i], e->saved[i], dy, e->dbuf,
                            reinterpret_cast<float*>(e->ugrad[u]), e->s_comp)))
       return rc;
-    if ((rc = comp_end(a))) return rc;
+    if ((rc = comp_end(a, &b))) return rc;
     dy = e->dbuf;
-    SF_HIP(hipEventRecord(e->ev_grad_ready[u], e->s_comp));
     SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
     int k = 0;
     if ((rc = wait_slot(e, &k))) return rc;
-    hipEvent_t b0 = timing_event(e), b1 = timing_event(e);
-    if (!b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
-    SF_HIP(hipStreamWaitEvent(e->s_d2h, e->ev_grad_ready[u], 0));
-    SF_HIP(hipEventRecord(b0, e->s_d2h));
-    SF_HIP(hipMemcpyAsync(c.h_grad_slots[k], e->ugrad[u], e->L.grad_bytes, hipMemcpyDeviceToHost, e->s_d2h));
-    SF_HIP(hipEventRecord(b1, e->s_d2h));
+    hipEvent_t done;
+    if ((rc = timed_d2h(e, c.h_grad_slots[k], e->ugrad[u], e->L.grad_bytes, b, &done))) return rc;
     SF_HIP(hipEventRecord(e->ev_grad_free[u], e->s_d2h));
-    if ((rc = record_interval(e, b0, b1, 2, static_cast<double>(e->L.grad_bytes)))) return rc;
-    if (adam) push_job(e, Job{i, k, b1});
+    if (adam) push_job(e, Job{kLayer, i, k, done});
   }
 
-  // ---------------- embedding backward
-  if (head) {
+  // ---------------- embedding backward (+ its device Adam)
+  if (head && !head_host) {
     if ((rc = comp_begin(&a))) return rc;
     if ((rc = sf_embed_bwd(ctx, e->dbuf, ids, hg, e->s_comp))) return rc;
-    if ((rc = comp_end(a))) return rc;
-    hipEvent_t ready = timing_event(e), b0 = timing_event(e), b1 = timing_event(e);
-    if (!ready || !b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
-    SF_HIP(hipEventRecord(ready, e->s_comp));
-    SF_HIP(hipStreamWaitEvent(e->s_d2h, ready, 0));
-    SF_HIP(hipEventRecord(b0, e->s_d2h));
-    SF_HIP(hipMemcpyAsync(c.h_head_grads, hg, VH * 4, hipMemcpyDeviceToHost, e->s_d2h));
-    SF_HIP(hipEventRecord(b1, e->s_d2h));
-    if ((rc = record_interval(e, b0, b1, 2, static_cast<double>(VH * 4)))) return rc;
-    if (adam) push_job(e, Job{-1, -1, b1});
+    if (adam && (rc = dev_adam(0, VH, c.d_E))) return rc;
+    if ((rc = comp_end(a, nullptr))) return rc;
+  }
+  // ---------------- embedding backward on the host path: sparse rows of the ids present
+  if (head && head_host) {
+    int32_t* hgi = reinterpret_cast<int32_t*>(hg);
+    if ((rc = comp_begin(&a))) return rc;
+    SF_HIP(embed_bwd_sparse(d.dtype, e->dbuf, ids, hgi + e->sp.ids, hg + e->sp.rows, hgi, hgi + e->sp.scratch,
+                            static_cast<int>(d.T), d.H, d.V, e->s_comp));
+    if ((rc = comp_end(a, &b))) return rc;
+    hipEvent_t done;
+    if ((rc = timed_d2h(e, c.h_head_grads, hg, e->sp.copy_words * 4, b, &done))) return rc;
+    if (adam) {
+      // the embedding upload must not overtake this step's gather
+      SF_HIP(hipStreamWaitEvent(e->s_head, b, 0));
+      push_job(e, Job{kEmbed, -1, -1, done});
+    }
   }
 
   SF_HIP(hipStreamSynchronize(e->s_comp));
   SF_HIP(hipStreamSynchronize(e->s_h2d));
   SF_HIP(hipStreamSynchronize(e->s_d2h));
   drain(e);
-  if (e->adam_error) return fail(SF_ERR_HIP, "a gradient copy failed before Adam");
-
-  // updated embedding / head parameters back to the device for the next step
-  if (head && adam) {
-    const char* hp = static_cast<const char*>(c.h_head_params);
-    hipEvent_t b0 = timing_event(e), b1 = timing_event(e);
-    if (!b0 || !b1) return fail(SF_ERR_HIP, "event pool exhausted");
-    SF_HIP(hipEventRecord(b0, e->s_h2d));
-    SF_HIP(hipMemcpyAsync(c.d_E, hp, VH * d.e, hipMemcpyHostToDevice, e->s_h2d));
-    SF_HIP(hipMemcpyAsync(c.d_gf, hp + VH * d.e, d.H * d.e, hipMemcpyHostToDevice, e->s_h2d));
-    SF_HIP(hipMemcpyAsync(c.d_wlm, hp + (VH + d.H) * d.e, VH * d.e, hipMemcpyHostToDevice, e->s_h2d));
-    SF_HIP(hipEventRecord(b1, e->s_h2d));
-    if ((rc = record_interval(e, b0, b1, 1, static_cast<double>((2 * VH + d.H) * d.e)))) return rc;
-    SF_HIP(hipStreamSynchronize(e->s_h2d));
+  SF_HIP(hipStreamSynchronize(e->s_head));
+  {
+    std::lock_guard<std::mutex> lk(e->mu);
+    if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
   }
   if (st) {
     if ((rc = fill_stats(e, ev0, st))) return rc;
@@ -536,10 +672,19 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   for (int k = 0; k < c.n_grad_slots; ++k)
     if (!c.h_grad_slots[k] || !is_pinned(c.h_grad_slots[k]))
       return fail(SF_ERR_NOT_PINNED, "h_grad_slots[%d] is not pinned host memory", k);
+  const SparseLayout sp = sparse_layout(d.T, d.H);
+  const bool head_host = (c.flags & SF_ENGINE_HEAD_HOST_ADAM) != 0;
   if (head) {
-    if (!c.d_E || !c.d_gf || !c.d_wlm || !c.d_head_grads || !c.h_head_grads)
-      return fail(SF_ERR_ARG, "SF_ENGINE_HEAD needs d_E, d_gf, d_wlm, d_head_grads, h_head_grads");
+    if (!c.d_E || !c.d_gf || !c.d_wlm || !c.d_head_grads)
+      return fail(SF_ERR_ARG, "SF_ENGINE_HEAD needs d_E, d_gf, d_wlm and d_head_grads");
+    if (adam && !head_host && !c.d_head_state)
+      return fail(SF_ERR_ARG, "SF_ENGINE_HEAD with SF_ENGINE_ADAM needs d_head_state (device Adam of the head)");
+  }
+  if (head && head_host) {
+    if (!c.h_head_grads) return fail(SF_ERR_ARG, "SF_ENGINE_HEAD_HOST_ADAM needs h_head_grads");
     if (!is_pinned(c.h_head_grads)) return fail(SF_ERR_NOT_PINNED, "h_head_grads is not pinned");
+    if (sp.total > static_cast<size_t>(d.V) * d.H)
+      return fail(SF_ERR_UNSUPPORTED, "batch*seq too large for the sparse embedding gradient block");
     if (adam) {
       if (!c.h_head_params || !c.h_head_master || !c.h_head_m || !c.h_head_v)
         return fail(SF_ERR_ARG, "SF_ENGINE_HEAD with ADAM needs h_head_params/master/m/v");
@@ -556,14 +701,19 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   e->W = W;
   e->unit_bytes = unit;
   e->x_bytes = align256(static_cast<size_t>(d.T) * d.H * d.e);
-  e->head_elems = head ? 2 * static_cast<size_t>(d.V) * d.H + d.H : 0;
+  e->sp = sp;
+  if (head) {
+    e->slot_of_row.assign(d.V, -1);
+    e->zero_row.assign(d.H, 0.0f);
+  }
   e->s_comp = static_cast<hipStream_t>(c.compute_stream);
   auto cleanup = [&](sf_status st) {
     sf_engine_destroy(e);
     return st;
   };
   if (hipStreamCreateWithFlags(&e->s_h2d, hipStreamNonBlocking) != hipSuccess ||
-      hipStreamCreateWithFlags(&e->s_d2h, hipStreamNonBlocking) != hipSuccess)
+      hipStreamCreateWithFlags(&e->s_d2h, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&e->s_head, hipStreamNonBlocking) != hipSuccess)
     return cleanup(fail(SF_ERR_HIP, "stream creation failed"));
   char* pool = static_cast<char*>(c.d_pool);
   for (int u = 0; u < W; ++u) {
@@ -586,9 +736,9 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
     }
     return true;
   };
-  if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_ready) || !mk(e->ev_grad_free))
+  if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_free))
     return cleanup(fail(SF_ERR_HIP, "event creation failed"));
-  for (int i = 0; i < 8 * e->nl + 32; ++i) {
+  for (int i = 0; i < 8 * e->nl + 64; ++i) {
     hipEvent_t ev;
     if (hipEventCreate(&ev) != hipSuccess) return cleanup(fail(SF_ERR_HIP, "event creation failed"));
     e->tev.push_back(ev);
@@ -616,6 +766,7 @@ sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float*
     (void)hipStreamSynchronize(e->s_h2d);
     (void)hipStreamSynchronize(e->s_d2h);
     drain(e);
+    (void)hipStreamSynchronize(e->s_head);
     e->failed = true;
     return fail(rc, "%s", msg.c_str());
   }
@@ -657,12 +808,12 @@ sf_status sf_engine_destroy(sf_engine* e) {
     e->dispatcher.join();
   }
   e->pool.reset();
-  if (e->s_h2d) (void)hipStreamSynchronize(e->s_h2d);
-  if (e->s_d2h) (void)hipStreamSynchronize(e->s_d2h);
-  for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_ready, &e->ev_grad_free, &e->tev})
+  for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
+    if (s) (void)hipStreamSynchronize(s);
+  for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_free, &e->tev})
     for (hipEvent_t ev : *v) (void)hipEventDestroy(ev);
-  if (e->s_h2d) (void)hipStreamDestroy(e->s_h2d);
-  if (e->s_d2h) (void)hipStreamDestroy(e->s_d2h);
+  for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
+    if (s) (void)hipStreamDestroy(s);
   delete e;
   return SF_OK;
 }

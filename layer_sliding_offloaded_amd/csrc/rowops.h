@@ -22,6 +22,19 @@ hipError_t embed_bwd(int dtype, const void* dx0, const int32_t* ids, float* dE, 
                      hipStream_t s);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
+// Device Adam over n fp32 elements with precomputed coefficients
+// (o = 1 - b, ib = 1 / bias correction); out receives the storage-dtype copy.
+hipError_t adam_device(int dtype, float* p, float* m, float* v, const float* g, void* out, int64_t n, float b1,
+                       float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s);
+
+// Sparse embedding gradient: for the n distinct valid ids (n -> *count, in
+// order of first occurrence), out_ids[s] is the id and out_rows[s] ([H] fp32)
+// the sum of dx0 over its tokens in increasing t -- the nonzero rows of
+// embed_bwd, bit for bit.  scratch: 2 * rows int32.  out_ids and out_rows
+// need room for `rows` entries.
+hipError_t embed_bwd_sparse(int dtype, const void* dx0, const int32_t* ids, int32_t* out_ids, float* out_rows,
+                            int32_t* count, int32_t* scratch, int rows, int H, int V, hipStream_t s);
+
 hipError_t ce_rows(int dtype, const float* logits, const int32_t* ids, void* dlogits, float* loss_rows, int t0,
                    int R, int V, int S, float inv_n, hipStream_t s);
 hipError_t loss_reduce(const float* loss_rows, float* loss, int rows, float inv_n, hipStream_t s);

@@ -213,6 +213,133 @@ embed_bwd_kernel(const T* __restrict__ dx0, const int32_t* __restrict__ ids, flo
   }
 }
 
+// Sparse embedding gradient, stage 1: first[t] = 1 if token t is the first
+// occurrence of its (valid) id.  The block stages all ids in LDS when they
+// fit (rows <= kIdsInLds), so the scan over earlier tokens reads LDS.
+constexpr int kIdsInLds = 16384;
+
+__global__ void __launch_bounds__(256)
+embed_first_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ first, int rows, int V) {
+  __shared__ int32_t s_ids[kIdsInLds];
+  const bool staged = rows <= kIdsInLds;
+  const int t0 = blockIdx.x * 4;
+  if (staged) {
+    const int lim = min(rows, t0 + 4);  // only ids before the block's last token are read
+    for (int i = threadIdx.x; i < lim; i += 256) s_ids[i] = ids[i];
+    __syncthreads();
+  }
+  const int t = t0 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= rows) return;
+  const int id = ids[t];
+  bool earlier = false;
+  for (int base = 0; base < t && !earlier; base += 64) {
+    const int u = base + lane;
+    const bool hit = (u < t) && (staged ? s_ids[u] : ids[u]) == id;
+    earlier = __ballot(hit) != 0;
+  }
+  if (lane == 0) first[t] = (!earlier && id >= 0 && id < V) ? 1 : 0;
+}
+
+// Stage 2: exclusive prefix sum of first[] -> slot[], and the count.  One
+// block of 1024 threads; thread j owns a contiguous run of ceil(rows/1024).
+__global__ void __launch_bounds__(1024)
+embed_scan_kernel(const int32_t* __restrict__ first, int32_t* __restrict__ slot, int32_t* __restrict__ count,
+                  int rows) {
+  __shared__ int32_t part[1024];
+  const int per = (rows + 1023) / 1024;
+  const int b = threadIdx.x * per, e = min(rows, b + per);
+  int s = 0;
+  for (int i = b; i < e; ++i) s += first[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
+    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;  // exclusive prefix of this thread's run
+  for (int i = b; i < e; ++i) {
+    slot[i] = run;
+    run += first[i];
+  }
+  if (threadIdx.x == 1023) *count = part[1023];
+}
+
+// Stage 3: the wave of a first-occurrence token t sums dx0 over every token
+// with the same id in increasing t and writes it to out_rows[slot[t]].
+template <typename T>
+__global__ void __launch_bounds__(256)
+embed_rows_kernel(const T* __restrict__ dx0, const int32_t* __restrict__ ids, const int32_t* __restrict__ first,
+                  const int32_t* __restrict__ slot, int32_t* __restrict__ out_ids, float* __restrict__ out_rows,
+                  int rows, int H) {
+  constexpr int VE = 16 / sizeof(T);
+  __shared__ int32_t s_ids[kIdsInLds];
+  const bool staged = rows <= kIdsInLds;
+  if (staged) {
+    for (int i = threadIdx.x; i < rows; i += 256) s_ids[i] = ids[i];
+    __syncthreads();
+  }
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= rows || !first[t]) return;
+  const int id = ids[t];
+  const int s = slot[t];
+  if (lane == 0) out_ids[s] = id;
+  float* out = out_rows + static_cast<int64_t>(s) * H;
+  for (int c0 = 0; c0 < H; c0 += 64 * VE) {
+    const int c = c0 + lane * VE;
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+    for (int base = t; base < rows; base += 64) {
+      const int u = base + lane;
+      unsigned long long m = __ballot(u < rows && (staged ? s_ids[u] : ids[u]) == id);
+      while (m) {
+        const int k = __ffsll(static_cast<long long>(m)) - 1;
+        m &= m - 1;
+        if (c < H) {
+          float f[VE];
+          load_vec<T>(dx0 + static_cast<int64_t>(base + k) * H + c, f);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[e] += f[e];
+        }
+      }
+    }
+    if (c < H)
+#pragma unroll
+      for (int e = 0; e < VE; e += 4)
+        *reinterpret_cast<float4*>(out + c + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  }
+}
+
+// Adam on the device over n fp32 elements (the same arithmetic, operation
+// for operation, as the host loop): m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+// p -= lr (m / bc1) / (sqrt(v / bc2) + eps); out = storage copy of p.
+template <typename TO>
+__global__ void __launch_bounds__(256)
+adam_device_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v, const float* __restrict__ g,
+                   TO* __restrict__ out, int64_t n, float b1, float b2, float o1, float o2, float ib1, float ib2,
+                   float lr, float eps) {
+  // no fused multiply-add; sqrtf and '/' are correctly rounded (HIP's default
+  // for fp32), so every operation rounds exactly as the host loop's
+#pragma clang fp contract(off)
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
+    const float gi = g[i];
+    const float mi = b1 * m[i] + o1 * gi;
+    const float vi = b2 * v[i] + o2 * gi * gi;
+    m[i] = mi;
+    v[i] = vi;
+    const float den = sqrtf(vi * ib2) + eps;
+    const float pi = p[i] - lr * (mi * ib1) / den;
+    p[i] = pi;
+    if constexpr (sizeof(TO) == 2) out[i].u = f2bf(pi);
+    else out[i] = pi;
+  }
+}
+
 // Cross-entropy rows of one LCE chunk.  logits [R, V] fp32 for tokens
 // t0 .. t0+R-1.  Token t (position s = t mod S) targets ids[t + 1] unless
 // s = S - 1.  Writes dlogits = (softmax - onehot) / N (storage dtype) and the
@@ -350,6 +477,36 @@ hipError_t embed_bwd(int dtype, const void* dx0, const int32_t* ids, float* dE, 
   else
     hipLaunchKernelGGL(embed_bwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const float*>(dx0),
                        ids, dE, rows, H, V);
+  return hipGetLastError();
+}
+
+hipError_t embed_bwd_sparse(int dtype, const void* dx0, const int32_t* ids, int32_t* out_ids, float* out_rows,
+                            int32_t* count, int32_t* scratch, int rows, int H, int V, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  int32_t* first = scratch;
+  int32_t* slot = scratch + rows;
+  const dim3 g((rows + 3) / 4);
+  hipLaunchKernelGGL(embed_first_kernel, g, dim3(256), 0, s, ids, first, rows, V);
+  hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, first, slot, count, rows);
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_rows_kernel<bf16>, g, dim3(256), 0, s, static_cast<const bf16*>(dx0), ids, first, slot,
+                       out_ids, out_rows, rows, H);
+  else
+    hipLaunchKernelGGL(embed_rows_kernel<float>, g, dim3(256), 0, s, static_cast<const float*>(dx0), ids, first,
+                       slot, out_ids, out_rows, rows, H);
+  return hipGetLastError();
+}
+
+hipError_t adam_device(int dtype, float* p, float* m, float* v, const float* g, void* out, int64_t n, float b1,
+                       float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 32);
+  if (dtype == 1)
+    hipLaunchKernelGGL(adam_device_kernel<bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, m, v, g,
+                       static_cast<bf16*>(out), n, b1, b2, o1, o2, ib1, ib2, lr, eps);
+  else
+    hipLaunchKernelGGL(adam_device_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, m, v, g,
+                       static_cast<float*>(out), n, b1, b2, o1, o2, ib1, ib2, lr, eps);
   return hipGetLastError();
 }
 

@@ -119,7 +119,7 @@ class Engine:
     """
 
     def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
-                 adam_threads=0, adam_hp=None, stream=None):
+                 adam_threads=0, adam_hp=None, stream=None, head_adam="device"):
         import ctypes
         hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
         self.w = w
@@ -146,6 +146,9 @@ class Engine:
             return ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
 
         flags = (sf.SF_ENGINE_ADAM if adam else 0) | (sf.SF_ENGINE_HEAD if head is not None else 0)
+        if head is not None and head_adam == "host":
+            flags |= sf.SF_ENGINE_HEAD_HOST_ADAM
+        self.head_adam = head_adam
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         cfg = sf.SfEngineCfg()
         cfg.n_layers, cfg.window, cfg.n_grad_slots, cfg.flags = self.nl, window, n_grad_slots, flags
@@ -173,6 +176,11 @@ class Engine:
             self.h_head_master = flat.astype(np.float32).copy()
             self.h_head_m = np.zeros_like(self.h_head_master)
             self.h_head_v = np.zeros_like(self.h_head_master)
+            if head_adam == "device":
+                nh = self.h_head_master.size
+                self.d_head_state = torch.zeros(3 * nh, dtype=torch.float32, device="cuda")
+                self.d_head_state[:nh].copy_(torch.from_numpy(self.h_head_master))
+                cfg.d_head_state = self.d_head_state.data_ptr()
             cfg.d_E, cfg.d_gf, cfg.d_wlm = self.d_E.data_ptr(), self.d_gf.data_ptr(), self.d_wlm.data_ptr()
             cfg.d_head_grads = self.d_head_grads.data_ptr()
             cfg.h_head_params = self.h_head_params.data_ptr()

@@ -76,14 +76,27 @@ def manual_step(w, layers, head, ids, chunk, t, hp, masters, moments, head_state
     return lv, new_layers, hout, grads, hgn
 
 
-@pytest.mark.parametrize("window,slots,n_layers", [(2, 2, 4), (3, 3, 5), (2, 2, 1)])
-def test_engine_matches_resident_bitwise(window, slots, n_layers):
+def engine_head_state(eng):
+    """(fp32 master, storage bits) of the engine's embedding/head after a step."""
+    if eng.head_adam == "host":
+        return eng.h_head_master, eng.h_head_params.view(torch.int16).numpy().view(np.uint16)
+    torch.cuda.synchronize()
+    nh = eng.h_head_master.size
+    master = eng.d_head_state[:nh].cpu().numpy()
+    bits = torch.cat([eng.d_E.reshape(-1), eng.d_gf.reshape(-1), eng.d_wlm.reshape(-1)]).view(torch.int16)
+    return master, bits.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("window,slots,n_layers,head_adam", [(2, 2, 4, "device"), (2, 2, 4, "host"),
+                                                             (3, 3, 5, "device"), (2, 2, 1, "host")])
+def test_engine_matches_resident_bitwise(window, slots, n_layers, head_adam):
     w = STACK.with_(n_layers=n_layers)
-    say("engine", window, slots, n_layers, w)
+    say("engine", window, slots, n_layers, head_adam, w)
     layers, head = make_stack(w, n_layers)
     ids = si.token_ids(w)
     hp = si.ADAM
-    eng = rt.Engine(w, layers, head, window=window, n_grad_slots=slots, adam=True, chunk=96, adam_hp=hp)
+    eng = rt.Engine(w, layers, head, window=window, n_grad_slots=slots, adam=True, chunk=96, adam_hp=hp,
+                    head_adam=head_adam)
     L = eng.layout
     masters = [rt.master_from_params(L, p) for p in layers]
     moments = [(np.zeros_like(m), np.zeros_like(m)) for m in masters]
@@ -100,8 +113,9 @@ def test_engine_matches_resident_bitwise(window, slots, n_layers):
         for i in range(n_layers):
             assert np.array_equal(eng.h_master[i], masters[i]), (t, i)
             assert np.array_equal(eng.h_params[i].numpy().view(np.uint16), new_layers[i]), (t, i)
-        assert np.array_equal(eng.h_head_master, head_state[0])
-        assert np.array_equal(eng.h_head_params.view(torch.int16).numpy().view(np.uint16), hout)
+        master, bits = engine_head_state(eng)
+        assert np.array_equal(master, head_state[0])
+        assert np.array_equal(bits, hout)
         # next step's inputs for the manual path: the bf16 copies Adam wrote
         shapes = {k: v.shape for k, v in layers[0].items()}
         cur_layers = [rt.unpack_params(L, torch.from_numpy(nl.view(np.uint8)), shapes, w) for nl in new_layers]
@@ -112,6 +126,40 @@ def test_engine_matches_resident_bitwise(window, slots, n_layers):
         assert 0.0 <= st["overlap_pct"] <= 100.0 + 1e-6 and st["h2d_bytes"] > 0 and st["d2h_bytes"] > 0
         assert st["busy_ms"] <= st["span_ms"] + 1e-3
     eng.close()
+
+
+@pytest.mark.parametrize("dtype", [sf.SF_BF16, sf.SF_F32])
+def test_device_adam_matches_host_bitwise_and_oracle(dtype):
+    say("device-adam", dtype)
+    rng = np.random.default_rng(3)
+    n = 1_000_003
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hp = si.ADAM
+    hp_, hm, hv = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    dp = torch.from_numpy(p0.copy()).cuda()
+    dm = torch.zeros(n, device="cuda")
+    dv = torch.zeros(n, device="cuda")
+    out = torch.empty(n, dtype=torch.bfloat16 if dtype == sf.SF_BF16 else torch.float32, device="cuda")
+    hb = np.zeros(n, np.uint16)
+    p64, m64, v64 = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in (1, 2, 3):
+        g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-5, 0, n)).astype(np.float32)
+        dg = torch.from_numpy(g).cuda()
+        sf.sf_adam_device(dtype, dp.data_ptr(), dm.data_ptr(), dv.data_ptr(), dg.data_ptr(), out.data_ptr(), n, t,
+                          hp["lr"], hp["b1"], hp["b2"], hp["eps"], rt.stream_handle())
+        sf.sf_adam_host(hp_.ctypes.data, hm.ctypes.data, hv.ctypes.data, g.ctypes.data,
+                        hb.ctypes.data if dtype == sf.SF_BF16 else None, n, t, hp["lr"], hp["b1"], hp["b2"],
+                        hp["eps"], 4)
+        p64, m64, v64 = oracle.adam_step(p64, m64, v64, g.astype(np.float64), t, hp["lr"], hp["b1"], hp["b2"],
+                                         hp["eps"])
+        torch.cuda.synchronize()
+        assert np.array_equal(dp.cpu().numpy(), hp_)
+        assert np.array_equal(dm.cpu().numpy(), hm) and np.array_equal(dv.cpu().numpy(), hv)
+        if dtype == sf.SF_BF16:
+            assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), hb)
+        else:
+            assert np.array_equal(out.cpu().numpy(), hp_)
+        assert rel(hp_, p64) <= 1e-6
 
 
 def test_engine_step_matches_oracle():
