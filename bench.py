@@ -63,8 +63,10 @@ def time_gemms(w, sf, torch, reps=20):
         B = torch.randn(b_shape, device="cuda").to(tdt)
         C = torch.empty((M, N), device="cuda", dtype=torch.float32 if lay == 2 else tdt)
         f32out = 1 if lay == 2 else 0
+        wsb = sf.sf_gemm_workspace_bytes(M, N, K)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
         call = lambda: sf.sf_gemm(dt, lay, f32out, M, N, K, A.data_ptr(), a_shape[1], B.data_ptr(), b_shape[1],
-                                  C.data_ptr(), N, s.cuda_stream)
+                                  C.data_ptr(), N, s.cuda_stream, ws.data_ptr(), wsb)
         for _ in range(3):
             call()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

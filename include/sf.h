@@ -172,10 +172,16 @@ sf_status sf_head_fwd_bwd(sf_ctx* ctx, const void* d_gf, const void* d_wlm, cons
  * (elements).  C: fp32 when out_f32 != 0, else the storage dtype, leading
  * dimension ldc; overwritten.  The contiguous dimension of every operand
  * (and N) must be a multiple of 8; M, N, K >= 0 otherwise arbitrary.
+ * d_workspace (may be NULL) lets a GEMM with few output tiles split K into
+ * fp32 partial sums reduced in a fixed order (deterministic); it is used
+ * only when workspace_bytes >= sf_gemm_workspace_bytes(M, N, K).
  */
 sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K,
                   const void* d_A, int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc,
-                  sf_stream stream);
+                  void* d_workspace, size_t workspace_bytes, sf_stream stream);
+
+/* Workspace bytes sf_gemm can use for split-K at these sizes (0 = none). */
+size_t sf_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* x0[t] = E[ids[t]] for t < T.  E [V, H] storage dtype, x0 [T, H]. */
 sf_status sf_embed_fwd(sf_ctx* ctx, const void* d_E, const int32_t* d_ids, void* d_x0, sf_stream stream);

@@ -131,6 +131,21 @@ WorkLayout work_layout(const Dims& d, int head_chunk_rows) {
   w.dqkv = take(T * d.Nqkv * e);
   w.dxn = take(T * d.H * e);
   w.gain_partial = take(static_cast<size_t>(kGainChunks) * d.H * 4);
+  // split-K scratch: the largest any projection of the layer or head asks for
+  {
+    const int Ti = static_cast<int>(d.T);
+    size_t sk = 0;
+    auto upd = [&](int M, int N, int K) { sk = std::max(sk, gemm_splitk_bytes(M, N, K)); };
+    upd(Ti, d.Nqkv, d.H); upd(Ti, d.H, d.Nq); upd(Ti, 2 * d.F, d.H); upd(Ti, d.H, d.F);
+    upd(Ti, d.F, d.H); upd(d.H, d.F, Ti); upd(Ti, d.H, 2 * d.F); upd(2 * d.F, d.H, Ti);
+    upd(Ti, d.Nq, d.H); upd(d.H, d.Nq, Ti); upd(Ti, d.H, d.Nqkv); upd(d.Nqkv, d.H, Ti);
+    if (d.V > 0) {
+      const int R = std::min(Ti, head_chunk_rows > 0 ? head_chunk_rows : 1);
+      upd(R, d.V, d.H); upd(R, d.H, d.V); upd(d.V, d.H, R);
+    }
+    w.splitk = take(sk);
+    w.splitk_bytes = sk;
+  }
   w.total = o;
   if (d.V > 0) {
     const size_t R = static_cast<size_t>(head_chunk_rows > 0 ? head_chunk_rows : 1);
@@ -262,6 +277,8 @@ sf_status sf_layer_fwd(sf_ctx* c, const void* d_w, const void* d_x, void* d_y, v
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int T = static_cast<int>(d.T);
   char* ws = c->ws;
+  float* const skw = reinterpret_cast<float*>(c->ws + c->work.splitk);
+  const size_t skb = c->work.splitk_bytes;
 
   void* xn = at(d_saved, sv.xn);
   float* r1 = reinterpret_cast<float*>(at(d_saved, sv.r1));
@@ -285,7 +302,7 @@ sf_status sf_layer_fwd(sf_ctx* c, const void* d_w, const void* d_x, void* d_y, v
   g.rope_cos = reinterpret_cast<const float*>(ws + c->work.rope_cos);
   g.rope_sin = reinterpret_cast<const float*>(ws + c->work.rope_sin);
   g.seq = d.S; g.head_dim = d.d; g.rope_cols = d.Nq + d.Nkv;
-  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Rope, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Rope, g, s, skw, skb));
 
   AttnArgs at_;
   at_.qkv = qkv; at_.ld_qkv = d.Nqkv;
@@ -300,7 +317,7 @@ sf_status sf_layer_fwd(sf_ctx* c, const void* d_w, const void* d_x, void* d_y, v
   g.B = at(d_w, L.off[SF_WO]); g.ldb = d.Nq;
   g.C = h; g.ldc = d.H; g.R = d_x; g.ldr = d.H;
   g.M = T; g.N = d.H; g.K = d.Nq;
-  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Resid, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Resid, g, s, skw, skb));
 
   SF_HIP(rmsnorm_fwd(d.dtype, h, at(d_w, L.off[SF_G2]), hn, r2, T, d.H, d.eps, s));
 
@@ -309,14 +326,14 @@ sf_status sf_layer_fwd(sf_ctx* c, const void* d_w, const void* d_x, void* d_y, v
   g.B = at(d_w, L.off[SF_WG]); g.ldb = d.H;
   g.C = G; g.C2 = U; g.C3 = a; g.ldc = d.F;
   g.M = T; g.N = 2 * d.F; g.K = d.H; g.ffn = d.F;
-  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::SwigluFwd, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::SwigluFwd, g, s, skw, skb));
 
   g = GemmArgs();
   g.A = a; g.lda = d.F;
   g.B = at(d_w, L.off[SF_WD]); g.ldb = d.F;
   g.C = d_y; g.ldc = d.H; g.R = h; g.ldr = d.H;
   g.M = T; g.N = d.H; g.K = d.F;
-  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Resid, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::Resid, g, s, skw, skb));
   return SF_OK;
 }
 
@@ -331,6 +348,8 @@ sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int T = static_cast<int>(d.T);
   char* ws = c->ws;
+  float* const skw = reinterpret_cast<float*>(c->ws + c->work.splitk);
+  const size_t skb = c->work.splitk_bytes;
   char* dw = reinterpret_cast<char*>(d_dw);
 
   const void* xn = at(d_saved, sv.xn);
@@ -360,28 +379,28 @@ sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* 
   g.C = dGU; g.C2 = dGU + static_cast<size_t>(d.F) * d.e; g.ldc = 2 * d.F;
   g.R = G; g.R2 = U; g.ldr = d.F;
   g.M = T; g.N = d.F; g.K = d.H;
-  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::SwigluBwd, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::SwigluBwd, g, s, skw, skb));
   // dWd = dy^T a
   g = GemmArgs();
   g.A = d_dy; g.lda = d.H;
   g.B = a; g.ldb = d.F;
   g.C = dw + L.grad_off[SF_WD]; g.ldc = d.F;
   g.M = d.H; g.N = d.F; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
   // dhn = [dG | dU] [Wg; Wu]
   g = GemmArgs();
   g.A = dGU; g.lda = 2 * d.F;
   g.B = at(d_w, L.off[SF_WG]); g.ldb = d.H;
   g.C = dhn; g.ldc = d.H;
   g.M = T; g.N = d.H; g.K = 2 * d.F;
-  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s, skw, skb));
   // [dWg; dWu] = [dG | dU]^T hn
   g = GemmArgs();
   g.A = dGU; g.lda = 2 * d.F;
   g.B = hn; g.ldb = d.H;
   g.C = dw + L.grad_off[SF_WG]; g.ldc = d.H;
   g.M = 2 * d.F; g.N = d.H; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
   // RMSNorm-2 backward (+ residual dy) -> dh, dg2
   SF_HIP(rmsnorm_bwd(d.dtype, dhn, h, r2, at(d_w, L.off[SF_G2]), d_dy, dh, partial, kGainChunks,
                      reinterpret_cast<float*>(dw + L.grad_off[SF_G2]), T, d.H, s));
@@ -391,14 +410,14 @@ sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* 
   g.B = at(d_w, L.off[SF_WO]); g.ldb = d.Nq;
   g.C = dA; g.ldc = d.Nq;
   g.M = T; g.N = d.Nq; g.K = d.H;
-  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s, skw, skb));
   // dWo = dh^T A
   g = GemmArgs();
   g.A = dh; g.lda = d.H;
   g.B = O; g.ldb = d.Nq;
   g.C = dw + L.grad_off[SF_WO]; g.ldc = d.Nq;
   g.M = d.H; g.N = d.Nq; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
   // attention backward (+ inverse RoPE) -> [dq | dk | dv]
   AttnArgs at_;
   at_.qkv = qkv; at_.ld_qkv = d.Nqkv;
@@ -417,14 +436,14 @@ sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* 
   g.B = at(d_w, L.off[SF_WQ]); g.ldb = d.H;
   g.C = dxn; g.ldc = d.H;
   g.M = T; g.N = d.H; g.K = d.Nqkv;
-  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s, skw, skb));
   // dWqkv = [dq | dk | dv]^T xn
   g = GemmArgs();
   g.A = dqkv; g.lda = d.Nqkv;
   g.B = xn; g.ldb = d.H;
   g.C = dw + L.grad_off[SF_WQ]; g.ldc = d.H;
   g.M = d.Nqkv; g.N = d.H; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s));
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
   // RMSNorm-1 backward (+ residual dh) -> dx, dg1
   SF_HIP(rmsnorm_bwd(d.dtype, dxn, d_x, r1, at(d_w, L.off[SF_G1]), dh, d_dx, partial, kGainChunks,
                      reinterpret_cast<float*>(dw + L.grad_off[SF_G1]), T, d.H, s));
@@ -443,6 +462,8 @@ sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int T = static_cast<int>(d.T);
   char* ws = c->ws;
+  float* const skw = reinterpret_cast<float*>(c->ws + c->work.splitk);
+  const size_t skb = c->work.splitk_bytes;
   void* hf = ws + wl.hf;
   float* rf = reinterpret_cast<float*>(ws + wl.rf);
   char* dhf = ws + wl.dhf;
@@ -462,28 +483,34 @@ sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const 
     g.B = d_wlm; g.ldb = d.H;
     g.C = logits; g.ldc = d.V;
     g.M = rows; g.N = d.V; g.K = d.H;
-    SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::StoreF32, g, s));
+    SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::StoreF32, g, s, skw, skb));
     SF_HIP(ce_rows(d.dtype, logits, d_ids, dlogits, loss_rows, r0, rows, d.V, d.S, inv_n, s));
     g = GemmArgs();
     g.A = dlogits; g.lda = d.V;
     g.B = d_wlm; g.ldb = d.H;
     g.C = dhf + static_cast<size_t>(r0) * d.H * d.e; g.ldc = d.H;
     g.M = rows; g.N = d.H; g.K = d.V;
-    SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s));
+    SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s, skw, skb));
     g = GemmArgs();
     g.A = dlogits; g.lda = d.V;
     g.B = hfc; g.ldb = d.H;
     g.C = d_dwlm; g.ldc = d.H;
     g.M = d.V; g.N = d.H; g.K = rows;
-    SF_HIP(gemm(d.dtype, GemmLayout::TN, r0 == 0 ? Epi::StoreF32 : Epi::AccF32, g, s));
+    SF_HIP(gemm(d.dtype, GemmLayout::TN, r0 == 0 ? Epi::StoreF32 : Epi::AccF32, g, s, skw, skb));
   }
   SF_HIP(loss_reduce(loss_rows, d_loss, T, inv_n, s));
   SF_HIP(rmsnorm_bwd(d.dtype, dhf, d_x, rf, d_gf, nullptr, d_dx, partial, kGainChunks, d_dgf, T, d.H, s));
   return SF_OK;
 }
 
+size_t sf_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return gemm_splitk_bytes(M, N, K);
+}
+
 sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* d_A,
-                  int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc, sf_stream stream) {
+                  int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc, void* d_workspace,
+                  size_t workspace_bytes, sf_stream stream) {
   if (dtype != SF_F32 && dtype != SF_BF16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
   if (layout < 0 || layout > 2) return fail(SF_ERR_ARG, "bad layout %d", layout);
   if (M < 0 || N < 0 || K < 0) return fail(SF_ERR_ARG, "negative size");
@@ -500,8 +527,10 @@ sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int
   g.B = d_B; g.ldb = ldb;
   g.C = d_C; g.ldc = ldc;
   g.M = M; g.N = N; g.K = K;
+  if (d_workspace && !aligned16(d_workspace)) return fail(SF_ERR_ALIGN, "workspace is not 16-byte aligned");
   SF_HIP(gemm(dtype, static_cast<GemmLayout>(layout), out_f32 ? Epi::StoreF32 : Epi::Store, g,
-              static_cast<hipStream_t>(stream)));
+              static_cast<hipStream_t>(stream), static_cast<float*>(d_workspace),
+              d_workspace ? workspace_bytes : 0));
   return SF_OK;
 }
 

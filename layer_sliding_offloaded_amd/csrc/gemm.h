@@ -39,10 +39,20 @@ struct GemmArgs {
   const float* rope_sin = nullptr;
   int seq = 1, head_dim = 64, rope_cols = 0;
   int ffn = 0;                      // SwigluFwd: F (B rows F.. are Wu)
+  // set by gemm(): k-range per grid row and split-K partial buffer
+  int kchunk = 0;
+  float* partial = nullptr;
 };
 
 // dtype: 0 = fp32 storage, 1 = bf16 storage (inputs A, B and storage outputs).
-hipError_t gemm(int dtype, GemmLayout layout, Epi epi, const GemmArgs& g, hipStream_t stream);
+// ws/ws_bytes: optional scratch for split-K (Store / StoreF32 epilogues with
+// few output tiles): fp32 partial sums per k-range, then a fixed-order
+// reduction -- deterministic.  Without enough scratch the GEMM runs unsplit.
+hipError_t gemm(int dtype, GemmLayout layout, Epi epi, const GemmArgs& g, hipStream_t stream,
+                float* ws = nullptr, size_t ws_bytes = 0);
+
+// Scratch bytes gemm() uses for split-K at these sizes (0: no split).
+size_t gemm_splitk_bytes(int M, int N, int K);
 
 // Which tile configuration gemm() picks for (M, N); for measurement.
 int gemm_tile_config(int M, int N);

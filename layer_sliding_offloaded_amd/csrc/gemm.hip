@@ -151,6 +151,17 @@ struct Loader {
   }
 };
 
+// Split-K factor for a grid of `tiles` output tiles: grids that already
+// cover most CUs run unsplit; smaller ones aim for ~384 blocks while keeping
+// every k-range at least 512 deep.
+int splitk_factor(int tiles, int K) {
+  if (tiles >= 192) return 1;
+  int S = (384 + tiles - 1) / tiles;
+  S = std::min(S, K / 512);
+  S = std::min(S, 16);
+  return S < 2 ? 1 : S;
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 template <typename T>
@@ -222,9 +233,12 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (g.K + BKE - 1) / BKE;
-  la.load(A, g.lda, 0, g.K, tid, amap);
-  lb.load(B, g.ldb, 0, g.K, tid, bmap);
+  // split-K: blockIdx.y owns k in [kbeg, kend)
+  const int kbeg = blockIdx.y * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + BKE - 1) / BKE : 0;
+  la.load(A, g.lda, kbeg, kend, tid, amap);
+  lb.load(B, g.ldb, kbeg, kend, tid, bmap);
   la.store(smem[0], tid);
   lb.store(smem[0] + BM * ROW, tid);
   __syncthreads();
@@ -233,8 +247,8 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) {
-      la.load(A, g.lda, (kt + 1) * BKE, g.K, tid, amap);
-      lb.load(B, g.ldb, (kt + 1) * BKE, g.K, tid, bmap);
+      la.load(A, g.lda, kbeg + (kt + 1) * BKE, kend, tid, amap);
+      lb.load(B, g.ldb, kbeg + (kt + 1) * BKE, kend, tid, bmap);
     }
     const T* As = smem[buf];
     const T* Bs = smem[buf] + BM * ROW;
@@ -317,6 +331,13 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
         const f32x4 a = acc[i][j];
         float o[4] = {a[0], a[1], a[2], a[3]};
         const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
+        if constexpr (E == Epi::Store || E == Epi::StoreF32) {
+          if (g.partial) {  // split-K: fp32 partial sums of this k-range
+            float* p = g.partial + (static_cast<int64_t>(blockIdx.y) * g.M + m) * g.N + n;
+            *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+            continue;
+          }
+        }
         if constexpr (E == Epi::Store) {
           store4<T>(static_cast<T*>(g.C) + off, o);
         } else if constexpr (E == Epi::StoreF32) {
@@ -350,55 +371,88 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
   }
 }
 
+// out[m, n] = sum over s (in order) of partial[s][m][n]; 4 columns per thread.
+template <typename TO>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ partial, TO* __restrict__ out, int M, int N, int64_t ldo, int S) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t MN = static_cast<int64_t>(M) * N;
+  if (i >= MN) return;
+  float4 acc = *reinterpret_cast<const float4*>(partial + i);
+  for (int s = 1; s < S; ++s) {
+    const float4 p = *reinterpret_cast<const float4*>(partial + s * MN + i);
+    acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+  }
+  const int64_t m = i / N, n = i % N;
+  const float o[4] = {acc.x, acc.y, acc.z, acc.w};
+  if constexpr (sizeof(TO) == 2) store4<TO>(out + m * ldo + n, o);
+  else *reinterpret_cast<float4*>(out + m * ldo + n) = acc;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
-hipError_t launch(const GemmArgs& g, hipStream_t s) {
-  const int ntm = (g.M + BM - 1) / BM;
-  const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
+hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_bytes) {
+  const int ntm = (g_in.M + BM - 1) / BM;
+  const int ncols = (E == Epi::SwigluFwd) ? 2 * g_in.ffn : g_in.N;
   const int ntn = (ncols + BN - 1) / BN;
   if (ntm == 0 || ntn == 0) return hipSuccess;
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn), dim3(NT), 0, s, g, ntm, ntn);
+  GemmArgs g = g_in;
+  int S = 1;
+  if constexpr (E == Epi::Store || E == Epi::StoreF32) {
+    S = splitk_factor(ntm * ntn, g.K);
+    if (S > 1 && (!ws || static_cast<size_t>(S) * g.M * g.N * 4 > ws_bytes)) S = 1;
+  }
+  g.kchunk = S > 1 ? ((g.K + S - 1) / S + 63) / 64 * 64 : g.K;
+  if (S > 1) {
+    S = (g.K + g.kchunk - 1) / g.kchunk;
+    g.partial = ws;
+  }
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm, ntn);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t n4 = (static_cast<int64_t>(g.M) * g.N + 3) / 4;
+  const dim3 rg(static_cast<unsigned>((n4 + 255) / 256));
+  if constexpr (E == Epi::Store)
+    hipLaunchKernelGGL(splitk_reduce_kernel<T>, rg, dim3(256), 0, s, ws, static_cast<T*>(g.C), g.M, g.N, g.ldc, S);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<float>, rg, dim3(256), 0, s, ws, static_cast<float*>(g.C), g.M, g.N,
+                       g.ldc, S);
   return hipGetLastError();
 }
 
 // Tile configurations: 0 = 256x256 (8 waves of 128x64), 1 = 128x128 (4 waves of 64x64).
 template <typename T, GemmLayout LAY, Epi E>
-hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s) {
+hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t wsb) {
   if (gemm_tile_config(g.M, (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N) == 0)
-    return launch<T, 256, 256, 128, 64, LAY, E>(g, s);
-  return launch<T, 128, 128, 64, 64, LAY, E>(g, s);
+    return launch<T, 256, 256, 128, 64, LAY, E>(g, s, ws, wsb);
+  return launch<T, 128, 128, 64, 64, LAY, E>(g, s, ws, wsb);
 }
 
 template <typename T>
-hipError_t dispatch(GemmLayout lay, Epi epi, const GemmArgs& g, hipStream_t s) {
+hipError_t dispatch(GemmLayout lay, Epi epi, const GemmArgs& g, hipStream_t s, float* ws, size_t wsb) {
+#define SF_CASE(L, E) \
+  case Epi::E: return dispatch_tiles<T, GemmLayout::L, Epi::E>(g, s, ws, wsb);
   switch (lay) {
     case GemmLayout::NT:
       switch (epi) {
-        case Epi::Store: return dispatch_tiles<T, GemmLayout::NT, Epi::Store>(g, s);
-        case Epi::StoreF32: return dispatch_tiles<T, GemmLayout::NT, Epi::StoreF32>(g, s);
-        case Epi::Resid: return dispatch_tiles<T, GemmLayout::NT, Epi::Resid>(g, s);
-        case Epi::Rope: return dispatch_tiles<T, GemmLayout::NT, Epi::Rope>(g, s);
-        case Epi::SwigluFwd: return dispatch_tiles<T, GemmLayout::NT, Epi::SwigluFwd>(g, s);
+        SF_CASE(NT, Store) SF_CASE(NT, StoreF32) SF_CASE(NT, Resid) SF_CASE(NT, Rope) SF_CASE(NT, SwigluFwd)
         default: break;
       }
       break;
     case GemmLayout::NN:
       switch (epi) {
-        case Epi::Store: return dispatch_tiles<T, GemmLayout::NN, Epi::Store>(g, s);
-        case Epi::StoreF32: return dispatch_tiles<T, GemmLayout::NN, Epi::StoreF32>(g, s);
-        case Epi::SwigluBwd: return dispatch_tiles<T, GemmLayout::NN, Epi::SwigluBwd>(g, s);
+        SF_CASE(NN, Store) SF_CASE(NN, StoreF32) SF_CASE(NN, SwigluBwd)
         default: break;
       }
       break;
     case GemmLayout::TN:
       switch (epi) {
-        case Epi::Store: return dispatch_tiles<T, GemmLayout::TN, Epi::Store>(g, s);
-        case Epi::StoreF32: return dispatch_tiles<T, GemmLayout::TN, Epi::StoreF32>(g, s);
-        case Epi::AccF32: return dispatch_tiles<T, GemmLayout::TN, Epi::AccF32>(g, s);
+        SF_CASE(TN, Store) SF_CASE(TN, StoreF32) SF_CASE(TN, AccF32)
         default: break;
       }
       break;
   }
+#undef SF_CASE
   return hipErrorInvalidValue;
 }
 
@@ -409,9 +463,17 @@ int gemm_tile_config(int M, int N) {
   return big >= 256 ? 0 : 1;
 }
 
-hipError_t gemm(int dtype, GemmLayout layout, Epi epi, const GemmArgs& g, hipStream_t stream) {
-  if (dtype == 1) return dispatch<bf16>(layout, epi, g, stream);
-  return dispatch<float>(layout, epi, g, stream);
+size_t gemm_splitk_bytes(int M, int N, int K) {
+  const int bm = gemm_tile_config(M, N) == 0 ? 256 : 128;
+  const int tiles = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
+  const int S = splitk_factor(tiles, K);
+  return S > 1 ? static_cast<size_t>(S) * M * N * 4 : 0;
+}
+
+hipError_t gemm(int dtype, GemmLayout layout, Epi epi, const GemmArgs& g, hipStream_t stream, float* ws,
+                size_t ws_bytes) {
+  if (dtype == 1) return dispatch<bf16>(layout, epi, g, stream, ws, ws_bytes);
+  return dispatch<float>(layout, epi, g, stream, ws, ws_bytes);
 }
 
 }  // namespace sf

@@ -34,7 +34,7 @@ struct SavedLayout {
 };
 // Offsets of the per-context workspace.
 struct WorkLayout {
-  size_t rope_cos, rope_sin, dGU, dhn, dh, dA, dsum, dqkv, dxn, gain_partial, total;
+  size_t rope_cos, rope_sin, dGU, dhn, dh, dA, dsum, dqkv, dxn, gain_partial, splitk, splitk_bytes, total;
   // head (appended when vocab > 0)
   size_t hf, rf, dhf, logits, dlogits, loss_rows, head_total;
 };

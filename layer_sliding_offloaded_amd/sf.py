@@ -83,7 +83,7 @@ class SfError(RuntimeError):
 
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
-    "sf_gemm", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_create", "sf_slide_step",
+    "sf_gemm", "sf_gemm_workspace_bytes", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_create", "sf_slide_step",
     "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_destroy", "sf_last_error",
 )
 
@@ -106,7 +106,8 @@ def load():
         "sf_layer_fwd": [P, P, P, P, P, P],
         "sf_layer_bwd": [P, P, P, P, P, P, P, P],
         "sf_head_fwd_bwd": [P, P, P, P, P, P, P, P, P, P],
-        "sf_gemm": [i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int64, P],
+        "sf_gemm": [i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int64,
+                    P, _size_t, P],
         "sf_embed_fwd": [P, P, P, P, P],
         "sf_embed_bwd": [P, P, P, P, P],
         "sf_adam_host": [P, P, P, P, P, _size_t, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
@@ -124,6 +125,8 @@ def load():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = i32
+    lib.sf_gemm_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sf_gemm_workspace_bytes.restype = _size_t
     lib.sf_last_error.argtypes = []
     lib.sf_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -173,8 +176,12 @@ def sf_head_fwd_bwd(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, s
     _check(load().sf_head_fwd_bwd(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream))
 
 
-def sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream):
-    _check(load().sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream))
+def sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream, d_ws=None, ws_bytes=0):
+    _check(load().sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, d_ws, ws_bytes, stream))
+
+
+def sf_gemm_workspace_bytes(M, N, K):
+    return load().sf_gemm_workspace_bytes(M, N, K)
 
 
 def sf_embed_fwd(ctx, d_E, d_ids, d_x0, stream):

@@ -12,7 +12,9 @@ from tests.gpu.helpers import rel, say
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(128, 256, 64), (200, 688, 256), (1000, 520, 1376), (37, 8, 8), (4096, 1024, 520), (300, 3072, 2048)]
+# the last two have few output tiles and a long K: split-K applies when a workspace is given
+SHAPES = [(128, 256, 64), (200, 688, 256), (1000, 520, 1376), (37, 8, 8), (4096, 1024, 520), (300, 3072, 2048),
+          (512, 1024, 32000), (1024, 1024, 2600)]
 
 
 @pytest.mark.parametrize("layout", [0, 1, 2], ids=["NT", "NN", "TN"])
@@ -34,15 +36,19 @@ def test_gemm_parity(layout, dtype, M, N, K):
     b64 = B.double().numpy()
     ref = (a64.T if layout == 2 else a64) @ (b64.T if layout == 0 else b64)
     dA, dB = A.cuda(), B.cuda()
+    wsb = sf.sf_gemm_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
     out = {}
-    for out_f32 in (1, 0):
-        C = torch.full((M, N), float("nan"), dtype=torch.float32 if out_f32 else tdt, device="cuda")
-        sf.sf_gemm(dtype, layout, out_f32, M, N, K, dA.data_ptr(), a_shape[1], dB.data_ptr(), b_shape[1],
-                   C.data_ptr(), N, rt.stream_handle())
-        torch.cuda.synchronize()
-        out[out_f32] = C.double().cpu().numpy()
-    tol = 1e-5 if dtype == sf.SF_F32 else 1e-5
-    assert rel(out[1], ref) <= tol
-    # storage-dtype output: one rounding of the fp32 result
-    tol_s = 1e-6 if dtype == sf.SF_F32 else 4e-3
-    assert rel(out[0], ref) <= tol_s
+    for split in (False, True):
+        for out_f32 in (1, 0):
+            C = torch.full((M, N), float("nan"), dtype=torch.float32 if out_f32 else tdt, device="cuda")
+            sf.sf_gemm(dtype, layout, out_f32, M, N, K, dA.data_ptr(), a_shape[1], dB.data_ptr(), b_shape[1],
+                       C.data_ptr(), N, rt.stream_handle(), ws.data_ptr() if split else None, wsb if split else 0)
+            torch.cuda.synchronize()
+            out[split, out_f32] = C.double().cpu().numpy()
+        # fp32 accumulation over K terms: relative error ~ sqrt(K) 2^-24 (1e-5 at K = 32000)
+        tol = 1e-5
+        assert rel(out[split, 1], ref) <= tol, (split, rel(out[split, 1], ref))
+        # storage-dtype output: one more rounding of the fp32 result (bf16: 2^-9)
+        tol_s = 1e-5 if dtype == sf.SF_F32 else 4e-3
+        assert rel(out[split, 0], ref) <= tol_s

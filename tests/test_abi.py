@@ -27,7 +27,7 @@ def lib():
 
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "sf.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:sf_status|const char\*)\s+(sf_[a-z0-9_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:sf_status|const char\*|size_t)\s+(sf_[a-z0-9_]+)\s*\(", text, re.M)))
 
 
 def test_every_declared_symbol_is_exported(lib):
