@@ -49,6 +49,7 @@ from .layer import (  # noqa: F401
     swiglu_fwd,
     swiglu_bwd,
     layer_fwd,
+    layer_fwd_rows,
     layer_bwd,
 )
 from .head import embed_fwd, embed_bwd, head_fwd_bwd  # noqa: F401

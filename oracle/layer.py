@@ -238,6 +238,44 @@ def layer_fwd(p, x, sh):
     return y, cache
 
 
+def layer_fwd_rows(p, x, rows, sh):
+    """y of one sequence at selected positions only (for sequences too long
+    for the full oracle).  x: [S, H] one sequence; rows: increasing indices.
+
+    Same steps as ``layer_fwd``: keys and values are needed at every position
+    up to the last selected row; queries, the attention output and the MLP
+    only at the selected rows.
+    """
+    S, H = x.shape
+    nh, nkv, d = sh.n_heads, sh.n_kv_heads, sh.head_dim
+    last = int(rows[-1]) + 1
+    xs = x[:last]
+    xn, _, _ = rmsnorm_fwd(xs, p["g1"], sh.eps)
+    cos, sin = rope_angles(last, d, sh.rope_base)
+    k = (xn @ p["Wk"].T).reshape(1, last, nkv, d)
+    v = (xn @ p["Wv"].T).reshape(1, last, nkv, d)
+    kr = rope_apply(k, cos, sin)[0]                          # [last, nkv, d]
+    v = v[0]
+    xr = xn[rows]
+    q = (xr @ p["Wq"].T).reshape(len(rows), nh, d)
+    half = d // 2
+    c, s = cos[rows][:, None, :], sin[rows][:, None, :]
+    qr = np.empty_like(q)
+    qr[..., :half] = q[..., :half] * c - q[..., half:] * s
+    qr[..., half:] = q[..., half:] * c + q[..., :half] * s
+    A = np.zeros((len(rows), nh * d))
+    for i, r in enumerate(rows):
+        for h in range(nh):
+            kap = _kv_head(h, nh, nkv)
+            z = (kr[: r + 1, kap] @ qr[i, h]) / np.sqrt(d)     # keys s' <= r
+            e = np.exp(z - np.max(z))
+            A[i, h * d:(h + 1) * d] = (e / np.sum(e)) @ v[: r + 1, kap]
+    h_ = x[rows] + A @ p["Wo"].T
+    hn, _, _ = rmsnorm_fwd(h_, p["g2"], sh.eps)
+    a = swiglu_fwd(hn @ p["Wg"].T, hn @ p["Wu"].T)
+    return h_ + a @ p["Wd"].T
+
+
 def layer_bwd(p, cache, dy, sh):
     """Backward of one block given dy [B, S, H].
 

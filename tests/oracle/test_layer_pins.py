@@ -126,6 +126,17 @@ def test_layer_forward_matches_hf_llama(sh):
     assert rel_l2(y - x, yh - x) <= 1e-5
 
 
+@pytest.mark.parametrize("sh", [TINY_MHA, TINY_GQA], ids=["mha", "gqa"])
+def test_layer_fwd_rows_equals_full_forward(sh):
+    """The row-restricted forward reproduces the full forward's rows."""
+    p, x, _ = tiny_params(sh, seed=5)
+    y, _ = oracle.layer_fwd(p, x, sh)
+    rows = np.array([0, 3, 4, 7])
+    for b in range(sh.batch):
+        yr = oracle.layer_fwd_rows(p, x[b], rows, sh)
+        assert np.max(np.abs(yr - y[b, rows])) <= 1e-13
+
+
 def test_attention_matches_torch_sdpa_gqa():
     rng = np.random.default_rng(7)
     B, S, nh, nkv, d = 2, 11, 6, 2, 8
