@@ -89,7 +89,11 @@ def cpu_baseline(w, target_s=12.0):
     import oracle
     import seeded_inputs as si
 
-    ws = w.with_(batch=1)
+    # batch 1, and a sequence prefix short enough for ~1.5 TFLOP of fp64 work per repetition
+    p_lin = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim * w.hidden + w.hidden * w.n_heads * w.head_dim \
+        + 3 * w.ffn * w.hidden
+    seq = min(w.seq, max(64, int(1.5e12 / (6.0 * p_lin)) // 64 * 64))
+    ws = w.with_(batch=1, seq=seq)
     p = {k: v.astype(np.float64) for k, v in si.layer_params(ws, 0).items()}
     x = si.layer_input(ws).astype(np.float64)
     dy = si.upstream_grad(ws).astype(np.float64)
@@ -120,6 +124,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adam-threads", type=int, default=0)
+    ap.add_argument("--no-adam", action="store_true",
+                    help="stream gradients out but skip the optimizer (default for the 123B-shaped slice, whose "
+                         "fp32 Adam states would need 133 GB of host memory)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the layer-sliding step is a "
@@ -140,12 +147,19 @@ def main():
         w = w.with_(n_layers=args.layers)
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
 
-    layers = [si.layer_params(w, l) for l in range(w.n_layers)]
+    adam = not args.no_adam and w.name != "slice123b-gqa-bf16"
+    t_setup = time.perf_counter()
+    layers = []
+    for l in range(w.n_layers):
+        layers.append(si.layer_params(w, l))
+        print(f"[bench] layer {l} parameters drawn ({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr,
+              flush=True)
     head = None
     if w.vocab:
         head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
-    eng = rt.Engine(w, layers, head, window=w.window, n_grad_slots=2, adam=True, chunk=2048,
+    eng = rt.Engine(w, layers, head, window=w.window, n_grad_slots=2, adam=adam, chunk=2048,
                     adam_threads=args.adam_threads)
+    print(f"[bench] engine ready ({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr, flush=True)
     if head is not None:
         d_in = torch.from_numpy(si.token_ids(w).reshape(-1)).cuda()
         d_dy = None
@@ -229,7 +243,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n_layers": w.n_layers, "window": w.window, "batch": w.batch,
                    "seq": w.seq, "hidden": w.hidden, "heads": w.n_heads, "kv_heads": w.n_kv_heads,
-                   "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab, "adam": "host fp32",
+                   "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab,
+                   "adam": ("host fp32 (layers), device fp32 (resident embedding/head)" if adam else "off"),
                    "parallelism": "none (1 GPU)"},
         "mfma_util_pct": round(100.0 * layer_tflops / peak, 2),
         "kernel_tokens_per_s_per_layer": round(T / (layer_ms * 1e-3), 1),
