@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adam-threads", type=int, default=0)
+    ap.add_argument("--trace", default=None,
+                    help="write the last timed step's engine timeline (kind, start_ms, end_ms, info) as CSV")
     ap.add_argument("--no-adam", action="store_true",
                     help="stream gradients out but skip the optimizer (default for the 123B-shaped slice, whose "
                          "fp32 Adam states would need 133 GB of host memory)")
@@ -180,6 +182,11 @@ def main():
     ms_step = 1000.0 * elapsed / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, loss {loss:.4f}", file=sys.stderr, flush=True)
     med = {k: float(np.median([s[k] for s in stats])) for k in stats[0]}
+    if args.trace:
+        with open(args.trace, "w") as f:
+            f.write("kind,start_ms,end_ms,info\n")
+            for k, a, b, x in eng.trace():
+                f.write(f"{k},{a:.4f},{b:.4f},{x:.0f}\n")
     eng.close()
     del eng
 

@@ -242,7 +242,10 @@ enum {
  *       parameter layout (storage dtype).  Streamed to the device twice per
  *       step (forward and backward) except for the last `window` layers,
  *       which stay resident across the forward/backward turnaround.  With
- *       SF_ENGINE_ADAM the updated parameters are written back here.
+ *       SF_ENGINE_ADAM the updated parameters are written back here, and
+ *       those of layers 0 .. window-1 are also uploaded to their units
+ *       before sf_slide_step returns (the next step starts from them): do
+ *       not change h_params between steps of an engine with Adam.
  *   h_master/h_m/h_v[l]: host fp32 master weights and Adam moments of
  *       layer l in the fp32 gradient layout (grad_off / grad_bytes_t); any
  *       host memory.  Required with SF_ENGINE_ADAM.  For SF_F32 storage
@@ -267,7 +270,7 @@ typedef struct {
   int32_t window;          /* >= 2 */
   int32_t n_grad_slots;    /* >= 2 */
   int32_t flags;
-  int32_t adam_threads;    /* <= 0: one per available core */
+  int32_t adam_threads;    /* <= 0: one per available core, less two */
   float lr, b1, b2, eps;
   void* d_pool;
   size_t pool_bytes;
@@ -336,6 +339,22 @@ sf_status sf_slide_step(sf_engine* eng, const void* d_in, const void* d_dy, floa
  * gradient of layer 0 after the last step.  For tests and inspection. */
 sf_status sf_engine_layer_input(sf_engine* eng, int32_t layer, void** d_x);
 sf_status sf_engine_dx0(sf_engine* eng, void** d_dx0);
+
+/*
+ * Timeline of the last completed step, for inspecting the overlap the
+ * engine's design rests on (de/es/fr §2A: copies and host updates hidden
+ * under device compute).  Writes min(capacity, rows) rows of 4 doubles to
+ * out (host memory owned by the caller) and the total row count to *n_rows;
+ * capacity 0 with out NULL just returns the count.  Row = {kind, start_ms,
+ * end_ms, info}: kind 0 = compute interval (a kernel sequence on the
+ * compute stream), 1 = H2D copy, 2 = D2H copy (info = bytes), 3 = host Adam
+ * job on a layer's gradient range, 4 = host Adam of the LM head, 5 = host
+ * Adam of the embedding (info = layer index or -1).  Times are ms after the
+ * step's first device event; device rows come from HIP events, Adam rows
+ * from the host clock aligned to that event (error: the latency of one
+ * event record, microseconds).  Rows are grouped by source, not sorted.
+ */
+sf_status sf_engine_trace(sf_engine* eng, double* out, int32_t capacity, int32_t* n_rows);
 
 sf_status sf_engine_destroy(sf_engine* eng);
 

@@ -339,6 +339,15 @@ sf_status sf_layer_fwd(sf_ctx* c, const void* d_w, const void* d_x, void* d_y, v
 
 sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy,
                        void* d_dx, float* d_dw, sf_stream stream) {
+  return sf::layer_bwd(c, d_w, d_x, d_saved, d_dy, d_dx, d_dw, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace sf {
+
+sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy, void* d_dx,
+                    float* d_dw, sf_stream stream, hipEvent_t ffn_done) {
   if (sf_status st = check_ctx(c)) return st;
   if (sf_status st = check_ptrs({d_w, d_x, d_saved, d_dy, d_dx, d_dw})) return st;
   const Dims& d = c->dims;
@@ -401,6 +410,8 @@ sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* 
   g.C = dw + L.grad_off[SF_WG]; g.ldc = d.H;
   g.M = 2 * d.F; g.N = d.H; g.K = T;
   SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
+  // the MLP weight gradients (Wg, Wu, Wd) are final from here on
+  if (ffn_done) SF_HIP(hipEventRecord(ffn_done, s));
   // RMSNorm-2 backward (+ residual dy) -> dh, dg2
   SF_HIP(rmsnorm_bwd(d.dtype, dhn, h, r2, at(d_w, L.off[SF_G2]), d_dy, dh, partial, kGainChunks,
                      reinterpret_cast<float*>(dw + L.grad_off[SF_G2]), T, d.H, s));
@@ -449,6 +460,10 @@ sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* 
                      reinterpret_cast<float*>(dw + L.grad_off[SF_G1]), T, d.H, s));
   return SF_OK;
 }
+
+}  // namespace sf
+
+extern "C" {
 
 sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
                           float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream) {

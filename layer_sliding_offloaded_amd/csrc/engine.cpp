@@ -25,6 +25,13 @@
 // iteration's gradients and only affects the next iteration, so the result
 // equals plain synchronous training.
 //
+// Gradients leave in ranges of at most an eighth of a layer (>= 1 MiB), and
+// Adam of a range starts as soon as its copy lands, so copy and update of
+// one layer overlap.  The backward ends with layers W-1 .. 0, which are
+// also the first the next forward needs: their updated ranges go straight
+// back into their units, each upload overlapping the Adam of the next range,
+// and the next step's forward starts without waiting for them.
+//
 // Embedding and LM head (resident in HBM, updated by host Adam like a
 // layer): the LM-head and final-norm gradients leave right after the head
 // and are applied (and their parameters uploaded again) while the layer
@@ -35,6 +42,7 @@
 #include <atomic>
 #include <chrono>
 #include <condition_variable>
+#include <cstdint>
 #include <cstring>
 #include <deque>
 #include <functional>
@@ -52,7 +60,10 @@ namespace sf {
 
 namespace {
 
-// A fixed pool of worker threads running index-parallel loops.
+// A fixed pool of worker threads running index-parallel loops.  Adam jobs
+// arrive back to back (one per gradient range), so idle workers spin for a
+// short while before sleeping: waking a sleeping thread costs tens of
+// microseconds per job.
 class Pool {
  public:
   explicit Pool(int n) {
@@ -61,60 +72,87 @@ class Pool {
   ~Pool() {
     {
       std::lock_guard<std::mutex> lk(mu_);
-      stop_ = true;
+      stop_.store(true);
     }
     cv_.notify_all();
     for (auto& t : th_) t.join();
   }
-  // Run fn(0 .. n-1) on the pool and the calling thread; returns when done.
+  // Run fn(0 .. n-1) on the pool and the calling thread; returns when done
+  // and no worker still refers to this call.
   void run(size_t n, const std::function<void(size_t)>& fn) {
     if (n == 0) return;
+    Task t;
+    t.fn = &fn;
+    t.n = n;
     {
       std::lock_guard<std::mutex> lk(mu_);
-      fn_ = &fn;
-      n_ = n;
-      next_.store(0);
-      done_ = 0;
-      ++gen_;
+      cur_ = &t;
+      gen_.fetch_add(1, std::memory_order_release);
     }
     cv_.notify_all();
-    work();
-    std::unique_lock<std::mutex> lk(mu_);
-    cv_done_.wait(lk, [&] { return done_ == n_; });
-    fn_ = nullptr;
+    work(t);
+    {
+      // no new worker may pick the task up from here on
+      std::lock_guard<std::mutex> lk(mu_);
+      cur_ = nullptr;
+    }
+    auto finished = [&] { return t.done.load(std::memory_order_acquire) == n && active_.load() == 0; };
+    for (int spin = 0; !finished(); ++spin) {
+      if (spin < (1 << 16)) {
+        cpu_relax();
+      } else {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_done_.wait(lk, finished);
+      }
+    }
   }
 
  private:
-  void work() {
+  struct Task {
+    const std::function<void(size_t)>* fn = nullptr;
+    size_t n = 0;
+    std::atomic<size_t> next{0}, done{0};
+  };
+  static void cpu_relax() { __builtin_ia32_pause(); }
+  static void work(Task& t) {
     for (;;) {
-      const size_t i = next_.fetch_add(1);
-      if (i >= n_) break;
-      (*fn_)(i);
-      std::lock_guard<std::mutex> lk(mu_);
-      if (++done_ == n_) cv_done_.notify_all();
+      const size_t i = t.next.fetch_add(1);
+      if (i >= t.n) break;
+      (*t.fn)(i);
+      t.done.fetch_add(1, std::memory_order_acq_rel);
     }
   }
   void loop() {
     uint64_t seen = 0;
     for (;;) {
+      // spin about 100 us for the next task, then sleep
+      for (int spin = 0; spin < 20000 && gen_.load(std::memory_order_acquire) == seen && !stop_.load(); ++spin)
+        cpu_relax();
+      Task* t = nullptr;
       {
         std::unique_lock<std::mutex> lk(mu_);
-        cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
-        if (stop_) return;
-        seen = gen_;
-        if (!fn_) continue;
+        cv_.wait(lk, [&] { return stop_.load() || gen_.load() != seen; });
+        if (stop_.load()) return;
+        seen = gen_.load();
+        t = cur_;
+        if (t) active_.fetch_add(1);
       }
-      work();
+      if (!t) continue;
+      work(*t);
+      {
+        std::lock_guard<std::mutex> lk(mu_);
+        active_.fetch_sub(1);
+      }
+      cv_done_.notify_all();
     }
   }
   std::vector<std::thread> th_;
   std::mutex mu_;
   std::condition_variable cv_, cv_done_;
-  const std::function<void(size_t)>* fn_ = nullptr;
-  size_t n_ = 0, done_ = 0;
-  std::atomic<size_t> next_{0};
-  uint64_t gen_ = 0;
-  bool stop_ = false;
+  Task* cur_ = nullptr;
+  std::atomic<int> active_{0};
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<bool> stop_{false};
 };
 
 enum JobKind { kLayer = 0, kHeadLm = 1, kEmbed = 2 };
@@ -124,12 +162,21 @@ struct Job {
   int layer;  // kLayer
   int slot;   // host gradient slot (kLayer)
   hipEvent_t ready;
+  size_t lo = 0, hi = 0;  // kLayer: byte range of the layer's fp32 gradients
+  bool first = false;     // kLayer: the layer's first range
+  bool last = false;      // kLayer: the layer's final range (frees the slot)
 };
 
 struct Interval {
   hipEvent_t a, b;
   int kind;  // 0 compute, 1 H2D, 2 D2H
   double bytes;
+};
+
+// One row of the step trace: what, when (ms after the step's first device
+// event), and its bytes (copies) or layer (Adam jobs).
+struct TraceRow {
+  double kind, start, end, info;
 };
 
 double now_ms() {
@@ -174,6 +221,8 @@ struct sf_engine {
   sf_layout L{};
   int nl = 0, W = 0;
   size_t unit_bytes = 0, x_bytes = 0;
+  size_t chunk_bytes = 0;  // gradient D2H / Adam / re-upload granularity
+  bool preloaded = false;  // units 0..W-1 hold this step's layers 0..W-1 already
   hipStream_t s_comp = nullptr, s_h2d = nullptr, s_d2h = nullptr, s_head = nullptr;
   std::vector<char*> uparam, ugrad, x, saved;
   char* dbuf = nullptr;
@@ -202,7 +251,11 @@ struct sf_engine {
   bool stop = false;
   std::string job_error;
   AdamCoef coef{};
+  int n_threads = 1;  // Adam threads: the pool plus the dispatcher
   double adam_ms = 0;
+  double host_t0 = 0;                 // host clock at the step's first device event
+  std::vector<TraceRow> adam_rows;    // host Adam jobs of the current step (under mu)
+  std::vector<TraceRow> trace;        // the last completed step
 };
 
 namespace sf {
@@ -243,10 +296,14 @@ struct Seg {
 
 void run_adam(sf_engine* e, float* p, float* m, float* v, const float* g, void* out, bool out_is_master,
               const std::vector<Seg>& segs) {
-  constexpr size_t kChunk = 1 << 18;
+  // about four tasks per thread, each 16K .. 256K elements
+  size_t total = 0;
+  for (const Seg& s : segs) total += s.n;
+  const size_t per = total / (4 * static_cast<size_t>(e->n_threads)) / 64 * 64;
+  const size_t chunk = std::min<size_t>(1 << 18, std::max<size_t>(1 << 14, per));
   std::vector<Seg> tasks;
   for (const Seg& s : segs)
-    for (size_t b = 0; b < s.n; b += kChunk) tasks.push_back({s.off + b, std::min(kChunk, s.n - b), s.out_off + b});
+    for (size_t b = 0; b < s.n; b += chunk) tasks.push_back({s.off + b, std::min(chunk, s.n - b), s.out_off + b});
   const bool bf = e->d.dtype == SF_BF16;
   const AdamCoef c = e->coef;
   e->pool->run(tasks.size(), [&](size_t i) {
@@ -310,15 +367,46 @@ sf_status run_embed_adam(sf_engine* e) {
   return rc;
 }
 
+// Adam segments and the parameter byte range [plo, phi) that belong to the
+// gradient bytes [lo, hi) of a layer (the range may span tensors; padding
+// between tensors is skipped).
+struct ChunkMap {
+  std::vector<Seg> segs;
+  size_t plo = SIZE_MAX, phi = 0;
+};
+ChunkMap chunk_map(const sf_layout& L, int eb, size_t lo, size_t hi) {
+  ChunkMap cm;
+  for (int t = 0; t < SF_NTENSORS; ++t) {
+    const size_t a = std::max(lo, L.grad_off[t]), b = std::min(hi, L.grad_off[t] + L.grad_bytes_t[t]);
+    if (a >= b) continue;
+    const size_t i0 = (a - L.grad_off[t]) / 4, i1 = (b - L.grad_off[t]) / 4;
+    cm.segs.push_back({a / 4, i1 - i0, L.off[t] / eb + i0});
+    cm.plo = std::min(cm.plo, L.off[t] + i0 * eb);
+    cm.phi = std::max(cm.phi, L.off[t] + i1 * eb);
+  }
+  return cm;
+}
+
 sf_status run_job(sf_engine* e, const Job& j) {
   const sf_engine_cfg& c = e->cfg;
   const size_t VH = static_cast<size_t>(e->d.V) * e->d.H;
   if (j.kind == kLayer) {
-    std::vector<Seg> segs;
-    for (int t = 0; t < SF_NTENSORS; ++t)
-      segs.push_back({e->L.grad_off[t] / 4, e->L.grad_bytes_t[t] / 4, e->L.off[t] / e->d.e});
+    const ChunkMap cm = chunk_map(e->L, e->d.e, j.lo, j.hi);
     run_adam(e, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot], c.h_params[j.layer],
-             c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), segs);
+             c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), cm.segs);
+    // Layers 0 .. W-1 open the next step's forward and finish their backward
+    // last: upload each updated range into the layer's unit right away, so
+    // the upload of one range overlaps the Adam of the next.
+    if (j.layer < e->W) {
+      const int u = j.layer;
+      if (j.first) SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_param_free[u], 0));
+      if (cm.phi > cm.plo) {
+        if (sf_status rc = timed_h2d(e, e->uparam[u] + cm.plo, static_cast<const char*>(c.h_params[j.layer]) + cm.plo,
+                                     cm.phi - cm.plo, e->s_h2d))
+          return rc;
+      }
+      if (j.last) SF_HIP(hipEventRecord(e->ev_param_ready[u], e->s_h2d));
+    }
     return SF_OK;
   }
   if (j.kind == kHeadLm) {
@@ -353,11 +441,12 @@ void dispatcher_loop(sf_engine* e) {
       const sf_status rc = run_job(e, j);
       if (rc != SF_OK) err = sf_last_error();
     }
-    const double dt = now_ms() - t0;
+    const double t1 = now_ms();
     std::lock_guard<std::mutex> lk(e->mu);
     if (!err.empty() && e->job_error.empty()) e->job_error = err;
-    e->adam_ms += dt;
-    if (j.kind == kLayer) e->slot_free[j.slot] = true;
+    e->adam_ms += t1 - t0;
+    e->adam_rows.push_back({3.0 + j.kind, t0 - e->host_t0, t1 - e->host_t0, static_cast<double>(j.layer)});
+    if (j.kind == kLayer && j.last) e->slot_free[j.slot] = true;
     --e->pending;
     e->cv.notify_all();
   }
@@ -391,10 +480,12 @@ double union_ms(std::vector<std::pair<double, double>> v) {
 sf_status fill_stats(sf_engine* e, hipEvent_t ev0, sf_step_stats* st) {
   std::vector<std::pair<double, double>> comp, copy, h2d, d2h;
   double lo = 1e300, hi = -1e300, hb = 0, db = 0;
+  e->trace.clear();
   for (const Interval& x : e->iv) {
     float a = 0, b = 0;
     SF_HIP(hipEventElapsedTime(&a, ev0, x.a));
     SF_HIP(hipEventElapsedTime(&b, ev0, x.b));
+    e->trace.push_back({static_cast<double>(x.kind), a, b, x.bytes});
     lo = std::min(lo, static_cast<double>(a));
     hi = std::max(hi, static_cast<double>(b));
     if (x.kind == 0) comp.push_back({a, b});
@@ -480,6 +571,11 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   hipEvent_t ev0 = timing_event(e);
   if (!ev0) return fail(SF_ERR_HIP, "event pool exhausted");
   SF_HIP(hipEventRecord(ev0, e->s_comp));
+  e->host_t0 = now_ms();
+  {
+    std::lock_guard<std::mutex> lk(e->mu);
+    e->adam_rows.clear();
+  }
   // The side streams start after everything the caller queued before this call.
   SF_HIP(hipStreamWaitEvent(e->s_h2d, ev0, 0));
   SF_HIP(hipStreamWaitEvent(e->s_d2h, ev0, 0));
@@ -514,9 +610,12 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   for (int i = 1; i <= nl; ++i) xin[i] = e->x[i];
 
   // ---------------- forward: layer i in unit i % W, prefetch i + 1
-  if ((rc = prefetch(e, 0))) return rc;
+  // (layers below W were uploaded at the end of the previous step, right
+  // after their Adam, when that step ran Adam)
+  auto fetch = [&](int j) { return (e->preloaded && j < W) ? SF_OK : prefetch(e, j); };
+  if ((rc = fetch(0))) return rc;
   for (int i = 0; i < nl; ++i) {
-    if (i + 1 < nl && (rc = prefetch(e, i + 1))) return rc;
+    if (i + 1 < nl && (rc = fetch(i + 1))) return rc;
     const int u = i % W;
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
     if ((rc = comp_begin(&a))) return rc;
@@ -532,11 +631,11 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   // device Adam of a resident head tensor: master/m/v at element offset `off`
   // of d_head_state's three regions, gradient at the same offset of hg
   const size_t NH = 2 * VH + d.H;
-  auto dev_adam = [&](size_t off, size_t n, void* out) -> sf_status {
+  auto dev_adam = [&](size_t off, size_t n, void* out, hipStream_t st_) -> sf_status {
     float* st = c.d_head_state;
     const AdamCoef& k = e->coef;
     SF_HIP(adam_device(d.dtype, st + off, st + NH + off, st + 2 * NH + off, hg + off, out, static_cast<int64_t>(n),
-                       k.b1, k.b2, k.one_b1, k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, e->s_comp));
+                       k.b1, k.b2, k.one_b1, k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, st_));
     return SF_OK;
   };
   if (head) {
@@ -544,10 +643,19 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if ((rc = sf_head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
                               e->s_comp)))
       return rc;
-    if (adam && !head_host) {
-      if ((rc = dev_adam(VH, d.H, c.d_gf)) || (rc = dev_adam(VH + d.H, VH, c.d_wlm))) return rc;
-    }
     if ((rc = comp_end(a, &b))) return rc;
+    if (adam && !head_host) {
+      // LM head and final gain: updated on the head stream while the layer
+      // backward runs (nothing later in the step reads them)
+      hipEvent_t ha = timing_event(e), hb = timing_event(e);
+      if (!ha || !hb) return fail(SF_ERR_HIP, "event pool exhausted");
+      SF_HIP(hipStreamWaitEvent(e->s_head, b, 0));
+      SF_HIP(hipEventRecord(ha, e->s_head));
+      if ((rc = dev_adam(VH, d.H, c.d_gf, e->s_head)) || (rc = dev_adam(VH + d.H, VH, c.d_wlm, e->s_head)))
+        return rc;
+      SF_HIP(hipEventRecord(hb, e->s_head));
+      if ((rc = record_interval(e, ha, hb, 0, 0))) return rc;
+    }
     if (head_host) {
       hipEvent_t done;
       if ((rc = timed_d2h(e, c.h_head_grads + VH, hg + VH, (VH + d.H) * 4, b, &done))) return rc;
@@ -568,25 +676,50 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_grad_free[u], 0));
     if ((rc = comp_begin(&a))) return rc;
-    if ((rc = sf_layer_bwd(ctx, e->uparam[u], xin[i], e->saved[i], dy, e->dbuf,
-                           reinterpret_cast<float*>(e->ugrad[u]), e->s_comp)))
+    hipEvent_t ffn = timing_event(e);
+    if (!ffn) return fail(SF_ERR_HIP, "event pool exhausted");
+    if ((rc = layer_bwd(ctx, e->uparam[u], xin[i], e->saved[i], dy, e->dbuf, reinterpret_cast<float*>(e->ugrad[u]),
+                        e->s_comp, ffn)))
       return rc;
     if ((rc = comp_end(a, &b))) return rc;
     dy = e->dbuf;
     SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
     int k = 0;
     if ((rc = wait_slot(e, &k))) return rc;
-    hipEvent_t done;
-    if ((rc = timed_d2h(e, c.h_grad_slots[k], e->ugrad[u], e->L.grad_bytes, b, &done))) return rc;
+    // Gradients leave in ranges and Adam of a range starts as soon as it
+    // lands; the MLP weights' gradients (most of a layer) go first, right
+    // after the MLP half of the backward.
+    const size_t gb = e->L.grad_bytes;
+    const size_t f0 = e->L.grad_off[SF_WG], f1 = e->L.grad_off[SF_WD] + e->L.grad_bytes_t[SF_WD];
+    const struct {
+      size_t lo, hi;
+      hipEvent_t after;
+    } parts[3] = {{f0, f1, ffn}, {0, f0, b}, {f1, gb, b}};
+    std::vector<Job> rj;
+    for (const auto& pt : parts) {
+      for (size_t lo = pt.lo; lo < pt.hi; lo += e->chunk_bytes) {
+        Job jb{kLayer, i, k, nullptr};
+        jb.lo = lo;
+        jb.hi = std::min(pt.hi, lo + e->chunk_bytes);
+        if ((rc = timed_d2h(e, reinterpret_cast<char*>(c.h_grad_slots[k]) + lo, e->ugrad[u] + lo, jb.hi - lo,
+                            pt.after, &jb.ready)))
+          return rc;
+        rj.push_back(jb);
+      }
+    }
+    if (adam) {
+      rj.front().first = true;
+      rj.back().last = true;
+      for (const Job& jb : rj) push_job(e, jb);
+    }
     SF_HIP(hipEventRecord(e->ev_grad_free[u], e->s_d2h));
-    if (adam) push_job(e, Job{kLayer, i, k, done});
   }
 
   // ---------------- embedding backward (+ its device Adam)
   if (head && !head_host) {
     if ((rc = comp_begin(&a))) return rc;
     if ((rc = sf_embed_bwd(ctx, e->dbuf, ids, hg, e->s_comp))) return rc;
-    if (adam && (rc = dev_adam(0, VH, c.d_E))) return rc;
+    if (adam && (rc = dev_adam(0, VH, c.d_E, e->s_comp))) return rc;
     if ((rc = comp_end(a, nullptr))) return rc;
   }
   // ---------------- embedding backward on the host path: sparse rows of the ids present
@@ -606,19 +739,20 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   }
 
   SF_HIP(hipStreamSynchronize(e->s_comp));
-  SF_HIP(hipStreamSynchronize(e->s_h2d));
   SF_HIP(hipStreamSynchronize(e->s_d2h));
-  drain(e);
+  drain(e);  // Adam jobs; they queue the re-upload of layers 0 .. W-1
+  SF_HIP(hipStreamSynchronize(e->s_h2d));
   SF_HIP(hipStreamSynchronize(e->s_head));
   {
     std::lock_guard<std::mutex> lk(e->mu);
     if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
   }
-  if (st) {
-    if ((rc = fill_stats(e, ev0, st))) return rc;
-    std::lock_guard<std::mutex> lk(e->mu);
-    st->adam_ms = e->adam_ms;
-  }
+  e->preloaded = adam;
+  sf_step_stats local{};
+  if ((rc = fill_stats(e, ev0, st ? st : &local))) return rc;
+  std::lock_guard<std::mutex> lk(e->mu);
+  if (st) st->adam_ms = e->adam_ms;
+  e->trace.insert(e->trace.end(), e->adam_rows.begin(), e->adam_rows.end());
   return SF_OK;
 }
 
@@ -701,6 +835,11 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   e->W = W;
   e->unit_bytes = unit;
   e->x_bytes = align256(static_cast<size_t>(d.T) * d.H * d.e);
+  {
+    // at most 8 ranges per layer, none under 1 MiB
+    const size_t n = std::max<size_t>(1, std::min<size_t>(8, L.grad_bytes >> 20));
+    e->chunk_bytes = align256((L.grad_bytes + n - 1) / n);
+  }
   e->sp = sp;
   if (head) {
     e->slot_of_row.assign(d.V, -1);
@@ -738,14 +877,18 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   };
   if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_free))
     return cleanup(fail(SF_ERR_HIP, "event creation failed"));
-  for (int i = 0; i < 8 * e->nl + 64; ++i) {
+  for (int i = 0; i < 24 * e->nl + 64; ++i) {
     hipEvent_t ev;
     if (hipEventCreate(&ev) != hipSuccess) return cleanup(fail(SF_ERR_HIP, "event creation failed"));
     e->tev.push_back(ev);
   }
   e->slot_free.assign(c.n_grad_slots, true);
-  const int nt = c.adam_threads > 0 ? c.adam_threads : default_threads();
-  e->pool.reset(new Pool(std::max(0, nt - 1)));
+  // default: every available core but two (the thread that queues device
+  // work and the HIP runtime's own), so a preempted Adam worker does not
+  // stall a whole gradient range
+  const int nt = c.adam_threads > 0 ? c.adam_threads : std::max(1, default_threads() - 2);
+  e->n_threads = std::max(1, nt);
+  e->pool.reset(new Pool(e->n_threads - 1));
   e->dispatcher = std::thread(dispatcher_loop, e);
   *out = e;
   return SF_OK;
@@ -763,9 +906,9 @@ sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float*
     // Leave no work in flight: finish the streams and any queued Adam jobs.
     const std::string msg = sf_last_error();
     (void)hipStreamSynchronize(e->s_comp);
-    (void)hipStreamSynchronize(e->s_h2d);
     (void)hipStreamSynchronize(e->s_d2h);
     drain(e);
+    (void)hipStreamSynchronize(e->s_h2d);
     (void)hipStreamSynchronize(e->s_head);
     e->failed = true;
     return fail(rc, "%s", msg.c_str());
@@ -794,6 +937,21 @@ sf_status sf_engine_layer_input(sf_engine* e, int32_t layer, void** d_x) {
 sf_status sf_engine_dx0(sf_engine* e, void** d_dx0) {
   if (!e || !d_dx0) return fail(SF_ERR_ARG, "bad argument");
   *d_dx0 = e->dbuf;
+  return SF_OK;
+}
+
+sf_status sf_engine_trace(sf_engine* e, double* out, int32_t capacity, int32_t* n_rows) {
+  if (!e || !n_rows || capacity < 0 || (capacity > 0 && !out)) return fail(SF_ERR_ARG, "bad argument");
+  const size_t n = e->trace.size();
+  *n_rows = static_cast<int32_t>(n);
+  const size_t m = std::min(n, static_cast<size_t>(capacity));
+  for (size_t i = 0; i < m; ++i) {
+    const TraceRow& r = e->trace[i];
+    out[4 * i + 0] = r.kind;
+    out[4 * i + 1] = r.start;
+    out[4 * i + 2] = r.end;
+    out[4 * i + 3] = r.info;
+  }
   return SF_OK;
 }
 

@@ -46,6 +46,14 @@ WorkLayout work_layout(const Dims& d, int head_chunk_rows);
 
 }  // namespace sf
 
+struct sf_ctx;
+namespace sf {
+// sf_layer_bwd with an optional event recorded on the stream once the MLP
+// weight gradients (Wg, Wu, Wd) are complete, before the attention half.
+sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy, void* d_dx,
+                    float* d_dw, sf_stream stream, hipEvent_t ffn_done);
+}  // namespace sf
+
 struct sf_ctx {
   sf::Dims dims;
   sf_layout layout;

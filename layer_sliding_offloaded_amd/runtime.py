@@ -197,6 +197,10 @@ class Engine:
         loss, st = sf.sf_slide_step(self.eng, d_in.data_ptr(), None if d_dy is None else d_dy.data_ptr())
         return loss, st.as_dict()
 
+    def trace(self):
+        """The last step's timeline: list of (kind name, start_ms, end_ms, info)."""
+        return [(sf.TRACE_KINDS[int(k)], a, b, x) for k, a, b, x in sf.sf_engine_trace(self.eng)]
+
     def close(self):
         if getattr(self, "eng", None):
             sf.sf_engine_destroy(self.eng)

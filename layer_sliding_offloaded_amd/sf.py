@@ -84,7 +84,7 @@ class SfError(RuntimeError):
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
     "sf_gemm", "sf_gemm_workspace_bytes", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_create", "sf_slide_step",
-    "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_destroy", "sf_last_error",
+    "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_destroy", "sf_last_error",
 )
 
 _lib = None
@@ -119,6 +119,7 @@ def load():
         "sf_slide_step": [P, P, P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(SfStepStats)],
         "sf_engine_layer_input": [P, i32, ctypes.POINTER(P)],
         "sf_engine_dx0": [P, ctypes.POINTER(P)],
+        "sf_engine_trace": [P, ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(i32)],
         "sf_engine_destroy": [P],
     }
     for name, args in sig.items():
@@ -232,6 +233,19 @@ def sf_engine_dx0(eng):
     p = _vp()
     _check(load().sf_engine_dx0(eng, ctypes.byref(p)))
     return p.value
+
+
+TRACE_KINDS = {0: "compute", 1: "h2d", 2: "d2h", 3: "adam", 4: "adam_head", 5: "adam_embed"}
+
+
+def sf_engine_trace(eng):
+    """Rows (kind, start_ms, end_ms, info) of the last step's timeline, sorted by start."""
+    n = ctypes.c_int32(0)
+    _check(load().sf_engine_trace(eng, None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_double * (4 * max(1, n.value)))()
+    _check(load().sf_engine_trace(eng, buf, n.value, ctypes.byref(n)))
+    rows = [tuple(buf[4 * i:4 * i + 4]) for i in range(n.value)]
+    return sorted(rows, key=lambda r: (r[1], r[0]))
 
 
 def sf_engine_destroy(eng):

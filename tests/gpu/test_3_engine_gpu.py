@@ -125,6 +125,14 @@ def test_engine_matches_resident_bitwise(window, slots, n_layers, head_adam):
                         Wlm=hf[VH + w.hidden:].reshape(w.vocab, w.hidden))
         assert 0.0 <= st["overlap_pct"] <= 100.0 + 1e-6 and st["h2d_bytes"] > 0 and st["d2h_bytes"] > 0
         assert st["busy_ms"] <= st["span_ms"] + 1e-3
+        tr = eng.trace()
+        kinds = {r[0] for r in tr}
+        assert {"compute", "h2d", "d2h", "adam"} <= kinds, kinds
+        assert all(r[1] <= r[2] for r in tr)
+        # every layer's gradients leave and are updated (in one or more ranges)
+        assert {int(r[3]) for r in tr if r[0] == "adam"} == set(range(n_layers))
+        d2h = sum(r[3] for r in tr if r[0] == "d2h")
+        assert d2h == st["d2h_bytes"]
     eng.close()
 
 
