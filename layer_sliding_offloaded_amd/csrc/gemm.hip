@@ -184,30 +184,10 @@ __device__ __forceinline__ void load4(const T* p, float* v) {
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-gemm_kernel(const GemmArgs g, int ntm, int ntn) {
-  constexpr bool AKC = (LAY != GemmLayout::TN);
-  constexpr bool BKC = (LAY == GemmLayout::NT);
-  constexpr int NW = (BM / WM) * (BN / WN);
-  constexpr int NT = NW * 64;
-  constexpr int VE = 16 / sizeof(T);
-  constexpr int BKE = kStageBytes / sizeof(T);
-  constexpr int ROW = BKE + VE;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int WGM = BM / WM;
-  static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
-
-  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * ROW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int wm = w % WGM, wn = w / WGM;
-
-  // Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
-  // contiguous range of tiles, then walk that range in groups of 8 tile-rows
-  // so the A rows and B columns a group shares stay in that XCD's L2.
+// Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
+// contiguous range of tiles, then walk that range in groups of 8 tile-rows so
+// the A rows and B columns a group shares stay in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int ntm, int ntn, int* tm, int* tn) {
   const int ntiles = ntm * ntn;
   int t = blockIdx.x;
   if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
@@ -215,66 +195,14 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
   const int group = t / (GM * ntn);
   const int first_m = group * GM;
   const int gsize = min(ntm - first_m, GM);
-  const int tm = first_m + (t % (GM * ntn)) % gsize;
-  const int tn = (t % (GM * ntn)) / gsize;
-  const int m0 = tm * BM, n0 = tn * BN;
+  *tm = first_m + (t % (GM * ntn)) % gsize;
+  *tn = (t % (GM * ntn)) / gsize;
+}
 
-  const T* __restrict__ A = static_cast<const T*>(g.A);
-  const T* __restrict__ B = static_cast<const T*>(g.B);
-
-  Loader<T, BM, NT, AKC> la;
-  Loader<T, BN, NT, BKC> lb;
-  auto amap = [&](int r) { const int m = m0 + r; return m < g.M ? m : -1; };
-  auto bmap = [&](int r) { return ColMap<E, WN>::brow(r, n0, g, BN); };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // split-K: blockIdx.y owns k in [kbeg, kend)
-  const int kbeg = blockIdx.y * g.kchunk;
-  const int kend = min(g.K, kbeg + g.kchunk);
-  const int nk = kend > kbeg ? (kend - kbeg + BKE - 1) / BKE : 0;
-  la.load(A, g.lda, kbeg, kend, tid, amap);
-  lb.load(B, g.ldb, kbeg, kend, tid, bmap);
-  la.store(smem[0], tid);
-  lb.store(smem[0] + BM * ROW, tid);
-  __syncthreads();
-
-  const int lr = lane % 16, lg = lane / 16;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(A, g.lda, kbeg + (kt + 1) * BKE, kend, tid, amap);
-      lb.load(B, g.ldb, kbeg + (kt + 1) * BKE, kend, tid, bmap);
-    }
-    const T* As = smem[buf];
-    const T* Bs = smem[buf] + BM * ROW;
-#pragma unroll
-    for (int s = 0; s < BKE / (4 * VE); ++s) {
-      const int koff = s * 4 * VE + lg * VE;
-      uint4 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(As + (wm * WM + i * 16 + lr) * ROW + koff);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const uint4*>(Bs + (wn * WN + j * 16 + lr) * ROW + koff);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[j], af[i]);
-    }
-    if (kt + 1 < nk) {
-      la.store(smem[buf ^ 1], tid);
-      lb.store(smem[buf ^ 1] + BM * ROW, tid);
-    }
-    __syncthreads();
-  }
-
-  // ------------------------------------------------------------ epilogue
+// Fused epilogue of one wave's WM x WN accumulator tile.
+template <typename T, int WM, int WN, int FM, int FN, Epi E>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x4 (&acc)[FM][FN], int m0, int n0, int wm,
+                                         int wn, int lr, int lg, int BN) {
   // lane holds C[m][c .. c+3] with m = row lr of fragment i, c = 4*lg of
   // fragment j (tile-local slot numbering, mapped through ColMap).
 #pragma unroll
@@ -368,7 +296,284 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
         }
       }
     }
+    // one fragment row at a time: keeps the scheduler from pulling every
+    // accumulator out of the AGPRs at once
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_kernel(const GemmArgs g, int ntm, int ntn) {
+  constexpr bool AKC = (LAY != GemmLayout::TN);
+  constexpr bool BKC = (LAY == GemmLayout::NT);
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int NT = NW * 64;
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int BKE = kStageBytes / sizeof(T);
+  constexpr int ROW = BKE + VE;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int WGM = BM / WM;
+  static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
+
+  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * ROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wm = w % WGM, wn = w / WGM;
+
+  int tm, tn;
+  tile_coords(ntm, ntn, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const T* __restrict__ A = static_cast<const T*>(g.A);
+  const T* __restrict__ B = static_cast<const T*>(g.B);
+
+  Loader<T, BM, NT, AKC> la;
+  Loader<T, BN, NT, BKC> lb;
+  auto amap = [&](int r) { const int m = m0 + r; return m < g.M ? m : -1; };
+  auto bmap = [&](int r) { return ColMap<E, WN>::brow(r, n0, g, BN); };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // split-K: blockIdx.y owns k in [kbeg, kend)
+  const int kbeg = blockIdx.y * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + BKE - 1) / BKE : 0;
+  la.load(A, g.lda, kbeg, kend, tid, amap);
+  lb.load(B, g.ldb, kbeg, kend, tid, bmap);
+  la.store(smem[0], tid);
+  lb.store(smem[0] + BM * ROW, tid);
+  __syncthreads();
+
+  const int lr = lane % 16, lg = lane / 16;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      la.load(A, g.lda, kbeg + (kt + 1) * BKE, kend, tid, amap);
+      lb.load(B, g.ldb, kbeg + (kt + 1) * BKE, kend, tid, bmap);
+    }
+    const T* As = smem[buf];
+    const T* Bs = smem[buf] + BM * ROW;
+#pragma unroll
+    for (int s = 0; s < BKE / (4 * VE); ++s) {
+      const int koff = s * 4 * VE + lg * VE;
+      uint4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(As + (wm * WM + i * 16 + lr) * ROW + koff);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(Bs + (wn * WN + j * 16 + lr) * ROW + koff);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[j], af[i]);
+    }
+    if (kt + 1 < nk) {
+      la.store(smem[buf ^ 1], tid);
+      lb.store(smem[buf ^ 1] + BM * ROW, tid);
+    }
+    __syncthreads();
+  }
+
+  epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
+}
+
+// ----------------------------------------------------------------------------
+// bf16 kernel with global -> LDS direct loads (gfx950).
+//
+// Operands are copied from HBM straight into LDS by buffer loads (no
+// staging registers, no VALU transposes): each wave instruction moves 1 KB,
+// 16 B per lane, and lanes past a matrix edge (or past the k-range) read
+// through an out-of-range buffer offset, which the hardware turns into
+// zeros.  Per stage (64 k) the block holds, for each operand, either
+//  - [row][k] (k-contiguous operands): 128-byte rows whose 16-byte slots are
+//    XOR-swizzled by row, so 16 lanes reading one k-chunk of 16 consecutive
+//    rows hit 16 distinct bank groups, or
+//  - [k][row] (row-contiguous operands: the transposed side of NN / TN):
+//    the tile exactly as it lies in HBM, slots swizzled by k, read with the
+//    LDS transpose load (ds_read_b64_tr_b16), which hands each lane four
+//    consecutive k of one row -- the MFMA operand layout -- directly.
+// Two stages are double-buffered; one barrier per stage.
+namespace direct {
+
+constexpr int kBK = 64;              // k per stage
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every operand's extent
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// [k][row] slot swizzle: 16 lanes of one transpose read cover 4 consecutive k
+// (the same two slots each); lanes 16 apart cover k 8 apart.  This map sends
+// those 8 k-rows to 8 distinct slot pairs.
+__device__ __forceinline__ int kswz(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+// [row][k] slot swizzle
+__device__ __forceinline__ int rswz(int row) { return (row >> 1) & 7; }
+
+// Loads of one operand tile (ROWS x 64 k) for one wave: JW instructions of
+// 1 KB each.  KC: k-contiguous in HBM.
+template <int ROWS, int NW, bool KC>
+struct Direct {
+  static constexpr int NI = ROWS / 8;  // 1-KB instructions per stage
+  static_assert(NI % NW == 0, "tile rows must split evenly over the waves");
+  static constexpr int JW = NI / NW;
+  static constexpr int ROWB = ROWS * 2;  // [k][row]: bytes per k-row
+  static constexpr int KPI = 1024 / ROWB;  // [k][row]: k-rows per instruction
+  uint32_t base[JW];  // byte offset at k = 0, or kOOB
+  int kl[JW];         // k of this lane's 16 bytes within the stage
+
+  // KC: rowmap(r) = global row of tile row r or -1.  !KC: rows r0.. of `rows`.
+  template <typename RowMap>
+  __device__ __forceinline__ void init(int w, int lane, int64_t ld, int r0, int rows, RowMap rowmap) {
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const int idx = j * NW + w;
+      if constexpr (KC) {
+        const int row = idx * 8 + lane / 8;
+        const int ls = (lane % 8) ^ rswz(row);
+        const int gr = rowmap(row);
+        base[j] = gr >= 0 ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + ls * 8) * 2) : kOOB;
+        kl[j] = ls * 8;
+      } else {
+        const int b = lane * 16;
+        const int k = idx * KPI + b / ROWB;
+        const int ls = ((b % ROWB) / 16) ^ kswz(k);
+        const int r = r0 + ls * 8;
+        base[j] = r < rows ? static_cast<uint32_t>((static_cast<int64_t>(k) * ld + r) * 2) : kOOB;
+        kl[j] = k;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* region, int w, int k0, int kend,
+                                        int64_t ld) {
+    const uint32_t adv = KC ? static_cast<uint32_t>(k0) * 2u : static_cast<uint32_t>(k0 * ld * 2);
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const uint32_t off = (base[j] != kOOB && k0 + kl[j] < kend) ? base[j] + adv : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t*)(region + (j * NW + w) * 1024), 16,
+                                               static_cast<int>(off), 0, 0, 0);
+    }
+  }
+};
+
+// One 16-row x 32-k MFMA operand fragment (rows rb.., k-chunk ks) for lane
+// (lr = lane % 16, lg = lane / 16): 8 consecutive k of row rb + lr.
+template <int ROWS, bool KC>
+__device__ __forceinline__ uint4 frag(const char* region, int rb, int ks, int lr, int lg) {
+  if constexpr (KC) {
+    const int row = rb + lr;
+    const int slot = (ks * 4 + lg) ^ rswz(row);
+    return *reinterpret_cast<const uint4*>(region + row * 128 + slot * 16);
+  } else {
+    // lane s of a 16-lane group addresses 4 rows at one k; the transpose read
+    // returns to lane i the 4 k (k0 .. k0+3) of row i
+    const int row = rb + 4 * (lr & 3);
+    const int slot = row >> 3, half = (row >> 2) & 1;
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int k = ks * 32 + 8 * lg + 4 * t + (lr >> 2);
+      const char* p = region + k * (ROWS * 2) + ((slot ^ kswz(k)) * 16) + half * 8;
+      const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(const_cast<char*>(p)));
+      w[2 * t] = static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
+      w[2 * t + 1] = static_cast<uint16_t>(v[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[3])) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Byte extent of a row-major operand with `rows` rows of `cols` used
+// elements at stride ld.
+inline int64_t extent(int64_t rows, int64_t cols, int64_t ld) { return ((rows - 1) * ld + cols) * 2; }
+
+}  // namespace direct
+
+template <int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
+  using T = bf16;
+  constexpr bool AKC = (LAY != GemmLayout::TN);
+  constexpr bool BKC = (LAY == GemmLayout::NT);
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int WGM = BM / WM;
+  constexpr int STAGE = (BM + BN) * 128;
+  static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WGM, wn = w / WGM;
+  int tm, tn;
+  tile_coords(ntm, ntn, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), 0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.B), 0, b_bytes, 0x00020000);
+  direct::Direct<BM, NW, AKC> la;
+  direct::Direct<BN, NW, BKC> lb;
+  la.init(w, lane, g.lda, m0, g.M, [&](int r) { const int m = m0 + r; return m < g.M ? m : -1; });
+  lb.init(w, lane, g.ldb, n0, g.N, [&](int r) { return ColMap<E, WN>::brow(r, n0, g, BN); });
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kbeg = blockIdx.y * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + direct::kBK - 1) / direct::kBK : 0;
+  if (nk > 0) {
+    la.issue(ra, smem, w, kbeg, kend, g.lda);
+    lb.issue(rb, smem + BM * 128, w, kbeg, kend, g.ldb);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int lr = lane % 16, lg = lane / 16;
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* As = smem + (kt & 1) * STAGE;
+    const char* Bs = As + BM * 128;
+    // All of this stage's fragment reads are issued before the next stage's
+    // loads: the compiler orders a read of LDS after a load into LDS with a
+    // full wait on that load, which would expose its latency here.
+    uint4 af[2][FM], bfr[2][FN];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[ks][i] = direct::frag<BM, AKC>(As, wm * WM + i * 16, ks, lr, lg);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[ks][j] = direct::frag<BN, BKC>(Bs, wn * WN + j * 16, ks, lr, lg);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      char* nxt = smem + ((kt + 1) & 1) * STAGE;
+      la.issue(ra, nxt, w, kbeg + (kt + 1) * direct::kBK, kend, g.lda);
+      lb.issue(rb, nxt + BM * 128, w, kbeg + (kt + 1) * direct::kBK, kend, g.ldb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[ks][j], af[ks][i]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
 // out[m, n] = sum over s (in order) of partial[s][m][n]; 4 columns per thread.
@@ -389,8 +594,26 @@ splitk_reduce_kernel(const float* __restrict__ partial, TO* __restrict__ out, in
   else *reinterpret_cast<float4*>(out + m * ldo + n) = acc;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
-hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_bytes) {
+// Whether the direct-load kernel can take this product: 16-byte aligned
+// operands and rows, k in whole 8-element chunks, row-contiguous operands in
+// whole 8-row chunks, and byte offsets that fit the 31-bit buffer range.
+template <GemmLayout LAY, Epi E>
+bool direct_ok(const GemmArgs& g, int64_t* a_bytes, int64_t* b_bytes) {
+  constexpr bool AKC = (LAY != GemmLayout::TN);
+  constexpr bool BKC = (LAY == GemmLayout::NT);
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % 8 || g.lda % 8 || g.ldb % 8) return false;
+  if ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15u) return false;
+  if ((!AKC && g.M % 8) || (!BKC && g.N % 8)) return false;
+  const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
+  *a_bytes = AKC ? direct::extent(g.M, g.K, g.lda) : direct::extent(g.K, g.M, g.lda);
+  *b_bytes = BKC ? direct::extent(ncols, g.K, g.ldb) : direct::extent(g.K, g.N, g.ldb);
+  constexpr int64_t lim = (int64_t{1} << 31) - 1024;
+  return *a_bytes > 0 && *b_bytes > 0 && *a_bytes < lim && *b_bytes < lim;
+}
+
+template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, bool DIRECT = false>
+hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_bytes, int64_t a_bytes = 0,
+                  int64_t b_bytes = 0) {
   const int ntm = (g_in.M + BM - 1) / BM;
   const int ncols = (E == Epi::SwigluFwd) ? 2 * g_in.ffn : g_in.N;
   const int ntn = (ncols + BN - 1) / BN;
@@ -407,7 +630,13 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
     S = (g.K + g.kchunk - 1) / g.kchunk;
     g.partial = ws;
   }
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm, ntn);
+  if constexpr (DIRECT) {
+    static_assert(sizeof(T) == 2, "direct loads are bf16 only");
+    hipLaunchKernelGGL((gemm_direct_kernel<BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
+                       ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm, ntn);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t n4 = (static_cast<int64_t>(g.M) * g.N + 3) / 4;
@@ -420,10 +649,21 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
   return hipGetLastError();
 }
 
-// Tile configurations: 0 = 256x256 (8 waves of 128x64), 1 = 128x128 (4 waves of 64x64).
+// Tile configurations: 0 = 256x256 (8 waves of 128x64), 1 = 128x128 (register-staged kernel: 4 waves of
+// 64x64; direct-load kernel: 8 waves of 32x64).
 template <typename T, GemmLayout LAY, Epi E>
 hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t wsb) {
-  if (gemm_tile_config(g.M, (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N) == 0)
+  const int cfg = gemm_tile_config(g.M, (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N);
+  if constexpr (sizeof(T) == 2) {
+    int64_t ab = 0, bb = 0;
+    if (direct_ok<LAY, E>(g, &ab, &bb)) {
+      // 8 waves per block in both shapes: one wave per SIMD (4 waves of
+      // 128x128) leaves no other wave to cover LDS and barrier latency
+      if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, true>(g, s, ws, wsb, ab, bb);
+      return launch<T, 128, 128, 32, 64, LAY, E, true>(g, s, ws, wsb, ab, bb);
+    }
+  }
+  if (cfg == 0)
     return launch<T, 256, 256, 128, 64, LAY, E>(g, s, ws, wsb);
   return launch<T, 128, 128, 64, 64, LAY, E>(g, s, ws, wsb);
 }
