@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsf.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "rowops.hip"]
+HIP_SOURCES = ["gemm.hip", "attention.hip", "attn_direct.hip", "rowops.hip"]
 HOST_SOURCES = ["api.cpp", "engine.cpp", "adam.cpp"]
 
 HIPCC_FLAGS = [

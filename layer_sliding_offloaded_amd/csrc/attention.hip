@@ -583,11 +583,25 @@ hipError_t run_bwd(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t attention_fwd(int dtype, const AttnArgs& a, hipStream_t s) {
+  int64_t qkv_bytes = 0;
+  if (dtype == 1 && attention_direct_ok(a, &qkv_bytes)) return attention_fwd_direct(a, qkv_bytes, s);
   if (dtype == 1) return a.head_dim == 64 ? run_fwd<bf16, 64>(a, s) : run_fwd<bf16, 128>(a, s);
   return a.head_dim == 64 ? run_fwd<float, 64>(a, s) : run_fwd<float, 128>(a, s);
 }
 
 hipError_t attention_bwd(int dtype, const AttnArgs& a, hipStream_t s) {
+  int64_t qkv_bytes = 0;
+  if (dtype == 1 && attention_direct_ok(a, &qkv_bytes) && a.ld_dout % 8 == 0 &&
+      !(reinterpret_cast<uintptr_t>(a.dout) & 15u)) {
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.seq * a.n_heads;
+    if (a.head_dim == 64)
+      hipLaunchKernelGGL((attn_dot_kernel<bf16, 64>), dim3((rows + 255) / 256), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_dot_kernel<bf16, 128>), dim3((rows + 255) / 256), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return attention_bwd_direct(a, qkv_bytes, s);
+  }
   if (dtype == 1) return a.head_dim == 64 ? run_bwd<bf16, 64>(a, s) : run_bwd<bf16, 128>(a, s);
   return a.head_dim == 64 ? run_bwd<float, 64>(a, s) : run_bwd<float, 128>(a, s);
 }
