@@ -80,6 +80,26 @@ def time_gemms(w, sf, torch, reps=20):
     return out
 
 
+def stored_traffic(workload, role):
+    """HBM bytes per launch of a layer GEMM, from the committed rocprofv3
+    counter summary (profiles/gemm_traffic_<workload>.md), or None when there
+    is none or the GEMM source has changed since the counters were taken."""
+    from layer_sliding_offloaded_amd import prof
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    sha, table = None, None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("gemm_source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith("traffic_bytes:"):
+                table = json.loads(line.split(":", 1)[1])
+    if sha != prof.gemm_source_hash() or not table or role not in table:
+        return None
+    return table[role]
+
+
 def cpu_baseline(w, target_s=12.0):
     """The fp64 oracle, as it stands, on one layer fwd+bwd of a bounded slice
     (batch 1) of the workload, repeated until about target_s of CPU work."""
@@ -262,7 +282,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": f"gemm {dom_name} ({['NT', 'NN', 'TN'][dom['layout']]}, "
                                                 f"M={dom['M']} N={dom['N']} K={dom['K']})",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None},
+                     "frac": round(achieved / peak, 4), "traffic": stored_traffic(w.name, dom_name)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

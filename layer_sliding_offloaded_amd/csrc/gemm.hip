@@ -185,13 +185,15 @@ __device__ __forceinline__ void load4(const T* p, float* v) {
 }
 
 // Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
-// contiguous range of tiles, then walk that range in groups of 8 tile-rows so
-// the A rows and B columns a group shares stay in that XCD's L2.
+// contiguous range of tiles, then walk that range in groups of GM tile-rows
+// so the A rows and B columns a group shares stay in that XCD's L2.  With
+// few tiles per XCD (small GEMMs), GM = 4 makes each XCD's range a squarer
+// block of the output (fewer distinct A rows and B columns fetched).
 __device__ __forceinline__ void tile_coords(int ntm, int ntn, int* tm, int* tn) {
   const int ntiles = ntm * ntn;
   int t = blockIdx.x;
   if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
-  constexpr int GM = 8;
+  const int GM = ntiles <= 256 ? 4 : 8;
   const int group = t / (GM * ntn);
   const int first_m = group * GM;
   const int gsize = min(ntm - first_m, GM);

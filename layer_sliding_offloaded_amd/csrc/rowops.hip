@@ -95,13 +95,14 @@ rmsnorm_bwd_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const 
 }
 
 // Gain gradient, stage 1: partial[chunk][j] = sum over the chunk's rows of
-// dout[t, j] * xin[t, j] * r[t].  Thread owns VE adjacent columns.
+// dout[t, j] * xin[t, j] * r[t].  One wave per (column slice, chunk); a lane
+// owns VE adjacent columns.
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64)
 gain_partial_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const float* __restrict__ r,
                     float* __restrict__ partial, int rows, int H, int rows_per_chunk) {
   constexpr int VE = 16 / sizeof(T);
-  const int col = (blockIdx.x * 256 + threadIdx.x) * VE;
+  const int col = (blockIdx.x * 64 + threadIdx.x) * VE;
   const int chunk = blockIdx.y;
   if (col >= H) return;
   float acc[VE];
@@ -122,14 +123,32 @@ gain_partial_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const
   for (int e = 0; e < VE; e += 4) *reinterpret_cast<float4*>(p + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
 }
 
-// Gain gradient, stage 2: dg[j] = sum over chunks (in order) of partial.
+// Gain gradient, stage 2: dg[j] = sum over the chunks of partial, in a fixed
+// order: four groups of consecutive chunks, each summed in order (loads
+// issued eight at a time), then the group sums in order.  Block = 64 columns
+// x 4 groups.
 __global__ void __launch_bounds__(256)
 gain_reduce_kernel(const float* __restrict__ partial, float* __restrict__ dg, int nchunks, int H) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= H) return;
+  __shared__ float part[4][64];
+  const int c64 = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c64;
+  const int per = (nchunks + 3) / 4;
+  const int c0 = grp * per, c1 = min(nchunks, c0 + per);
   float s = 0.f;
-  for (int c = 0; c < nchunks; ++c) s += partial[static_cast<int64_t>(c) * H + j];
-  dg[j] = s;
+  if (j < H) {
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = partial[static_cast<int64_t>(c + u) * H + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; c < c1; ++c) s += partial[static_cast<int64_t>(c) * H + j];
+  }
+  part[grp][c64] = s;
+  __syncthreads();
+  if (grp == 0 && j < H) dg[j] = ((part[0][c64] + part[1][c64]) + part[2][c64]) + part[3][c64];
 }
 
 // x0[t] = E[ids[t]]; an id outside [0, V) yields a NaN row.
@@ -430,21 +449,21 @@ hipError_t rmsnorm_bwd(int dtype, const void* dout, const void* xin, const float
   if (rows <= 0) return hipSuccess;
   const int VE = dtype == 1 ? 8 : 4;
   const int rpc = (rows + nchunks - 1) / nchunks;
-  const dim3 pg((H / VE + 255) / 256, nchunks);
+  const dim3 pg((H / VE + 63) / 64, nchunks);
   if (dtype == 1) {
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s,
                        static_cast<const bf16*>(dout), static_cast<const bf16*>(xin), r, static_cast<const bf16*>(g),
                        static_cast<const bf16*>(resid), static_cast<bf16*>(dx), rows, H);
-    hipLaunchKernelGGL(gain_partial_kernel<bf16>, pg, dim3(256), 0, s, static_cast<const bf16*>(dout),
+    hipLaunchKernelGGL(gain_partial_kernel<bf16>, pg, dim3(64), 0, s, static_cast<const bf16*>(dout),
                        static_cast<const bf16*>(xin), r, partial, rows, H, rpc);
   } else {
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s,
                        static_cast<const float*>(dout), static_cast<const float*>(xin), r, static_cast<const float*>(g),
                        static_cast<const float*>(resid), static_cast<float*>(dx), rows, H);
-    hipLaunchKernelGGL(gain_partial_kernel<float>, pg, dim3(256), 0, s, static_cast<const float*>(dout),
+    hipLaunchKernelGGL(gain_partial_kernel<float>, pg, dim3(64), 0, s, static_cast<const float*>(dout),
                        static_cast<const float*>(xin), r, partial, rows, H, rpc);
   }
-  hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + 255) / 256), dim3(256), 0, s, partial, dg, nchunks, H);
+  hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + 63) / 64), dim3(256), 0, s, partial, dg, nchunks, H);
   return hipGetLastError();
 }
 

@@ -1,0 +1,245 @@
+"""Profiling helpers: HBM traffic of the layer GEMMs from rocprofv3 counters,
+and per-kernel duration summaries of a rocprofv3 kernel trace.
+
+Modes:
+
+* ``probe``: run, once each after a warm-up, a plain device copy of a known
+  size (the calibration kernel) and then every layer GEMM of a workload,
+  launched alone through ``sf_gemm`` exactly as ``bench.py`` times them.
+  Meant to run under ``rocprofv3 --pmc FETCH_SIZE`` and, separately,
+  ``rocprofv3 --pmc WRITE_SIZE``.
+* ``summarize``: read the two counter CSVs, scale each GEMM's counter by
+  (copy bytes / copy counter) -- the factor that turns the counter into
+  bytes on this machine -- and print a markdown table plus the
+  machine-readable lines ``bench.py`` reads.
+* ``kernels``: per (kernel, grid) launch count, total and average duration
+  from a rocprofv3 ``--kernel-trace`` database (``*_results.db``).
+* ``gemm-runs``: from the same database, the average duration of each layer
+  GEMM in ``bench.py``'s own per-GEMM timing loop (to set against the
+  durations ``bench.py`` measures with HIP events).
+
+    python -m layer_sliding_offloaded_amd.prof probe --workload stack4-h1024-bf16
+    python -m layer_sliding_offloaded_amd.prof summarize FETCH_CSV WRITE_CSV --workload stack4-h1024-bf16
+    python -m layer_sliding_offloaded_amd.prof kernels RESULTS_DB [--top N]
+    python -m layer_sliding_offloaded_amd.prof gemm-runs RESULTS_DB --workload W
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 256 << 20
+
+
+def gemm_source_hash():
+    """sha256 of the GEMM kernel source: a stored traffic figure is valid only for it."""
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm.h", "common.h"):
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _gemms(workload):
+    sys.path.insert(0, os.path.dirname(HERE))
+    import bench
+    import seeded_inputs as si
+    return bench.layer_gemms(si.WORKLOADS[workload])
+
+
+def probe(workload):
+    import torch
+
+    from layer_sliding_offloaded_amd import sf
+    sf.load()
+    s = torch.cuda.current_stream()
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    calls = []
+    for name, lay, M, N, K in _gemms(workload):
+        a_shape = (K, M) if lay == 2 else (M, K)
+        b_shape = (N, K) if lay == 0 else (K, N)
+        A = torch.randn(a_shape, device="cuda").to(torch.bfloat16)
+        B = torch.randn(b_shape, device="cuda").to(torch.bfloat16)
+        C = torch.empty((M, N), device="cuda", dtype=torch.float32 if lay == 2 else torch.bfloat16)
+        wsb = sf.sf_gemm_workspace_bytes(M, N, K)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        calls.append((name, (A, B, C, ws),
+                      lambda A=A, B=B, C=C, ws=ws, lay=lay, M=M, N=N, K=K, a=a_shape, b=b_shape, wsb=wsb:
+                      sf.sf_gemm(sf.SF_BF16, lay, 1 if lay == 2 else 0, M, N, K, A.data_ptr(), a[1], B.data_ptr(),
+                                 b[1], C.data_ptr(), N, s.cuda_stream, ws.data_ptr(), wsb)))
+    # warm-up (not counted by the summary: it takes the last launch of each kind)
+    dst.copy_(src)
+    for _, _, f in calls:
+        f()
+    torch.cuda.synchronize()
+    print("probe: copy", flush=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for name, _, f in calls:
+        print("probe:", name, flush=True)
+        f()
+        torch.cuda.synchronize()
+
+
+def _rows(path):
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _dispatches(path, counter):
+    """[(kernel name, value)] in dispatch order for one counter (summed over its instances)."""
+    acc = {}
+    for r in _rows(path):
+        if not r["Counter_Name"].startswith(counter):
+            continue
+        k = int(r["Dispatch_Id"])
+        name, v = acc.get(k, (r["Kernel_Name"], 0.0))
+        acc[k] = (name, v + float(r["Counter_Value"]))
+    return [acc[k] for k in sorted(acc)]
+
+
+def summarize(fetch_csv, write_csv, workload):
+    gemms = _gemms(workload)
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = _dispatches(path, counter)
+        # the measured pass ends the run: the calibration copy, then one
+        # sf_gemm per role (a split-K launch is a GEMM kernel followed by its
+        # reduction); the copy is the dispatch just before that GEMM run
+        idx = len(d) - 1
+        while idx >= 0 and ("gemm" in d[idx][0] or "splitk_reduce" in d[idx][0]):
+            idx -= 1
+        copy_kib = d[idx][1]
+        factor = COPY_BYTES / (copy_kib * 1024.0) if copy_kib > 0 else float("nan")
+        rest = d[idx + 1:]
+        per_role, i = {}, 0
+        for name, lay, M, N, K in gemms:
+            if i >= len(rest):
+                break
+            kib = rest[i][1]
+            i += 1
+            while i < len(rest) and "splitk_reduce" in rest[i][0]:
+                kib += rest[i][1]
+                i += 1
+            per_role[name] = kib
+        out[counter] = (copy_kib, factor, per_role)
+    fk, ff, fr = out["FETCH_SIZE"]
+    wk, wf, wr = out["WRITE_SIZE"]
+    print(f"calibration: {COPY_BYTES} B device copy reads FETCH_SIZE {fk:.0f} KiB (factor {ff:.4f}), "
+          f"WRITE_SIZE {wk:.0f} KiB (factor {wf:.4f})")
+    print()
+    print("| GEMM | layout | M x N x K | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) | "
+          "algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|---|---|")
+    traffic = {}
+    for name, lay, M, N, K in gemms:
+        if name not in fr or name not in wr:
+            continue
+        b = fr[name] * 1024 * ff + wr[name] * 1024 * wf
+        outb = 4 if lay == 2 else 2
+        alg = 2 * (M * K + N * K) + outb * M * N
+        traffic[name] = round(b)
+        print(f"| {name} | {'NT NN TN'.split()[lay]} | {M} x {N} x {K} | {fr[name]:.0f} | {wr[name]:.0f} | "
+              f"{b / 1e6:.1f} MB | {alg / 1e6:.1f} MB | {b / alg:.2f} |")
+    print()
+    print("gemm_source_sha256: " + gemm_source_hash())
+    print("traffic_bytes: " + json.dumps(traffic))
+
+
+def short_name(n):
+    """Kernel name without namespaces, return type and argument list."""
+    n = n.replace("(anonymous namespace)::", "").replace("void ", "").replace("sf::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and i > 0:
+            return n[:i]
+    return n
+
+
+def kernels(db_path, top):
+    """Per (kernel, grid size): launches, total ms, average us, share of the total."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    name_col = "kernel_name" if "kernel_name" in cols else "name"
+    grid = [c for c in ("grid_size", "grid_x") if c in cols]
+    q = f"select {name_col}, start, end" + (", " + ", ".join(c for c in ("grid_x", "grid_y", "grid_z") if c in cols)
+                                            if "grid_x" in cols else "") + " from kernels"
+    agg = {}
+    for row in con.execute(q):
+        key = (short_name(row[0]), tuple(row[3:]))
+        n, t = agg.get(key, (0, 0.0))
+        agg[key] = (n + 1, t + (row[2] - row[1]) / 1e6)
+    total = sum(t for _, t in agg.values())
+    print("| launches | total ms | avg us | % | kernel | grid |")
+    print("|---:|---:|---:|---:|:---|:---|")
+    for (name, g), (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+        print(f"| {n} | {t:.3f} | {1000 * t / n:.2f} | {100 * t / total:.2f} | `{name}` | {'x'.join(map(str, g))} |")
+    print(f"\ntotal kernel time {total:.3f} ms over {sum(n for n, _ in agg.values())} launches")
+
+
+def gemm_runs(db_path, workload, min_run=20):
+    """The per-role GEMM timing loops of bench.py in a kernel trace: maximal
+    runs of >= min_run consecutive launches of one (GEMM kernel, grid),
+    split-K reductions in between counted with the GEMM they finish; the last
+    12 such runs are the 12 roles in bench.py's order."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    name_col = "kernel_name" if "kernel_name" in cols else "name"
+    rows = con.execute(f"select {name_col}, start, end, grid_x, grid_y from kernels order by start").fetchall()
+    runs, cur = [], None
+    for name, t0, t1, gx, gy in rows:
+        sn = short_name(name)
+        if "splitk_reduce" in sn:
+            if cur is not None:
+                cur["reduce"].append((t1 - t0) / 1e3)
+            continue
+        key = (sn, gx, gy)
+        if cur is not None and cur["key"] == key:
+            cur["gemm"].append((t1 - t0) / 1e3)
+        else:
+            if cur is not None and len(cur["gemm"]) >= min_run:
+                runs.append(cur)
+            cur = {"key": key, "gemm": [(t1 - t0) / 1e3], "reduce": []}
+    if cur is not None and len(cur["gemm"]) >= min_run:
+        runs.append(cur)
+    roles = _gemms(workload)
+    runs = runs[-len(roles):]
+    print("| role | kernel | grid | launches | GEMM avg us | split-K reduce avg us | per sf_gemm call us |")
+    print("|---|---|---|---:|---:|---:|---:|")
+    for (name, lay, M, N, K), r in zip(roles, runs):
+        g = sum(r["gemm"]) / len(r["gemm"])
+        red = sum(r["reduce"]) / len(r["reduce"]) if r["reduce"] else 0.0
+        k, gx, gy = r["key"]
+        print(f"| {name} | `{k}` | {gx}x{gy} | {len(r['gemm'])} | {g:.2f} | {red:.2f} | {g + red:.2f} |")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs"])
+    ap.add_argument("files", nargs="*")
+    ap.add_argument("--workload", default="stack4-h1024-bf16")
+    ap.add_argument("--top", type=int, default=30)
+    a = ap.parse_args()
+    if a.mode == "probe":
+        probe(a.workload)
+    elif a.mode == "summarize":
+        summarize(a.files[0], a.files[1], a.workload)
+    elif a.mode == "gemm-runs":
+        gemm_runs(a.files[0], a.workload)
+    else:
+        kernels(a.files[0], a.top)
+
+
+if __name__ == "__main__":
+    main()
