@@ -9,6 +9,7 @@
 // vectorise (AVX2/FMA) and is split across threads in cache-sized chunks.
 #include "adam.h"
 
+#include <immintrin.h>
 #include <sched.h>
 
 #include <algorithm>
@@ -44,32 +45,77 @@ AdamCoef adam_coef(int64_t step, float lr, float b1, float b2, float eps) {
   return c;
 }
 
+namespace {
+
+// 16 elements with the bf16 copy streamed out (non-temporal: the copy is not
+// read again on the host, so it skips the read-for-ownership of its lines).
+// Same operations in the same order as the scalar loop (no contraction), so
+// the results are bitwise identical.
+inline void adam16_bf16_stream(float* p, float* m, float* v, const float* g, uint16_t* pb, const AdamCoef& c) {
+  const __m256 b1 = _mm256_set1_ps(c.b1), b2 = _mm256_set1_ps(c.b2);
+  const __m256 o1 = _mm256_set1_ps(c.one_b1), o2 = _mm256_set1_ps(c.one_b2);
+  const __m256 ib1 = _mm256_set1_ps(c.inv_bc1), ib2 = _mm256_set1_ps(c.inv_bc2);
+  const __m256 lr = _mm256_set1_ps(c.lr), eps = _mm256_set1_ps(c.eps);
+  __m256i bits[2];
+  for (int h = 0; h < 2; ++h) {
+    const __m256 gi = _mm256_loadu_ps(g + 8 * h);
+    const __m256 mi = _mm256_add_ps(_mm256_mul_ps(b1, _mm256_loadu_ps(m + 8 * h)), _mm256_mul_ps(o1, gi));
+    const __m256 vi =
+        _mm256_add_ps(_mm256_mul_ps(b2, _mm256_loadu_ps(v + 8 * h)), _mm256_mul_ps(_mm256_mul_ps(o2, gi), gi));
+    _mm256_storeu_ps(m + 8 * h, mi);
+    _mm256_storeu_ps(v + 8 * h, vi);
+    const __m256 num = _mm256_mul_ps(lr, _mm256_mul_ps(mi, ib1));
+    const __m256 den = _mm256_add_ps(_mm256_sqrt_ps(_mm256_mul_ps(vi, ib2)), eps);
+    const __m256 pi = _mm256_sub_ps(_mm256_loadu_ps(p + 8 * h), _mm256_div_ps(num, den));
+    _mm256_storeu_ps(p + 8 * h, pi);
+    // round to nearest even: b + 0x7FFF + ((b >> 16) & 1), keep the high half
+    const __m256i b = _mm256_castps_si256(pi);
+    const __m256i odd = _mm256_and_si256(_mm256_srli_epi32(b, 16), _mm256_set1_epi32(1));
+    bits[h] = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(b, _mm256_set1_epi32(0x7FFF)), odd), 16);
+  }
+  // packus interleaves 128-bit lanes: [a0-3 b0-3 a4-7 b4-7] -> restore element order
+  const __m256i packed = _mm256_permute4x64_epi64(_mm256_packus_epi32(bits[0], bits[1]), 0xD8);
+  _mm256_stream_si256(reinterpret_cast<__m256i*>(pb), packed);
+}
+
+}  // namespace
+
 void adam_range(float* __restrict p, float* __restrict m, float* __restrict v, const float* __restrict g,
                 uint16_t* __restrict pb, size_t n, const AdamCoef& c) {
   const float b1 = c.b1, b2 = c.b2, o1 = c.one_b1, o2 = c.one_b2;
   const float ib1 = c.inv_bc1, ib2 = c.inv_bc2, lr = c.lr, eps = c.eps;
   if (pb) {
+    // scalar head up to a 32-byte aligned bf16 address, 16-element blocks, scalar tail
+    size_t i0 = 0;
+    while (i0 < n && (reinterpret_cast<uintptr_t>(pb + i0) & 31u)) ++i0;
+    size_t i1 = i0 + (n - i0) / 16 * 16;
+    if (i1 <= i0) i0 = i1 = n;
+    for (size_t i = i0; i < i1; i += 16) adam16_bf16_stream(p + i, m + i, v + i, g + i, pb + i, c);
+    _mm_sfence();
+    auto scalar = [&](size_t a, size_t b) {
+      for (size_t i = a; i < b; ++i) {
+        const float gi = g[i];
+        const float mi = b1 * m[i] + o1 * gi;
+        const float vi = b2 * v[i] + o2 * gi * gi;
+        m[i] = mi;
+        v[i] = vi;
+        const float pi = p[i] - lr * (mi * ib1) / (std::sqrt(vi * ib2) + eps);
+        p[i] = pi;
+        pb[i] = f32_to_bf16(pi);
+      }
+    };
+    scalar(0, i0);
+    scalar(i1, n);
+    return;
+  }
 #pragma GCC ivdep
-    for (size_t i = 0; i < n; ++i) {
-      const float gi = g[i];
-      const float mi = b1 * m[i] + o1 * gi;
-      const float vi = b2 * v[i] + o2 * gi * gi;
-      m[i] = mi;
-      v[i] = vi;
-      const float pi = p[i] - lr * (mi * ib1) / (std::sqrt(vi * ib2) + eps);
-      p[i] = pi;
-      pb[i] = f32_to_bf16(pi);
-    }
-  } else {
-#pragma GCC ivdep
-    for (size_t i = 0; i < n; ++i) {
-      const float gi = g[i];
-      const float mi = b1 * m[i] + o1 * gi;
-      const float vi = b2 * v[i] + o2 * gi * gi;
-      m[i] = mi;
-      v[i] = vi;
-      p[i] = p[i] - lr * (mi * ib1) / (std::sqrt(vi * ib2) + eps);
-    }
+  for (size_t i = 0; i < n; ++i) {
+    const float gi = g[i];
+    const float mi = b1 * m[i] + o1 * gi;
+    const float vi = b2 * v[i] + o2 * gi * gi;
+    m[i] = mi;
+    v[i] = vi;
+    p[i] = p[i] - lr * (mi * ib1) / (std::sqrt(vi * ib2) + eps);
   }
 }
 

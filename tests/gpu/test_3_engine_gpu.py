@@ -170,6 +170,33 @@ def test_device_adam_matches_host_bitwise_and_oracle(dtype):
         assert rel(hp_, p64) <= 1e-6
 
 
+@pytest.mark.parametrize("n,off", [(1, 0), (17, 3), (100_003, 5), (4096, 8)])
+def test_host_adam_vector_path_bitwise(n, off):
+    """The host Adam's 16-wide streamed path, its unaligned head and its tail
+    give the same bits as the device kernel on the same inputs."""
+    say("host-adam-vector", n, off)
+    rng = np.random.default_rng(11 + n)
+    hp = si.ADAM
+    p0 = (rng.standard_normal(n + off) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(n + off) * 10.0 ** rng.uniform(-5, 0, n + off)).astype(np.float32)
+    m0 = (rng.standard_normal(n + off) * 1e-3).astype(np.float32)
+    v0 = (rng.random(n + off) * 1e-5).astype(np.float32)
+    hp_, hm, hv = p0.copy(), m0.copy(), v0.copy()
+    hb = np.zeros(n + off, np.uint16)
+    sf.sf_adam_host(hp_[off:].ctypes.data, hm[off:].ctypes.data, hv[off:].ctypes.data, g[off:].ctypes.data,
+                    hb[off:].ctypes.data, n, 2, hp["lr"], hp["b1"], hp["b2"], hp["eps"], 3)
+    dp, dm, dv = (torch.from_numpy(a[off:].copy()).cuda() for a in (p0, m0, v0))
+    dg = torch.from_numpy(g[off:].copy()).cuda()
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    sf.sf_adam_device(sf.SF_BF16, dp.data_ptr(), dm.data_ptr(), dv.data_ptr(), dg.data_ptr(), out.data_ptr(), n, 2,
+                      hp["lr"], hp["b1"], hp["b2"], hp["eps"], rt.stream_handle())
+    torch.cuda.synchronize()
+    assert np.array_equal(dp.cpu().numpy(), hp_[off:])
+    assert np.array_equal(dm.cpu().numpy(), hm[off:]) and np.array_equal(dv.cpu().numpy(), hv[off:])
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), hb[off:])
+    assert np.array_equal(hp_[:off], p0[:off]) and np.all(hb[:off] == 0)
+
+
 def test_engine_step_matches_oracle():
     w = STACK
     say("engine-vs-oracle", w)
