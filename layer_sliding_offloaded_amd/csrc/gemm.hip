@@ -151,15 +151,16 @@ struct Loader {
   }
 };
 
-// Split-K factor for a grid of `tiles` output tiles: grids that already
-// cover most CUs run unsplit; smaller ones aim for ~384 blocks while keeping
-// every k-range at least 512 deep.
+// Split-K factor for a grid of `tiles` output tiles: grids that cover most
+// CUs run unsplit; smaller ones double the split while the blocks still fit
+// one pass over the 256 CUs and every k-range stays at least 1024 deep
+// (measured: a split of short k-ranges costs more in partial-sum traffic and
+// the reduction than it gains).
 int splitk_factor(int tiles, int K) {
-  if (tiles >= 192) return 1;
-  int S = (384 + tiles - 1) / tiles;
-  S = std::min(S, K / 512);
-  S = std::min(S, 16);
-  return S < 2 ? 1 : S;
+  if (tiles >= 160) return 1;
+  int S = 1;
+  while (S < 8 && tiles * S * 2 <= 256 && K / (S * 2) >= 1024) S *= 2;
+  return S;
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
@@ -492,6 +493,92 @@ __device__ __forceinline__ uint4 frag(const char* region, int rb, int ks, int lr
   }
 }
 
+// ---- k-depth-generic variants for the multi-stage pipeline ----------------
+// [row][k] tiles with BK*2-byte rows: slot XOR by row so the 16 rows of one
+// fragment read hit distinct bank groups (128-byte rows: pairs of rows share
+// a 256-byte bank span; 64-byte rows: groups of four do).
+template <int BK>
+__device__ __forceinline__ int rswzk(int row) {
+  if constexpr (BK == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+
+// Loads of one operand tile (ROWS x BK) for one wave, 1-KB instructions.
+template <int ROWS, int NW, bool KC, int BK>
+struct DirectK {
+  static constexpr int RB = BK * 2;                  // [row][k]: bytes per row
+  static constexpr int RPI = 1024 / RB;              // [row][k]: rows per instruction
+  static constexpr int ROWB = ROWS * 2;              // [k][row]: bytes per k-row
+  static constexpr int KPI = 1024 / ROWB;            // [k][row]: k-rows per instruction
+  static constexpr int NI = ROWS * BK * 2 / 1024;    // instructions per stage
+  static_assert(NI % NW == 0, "tile must split evenly over the waves");
+  static constexpr int JW = NI / NW;
+  uint32_t base[JW];
+  int kl[JW];
+
+  template <typename RowMap>
+  __device__ __forceinline__ void init(int w, int lane, int64_t ld, int r0, int rows, RowMap rowmap) {
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const int idx = j * NW + w;
+      if constexpr (KC) {
+        const int row = idx * RPI + lane / (BK / 8);
+        const int ls = (lane % (BK / 8)) ^ rswzk<BK>(row);
+        const int gr = rowmap(row);
+        base[j] = gr >= 0 ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + ls * 8) * 2) : kOOB;
+        kl[j] = ls * 8;
+      } else {
+        const int b = lane * 16;
+        const int k = idx * KPI + b / ROWB;
+        const int ls = ((b % ROWB) / 16) ^ kswz(k);
+        const int r = r0 + ls * 8;
+        base[j] = r < rows ? static_cast<uint32_t>((static_cast<int64_t>(k) * ld + r) * 2) : kOOB;
+        kl[j] = k;
+      }
+    }
+  }
+  // k0 at or past kend: every lane out of range (the load still counts)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* region, int w, int k0, int kend,
+                                        int64_t ld) {
+    const uint32_t adv = KC ? static_cast<uint32_t>(k0) * 2u : static_cast<uint32_t>(static_cast<int64_t>(k0) * ld * 2);
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const uint32_t off = (base[j] != kOOB && k0 + kl[j] < kend) ? base[j] + adv : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t*)(region + (j * NW + w) * 1024), 16,
+                                               static_cast<int>(off), 0, 0, 0);
+    }
+  }
+};
+
+template <int ROWS, bool KC, int BK>
+__device__ __forceinline__ uint4 fragk(const char* region, int rb, int ks, int lr, int lg) {
+  if constexpr (KC) {
+    const int row = rb + lr;
+    const int slot = (ks * 4 + lg) ^ rswzk<BK>(row);
+    return *reinterpret_cast<const uint4*>(region + row * (BK * 2) + slot * 16);
+  } else {
+    return frag<ROWS, false>(region, rb, ks, lr, lg);
+  }
+}
+
+// s_waitcnt for vector memory only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence: the waits before it are explicit
+// (a fenced barrier would also wait for the loads still in flight into the
+// other stages).  The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Byte extent of a row-major operand with `rows` rows of `cols` used
 // elements at stride ld.
 inline int64_t extent(int64_t rows, int64_t cols, int64_t ld) { return ((rows - 1) * ld + cols) * 2; }
@@ -578,6 +665,103 @@ gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes)
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
+// Multi-stage variant: NS = 4 stages of BK k each, every stage in its own LDS
+// array (so the compiler can see that reading one stage does not alias the
+// loads into another) and the loop unrolled by 4.  The loads of stage kt + 3
+// are issued after the fragment reads of stage kt; the wait at the end of a
+// stage lets the two newer stages stay in flight.
+template <int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
+  using T = bf16;
+  constexpr int NS = 4;
+  constexpr bool AKC = (LAY != GemmLayout::TN);
+  constexpr bool BKC = (LAY == GemmLayout::NT);
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int WGM = BM / WM;
+  constexpr int KS = BK / 32;
+  constexpr int ABYTES = BM * BK * 2;
+  constexpr int STAGE = (BM + BN) * BK * 2;
+  static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
+  __shared__ __attribute__((aligned(1024))) char S0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char S1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char S2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char S3[STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WGM, wn = w / WGM;
+  int tm, tn;
+  tile_coords(ntm, ntn, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), 0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.B), 0, b_bytes, 0x00020000);
+  direct::DirectK<BM, NW, AKC, BK> la;
+  direct::DirectK<BN, NW, BKC, BK> lb;
+  constexpr int JPS = direct::DirectK<BM, NW, AKC, BK>::JW + direct::DirectK<BN, NW, BKC, BK>::JW;
+  la.init(w, lane, g.lda, m0, g.M, [&](int r) { const int m = m0 + r; return m < g.M ? m : -1; });
+  lb.init(w, lane, g.ldb, n0, g.N, [&](int r) { return ColMap<E, WN>::brow(r, n0, g, BN); });
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kbeg = blockIdx.y * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  auto issue = [&](char* st, int kt) {
+    la.issue(ra, st, w, kbeg + kt * BK, kend, g.lda);
+    lb.issue(rb, st + ABYTES, w, kbeg + kt * BK, kend, g.ldb);
+  };
+  const int lr = lane % 16, lg = lane / 16;
+  auto body = [&](int kt, const char* cur, char* nxt) {
+    uint4 af[KS][FM], bfr[KS][FN];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[ks][i] = direct::fragk<BM, AKC, BK>(cur, wm * WM + i * 16, ks, lr, lg);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[ks][j] = direct::fragk<BN, BKC, BK>(cur + ABYTES, wn * WN + j * 16, ks, lr, lg);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue(nxt, kt + NS - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[ks][j], af[ks][i]);
+    // stage kt + 1 complete; stages kt + 2, kt + 3 may still be loading
+    direct::wait_vm<(NS - 2) * JPS>();
+    direct::bar();
+  };
+
+  if (nk > 0) {
+    issue(S0, 0);
+    issue(S1, 1);
+    issue(S2, 2);
+    direct::wait_vm<(NS - 2) * JPS>();
+    direct::bar();
+    for (int kt = 0; kt < nk; kt += NS) {
+      body(kt, S0, S3);
+      if (kt + 1 < nk) body(kt + 1, S1, S0);
+      if (kt + 2 < nk) body(kt + 2, S2, S1);
+      if (kt + 3 < nk) body(kt + 3, S3, S2);
+    }
+    direct::wait_vm<0>();  // no load into LDS outlives the block
+  }
+
+  epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
+}
+
 // out[m, n] = sum over s (in order) of partial[s][m][n]; 4 columns per thread.
 template <typename TO>
 __global__ void __launch_bounds__(256)
@@ -613,7 +797,9 @@ bool direct_ok(const GemmArgs& g, int64_t* a_bytes, int64_t* b_bytes) {
   return *a_bytes > 0 && *b_bytes > 0 && *a_bytes < lim && *b_bytes < lim;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, bool DIRECT = false>
+// KIND 0: register-staged kernel; 1: direct loads, 2 stages of 64 k; 2: direct
+// loads, 4 stages of BK k.
+template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, int KIND = 0, int BK = 64>
 hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_bytes, int64_t a_bytes = 0,
                   int64_t b_bytes = 0) {
   const int ntm = (g_in.M + BM - 1) / BM;
@@ -632,7 +818,11 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
     S = (g.K + g.kchunk - 1) / g.kchunk;
     g.partial = ws;
   }
-  if constexpr (DIRECT) {
+  if constexpr (KIND == 2) {
+    static_assert(sizeof(T) == 2, "direct loads are bf16 only");
+    hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, WM, WN, BK, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
+                       ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
+  } else if constexpr (KIND == 1) {
     static_assert(sizeof(T) == 2, "direct loads are bf16 only");
     hipLaunchKernelGGL((gemm_direct_kernel<BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
                        ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
@@ -659,10 +849,15 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
   if constexpr (sizeof(T) == 2) {
     int64_t ab = 0, bb = 0;
     if (direct_ok<LAY, E>(g, &ab, &bb)) {
-      // 8 waves per block in both shapes: one wave per SIMD (4 waves of
-      // 128x128) leaves no other wave to cover LDS and barrier latency
-      if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, true>(g, s, ws, wsb, ab, bb);
-      return launch<T, 128, 128, 32, 64, LAY, E, true>(g, s, ws, wsb, ab, bb);
+      // Measured choices: large grids take 4 stages of 32 k (256x256, 8 waves
+      // of 128x64); grids of 128x128 tiles take 4 stages of 64 k with 8
+      // waves of 32x64, or 2 stages when there are enough tiles to keep
+      // every CU busy without a deep pipeline.
+      if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, 2, 32>(g, s, ws, wsb, ab, bb);
+      const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
+      const long t128 = static_cast<long>((g.M + 127) / 128) * ((ncols + 127) / 128);
+      if (t128 >= 320) return launch<T, 128, 128, 32, 64, LAY, E, 1>(g, s, ws, wsb, ab, bb);
+      return launch<T, 128, 128, 32, 64, LAY, E, 2, 64>(g, s, ws, wsb, ab, bb);
     }
   }
   if (cfg == 0)

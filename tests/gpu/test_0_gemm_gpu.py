@@ -14,7 +14,9 @@ pytestmark = pytest.mark.gpu
 
 # the last two have few output tiles and a long K: split-K applies when a workspace is given
 SHAPES = [(128, 256, 64), (200, 688, 256), (1000, 520, 1376), (37, 8, 8), (4096, 1024, 520), (300, 3072, 2048),
-          (512, 1024, 32000), (1024, 1024, 2600)]
+          (512, 1024, 32000), (1024, 1024, 2600),
+          # >= 256 tiles of 256 x 256: the large-grid kernels, ragged in M, N and K (K % 32 = 8)
+          (4104, 4112, 1000)]
 
 
 @pytest.mark.parametrize("layout", [0, 1, 2], ids=["NT", "NN", "TN"])
