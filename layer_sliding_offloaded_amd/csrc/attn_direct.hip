@@ -54,10 +54,6 @@ __device__ __forceinline__ int tswz(int r) {
   else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
-__device__ __forceinline__ uint32_t pk2(int16_t lo, int16_t hi) {
-  return static_cast<uint16_t>(lo) | (static_cast<uint32_t>(static_cast<uint16_t>(hi)) << 16);
-}
-
 __device__ __forceinline__ uint4 pack8(const f32x4& a, const f32x4& b) {
   return make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3]));
 }
@@ -106,41 +102,47 @@ struct TileLoad {
   }
 };
 
-// A-operand fragment along d from a kind-0 tile: rows rb.. (16), d-chunk c
-// (32 wide): lane gets 8 consecutive d of row rb + lr.
-__device__ __forceinline__ uint4 frag_d(const char* t, int rb, int c, int lr, int lg) {
-  const int r = rb + lr;
-  const int slot = ((c & 1) * 4 + lg) ^ rswz(r);
-  return *reinterpret_cast<const uint4*>(t + (c >> 1) * 8192 + r * 128 + slot * 16);
-}
+// Fragment reads.  Every address splits into a lane part, fixed for the
+// whole kernel and computed once (the ofs_* helpers), and a part that is a
+// compile-time constant of the unrolled loops (16-row group, k-chunk), which
+// the LDS instructions take as an immediate offset.  The swizzles depend on a
+// row's low four bits only, and every fragment starts on a 16-row boundary,
+// so the lane part is the same for every fragment of a tile.
 
-// A-operand fragment along the sequence from a kind-1 tile [row][D]: output
-// rows = d (16 from db), k = tile rows {32 j + 4 lg .. +3} and
-// {32 j + 16 + 4 lg .. +3} -- the order in which a lane holds its
-// probabilities (pack8 of fragments 2j, 2j+1).
+// kind-0 tile ([row][64-d blocks]), A operand along d: rows rb + lr, d-chunk c
+// (32 wide, lane gets d 32c + 8 lg ..).  Full offset = ofs + rb * 128.
+__device__ __forceinline__ int ofs_d0(int c, int lr, int lg) {
+  return (c >> 1) * 8192 + lr * 128 + ((((c & 1) * 4 + lg) ^ rswz(lr)) * 16);
+}
+// kind-1 tile ([row][D]), A operand along d.  Full offset = ofs + rb * D * 2.
 template <int D>
-__device__ __forceinline__ uint4 frag_t(const char* t, int db, int j, int lr, int lg) {
+__device__ __forceinline__ int ofs_d1(int c, int lr, int lg) {
+  return lr * (D * 2) + (((c * 4 + lg) ^ tswz<D>(lr)) * 16);
+}
+// kind-1 tile read transposed: output rows d = db + (0..15), k = tile rows
+// {32 j + 4 lg .. +3} (h = 0) and {32 j + 16 + 4 lg .. +3} (h = 1) -- the
+// order in which a lane holds its probabilities (pack8 of fragments 2j,
+// 2j+1).  Full offset = ofs + (32 j + 16 h) * D * 2.
+template <int D>
+__device__ __forceinline__ int ofs_t(int db, int lr, int lg) {
+  const int rl = 4 * lg + (lr >> 2);  // row within the 16-row group this lane addresses
   const int d = db + 4 * (lr & 3);
-  const int slot = d >> 3, half = (d >> 2) & 1;
-  uint32_t w[4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 32 * j + 16 * h + 4 * lg + (lr >> 2);
-    const char* p = t + r * (D * 2) + ((slot ^ tswz<D>(r)) * 16) + half * 8;
-    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<char*>(p)));
-    w[2 * h] = pk2(v[0], v[1]);
-    w[2 * h + 1] = pk2(v[2], v[3]);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return rl * (D * 2) + (((d >> 3) ^ tswz<D>(rl)) * 16) + ((d >> 2) & 1) * 8;
 }
 
-// A-operand fragment along d from a kind-1 tile [row][D]: rows rb.. (16),
-// d-chunk c (32 wide): lane gets 8 consecutive d of row rb + lr.
+__device__ __forceinline__ uint4 lds16(const char* t, int off) {
+  return *reinterpret_cast<const uint4*>(t + off);
+}
+__device__ __forceinline__ uint4 lds_tr(const char* t, int off0, int off1) {
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<char*>(t) + off0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<char*>(t) + off1));
+  const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+  return make_uint4(x.x, x.y, y.x, y.y);
+}
+// transposed fragment j of a kind-1 tile for the lane offset o (from ofs_t)
 template <int D>
-__device__ __forceinline__ uint4 frag_d1(const char* t, int rb, int c, int lr, int lg) {
-  const int r = rb + lr;
-  const int slot = (c * 4 + lg) ^ tswz<D>(r);
-  return *reinterpret_cast<const uint4*>(t + r * (D * 2) + slot * 16);
+__device__ __forceinline__ uint4 frag_t(const char* t, int o, int j) {
+  return lds_tr(t, o + 32 * j * (D * 2), o + (32 * j + 16) * (D * 2));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
@@ -200,6 +202,11 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
   float lsum[2] = {0.f, 0.f};
   const float sc = a.scale * kLog2e;
   const int nkv = (min(q0 + BQ, S) - 1) / BKV + 1;
+  int ko[DC], vo[FD];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) ko[c] = ofs_d0(c, lr, lg);
+#pragma unroll
+  for (int d = 0; d < FD; ++d) vo[d] = ofs_t<D>(d * 16, lr, lg);
 
   lk.issue(rs, K0, w, S, 0);
   lv.issue(rs, V0, w, S, 0);
@@ -224,45 +231,55 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
       for (int c = 0; c < DC; ++c) {
         uint4 kf[4];
 #pragma unroll
-        for (int fk = 0; fk < 4; ++fk) kf[fk] = frag_d(Kc, fk * 16, c, lr, lg);
+        for (int fk = 0; fk < 4; ++fk) kf[fk] = lds16(Kc, ko[c] + fk * 16 * 128);
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
           for (int fk = 0; fk < 4; ++fk) Mfma<bf16>::run(s[f][fk], kf[fk], qf[f][c]);
       }
-      const bool diag = (kv0 + BKV - 1 > qw);
+      // raw scores are scaled inside the exponent: p = 2^(s sc - m), with the
+      // running maximum m kept in scaled units (sc > 0)
+      if (kv0 + BKV - 1 > qw) {  // diagonal tile: mask keys after the row
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int fk = 0; fk < 4; ++fk)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (kv0 + fk * 16 + lg * 4 + v > qw + f * 16 + lr) s[f][fk][v] = -INFINITY;
+      }
+      float alpha[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        const int q = qw + f * 16 + lr;
         float mx = -INFINITY;
 #pragma unroll
         for (int fk = 0; fk < 4; ++fk)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float x = s[f][fk][v] * sc;
-            if (diag && kv0 + fk * 16 + lg * 4 + v > q) x = -INFINITY;
-            s[f][fk][v] = x;
-            mx = fmaxf(mx, x);
-          }
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[f][fk][v]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrow[f], mx);
-        const float alpha = exp2f(mrow[f] - mnew);
+        const float mnew = fmaxf(mrow[f], mx * sc);
+        alpha[f] = __builtin_amdgcn_exp2f(mrow[f] - mnew);
         mrow[f] = mnew;
         float ps = 0.f;
 #pragma unroll
         for (int fk = 0; fk < 4; ++fk)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float p = exp2f(s[f][fk][v] - mnew);
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[f][fk][v], sc, -mnew));
             s[f][fk][v] = p;
             ps += p;
           }
-        lsum[f] = lsum[f] * alpha + ps;
+        lsum[f] = lsum[f] * alpha[f] + ps;
+      }
+      // rescale the output only when some row's maximum moved
+      if (!__all(alpha[0] == 1.0f && alpha[1] == 1.0f)) {
 #pragma unroll
-        for (int d = 0; d < FD; ++d)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) oacc[f][d][v] *= alpha;
+          for (int d = 0; d < FD; ++d)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) oacc[f][d][v] *= alpha[f];
       }
       // O^T += V^T P^T: lane holds O[q = qw + 16 f + lr][d = 16 fd + 4 lg + v]
 #pragma unroll
@@ -271,7 +288,7 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
         const uint4 pf1 = pack8(s[1][2 * j], s[1][2 * j + 1]);
 #pragma unroll
         for (int d = 0; d < FD; ++d) {
-          const uint4 vf = frag_t<D>(Vc, d * 16, j, lr, lg);
+          const uint4 vf = frag_t<D>(Vc, vo[d], j);
           Mfma<bf16>::run(oacc[0][d], vf, pf0);
           Mfma<bf16>::run(oacc[1][d], vf, pf1);
         }
@@ -407,6 +424,12 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
     }
   };
 
+  int dof[DC], tof[FD];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) dof[c] = ofs_d1<D>(c, lr, lg);
+#pragma unroll
+  for (int d = 0; d < FD; ++d) tof[d] = ofs_t<D>(d * 16, lr, lg);
+
   auto step = [&](int it, const char* Qc, const char* Oc, const float* Lc, char* Qn, char* On, float* Ln) {
     if (it + 1 < nit) issue(it + 1, Qn, On, Ln);
     const int q0 = (qt0 + it % per_head) * BQ;
@@ -421,14 +444,16 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
       for (int c = 0; c < DC; ++c)
 #pragma unroll
         for (int fq = 0; fq < 4; ++fq) {
-          const uint4 qa = frag_d1<D>(Qc, fq * 16, c, lr, lg);
-          const uint4 da = frag_d1<D>(Oc, fq * 16, c, lr, lg);
+          const uint4 qa = lds16(Qc, dof[c] + fq * 16 * (D * 2));
+          const uint4 da = lds16(Oc, dof[c] + fq * 16 * (D * 2));
 #pragma unroll
           for (int fk = 0; fk < 2; ++fk) {
             Mfma<bf16>::run(p[fk][fq], qa, kf[fk][c]);
             Mfma<bf16>::run(dp[fk][fq], da, vf[fk][c]);
           }
         }
+      // keys after a query, or queries past the end, only near the diagonal / tail
+      const bool masked = (kvw + 31 > q0) || (q0 + BQ > S);
 #pragma unroll
       for (int fq = 0; fq < 4; ++fq) {
         const float4 lse4 = *reinterpret_cast<const float4*>(Lc + fq * 16 + lg * 4);
@@ -441,8 +466,8 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int q = q0 + fq * 16 + lg * 4 + v;
-            float pv = exp2f(p[fk][fq][v] * sc - lse[v]);
-            if (kv > q || q >= S) pv = 0.f;
+            float pv = __builtin_amdgcn_exp2f(fmaf(p[fk][fq][v], sc, -lse[v]));
+            if (masked && (kv > q || q >= S)) pv = 0.f;
             p[fk][fq][v] = pv;
             dp[fk][fq][v] = pv * (dp[fk][fq][v] - dsm[v]);  // dS
           }
@@ -459,8 +484,8 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
         }
 #pragma unroll
         for (int d = 0; d < FD; ++d) {
-          const uint4 oa = frag_t<D>(Oc, d * 16, j, lr, lg);
-          const uint4 qa = frag_t<D>(Qc, d * 16, j, lr, lg);
+          const uint4 oa = frag_t<D>(Oc, tof[d], j);
+          const uint4 qa = frag_t<D>(Qc, tof[d], j);
 #pragma unroll
           for (int fk = 0; fk < 2; ++fk) {
             Mfma<bf16>::run(dv[fk][d], oa, pb[fk]);
@@ -560,6 +585,11 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
     for (int d = 0; d < FD; ++d) dq[f][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc = a.scale * kLog2e;
   const int nkv = (min(q0 + BQ, S) - 1) / BKV + 1;
+  int dof[DC], tof[FD];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) dof[c] = ofs_d1<D>(c, lr, lg);
+#pragma unroll
+  for (int d = 0; d < FD; ++d) tof[d] = ofs_t<D>(d * 16, lr, lg);
 
   lk.issue(rs, K0, w, S, 0);
   lv.issue(rs, V0, w, S, 0);
@@ -584,14 +614,15 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
       for (int c = 0; c < DC; ++c)
 #pragma unroll
         for (int fk = 0; fk < 4; ++fk) {
-          const uint4 ka = frag_d1<D>(Kc, fk * 16, c, lr, lg);
-          const uint4 va = frag_d1<D>(Vc, fk * 16, c, lr, lg);
+          const uint4 ka = lds16(Kc, dof[c] + fk * 16 * (D * 2));
+          const uint4 va = lds16(Vc, dof[c] + fk * 16 * (D * 2));
 #pragma unroll
           for (int f = 0; f < 2; ++f) {
             Mfma<bf16>::run(s[f][fk], ka, qf[f][c]);
             Mfma<bf16>::run(dp[f][fk], va, df[f][c]);
           }
         }
+      const bool masked = (kv0 + BKV - 1 > qw) || (kv0 + BKV > S);
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         const int q = qw + f * 16 + lr;
@@ -600,8 +631,8 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int kv = kv0 + fk * 16 + lg * 4 + v;
-            float pv = exp2f(s[f][fk][v] * sc - lse[f]);
-            if (kv > q || kv >= S) pv = 0.f;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[f][fk][v], sc, -lse[f]));
+            if (masked && (kv > q || kv >= S)) pv = 0.f;
             s[f][fk][v] = pv * (dp[f][fk][v] - dsm[f]);  // dS
           }
       }
@@ -612,7 +643,7 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
         const uint4 sb1 = pack8(s[1][2 * j], s[1][2 * j + 1]);
 #pragma unroll
         for (int d = 0; d < FD; ++d) {
-          const uint4 ka = frag_t<D>(Kc, d * 16, j, lr, lg);
+          const uint4 ka = frag_t<D>(Kc, tof[d], j);
           Mfma<bf16>::run(dq[0][d], ka, sb0);
           Mfma<bf16>::run(dq[1][d], ka, sb1);
         }

@@ -9,20 +9,20 @@ namespace sf {
 
 // ----------------------------------------------------------------- bf16
 // bf16 is stored as raw uint16_t.  Conversion to fp32 is exact; conversion
-// from fp32 rounds to nearest, ties to even (inputs are finite).
+// from fp32 rounds to nearest, ties to even -- gfx950 does it in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction).
 struct bf16 { uint16_t u; };
+
+typedef __attribute__((ext_vector_type(2))) __bf16 hw_bf16x2;
 
 __device__ __forceinline__ float bf2f(uint16_t u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t b = __float_as_uint(f);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return static_cast<uint16_t>(b >> 16);
-}
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+  const hw_bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return static_cast<uint16_t>(pack2(f, 0.0f)); }
 
 // Element traits: the storage type of activations and weights.
 template <typename T> struct Elem;

@@ -856,7 +856,10 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
       if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, 2, 32>(g, s, ws, wsb, ab, bb);
       const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
       const long t128 = static_cast<long>((g.M + 127) / 128) * ((ncols + 127) / 128);
-      if (t128 >= 320) return launch<T, 128, 128, 32, 64, LAY, E, 1>(g, s, ws, wsb, ab, bb);
+      if (t128 >= 320) {
+        if constexpr (LAY == GemmLayout::TN) return launch<T, 128, 128, 64, 64, LAY, E, 2, 32>(g, s, ws, wsb, ab, bb);
+        return launch<T, 128, 128, 32, 64, LAY, E, 1>(g, s, ws, wsb, ab, bb);
+      }
       return launch<T, 128, 128, 32, 64, LAY, E, 2, 64>(g, s, ws, wsb, ab, bb);
     }
   }
