@@ -345,15 +345,15 @@ __device__ __forceinline__ void store4bf(bf16* p, const f32x4& v) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Block: 4 waves x 32 keys of one (b, KV head); loops over every query head
+// Block: NWV waves x 16 KF keys of one (b, KV head); loops over every query head
 // of the group and every 64-query tile at or after its first key.  Q and dO
 // tiles (kind 1) serve both the score recompute (along d) and the dK / dV
 // products (transposed, along the queries); log-sum-exp and D of the tile's
 // queries are staged next to them.
-template <int D>
-__global__ void __launch_bounds__(256)
+template <int D, int KF, int NWV>
+__global__ void __launch_bounds__(NWV * 64)
 attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes) {
-  constexpr int BKV = 128, BQ = 64, NW = 4;
+  constexpr int KW = 16 * KF, BKV = NWV * KW, BQ = 64, NW = NWV;
   constexpr int DC = D / 32;
   constexpr int FD = D / 16;
   constexpr int TB = BQ * D * 2;
@@ -372,7 +372,7 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
   const int64_t ld = a.ld_qkv;
   const int64_t bs = static_cast<int64_t>(b) * S;
   const int kv0 = blockIdx.x * BKV;  // block 0 holds the earliest keys, which see the most queries
-  const int kvw = kv0 + w * 32;
+  const int kvw = kv0 + w * KW;
   const int group = a.n_heads / a.n_kv;
 
   const __amdgpu_buffer_rsrc_t rq = rsrc(a.qkv, qkv_bytes);
@@ -382,9 +382,9 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
 
   // K, V fragments (B operand): lane supplies row kvw + 16 fk + lr, d-chunk lg
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
-  uint4 kf[2][DC], vf[2][DC];
+  uint4 kf[KF][DC], vf[KF][DC];
 #pragma unroll
-  for (int fk = 0; fk < 2; ++fk) {
+  for (int fk = 0; fk < KF; ++fk) {
     const int kv = kvw + fk * 16 + lr;
     const bf16* kr = qkv + (bs + kv) * ld + (a.n_heads + kvh) * D;
     const bf16* vr = qkv + (bs + kv) * ld + (a.n_heads + a.n_kv + kvh) * D;
@@ -394,9 +394,9 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
       vf[fk][c] = kv < S ? *reinterpret_cast<const uint4*>(vr + c * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
     }
   }
-  f32x4 dk[2][FD], dv[2][FD];
+  f32x4 dk[KF][FD], dv[KF][FD];
 #pragma unroll
-  for (int fk = 0; fk < 2; ++fk)
+  for (int fk = 0; fk < KF; ++fk)
 #pragma unroll
     for (int d = 0; d < FD; ++d) { dk[fk][d] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[fk][d] = f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -435,9 +435,9 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
     const int q0 = (qt0 + it % per_head) * BQ;
     if (q0 + BQ - 1 >= kvw) {
       // P^T, dP^T: lane holds X[q = q0 + 16 fq + 4 lg + v][kv = kvw + 16 fk + lr]
-      f32x4 p[2][4], dp[2][4];
+      f32x4 p[KF][4], dp[KF][4];
 #pragma unroll
-      for (int fk = 0; fk < 2; ++fk)
+      for (int fk = 0; fk < KF; ++fk)
 #pragma unroll
         for (int fq = 0; fq < 4; ++fq) { p[fk][fq] = f32x4{0.f, 0.f, 0.f, 0.f}; dp[fk][fq] = f32x4{0.f, 0.f, 0.f, 0.f}; }
 #pragma unroll
@@ -447,13 +447,13 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
           const uint4 qa = lds16(Qc, dof[c] + fq * 16 * (D * 2));
           const uint4 da = lds16(Oc, dof[c] + fq * 16 * (D * 2));
 #pragma unroll
-          for (int fk = 0; fk < 2; ++fk) {
+          for (int fk = 0; fk < KF; ++fk) {
             Mfma<bf16>::run(p[fk][fq], qa, kf[fk][c]);
             Mfma<bf16>::run(dp[fk][fq], da, vf[fk][c]);
           }
         }
       // keys after a query, or queries past the end, only near the diagonal / tail
-      const bool masked = (kvw + 31 > q0) || (q0 + BQ > S);
+      const bool masked = (kvw + KW - 1 > q0) || (q0 + BQ > S);
 #pragma unroll
       for (int fq = 0; fq < 4; ++fq) {
         const float4 lse4 = *reinterpret_cast<const float4*>(Lc + fq * 16 + lg * 4);
@@ -461,7 +461,7 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
         const float lse[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
         const float dsm[4] = {dsm4.x, dsm4.y, dsm4.z, dsm4.w};
 #pragma unroll
-        for (int fk = 0; fk < 2; ++fk) {
+        for (int fk = 0; fk < KF; ++fk) {
           const int kv = kvw + fk * 16 + lr;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -476,9 +476,9 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
       // dV^T += dO^T P, dK^T += Q^T dS: lane holds X[kv][d = 16 fd + 4 lg + v]
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        uint4 pb[2], sb[2];
+        uint4 pb[KF], sb[KF];
 #pragma unroll
-        for (int fk = 0; fk < 2; ++fk) {
+        for (int fk = 0; fk < KF; ++fk) {
           pb[fk] = pack8(p[fk][2 * j], p[fk][2 * j + 1]);
           sb[fk] = pack8(dp[fk][2 * j], dp[fk][2 * j + 1]);
         }
@@ -487,7 +487,7 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
           const uint4 oa = frag_t<D>(Oc, tof[d], j);
           const uint4 qa = frag_t<D>(Qc, tof[d], j);
 #pragma unroll
-          for (int fk = 0; fk < 2; ++fk) {
+          for (int fk = 0; fk < KF; ++fk) {
             Mfma<bf16>::run(dv[fk][d], oa, pb[fk]);
             Mfma<bf16>::run(dk[fk][d], qa, sb[fk]);
           }
@@ -507,7 +507,7 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
   }
 
 #pragma unroll
-  for (int fk = 0; fk < 2; ++fk) {
+  for (int fk = 0; fk < KF; ++fk) {
     const int kv = kvw + fk * 16 + lr;
     if (kv >= S) continue;
 #pragma unroll
@@ -526,12 +526,12 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
 }
 
 // -------------------------------------------------------------------- dQ
-// Block: 4 waves x 32 queries of one (b, h); key tiles of 64 (kind 1: the
+// Block: NWV waves x 16 F queries of one (b, h); key tiles of 64 (kind 1: the
 // score recompute reads K and V along d, the dQ product reads K transposed).
-template <int D>
-__global__ void __launch_bounds__(256)
+template <int D, int F, int NWV>
+__global__ void __launch_bounds__(NWV * 64)
 attn_dq_direct(const AttnArgs a, int qkv_bytes) {
-  constexpr int BQ = 128, BKV = 64, NW = 4;
+  constexpr int QW = 16 * F, BQ = NWV * QW, BKV = 64, NW = NWV;
   constexpr int DC = D / 32;
   constexpr int FD = D / 16;
   constexpr int TB = BKV * D * 2;
@@ -551,7 +551,7 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
   const int64_t ld = a.ld_qkv;
   const int64_t bs = static_cast<int64_t>(b) * S;
   const int q0 = qt * BQ;
-  const int qw = q0 + w * 32;
+  const int qw = q0 + w * QW;
 
   const __amdgpu_buffer_rsrc_t rs = rsrc(a.qkv, qkv_bytes);
   TileLoad<D, NW, 1> lk, lv;
@@ -561,11 +561,11 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
   // Q, dO fragments (B operand) and the rows' statistics
   const bf16* qbase = static_cast<const bf16*>(a.qkv) + bs * ld + h * D;
   const bf16* dbase = static_cast<const bf16*>(a.dout) + bs * a.ld_dout + h * D;
-  uint4 qf[2][DC], df[2][DC];
-  float lse[2], dsm[2];
+  uint4 qf[F][DC], df[F][DC];
+  float lse[F], dsm[F];
   const int64_t srow = (static_cast<int64_t>(b) * a.n_heads + h) * S;
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < F; ++f) {
     const int q = qw + f * 16 + lr;
     const bool ok = q < S;
 #pragma unroll
@@ -578,9 +578,9 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
     lse[f] = ok ? a.lse[srow + q] : 0.f;
     dsm[f] = ok ? a.dsum[srow + q] : 0.f;
   }
-  f32x4 dq[2][FD];
+  f32x4 dq[F][FD];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int d = 0; d < FD; ++d) dq[f][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc = a.scale * kLog2e;
@@ -603,11 +603,11 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
       lk.issue(rs, Kn, w, S - kv0 - BKV, adv);
       lv.issue(rs, Vn, w, S - kv0 - BKV, adv);
     }
-    if (kv0 <= qw + 31) {
+    if (kv0 <= qw + QW - 1) {
       // S, dP: lane holds X[q = qw + 16 f + lr][kv = kv0 + 16 fk + 4 lg + v]
-      f32x4 s[2][4], dp[2][4];
+      f32x4 s[F][4], dp[F][4];
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < F; ++f)
 #pragma unroll
         for (int fk = 0; fk < 4; ++fk) { s[f][fk] = f32x4{0.f, 0.f, 0.f, 0.f}; dp[f][fk] = f32x4{0.f, 0.f, 0.f, 0.f}; }
 #pragma unroll
@@ -617,14 +617,14 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
           const uint4 ka = lds16(Kc, dof[c] + fk * 16 * (D * 2));
           const uint4 va = lds16(Vc, dof[c] + fk * 16 * (D * 2));
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
+          for (int f = 0; f < F; ++f) {
             Mfma<bf16>::run(s[f][fk], ka, qf[f][c]);
             Mfma<bf16>::run(dp[f][fk], va, df[f][c]);
           }
         }
       const bool masked = (kv0 + BKV - 1 > qw) || (kv0 + BKV > S);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < F; ++f) {
         const int q = qw + f * 16 + lr;
 #pragma unroll
         for (int fk = 0; fk < 4; ++fk)
@@ -639,13 +639,14 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
       // dQ^T += K^T dS^T: lane holds dQ[q = qw + 16 f + lr][d = 16 fd + 4 lg + v]
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint4 sb0 = pack8(s[0][2 * j], s[0][2 * j + 1]);
-        const uint4 sb1 = pack8(s[1][2 * j], s[1][2 * j + 1]);
+        uint4 sb[F];
+#pragma unroll
+        for (int f = 0; f < F; ++f) sb[f] = pack8(s[f][2 * j], s[f][2 * j + 1]);
 #pragma unroll
         for (int d = 0; d < FD; ++d) {
           const uint4 ka = frag_t<D>(Kc, tof[d], j);
-          Mfma<bf16>::run(dq[0][d], ka, sb0);
-          Mfma<bf16>::run(dq[1][d], ka, sb1);
+#pragma unroll
+          for (int f = 0; f < F; ++f) Mfma<bf16>::run(dq[f][d], ka, sb[f]);
         }
       }
     }
@@ -658,7 +659,7 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
   }
 
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < F; ++f) {
     const int q = qw + f * 16 + lr;
     if (q >= S) continue;
 #pragma unroll
@@ -677,12 +678,19 @@ hipError_t run_bwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
   const int64_t T = static_cast<int64_t>(a.batch) * a.seq;
   const int64_t dout_bytes = ((T - 1) * a.ld_dout + static_cast<int64_t>(a.n_heads) * D) * 2;
   const int64_t stat_bytes = static_cast<int64_t>(a.batch) * a.n_heads * a.seq * 4;
-  hipLaunchKernelGGL((attn_dkdv_direct<D>), dim3((a.seq + 127) / 128, a.n_kv, a.batch), dim3(256), 0, s, a,
+  // Block shapes (measured; every shape gives the same bits): dK/dV with 4
+  // waves of 16 keys; dQ with 8 waves of 32 queries when that still makes
+  // two blocks per CU, else 8 waves of 16.
+  hipLaunchKernelGGL((attn_dkdv_direct<D, 1, 4>), dim3((a.seq + 63) / 64, a.n_kv, a.batch), dim3(256), 0, s, a,
                      static_cast<int>(qkv_bytes), static_cast<int>(dout_bytes), static_cast<int>(stat_bytes));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_dq_direct<D>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(256), 0, s, a,
-                     static_cast<int>(qkv_bytes));
+  if (static_cast<int64_t>((a.seq + 255) / 256) * a.n_heads * a.batch >= 512)
+    hipLaunchKernelGGL((attn_dq_direct<D, 2, 8>), dim3((a.seq + 255) / 256, a.n_heads, a.batch), dim3(512), 0, s, a,
+                       static_cast<int>(qkv_bytes));
+  else
+    hipLaunchKernelGGL((attn_dq_direct<D, 1, 8>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(512), 0, s, a,
+                       static_cast<int>(qkv_bytes));
   return hipGetLastError();
 }
 
