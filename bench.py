@@ -149,6 +149,9 @@ def main():
     ap.add_argument("--no-adam", action="store_true",
                     help="stream gradients out but skip the optimizer (default for the 123B-shaped slice, whose "
                          "fp32 Adam states would need 133 GB of host memory)")
+    ap.add_argument("--ckpt", action="store_true",
+                    help="sliding activation checkpointing: layer inputs wait in pinned host memory and each "
+                         "layer's forward is recomputed before its backward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the layer-sliding step is a "
@@ -180,7 +183,8 @@ def main():
     if w.vocab:
         head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
     eng = rt.Engine(w, layers, head, window=w.window, n_grad_slots=2, adam=adam, chunk=2048,
-                    adam_threads=args.adam_threads)
+                    adam_threads=args.adam_threads, ckpt=args.ckpt)
+    hbm = {"unit_pool_bytes": eng.pool.numel(), "activation_bytes": eng.act_bytes}
     print(f"[bench] engine ready ({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr, flush=True)
     if head is not None:
         d_in = torch.from_numpy(si.token_ids(w).reshape(-1)).cuda()
@@ -272,7 +276,8 @@ def main():
                    "seq": w.seq, "hidden": w.hidden, "heads": w.n_heads, "kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab,
                    "adam": ("host fp32 (layers), device fp32 (resident embedding/head)" if adam else "off"),
-                   "parallelism": "none (1 GPU)"},
+                   "activation_checkpointing": args.ckpt, "parallelism": "none (1 GPU)"},
+        "engine_hbm": hbm,
         "mfma_util_pct": round(100.0 * layer_tflops / peak, 2),
         "kernel_tokens_per_s_per_layer": round(T / (layer_ms * 1e-3), 1),
         "layer_fwd_bwd_ms": round(layer_ms, 4),

@@ -222,9 +222,16 @@ typedef struct sf_engine sf_engine;
 enum {
   SF_ENGINE_ADAM = 1,           /* run host Adam on every streamed-out gradient  */
   SF_ENGINE_HEAD = 2,           /* ids in; embedding + fused LinearCrossEntropy */
-  SF_ENGINE_HEAD_HOST_ADAM = 4  /* update the resident embedding / LM head on the
+  SF_ENGINE_HEAD_HOST_ADAM = 4, /* update the resident embedding / LM head on the
                                    host too (gradients out, parameters back in)
                                    instead of with sf_adam_device in HBM        */
+  SF_ENGINE_CKPT = 8            /* sliding activation checkpointing (de/es/fr
+                                   §2B): each layer's input leaves for h_ckpt
+                                   after it is produced and comes back before
+                                   the layer's backward, which first recomputes
+                                   the layer's forward; the device keeps a
+                                   fixed six [T, H] buffers and two saved sets
+                                   whatever n_layers is.  Same bits as without */
 };
 
 /*
@@ -235,9 +242,13 @@ enum {
  *       dtype, param_bytes rounded up to 256) followed by its fp32 gradients
  *       (grad_bytes rounded up to 256).  Layer l always uses unit l % window.
  *   d_act/act_bytes   : device region (256-B aligned) of at least
- *       sf_engine_act_bytes(): the n_layers + 1 layer inputs/outputs [T, H],
- *       the n_layers saved activation sets, one [T, H] gradient buffer and
- *       the device loss.
+ *       sf_engine_act_bytes_flags(): the n_layers + 1 layer inputs/outputs
+ *       [T, H], the n_layers saved activation sets, one [T, H] gradient
+ *       buffer and the device loss (with SF_ENGINE_CKPT: six [T, H] buffers,
+ *       two saved sets, the gradient buffer and the loss).
+ *   h_ckpt            : SF_ENGINE_CKPT with n_layers >= 2: pinned host,
+ *       n_layers - 1 layer inputs of act x bytes each (x = [T, H] in the
+ *       storage dtype rounded up to 256 bytes; layer l at l * x).
  *   h_params[l]       : pinned host, layer l flat parameters in the
  *       parameter layout (storage dtype).  Streamed to the device twice per
  *       step (forward and backward) except for the last `window` layers,
@@ -292,6 +303,7 @@ typedef struct {
   float* h_head_v;
   float* h_head_grads;
   float* d_head_state;
+  void* h_ckpt;
 } sf_engine_cfg;
 
 /* Per-step measurements (host wall clock and device events). */
@@ -311,7 +323,10 @@ typedef struct {
   float loss;
 } sf_step_stats;
 
-/* Device bytes the engine needs in d_act for `shape` and n_layers. */
+/* Device bytes the engine needs in d_act for `shape`, n_layers and the
+ * engine flags (SF_ENGINE_CKPT changes the layout); sf_engine_act_bytes is
+ * the same with flags 0. */
+sf_status sf_engine_act_bytes_flags(const sf_shape* shape, int32_t n_layers, int32_t flags, size_t* out);
 sf_status sf_engine_act_bytes(const sf_shape* shape, int32_t n_layers, size_t* out);
 
 sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** out);
@@ -336,7 +351,9 @@ sf_status sf_slide_step(sf_engine* eng, const void* d_in, const void* d_dy, floa
 
 /* Device pointer of layer l's input activation from the last step (l = 0..
  * n_layers; l = n_layers is the last layer's output), and of the input
- * gradient of layer 0 after the last step.  For tests and inspection. */
+ * gradient of layer 0 after the last step.  For tests and inspection.
+ * With SF_ENGINE_CKPT only l = n_layers - 1 and n_layers stay on the device
+ * (SF_ERR_UNSUPPORTED below that: the others are in h_ckpt). */
 sf_status sf_engine_layer_input(sf_engine* eng, int32_t layer, void** d_x);
 sf_status sf_engine_dx0(sf_engine* eng, void** d_dx0);
 

@@ -226,6 +226,16 @@ struct sf_engine {
   hipStream_t s_comp = nullptr, s_h2d = nullptr, s_d2h = nullptr, s_head = nullptr;
   std::vector<char*> uparam, ugrad, x, saved;
   char* dbuf = nullptr;
+  // activation checkpointing: layer inputs ring (3), checkpoint slots for the
+  // backward (2), recompute output scratch, saved sets (0: scratch, 1: last
+  // layer's, kept from the forward)
+  bool ckpt = false;
+  char* xr[3] = {nullptr, nullptr, nullptr};
+  char* cs[2] = {nullptr, nullptr};
+  char* ys = nullptr;
+  char* sv[2] = {nullptr, nullptr};
+  hipEvent_t ev_xfree[3] = {nullptr, nullptr, nullptr}, ev_cready[2] = {nullptr, nullptr},
+             ev_cfree[2] = {nullptr, nullptr}, ev_ckpt_out = nullptr;
   float* d_loss = nullptr;
   std::vector<hipEvent_t> ev_param_ready, ev_param_free, ev_grad_free;
   // timing events and intervals (shared with the dispatcher thread)
@@ -599,15 +609,32 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
 
   std::vector<const void*> xin(nl + 1);
   const int32_t* ids = static_cast<const int32_t*>(d_in);
+  const bool ck = e->ckpt;
+  // layer inputs: all resident, or (checkpointing) a ring of three
+  auto xslot = [&](int i) -> char* { return ck ? e->xr[i % 3] : e->x[i]; };
   if (head) {
     if ((rc = comp_begin(&a))) return rc;
-    if ((rc = sf_embed_fwd(ctx, c.d_E, ids, e->x[0], e->s_comp))) return rc;
-    if ((rc = comp_end(a, nullptr))) return rc;
-    xin[0] = e->x[0];
+    if ((rc = sf_embed_fwd(ctx, c.d_E, ids, xslot(0), e->s_comp))) return rc;
+    if ((rc = comp_end(a, &b))) return rc;
+    xin[0] = xslot(0);
   } else {
     xin[0] = d_in;
+    b = ev0;
   }
-  for (int i = 1; i <= nl; ++i) xin[i] = e->x[i];
+  for (int i = 1; i <= nl; ++i) xin[i] = xslot(i);
+  // checkpointing: x_i leaves for host memory as soon as it exists (layers
+  // 0 .. nl-2; the last layer keeps its saved activations)
+  char* hck = static_cast<char*>(c.h_ckpt);
+  // (without a head, x_0 is the caller's input and stays where it is)
+  auto ckpt_out = [&](int i, hipEvent_t ready) -> sf_status {
+    if (!ck || i > nl - 2 || (i == 0 && !head)) return SF_OK;
+    hipEvent_t done;
+    if (sf_status r = timed_d2h(e, hck + static_cast<size_t>(i) * e->x_bytes, xin[i], e->x_bytes, ready, &done))
+      return r;
+    SF_HIP(hipEventRecord(e->ev_xfree[i % 3], e->s_d2h));
+    return SF_OK;
+  };
+  if ((rc = ckpt_out(0, b))) return rc;
 
   // ---------------- forward: layer i in unit i % W, prefetch i + 1
   // (layers below W were uploaded at the end of the previous step, right
@@ -618,11 +645,27 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if (i + 1 < nl && (rc = fetch(i + 1))) return rc;
     const int u = i % W;
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
+    // the output slot held x_{i-2}: its copy to the host must be done
+    if (ck && i >= 2) SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_xfree[(i + 1) % 3], 0));
     if ((rc = comp_begin(&a))) return rc;
-    if ((rc = sf_layer_fwd(ctx, e->uparam[u], xin[i], e->x[i + 1], e->saved[i], e->s_comp))) return rc;
-    if ((rc = comp_end(a, nullptr))) return rc;
+    void* sv = ck ? e->sv[i == nl - 1 ? 1 : 0] : e->saved[i];
+    if ((rc = sf_layer_fwd(ctx, e->uparam[u], xin[i], xslot(i + 1), sv, e->s_comp))) return rc;
+    if ((rc = comp_end(a, &b))) return rc;
     SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
+    if ((rc = ckpt_out(i + 1, b))) return rc;
   }
+  if (ck && nl >= 2) SF_HIP(hipEventRecord(e->ev_ckpt_out, e->s_d2h));
+  // checkpoint of layer i back into slot i % 2 (after every checkpoint left
+  // and after the backward that last used the slot)
+  auto ckpt_in = [&](int i) -> sf_status {
+    if (!ck || i < 0 || i > nl - 2 || (i == 0 && !head)) return SF_OK;
+    SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_ckpt_out, 0));
+    SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_cfree[i % 2], 0));
+    if (sf_status r = timed_h2d(e, e->cs[i % 2], hck + static_cast<size_t>(i) * e->x_bytes, e->x_bytes, e->s_h2d))
+      return r;
+    SF_HIP(hipEventRecord(e->ev_cready[i % 2], e->s_h2d));
+    return SF_OK;
+  };
 
   // ---------------- head: loss, dx_L, dg_f, dW_lm; their Adam starts now
   const void* dy = d_dy;
@@ -669,18 +712,33 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   }
 
   // ---------------- backward: layer i in unit i % W, prefetch i - W + 1
+  // (checkpointing: the input of layer i - 1 comes back meanwhile, and every
+  // layer but the last recomputes its forward before its backward)
   for (int i = nl - 1; i >= 0; --i) {
     const int u = i % W;
     const int j = i - W + 1;
     if (j >= 0 && j < nl - W && (rc = prefetch(e, j))) return rc;
+    // the slot of layer i - 1 was last read by the backward of layer i + 1
+    if ((rc = ckpt_in(i - 1))) return rc;
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_grad_free[u], 0));
     if ((rc = comp_begin(&a))) return rc;
+    const void* xi = xin[i];
+    void* sv = ck ? e->sv[1] : e->saved[i];
+    if (ck && i < nl - 1) {
+      if (i > 0 || head) {
+        SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_cready[i % 2], 0));
+        xi = e->cs[i % 2];
+      }
+      sv = e->sv[0];
+      if ((rc = sf_layer_fwd(ctx, e->uparam[u], xi, e->ys, sv, e->s_comp))) return rc;
+    }
     hipEvent_t ffn = timing_event(e);
     if (!ffn) return fail(SF_ERR_HIP, "event pool exhausted");
-    if ((rc = layer_bwd(ctx, e->uparam[u], xin[i], e->saved[i], dy, e->dbuf, reinterpret_cast<float*>(e->ugrad[u]),
-                        e->s_comp, ffn)))
+    if ((rc = layer_bwd(ctx, e->uparam[u], xi, sv, dy, e->dbuf, reinterpret_cast<float*>(e->ugrad[u]), e->s_comp,
+                        ffn)))
       return rc;
+    if (ck && i < nl - 1) SF_HIP(hipEventRecord(e->ev_cfree[i % 2], e->s_comp));
     if ((rc = comp_end(a, &b))) return rc;
     dy = e->dbuf;
     SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
@@ -761,13 +819,21 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
 
 extern "C" {
 
-sf_status sf_engine_act_bytes(const sf_shape* shape, int32_t n_layers, size_t* out) {
+sf_status sf_engine_act_bytes_flags(const sf_shape* shape, int32_t n_layers, int32_t flags, size_t* out) {
   Dims d;
   if (sf_status st = check_shape(shape, &d)) return st;
   if (n_layers < 1 || !out) return fail(SF_ERR_ARG, "n_layers must be >= 1 and out non-NULL");
   const size_t xb = align256(static_cast<size_t>(d.T) * d.H * d.e);
-  *out = (n_layers + 1) * xb + n_layers * saved_layout(d).total + xb + 256;
+  const size_t sb = saved_layout(d).total;
+  if (flags & SF_ENGINE_CKPT)  // input ring 3, checkpoint slots 2, recompute output, 2 saved sets
+    *out = 6 * xb + 2 * sb + xb + 256;
+  else
+    *out = (n_layers + 1) * xb + n_layers * sb + xb + 256;
   return SF_OK;
+}
+
+sf_status sf_engine_act_bytes(const sf_shape* shape, int32_t n_layers, size_t* out) {
+  return sf_engine_act_bytes_flags(shape, n_layers, 0, out);
 }
 
 sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** out) {
@@ -795,7 +861,12 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   shp.vocab = d.V; shp.batch = d.B; shp.seq = d.S; shp.rms_eps = d.eps; shp.rope_base = d.rope_base;
   shp.dtype = d.dtype;
   size_t act = 0;
-  if (sf_status st = sf_engine_act_bytes(&shp, c.n_layers, &act)) return st;
+  if (sf_status st = sf_engine_act_bytes_flags(&shp, c.n_layers, c.flags, &act)) return st;
+  const bool ckpt = (c.flags & SF_ENGINE_CKPT) != 0;
+  if (ckpt && c.n_layers >= 2) {
+    if (!c.h_ckpt) return fail(SF_ERR_ARG, "SF_ENGINE_CKPT needs h_ckpt");
+    if (!is_pinned(c.h_ckpt)) return fail(SF_ERR_NOT_PINNED, "h_ckpt is not pinned host memory");
+  }
   if (c.act_bytes < act) return fail(SF_ERR_POOL, "activation region has %zu bytes, needs %zu", c.act_bytes, act);
   for (int l = 0; l < c.n_layers; ++l) {
     if (!c.h_params[l]) return fail(SF_ERR_ARG, "h_params[%d] is NULL", l);
@@ -861,10 +932,20 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   }
   char* act_p = static_cast<char*>(c.d_act);
   const size_t sb = ctx->saved.total;
-  for (int i = 0; i <= e->nl; ++i) e->x.push_back(act_p + i * e->x_bytes);
-  act_p += (e->nl + 1) * e->x_bytes;
-  for (int i = 0; i < e->nl; ++i) e->saved.push_back(act_p + i * sb);
-  act_p += e->nl * sb;
+  e->ckpt = ckpt;
+  if (ckpt) {
+    for (int k = 0; k < 3; ++k) e->xr[k] = act_p + k * e->x_bytes;
+    for (int k = 0; k < 2; ++k) e->cs[k] = act_p + (3 + k) * e->x_bytes;
+    e->ys = act_p + 5 * e->x_bytes;
+    act_p += 6 * e->x_bytes;
+    for (int k = 0; k < 2; ++k) e->sv[k] = act_p + k * sb;
+    act_p += 2 * sb;
+  } else {
+    for (int i = 0; i <= e->nl; ++i) e->x.push_back(act_p + i * e->x_bytes);
+    act_p += (e->nl + 1) * e->x_bytes;
+    for (int i = 0; i < e->nl; ++i) e->saved.push_back(act_p + i * sb);
+    act_p += e->nl * sb;
+  }
   e->dbuf = act_p;
   e->d_loss = reinterpret_cast<float*>(act_p + e->x_bytes);
   auto mk = [&](std::vector<hipEvent_t>& v) {
@@ -877,6 +958,13 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   };
   if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_free))
     return cleanup(fail(SF_ERR_HIP, "event creation failed"));
+  if (ckpt) {
+    std::vector<hipEvent_t*> evs = {&e->ev_xfree[0], &e->ev_xfree[1], &e->ev_xfree[2], &e->ev_cready[0],
+                                    &e->ev_cready[1], &e->ev_cfree[0], &e->ev_cfree[1], &e->ev_ckpt_out};
+    for (hipEvent_t* ev : evs)
+      if (hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess)
+        return cleanup(fail(SF_ERR_HIP, "event creation failed"));
+  }
   for (int i = 0; i < 24 * e->nl + 64; ++i) {
     hipEvent_t ev;
     if (hipEventCreate(&ev) != hipSuccess) return cleanup(fail(SF_ERR_HIP, "event creation failed"));
@@ -930,6 +1018,12 @@ sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float*
 
 sf_status sf_engine_layer_input(sf_engine* e, int32_t layer, void** d_x) {
   if (!e || !d_x || layer < 0 || layer > e->nl) return fail(SF_ERR_ARG, "bad argument");
+  if (e->ckpt) {
+    // only the last layer's input and output stay on the device
+    if (layer < e->nl - 1) return fail(SF_ERR_UNSUPPORTED, "layer %d's input lives in host memory (checkpointing)", layer);
+    *d_x = e->xr[layer % 3];
+    return SF_OK;
+  }
   *d_x = e->x[layer];
   return SF_OK;
 }
@@ -970,6 +1064,9 @@ sf_status sf_engine_destroy(sf_engine* e) {
     if (s) (void)hipStreamSynchronize(s);
   for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_free, &e->tev})
     for (hipEvent_t ev : *v) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : {e->ev_xfree[0], e->ev_xfree[1], e->ev_xfree[2], e->ev_cready[0], e->ev_cready[1],
+                        e->ev_cfree[0], e->ev_cfree[1], e->ev_ckpt_out})
+    if (ev) (void)hipEventDestroy(ev);
   for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
     if (s) (void)hipStreamDestroy(s);
   delete e;

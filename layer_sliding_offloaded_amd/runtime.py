@@ -116,10 +116,12 @@ class Engine:
 
     layers: list of per-layer parameter dicts (float32 storage values).
     head: None or dict with E [V, H], gf [H], Wlm [V, H] (float32 storage values).
+    ckpt: sliding activation checkpointing (layer inputs kept in pinned host
+    memory, each layer's forward recomputed before its backward).
     """
 
     def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
-                 adam_threads=0, adam_hp=None, stream=None, head_adam="device"):
+                 adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False):
         import ctypes
         hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
         self.w = w
@@ -131,8 +133,17 @@ class Engine:
         W = min(window, self.nl)
         unit = (L.param_bytes + 255) // 256 * 256 + (L.grad_bytes + 255) // 256 * 256
         self.pool = device_bytes(W * unit)
-        act = sf.sf_engine_act_bytes(shape, self.nl)
+        flags = (sf.SF_ENGINE_ADAM if adam else 0) | (sf.SF_ENGINE_HEAD if head is not None else 0)
+        if head is not None and head_adam == "host":
+            flags |= sf.SF_ENGINE_HEAD_HOST_ADAM
+        if ckpt:
+            flags |= sf.SF_ENGINE_CKPT
+        act = sf.sf_engine_act_bytes_flags(shape, self.nl, flags)
         self.act = device_bytes(act)
+        self.act_bytes = act
+        ebytes = 2 if w.dtype == "bf16" else 4
+        self.x_bytes = (shape.batch * shape.seq * shape.hidden * ebytes + 255) // 256 * 256
+        self.h_ckpt = pinned_bytes(max(self.nl - 1, 1) * self.x_bytes) if ckpt else None
         self.h_params = [pack_params(L, p, w, pinned_bytes(L.param_bytes)) for p in layers]
         self.h_master = [master_from_params(L, p) for p in layers]
         self.h_m = [np.zeros_like(m) for m in self.h_master]
@@ -145,9 +156,6 @@ class Engine:
             self._arrays.append(a)
             return ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
 
-        flags = (sf.SF_ENGINE_ADAM if adam else 0) | (sf.SF_ENGINE_HEAD if head is not None else 0)
-        if head is not None and head_adam == "host":
-            flags |= sf.SF_ENGINE_HEAD_HOST_ADAM
         self.head_adam = head_adam
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         cfg = sf.SfEngineCfg()
@@ -162,6 +170,8 @@ class Engine:
         cfg.h_v = parr([m.ctypes.data for m in self.h_v])
         cfg.h_grad_slots = parr([t.data_ptr() for t in self.h_slots])
         cfg.compute_stream = self.stream.cuda_stream
+        if ckpt:
+            cfg.h_ckpt = self.h_ckpt.data_ptr()
         if head is not None:
             V, H = w.vocab, w.hidden
             dt = storage_dtype(w)

@@ -32,6 +32,7 @@ TENSOR_NAMES = ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd", "g1", "g2")
 SF_ENGINE_ADAM = 1
 SF_ENGINE_HEAD = 2
 SF_ENGINE_HEAD_HOST_ADAM = 4
+SF_ENGINE_CKPT = 8
 
 _size_t = ctypes.c_size_t
 _vp = ctypes.c_void_p
@@ -61,7 +62,7 @@ class SfEngineCfg(ctypes.Structure):
                 ("h_grad_slots", ctypes.POINTER(_vp)), ("compute_stream", _vp),
                 ("d_E", _vp), ("d_gf", _vp), ("d_wlm", _vp), ("d_head_grads", _vp),
                 ("h_head_params", _vp), ("h_head_master", _vp), ("h_head_m", _vp), ("h_head_v", _vp),
-                ("h_head_grads", _vp), ("d_head_state", _vp)]
+                ("h_head_grads", _vp), ("d_head_state", _vp), ("h_ckpt", _vp)]
 
 
 class SfStepStats(ctypes.Structure):
@@ -83,7 +84,7 @@ class SfError(RuntimeError):
 
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
-    "sf_gemm", "sf_gemm_workspace_bytes", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_create", "sf_slide_step",
+    "sf_gemm", "sf_gemm_workspace_bytes", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_act_bytes_flags", "sf_engine_create", "sf_slide_step",
     "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_destroy", "sf_last_error",
 )
 
@@ -115,6 +116,7 @@ def load():
         "sf_adam_device": [i32, P, P, P, P, P, _size_t, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
                            ctypes.c_float, ctypes.c_float, P],
         "sf_engine_act_bytes": [ctypes.POINTER(SfShape), i32, ctypes.POINTER(_size_t)],
+        "sf_engine_act_bytes_flags": [ctypes.POINTER(SfShape), i32, i32, ctypes.POINTER(_size_t)],
         "sf_engine_create": [P, ctypes.POINTER(SfEngineCfg), ctypes.POINTER(P)],
         "sf_slide_step": [P, P, P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(SfStepStats)],
         "sf_engine_layer_input": [P, i32, ctypes.POINTER(P)],
@@ -206,6 +208,12 @@ def sf_adam_device(dtype, d_p, d_m, d_v, d_g, d_out, n, step, lr, b1, b2, eps, s
 def sf_engine_act_bytes(shape, n_layers):
     out = _size_t()
     _check(load().sf_engine_act_bytes(ctypes.byref(shape), n_layers, ctypes.byref(out)))
+    return out.value
+
+
+def sf_engine_act_bytes_flags(shape, n_layers, flags):
+    out = _size_t()
+    _check(load().sf_engine_act_bytes_flags(ctypes.byref(shape), n_layers, flags, ctypes.byref(out)))
     return out.value
 
 

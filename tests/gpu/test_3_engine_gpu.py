@@ -266,3 +266,65 @@ def test_engine_without_head_or_adam():
     assert st["h2d_bytes"] == (2 * 3 - 2) * L.param_bytes  # the last window of layers is reused
     c.close()
     eng.close()
+
+
+def _run_engine(w, layers, head, x, dy, steps, **kw):
+    """Steps an engine and returns per-step snapshots of everything it updates."""
+    eng = rt.Engine(w, layers, head, n_grad_slots=2, adam=True, chunk=96, adam_hp=si.ADAM, **kw)
+    d_in = torch.from_numpy(x.reshape(-1)).cuda() if head is not None else rt.to_storage_tensor(x, w).cuda()
+    d_dy = None if head is not None else rt.to_storage_tensor(dy, w).cuda()
+    n = w.tokens * w.hidden * 2
+    base = eng.act.data_ptr()
+    out = []
+    for _ in range(steps):
+        loss, st = eng.step(d_in, d_dy)
+        torch.cuda.synchronize()
+        snap = dict(loss=loss, st=st, master=[m.copy() for m in eng.h_master],
+                    params=[p.numpy().view(np.uint16).copy() for p in eng.h_params])
+        if head is not None:
+            snap["head"] = [a.copy() for a in engine_head_state(eng)]
+        od = sf.sf_engine_dx0(eng.eng) - base
+        oy = sf.sf_engine_layer_input(eng.eng, w.n_layers) - base
+        snap["dx0"] = eng.act[od:od + n].cpu().numpy().copy()
+        snap["y"] = eng.act[oy:oy + n].cpu().numpy().copy()
+        out.append(snap)
+    info = dict(act_bytes=eng.act_bytes, x_bytes=eng.x_bytes, trace=eng.trace())
+    eng.close()
+    return out, info
+
+
+@pytest.mark.parametrize("head_adam,window,n_layers", [("device", 2, 4), ("host", 3, 5), (None, 2, 3),
+                                                       ("device", 2, 2), ("device", 2, 1)])
+def test_engine_checkpointing_matches_plain_bitwise(head_adam, window, n_layers):
+    """Sliding activation checkpointing only moves layer inputs through host
+    memory and recomputes each layer's forward before its backward: every
+    result of the iteration is the same bits as with all activations resident."""
+    w = STACK.with_(n_layers=n_layers, vocab=STACK.vocab if head_adam else 0)
+    say("engine-ckpt", head_adam, window, n_layers, w)
+    layers = [si.layer_params(w, l, gains="random") for l in range(n_layers)]
+    if head_adam:
+        head = dict(E=si.embedding(w), gf=si.final_gain(w, gains="random"), Wlm=si.lm_head(w))
+        x, dy = si.token_ids(w), None
+        kw = dict(head_adam=head_adam)
+    else:
+        head, x, dy, kw = None, si.layer_input(w), si.upstream_grad(w), {}
+    ref, ri = _run_engine(w, layers, head, x, dy, 2, window=window, **kw)
+    got, gi = _run_engine(w, layers, head, x, dy, 2, window=window, ckpt=True, **kw)
+    for t, (a, b) in enumerate(zip(ref, got)):
+        if head is not None:  # (no loss without a head)
+            assert a["loss"] == b["loss"], t
+        for i in range(n_layers):
+            assert np.array_equal(a["master"][i], b["master"][i]), (t, i)
+            assert np.array_equal(a["params"][i], b["params"][i]), (t, i)
+        if head is not None:
+            assert np.array_equal(a["head"][0], b["head"][0]) and np.array_equal(a["head"][1], b["head"][1]), t
+        else:
+            assert np.array_equal(a["dx0"], b["dx0"]), t
+        assert np.array_equal(a["y"], b["y"]), t
+        # the checkpoints add one trip out and one back per layer input but
+        # the last layer's (and, without a head, the caller's x_0)
+        n_ck = max(n_layers - 1 - (0 if head is not None else 1), 0)
+        assert b["st"]["d2h_bytes"] - a["st"]["d2h_bytes"] == n_ck * gi["x_bytes"], t
+        assert b["st"]["h2d_bytes"] - a["st"]["h2d_bytes"] == n_ck * gi["x_bytes"], t
+    if n_layers >= 4:
+        assert gi["act_bytes"] < ri["act_bytes"]
