@@ -1,23 +1,28 @@
-// MFMA GEMM for gfx950 with LDS-staged, double-buffered tiles.
+// MFMA GEMM for gfx950.
 //
 // Every dense projection of the decoder block and of the LM head goes
-// through this kernel: the forward products y = x W^T (NT), the input
+// through these kernels: the forward products y = x W^T (NT), the input
 // gradients dX = dY W (NN) and the weight gradients dW = dY^T X (TN).  Fused
 // epilogues carry the elementwise steps that follow a product (RoPE on q/k,
 // SwiGLU forward and backward, the residual add, fp32 gradient stores), so
 // those tensors make one trip through HBM instead of three.
 //
 // Tile scheme.  A block computes a BM x BN output tile with NW = (BM/WM) *
-// (BN/WN) waves, each owning a WM x WN sub-tile built from 16x16 MFMA
-// fragments.  Per k-stage the block stages BM x 128 B of A and BN x 128 B of
-// B in LDS, always as [row][k] with 16 B of padding per row (row stride
-// 144 B: the 8 lanes of each 128-bit LDS access phase then hit distinct
-// banks).  Operands that are k-contiguous in HBM are copied as 16-byte
-// vectors; operands that are row-contiguous (the transposed side of NN/TN)
-// are read as 8x8 (bf16) or 4x4 (fp32) blocks and transposed in registers
-// before the LDS write, so the MFMA side never sees a strided read.
-// Global loads for stage k+1 are issued before the MFMAs of stage k and
-// written to the other LDS buffer after them: one barrier per stage.
+// (BN/WN) waves, each owning a WM x WN sub-tile built from 16x16x32 MFMA
+// fragments.  bf16 operands (the production path) are copied global -> LDS
+// by the buffer unit itself (buffer_load ... lds, no VGPR round trip) into
+// XOR-swizzled stage buffers: k-contiguous operands as [row][k], the
+// transposed side of NN / TN as [k][row] read back with the LDS transpose
+// load.  Three kernels share those helpers:
+//  - gemm_direct_kernel: 2 stages of 64 k (grids that fill the chip with
+//    128 x 128 tiles);
+//  - gemm_pipe_kernel: NS stages of BK k, the loads of stage kt + NS - 1
+//    issued while stage kt is multiplied (small grids);
+//  - gemm_pp_kernel: 256 x 256 tiles whose 8 waves split into two groups
+//    that alternate between a memory phase and an MFMA phase (large grids).
+// The register-staged gemm_kernel (loads through VGPRs, in-register 8x8 /
+// 4x4 transposes of row-contiguous operands, 144-byte padded LDS rows)
+// serves fp32 and operands the direct loads cannot take.
 //
 // Output fragments are computed transposed (MFMA A-operand = B tile) so each
 // lane ends with 4 consecutive output columns of one row: 8-byte (bf16) or
@@ -413,6 +418,20 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// One wave-wide global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4
+// with the lds flag): lane l's bytes at buffer offset voff land at LDS byte
+// address lds + 16 l.  Issued as inline assembly so that the compiler does
+// not track it as an LDS write: its wait-count pass cannot tell the stages of
+// a multi-stage pipeline apart across loop iterations and would make LDS
+// reads wait for every load in flight (vmcnt(0)).  The kernels order their
+// LDS reads after these loads themselves (wait_vm + bar).  M0 carries the
+// LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, uint32_t voff) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_t*)(lds)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(m0), "s"(rs) : "memory");
+}
+
 // [k][row] slot swizzle: 16 lanes of one transpose read cover 4 consecutive k
 // (the same two slots each); lanes 16 apart cover k 8 apart.  This map sends
 // those 8 k-rows to 8 distinct slot pairs.
@@ -460,8 +479,7 @@ struct Direct {
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
       const uint32_t off = (base[j] != kOOB && k0 + kl[j] < kend) ? base[j] + adv : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t*)(region + (j * NW + w) * 1024), 16,
-                                               static_cast<int>(off), 0, 0, 0);
+      dma16(rs, region + (j * NW + w) * 1024, off);
     }
   }
 };
@@ -544,8 +562,7 @@ struct DirectK {
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
       const uint32_t off = (base[j] != kOOB && k0 + kl[j] < kend) ? base[j] + adv : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t*)(region + (j * NW + w) * 1024), 16,
-                                               static_cast<int>(off), 0, 0, 0);
+      dma16(rs, region + (j * NW + w) * 1024, off);
     }
   }
 };
@@ -670,11 +687,11 @@ gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes)
 // loads into another) and the loop unrolled by 4.  The loads of stage kt + 3
 // are issued after the fragment reads of stage kt; the wait at the end of a
 // stage lets the two newer stages stay in flight.
-template <int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E>
+template <int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E, int NS>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
   using T = bf16;
-  constexpr int NS = 4;
+  static_assert(NS >= 3 && NS <= 6, "3 to 6 stages");
   constexpr bool AKC = (LAY != GemmLayout::TN);
   constexpr bool BKC = (LAY == GemmLayout::NT);
   constexpr int NW = (BM / WM) * (BN / WN);
@@ -687,7 +704,10 @@ gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
   __shared__ __attribute__((aligned(1024))) char S0[STAGE];
   __shared__ __attribute__((aligned(1024))) char S1[STAGE];
   __shared__ __attribute__((aligned(1024))) char S2[STAGE];
-  __shared__ __attribute__((aligned(1024))) char S3[STAGE];
+  __shared__ __attribute__((aligned(1024))) char S3[NS > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char S4[NS > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char S5[NS > 5 ? STAGE : 16];
+  char* const stage[6] = {S0, S1, S2, S3, S4, S5};
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -739,23 +759,142 @@ gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[ks][j], af[ks][i]);
-    // stage kt + 1 complete; stages kt + 2, kt + 3 may still be loading
+    // stage kt + 1 complete; stages kt + 2 .. kt + NS - 1 may still be loading
     direct::wait_vm<(NS - 2) * JPS>();
     direct::bar();
   };
 
   if (nk > 0) {
-    issue(S0, 0);
-    issue(S1, 1);
-    issue(S2, 2);
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(stage[u], u);
     direct::wait_vm<(NS - 2) * JPS>();
     direct::bar();
     for (int kt = 0; kt < nk; kt += NS) {
-      body(kt, S0, S3);
-      if (kt + 1 < nk) body(kt + 1, S1, S0);
-      if (kt + 2 < nk) body(kt + 2, S2, S1);
-      if (kt + 3 < nk) body(kt + 3, S3, S2);
+      // fully unrolled: each stage is its own LDS array, so the compiler sees
+      // that the fragment reads of one stage do not alias the loads of another
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        if (u == 0 || kt + u < nk) body(kt + u, stage[u], stage[(u + NS - 1) % NS]);
     }
+    direct::wait_vm<0>();  // no load into LDS outlives the block
+  }
+
+  epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
+}
+
+// Ping-pong variant: the 8 waves form two groups of four (one wave per SIMD
+// in each), and the groups alternate between a memory phase (fragment reads
+// of the next stage from LDS, loads of a later stage into LDS) and a compute
+// phase (the MFMAs of that stage), so that each SIMD's matrix unit always has
+// one wave feeding it while the other waits on memory.  A barrier separates
+// the phases; group 1 runs one phase behind group 0.  One fragment set per
+// wave suffices because a wave's own phases alternate.
+template <int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E, int NS>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_pp_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
+  using T = bf16;
+  static_assert(NS >= 3 && NS <= 6, "3 to 6 stages");
+  constexpr bool AKC = (LAY != GemmLayout::TN);
+  constexpr bool BKC = (LAY == GemmLayout::NT);
+  constexpr int NW = (BM / WM) * (BN / WN);
+  static_assert(NW == 8, "two groups of four waves");
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int WGM = BM / WM;
+  constexpr int KS = BK / 32;
+  constexpr int ABYTES = BM * BK * 2;
+  constexpr int STAGE = (BM + BN) * BK * 2;
+  static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
+  __shared__ __attribute__((aligned(1024))) char S0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char S1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char S2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char S3[NS > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char S4[NS > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char S5[NS > 5 ? STAGE : 16];
+  char* const stage[6] = {S0, S1, S2, S3, S4, S5};
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WGM, wn = w / WGM;
+  const bool late = w >= 4;  // group 1: one phase behind
+  int tm, tn;
+  tile_coords(ntm, ntn, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), 0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.B), 0, b_bytes, 0x00020000);
+  direct::DirectK<BM, NW, AKC, BK> la;
+  direct::DirectK<BN, NW, BKC, BK> lb;
+  constexpr int JPS = direct::DirectK<BM, NW, AKC, BK>::JW + direct::DirectK<BN, NW, BKC, BK>::JW;
+  la.init(w, lane, g.lda, m0, g.M, [&](int r) { const int m = m0 + r; return m < g.M ? m : -1; });
+  lb.init(w, lane, g.ldb, n0, g.N, [&](int r) { return ColMap<E, WN>::brow(r, n0, g, BN); });
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kbeg = blockIdx.y * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  auto issue = [&](char* st, int kt) {
+    la.issue(ra, st, w, kbeg + kt * BK, kend, g.lda);
+    lb.issue(rb, st + ABYTES, w, kbeg + kt * BK, kend, g.ldb);
+  };
+  const int lr = lane % 16, lg = lane / 16;
+  uint4 af[KS][FM], bfr[KS][FN];
+  // phase boundary: this wave's loads of the next stage anyone reads have
+  // landed, its fragment reads are in registers; then the barrier
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    direct::wait_vm<(NS - 2) * JPS>();
+    direct::bar();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // memory phase of stage kt: its fragments into registers, stage kt + NS - 1
+  // into the buffer stage kt - 1 used (both groups have read it by now)
+  auto mem = [&](int kt, const char* cur, char* nxt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[ks][j] = direct::fragk<BN, BKC, BK>(cur + ABYTES, wn * WN + j * 16, ks, lr, lg);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[ks][i] = direct::fragk<BM, AKC, BK>(cur, wm * WM + i * 16, ks, lr, lg);
+    }
+    issue(nxt, kt + NS - 1);
+  };
+  auto compute = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[ks][j], af[ks][i]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(stage[u], u);
+    sync();
+    if (late) sync();
+    for (int kt = 0; kt < nk; kt += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        if (u == 0 || kt + u < nk) {
+          mem(kt + u, stage[u], stage[(u + NS - 1) % NS]);
+          sync();
+          compute();
+          sync();
+        }
+      }
+    }
+    if (!late) sync();
     direct::wait_vm<0>();  // no load into LDS outlives the block
   }
 
@@ -798,8 +937,8 @@ bool direct_ok(const GemmArgs& g, int64_t* a_bytes, int64_t* b_bytes) {
 }
 
 // KIND 0: register-staged kernel; 1: direct loads, 2 stages of 64 k; 2: direct
-// loads, 4 stages of BK k.
-template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, int KIND = 0, int BK = 64>
+// loads, NS stages of BK k; 3: the same with two wave groups in ping-pong.
+template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, int KIND = 0, int BK = 64, int NS = 4>
 hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_bytes, int64_t a_bytes = 0,
                   int64_t b_bytes = 0) {
   const int ntm = (g_in.M + BM - 1) / BM;
@@ -818,9 +957,13 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
     S = (g.K + g.kchunk - 1) / g.kchunk;
     g.partial = ws;
   }
-  if constexpr (KIND == 2) {
+  if constexpr (KIND == 3) {
     static_assert(sizeof(T) == 2, "direct loads are bf16 only");
-    hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, WM, WN, BK, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
+    hipLaunchKernelGGL((gemm_pp_kernel<BM, BN, WM, WN, BK, LAY, E, NS>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
+                       ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
+  } else if constexpr (KIND == 2) {
+    static_assert(sizeof(T) == 2, "direct loads are bf16 only");
+    hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, WM, WN, BK, LAY, E, NS>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
                        ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
   } else if constexpr (KIND == 1) {
     static_assert(sizeof(T) == 2, "direct loads are bf16 only");
@@ -849,11 +992,12 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
   if constexpr (sizeof(T) == 2) {
     int64_t ab = 0, bb = 0;
     if (direct_ok<LAY, E>(g, &ab, &bb)) {
-      // Measured choices: large grids take 4 stages of 32 k (256x256, 8 waves
-      // of 128x64); grids of 128x128 tiles take 4 stages of 64 k with 8
-      // waves of 32x64, or 2 stages when there are enough tiles to keep
-      // every CU busy without a deep pipeline.
-      if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, 2, 32>(g, s, ws, wsb, ab, bb);
+      // Measured choices: grids of at least 160 256x256 tiles take the
+      // ping-pong kernel (8 waves of 128x64, 4 stages of 32 k); smaller grids
+      // take 128x128 tiles, 4 stages of 64 k with 8 waves of 32x64, or 2
+      // stages when there are enough tiles to keep every CU busy without a
+      // deep pipeline.
+      if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb);
       const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
       const long t128 = static_cast<long>((g.M + 127) / 128) * ((ncols + 127) / 128);
       if (t128 >= 320) {
@@ -900,7 +1044,7 @@ hipError_t dispatch(GemmLayout lay, Epi epi, const GemmArgs& g, hipStream_t s, f
 
 int gemm_tile_config(int M, int N) {
   const long big = static_cast<long>((M + 255) / 256) * ((N + 255) / 256);
-  return big >= 256 ? 0 : 1;
+  return big >= 160 ? 0 : 1;
 }
 
 size_t gemm_splitk_bytes(int M, int N, int K) {
