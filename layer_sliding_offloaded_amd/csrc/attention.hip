@@ -30,14 +30,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T>
-__device__ __forceinline__ void store4v(T* p, const float* v) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-  } else {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
 
 // Pack 8 fp32 (bf16) or take 4 fp32 as the 16-byte B-operand chunk.
 __device__ __forceinline__ uint4 pack_chunk_bf16(const f32x4& a, const f32x4& b) {
@@ -276,7 +268,7 @@ attn_fwd_kernel(const AttnArgs a) {
         float o[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[v] = oacc[f][d][v] * inv;
-        store4v<T>(obase + static_cast<int64_t>(q) * a.ld_out + d * 16 + lg * 4, o);
+        store4<T>(obase + static_cast<int64_t>(q) * a.ld_out + d * 16 + lg * 4, o);
       }
       if (lg == 0) a.lse[(static_cast<int64_t>(b) * a.n_heads + h) * S + q] = mrow[f] + log2f(l);
     }
@@ -447,9 +439,9 @@ attn_bwd_dkdv_kernel(const AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < FD; ++d) {
       float o[4] = {dk[d][0], dk[d][1], dk[d][2], dk[d][3]};
-      store4v<T>(dkp + d * 16 + lg * 4, o);
+      store4<T>(dkp + d * 16 + lg * 4, o);
       float o2[4] = {dv[d][0], dv[d][1], dv[d][2], dv[d][3]};
-      store4v<T>(dvp + d * 16 + lg * 4, o2);
+      store4<T>(dvp + d * 16 + lg * 4, o2);
     }
   }
 }
@@ -555,7 +547,7 @@ attn_bwd_dq_kernel(const AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < FD; ++d) {
       float o[4] = {dq[d][0], dq[d][1], dq[d][2], dq[d][3]};
-      store4v<T>(dqp + d * 16 + lg * 4, o);
+      store4<T>(dqp + d * 16 + lg * 4, o);
     }
   }
 }

@@ -33,7 +33,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kOOB = 0x80000000u;  // past every operand's extent
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // [row][64 d] blocks (128-byte rows): 16 lanes reading one 16-byte chunk of
@@ -96,8 +95,7 @@ struct TileLoad {
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
       const uint32_t o = row[j] < rows_left ? off[j] + adv : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t*)(lds + (j * NW + w) * 1024), 16, static_cast<int>(o),
-                                               0, 0, 0);
+      lds_dma16(rs, lds + (j * NW + w) * 1024, o);
     }
   }
 };
@@ -419,8 +417,7 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
       // wave 0: log-sum-exp, wave 1: D, one float per lane
       const int64_t st = ((static_cast<int64_t>(b) * a.n_heads + h) * S + q0 + lane) * 4;
       const uint32_t o = q0 + lane < S ? static_cast<uint32_t>(st) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? rl : rd, (lds_t*)(Ln + w * BQ), 4, static_cast<int>(o), 0,
-                                               0, 0);
+      lds_dma4(w == 0 ? rl : rd, Ln + w * BQ, o);
     }
   };
 

@@ -135,4 +135,36 @@ template <> struct Transpose<float> {
   static __device__ __forceinline__ void run(const uint4* v, uint4* o) { transpose4x4_b32(v, o); }
 };
 
+// Store 4 consecutive values in the storage dtype (8 or 16 bytes).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Wave-wide global -> LDS copies by the buffer unit (buffer_load ... with the
+// lds flag): lane l's 16 (or 4) bytes at buffer offset voff land at LDS byte
+// address lds + 16 l (+ 4 l).  Issued as inline assembly so that the
+// compiler does not track them as LDS writes: its wait-count pass cannot tell
+// the stages of a multi-stage pipeline apart across loop iterations and makes
+// LDS reads wait for every load in flight (vmcnt(0)), draining the pipeline.
+// Callers order their LDS reads after these loads themselves (s_waitcnt on
+// vmcnt, then a barrier).  M0 carries the LDS address; the kernels that use
+// these helpers use M0 for nothing else.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const void* lds, uint32_t voff) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(const_cast<void*>(lds))));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(m0), "s"(rs) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, const void* lds, uint32_t voff) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(const_cast<void*>(lds))));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(m0), "s"(rs) : "memory");
+}
+
 }  // namespace sf

@@ -171,14 +171,6 @@ int splitk_factor(int tiles, int K) {
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 template <typename T>
-__device__ __forceinline__ void store4(T* p, const float* v) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-  } else {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
-template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* v) {
   if constexpr (sizeof(T) == 2) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
@@ -415,22 +407,7 @@ constexpr int kBK = 64;              // k per stage
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every operand's extent
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// One wave-wide global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4
-// with the lds flag): lane l's bytes at buffer offset voff land at LDS byte
-// address lds + 16 l.  Issued as inline assembly so that the compiler does
-// not track it as an LDS write: its wait-count pass cannot tell the stages of
-// a multi-stage pipeline apart across loop iterations and would make LDS
-// reads wait for every load in flight (vmcnt(0)).  The kernels order their
-// LDS reads after these loads themselves (wait_vm + bar).  M0 carries the
-// LDS address; nothing else in these kernels uses M0.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, uint32_t voff) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_t*)(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-               :: "v"(voff), "s"(m0), "s"(rs) : "memory");
-}
 
 // [k][row] slot swizzle: 16 lanes of one transpose read cover 4 consecutive k
 // (the same two slots each); lanes 16 apart cover k 8 apart.  This map sends
@@ -479,7 +456,7 @@ struct Direct {
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
       const uint32_t off = (base[j] != kOOB && k0 + kl[j] < kend) ? base[j] + adv : kOOB;
-      dma16(rs, region + (j * NW + w) * 1024, off);
+      lds_dma16(rs, region + (j * NW + w) * 1024, off);
     }
   }
 };
@@ -562,7 +539,7 @@ struct DirectK {
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
       const uint32_t off = (base[j] != kOOB && k0 + kl[j] < kend) ? base[j] + adv : kOOB;
-      dma16(rs, region + (j * NW + w) * 1024, off);
+      lds_dma16(rs, region + (j * NW + w) * 1024, off);
     }
   }
 };

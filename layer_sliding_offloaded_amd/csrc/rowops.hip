@@ -408,6 +408,81 @@ ce_rows_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids
   }
 }
 
+// The same row computation with the whole row held in registers: 1024
+// threads, NV 16-byte vectors each (V <= 4096 NV, V % 4 == 0; NV <= 16, as
+// more would spill), so the logits make one trip through HBM (the two-pass
+// kernel above reads them twice).
+// The maximum is reduced first, then the sum of exp(x - max).
+template <typename T, int NV>
+__global__ void __launch_bounds__(1024)
+ce_rows_reg_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids, T* __restrict__ dlogits,
+                   float* __restrict__ loss_rows, int t0, int V, int S, float inv_n) {
+  __shared__ float red[16];
+  __shared__ float bc;
+  const int r = blockIdx.x;
+  const int t = t0 + r;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float4* lr = reinterpret_cast<const float4*>(logits + static_cast<int64_t>(r) * V);
+  T* dr = dlogits + static_cast<int64_t>(r) * V;
+  const int V4 = V / 4;
+  const bool has_target = (t % S) != S - 1;
+  if (!has_target) {
+    const float z[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int v = tid; v < V4; v += 1024) store4<T>(dr + 4 * v, z);
+    if (tid == 0) loss_rows[t] = 0.f;
+    return;
+  }
+  const int tgt = ids[t + 1];
+  float4 x[NV];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = tid + k * 1024;
+    x[k] = v < V4 ? lr[v] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    m = fmaxf(m, fmaxf(fmaxf(x[k].x, x[k].y), fmaxf(x[k].z, x[k].w)));
+  }
+  m = wave_max(m);
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  if (w == 0) {
+    float v = lane < 16 ? red[lane] : -INFINITY;
+    v = wave_max(v);
+    if (lane == 0) bc = v;
+  }
+  __syncthreads();
+  const float M = bc;
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    sum += (__expf(x[k].x - M) + __expf(x[k].y - M)) + (__expf(x[k].z - M) + __expf(x[k].w - M));
+  sum = wave_sum(sum);
+  __syncthreads();  // every wave has read bc
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  if (w == 0) {
+    float v = lane < 16 ? red[lane] : 0.f;
+    v = wave_sum(v);
+    if (lane == 0) bc = v;
+  }
+  __syncthreads();
+  const float lse = M + __logf(bc);
+  const bool ok = tgt >= 0 && tgt < V;
+  if (tid == 0) loss_rows[t] = ok ? (lse - logits[static_cast<int64_t>(r) * V + tgt]) : __builtin_nanf("");
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = tid + k * 1024;
+    if (v < V4) {
+      float p[4] = {__expf(x[k].x - lse), __expf(x[k].y - lse), __expf(x[k].z - lse), __expf(x[k].w - lse)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * v + q == tgt) p[q] -= 1.f;
+        p[q] = ok ? p[q] * inv_n : __builtin_nanf("");
+      }
+      store4<T>(dr + 4 * v, p);
+    }
+  }
+}
+
 // loss = (sum over t of loss_rows[t]) * inv_n, one block, fixed order.
 __global__ void __launch_bounds__(256)
 loss_reduce_kernel(const float* __restrict__ loss_rows, float* __restrict__ loss, int rows, float inv_n) {
@@ -532,6 +607,23 @@ hipError_t adam_device(int dtype, float* p, float* m, float* v, const float* g, 
 hipError_t ce_rows(int dtype, const float* logits, const int32_t* ids, void* dlogits, float* loss_rows, int t0,
                    int R, int V, int S, float inv_n, hipStream_t s) {
   if (R <= 0) return hipSuccess;
+  // whole row in registers when V fits 1024 threads x NV 16-byte vectors
+  const int nv = V % 4 ? 0 : (V + 4095) / 4096;
+#define SF_CE_REG(NV)                                                                                          \
+  if (nv <= NV) {                                                                                              \
+    if (dtype == 1)                                                                                            \
+      hipLaunchKernelGGL((ce_rows_reg_kernel<bf16, NV>), dim3(R), dim3(1024), 0, s, logits, ids,              \
+                         static_cast<bf16*>(dlogits), loss_rows, t0, V, S, inv_n);                             \
+    else                                                                                                       \
+      hipLaunchKernelGGL((ce_rows_reg_kernel<float, NV>), dim3(R), dim3(1024), 0, s, logits, ids,             \
+                         static_cast<float*>(dlogits), loss_rows, t0, V, S, inv_n);                            \
+    return hipGetLastError();                                                                                  \
+  }
+  if (nv > 0) {
+    SF_CE_REG(8)
+    SF_CE_REG(16)
+  }
+#undef SF_CE_REG
   if (dtype == 1)
     hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(R), dim3(256), 0, s, logits, ids, static_cast<bf16*>(dlogits),
                        loss_rows, t0, R, V, S, inv_n);

@@ -17,11 +17,17 @@ Modes:
 * ``gemm-runs``: from the same database, the average duration of each layer
   GEMM in ``bench.py``'s own per-GEMM timing loop (to set against the
   durations ``bench.py`` measures with HIP events).
+* ``head-study``: the chunked LM head + cross-entropy (``sf_head_fwd_bwd``)
+  at one shape for several chunk sizes, the largest being the whole token
+  count (every logit materialised at once): device bytes of the head's
+  workspace and of all its buffers, time per call and TFLOP/s.
 
     python -m layer_sliding_offloaded_amd.prof probe --workload stack4-h1024-bf16
     python -m layer_sliding_offloaded_amd.prof summarize FETCH_CSV WRITE_CSV --workload stack4-h1024-bf16
     python -m layer_sliding_offloaded_amd.prof kernels RESULTS_DB [--top N]
     python -m layer_sliding_offloaded_amd.prof gemm-runs RESULTS_DB --workload W
+    python -m layer_sliding_offloaded_amd.prof head-study --hidden 4096 --vocab 128256 --batch 4 --seq 2048 \
+        --chunks 8192,4096,2048,1024,512,256
 """
 
 import argparse
@@ -224,12 +230,85 @@ def gemm_runs(db_path, workload, min_run=20):
         print(f"| {name} | `{k}` | {gx}x{gy} | {len(r['gemm'])} | {g:.2f} | {red:.2f} | {g + red:.2f} |")
 
 
+def head_study(hidden, vocab, batch, seq, chunks, reps=5):
+    """Chunk-size sweep of the fused head (final RMSNorm, logits, cross
+    entropy, dx, dW_lm) on synthetic inputs: x ~ N(0, 1), W_lm ~ N(0, 0.02^2),
+    g_f = 1, ids ~ U[0, vocab)."""
+    import statistics
+
+    import torch
+
+    sys.path.insert(0, os.path.dirname(HERE))
+    import seeded_inputs as si
+    from layer_sliding_offloaded_amd import runtime as rt
+    from layer_sliding_offloaded_amd import sf
+    sf.load()
+    w = si.WORKLOADS["stack4-h1024-bf16"].with_(hidden=hidden, n_heads=hidden // 128, n_kv_heads=hidden // 128,
+                                                head_dim=128, vocab=vocab, batch=batch, seq=seq)
+    T = batch * seq
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(T, hidden, generator=gen, device="cuda").to(torch.bfloat16)
+    wlm = (torch.randn(vocab, hidden, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    gf = torch.ones(hidden, device="cuda").to(torch.bfloat16)
+    ids = torch.randint(0, vocab, (T,), generator=gen, device="cuda", dtype=torch.int32)
+    loss = torch.empty(1, device="cuda")
+    dx = torch.empty_like(x)
+    dgf = torch.empty(hidden, device="cuda")
+    dwlm = torch.empty(vocab, hidden, device="cuda")
+    fixed = sum(t.numel() * t.element_size() for t in (x, wlm, gf, ids, loss, dx, dgf, dwlm))
+    s = torch.cuda.current_stream()
+    flops = 6.0 * T * vocab * hidden
+    rows = []
+    for R in chunks:
+        shape = rt.shape_from(w)
+        L = sf.sf_layer_layout(shape, R)
+        full = rt.device_bytes(L.workspace_bytes + L.head_workspace_bytes)
+        ctx = sf.sf_ctx_create(shape, R, full.data_ptr(), full.numel())
+
+        def call():
+            sf.sf_head_fwd_bwd(ctx, gf.data_ptr(), wlm.data_ptr(), x.data_ptr(), ids.data_ptr(), loss.data_ptr(),
+                               dx.data_ptr(), dgf.data_ptr(), dwlm.data_ptr(), s.cuda_stream)
+
+        for _ in range(2):
+            call()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            call()
+            e1.record(s)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = statistics.median(times)
+        rows.append((R, L.head_workspace_bytes, ms, loss.item()))
+        print(f"[head-study] rows {R}: workspace {L.head_workspace_bytes / 2**20:.1f} MiB, {ms:.3f} ms", file=sys.stderr,
+              flush=True)
+        sf.sf_ctx_destroy(ctx)
+        del full
+        torch.cuda.synchronize()
+    base_ws = max(r[1] for r in rows)
+    print(f"Head shape: T = {batch} x {seq} = {T} tokens, hidden {hidden}, vocab {vocab} (bf16, fp32 dW_lm); "
+          f"fixed head buffers (x, dx, W_lm, dW_lm, g_f, dg_f, ids, loss): {fixed / 2**30:.3f} GiB.\n")
+    print("| chunk rows | head workspace (logits fp32 + dlogits bf16 + norm) | vs all rows at once | "
+          "head total (workspace + fixed) | vs all rows at once | ms per call | TFLOP/s | loss |")
+    print("|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for R, wsb, ms, lv in rows:
+        print(f"| {R} | {wsb / 2**30:.3f} GiB | {100.0 * (1 - wsb / base_ws):.1f} % less | "
+              f"{(wsb + fixed) / 2**30:.3f} GiB | {100.0 * (1 - (wsb + fixed) / (base_ws + fixed)):.1f} % less | "
+              f"{ms:.3f} | {flops / (ms * 1e-3) / 1e12:.0f} | {lv:.5f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs"])
+    ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs", "head-study"])
     ap.add_argument("files", nargs="*")
     ap.add_argument("--workload", default="stack4-h1024-bf16")
     ap.add_argument("--top", type=int, default=30)
+    ap.add_argument("--hidden", type=int, default=4096)
+    ap.add_argument("--vocab", type=int, default=128256)
+    ap.add_argument("--batch", type=int, default=4)
+    ap.add_argument("--seq", type=int, default=2048)
+    ap.add_argument("--chunks", default="8192,4096,2048,1024,512,256")
     a = ap.parse_args()
     if a.mode == "probe":
         probe(a.workload)
@@ -237,6 +316,8 @@ def main():
         summarize(a.files[0], a.files[1], a.workload)
     elif a.mode == "gemm-runs":
         gemm_runs(a.files[0], a.workload)
+    elif a.mode == "head-study":
+        head_study(a.hidden, a.vocab, a.batch, a.seq, [int(c) for c in a.chunks.split(",")])
     else:
         kernels(a.files[0], a.top)
 

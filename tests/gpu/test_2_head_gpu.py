@@ -51,6 +51,24 @@ def test_head_parity(dtype, tol, chunk):
     assert all(v <= tol for v in errs.values()), errs
 
 
+@pytest.mark.parametrize("dtype,tol,vocab", [("bf16", 2e-2, 65536), ("f32", 1e-4, 65544), ("bf16", 2e-2, 128256)])
+def test_head_parity_vocab_paths(dtype, tol, vocab):
+    """Cross-entropy rows held in registers (V <= 65536) and the two-pass
+    kernel above that (65544; a Llama-3-sized 128256 vocabulary)."""
+    w = BASE.with_(dtype=dtype, vocab=vocab, batch=2, seq=64)
+    say("head-vocab", dtype, vocab, w)
+    gf = si.final_gain(w, gains="random")
+    Wlm = si.lm_head(w)
+    x = si.layer_input(w)
+    ids = si.token_ids(w)
+    loss, dx, dgf, dwlm = run_head(w, 48, gf, Wlm, x, ids)
+    lo, dxo, dgfo, dwo = oracle.head_fwd_bwd(gf.astype(np.float64), Wlm.astype(np.float64), x.astype(np.float64),
+                                             ids, w.eps)
+    errs = {"loss": abs(loss - lo) / abs(lo), "dx": rel(dx, dxo), "dgf": rel(dgf, dgfo), "dWlm": rel(dwlm, dwo)}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(v <= tol for v in errs.values()), errs
+
+
 def test_head_zero_weight_loss_is_ln_v():
     w = BASE.with_(dtype="bf16", vocab=32000, seq=64)
     say("head-zero-weight", w)
