@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--no-adam", action="store_true",
                     help="stream gradients out but skip the optimizer (default for the 123B-shaped slice, whose "
                          "fp32 Adam states would need 133 GB of host memory)")
+    ap.add_argument("--grad-slots", type=int, default=2,
+                    help="pinned fp32 gradient slots shared by all layers (a ring; n_layers = one buffer per layer)")
     ap.add_argument("--ckpt", action="store_true",
                     help="sliding activation checkpointing: layer inputs wait in pinned host memory and each "
                          "layer's forward is recomputed before its backward")
@@ -182,9 +184,17 @@ def main():
     head = None
     if w.vocab:
         head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
-    eng = rt.Engine(w, layers, head, window=w.window, n_grad_slots=2, adam=adam, chunk=2048,
+    eng = rt.Engine(w, layers, head, window=w.window, n_grad_slots=args.grad_slots, adam=adam, chunk=2048,
                     adam_threads=args.adam_threads, ckpt=args.ckpt)
     hbm = {"unit_pool_bytes": eng.pool.numel(), "activation_bytes": eng.act_bytes}
+    # host memory the engine holds for the layers (pinned: bf16 params, fp32
+    # gradient slots, checkpoints; pageable: fp32 master weights and moments)
+    host = {"params_pinned": sum(t.numel() for t in eng.h_params),
+            "grad_slots_pinned": sum(t.numel() for t in eng.h_slots),
+            "checkpoints_pinned": eng.h_ckpt.numel() if eng.h_ckpt is not None else 0,
+            "master_m_v": sum(3 * m.nbytes for m in eng.h_master)}
+    host["total"] = sum(host.values())
+    host["grad_slots"] = args.grad_slots
     print(f"[bench] engine ready ({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr, flush=True)
     if head is not None:
         d_in = torch.from_numpy(si.token_ids(w).reshape(-1)).cuda()
@@ -278,6 +288,7 @@ def main():
                    "adam": ("host fp32 (layers), device fp32 (resident embedding/head)" if adam else "off"),
                    "activation_checkpointing": args.ckpt, "parallelism": "none (1 GPU)"},
         "engine_hbm": hbm,
+        "engine_host_bytes": host,
         "mfma_util_pct": round(100.0 * layer_tflops / peak, 2),
         "kernel_tokens_per_s_per_layer": round(T / (layer_ms * 1e-3), 1),
         "layer_fwd_bwd_ms": round(layer_ms, 4),

@@ -17,6 +17,13 @@ Modes:
 * ``gemm-runs``: from the same database, the average duration of each layer
   GEMM in ``bench.py``'s own per-GEMM timing loop (to set against the
   durations ``bench.py`` measures with HIP events).
+* ``rowops``: from a kernel trace of ``bench.py``, the HBM-bound kernels of
+  the layer and head (RMSNorm forward / backward, gain-gradient partials,
+  the attention-backward row dot, cross-entropy rows, embedding gather, the
+  device Adam of the embedding / LM head): median duration, algorithmic
+  bytes per launch for the workload, achieved GB/s and the fraction of the
+  8 TB/s HBM peak.  The median is taken over all launches; most of them are
+  bench.py's resident-layer loop, where nothing else runs.
 * ``head-study``: the chunked LM head + cross-entropy (``sf_head_fwd_bwd``)
   at one shape for several chunk sizes, the largest being the whole token
   count (every logit materialised at once): device bytes of the head's
@@ -26,6 +33,7 @@ Modes:
     python -m layer_sliding_offloaded_amd.prof summarize FETCH_CSV WRITE_CSV --workload stack4-h1024-bf16
     python -m layer_sliding_offloaded_amd.prof kernels RESULTS_DB [--top N]
     python -m layer_sliding_offloaded_amd.prof gemm-runs RESULTS_DB --workload W
+    python -m layer_sliding_offloaded_amd.prof rowops RESULTS_DB --workload W
     python -m layer_sliding_offloaded_amd.prof head-study --hidden 4096 --vocab 128256 --batch 4 --seq 2048 \
         --chunks 8192,4096,2048,1024,512,256
 """
@@ -230,6 +238,50 @@ def gemm_runs(db_path, workload, min_run=20):
         print(f"| {name} | `{k}` | {gx}x{gy} | {len(r['gemm'])} | {g:.2f} | {red:.2f} | {g + red:.2f} |")
 
 
+HBM_PEAK = 8.0e12
+
+
+def rowops(db_path, workload):
+    """Achieved HBM bandwidth of the row kernels (see the module docstring)."""
+    import sqlite3
+    import statistics
+    sys.path.insert(0, os.path.dirname(HERE))
+    import seeded_inputs as si
+    w = si.WORKLOADS[workload]
+    e = 2 if w.dtype == "bf16" else 4
+    T, H, V = w.tokens, w.hidden, w.vocab
+    nq = w.n_heads * w.head_dim
+    R = min(T, 2048)  # head chunk rows bench.py uses
+    con = sqlite3.connect(db_path)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    name_col = "kernel_name" if "kernel_name" in cols else "name"
+    rows = con.execute(f"select {name_col}, start, end, grid_x from kernels").fetchall()
+    # name fragment, launch filter (on its duration in us), algorithmic bytes per launch, what is counted
+    spec = [
+        ("rmsnorm_fwd_kernel", None, 2 * T * H * e + T * 4 + H * e, "x in, y out, r out"),
+        ("rmsnorm_bwd_kernel", None, 4 * T * H * e + T * 4 + H * e, "dy, x, residual in; dx out"),
+        ("gain_partial_kernel", None, 2 * T * H * e + T * 4 + 128 * H * 4, "dy, x in; 128 partial rows out"),
+        ("attn_dot_kernel", None, 2 * T * nq * e + T * w.n_heads * 4, "dA, O in; row sums out"),
+        ("ce_rows_reg_kernel", None, R * V * (4 + e) + R * 8, "fp32 logits in, dlogits out"),
+        ("ce_rows_kernel", None, R * V * (4 + e) + R * 8, "fp32 logits in (twice), dlogits out"),
+        ("embed_fwd_kernel", None, 2 * T * H * e + T * 4, "rows gathered, x0 out"),
+        # the [V, H] tensors' updates (the [H] final gain's take a few us)
+        ("adam_device_kernel", lambda us: us > 20.0, V * H * (7 * 4 + e), "g, p, m, v in; p, m, v, bf16 out ([V, H])"),
+    ]
+    print("| kernel | launches | median us | algorithmic bytes per launch | counted | GB/s | of 8 TB/s |")
+    print("|---|---:|---:|---:|---|---:|---:|")
+    for frag, gfilter, nbytes, what in spec:
+        d = [(t1 - t0) / 1e3 for n, t0, t1, gx in rows
+             if frag in short_name(n) and (gfilter is None or gfilter((t1 - t0) / 1e3))
+             and not (frag == "ce_rows_kernel" and "ce_rows_reg_kernel" in short_name(n))]
+        if not d or nbytes <= 0:
+            continue
+        us = statistics.median(d)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(f"| `{frag}` | {len(d)} | {us:.1f} | {nbytes / 1e6:.1f} MB | {what} | {gbs:.0f} | "
+              f"{100 * gbs * 1e9 / HBM_PEAK:.0f} % |")
+
+
 def head_study(hidden, vocab, batch, seq, chunks, reps=5):
     """Chunk-size sweep of the fused head (final RMSNorm, logits, cross
     entropy, dx, dW_lm) on synthetic inputs: x ~ N(0, 1), W_lm ~ N(0, 0.02^2),
@@ -300,7 +352,7 @@ def head_study(hidden, vocab, batch, seq, chunks, reps=5):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs", "head-study"])
+    ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs", "rowops", "head-study"])
     ap.add_argument("files", nargs="*")
     ap.add_argument("--workload", default="stack4-h1024-bf16")
     ap.add_argument("--top", type=int, default=30)
@@ -316,6 +368,8 @@ def main():
         summarize(a.files[0], a.files[1], a.workload)
     elif a.mode == "gemm-runs":
         gemm_runs(a.files[0], a.workload)
+    elif a.mode == "rowops":
+        rowops(a.files[0], a.workload)
     elif a.mode == "head-study":
         head_study(a.hidden, a.vocab, a.batch, a.seq, [int(c) for c in a.chunks.split(",")])
     else:
