@@ -30,6 +30,9 @@ namespace sf {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// forward softmax: largest growth (log2 units) of a row's running maximum
+// over its current shift before the shift is moved
+constexpr float kLazy = 8.0f;
 constexpr uint32_t kOOB = 0x80000000u;  // past every operand's extent
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -197,7 +200,10 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
 #pragma unroll
     for (int d = 0; d < FD; ++d) oacc[f][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrow[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
+  // row sums of the (bf16) probabilities, accumulated by MFMA against a
+  // fragment of ones: every element of lacc[f] holds the sum for row lr
+  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
   const float sc = a.scale * kLog2e;
   const int nkv = (min(q0 + BQ, S) - 1) / BKV + 1;
   int ko[DC], vo[FD];
@@ -246,6 +252,10 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
             for (int v = 0; v < 4; ++v)
               if (kv0 + fk * 16 + lg * 4 + v > qw + f * 16 + lr) s[f][fk][v] = -INFINITY;
       }
+      // The shift m of a row moves only when the tile's maximum exceeds it
+      // by more than kLazy (log2 units): probabilities stay <= 2^kLazy, and
+      // the output and row sum, which carry the same shift, are rescaled
+      // only then (softmax is invariant to a common shift of the exponents).
       float alpha[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
@@ -256,34 +266,33 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
           for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[f][fk][v]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrow[f], mx * sc);
+        const float ms = mx * sc;
+        const float mnew = ms > mrow[f] + kLazy ? ms : mrow[f];
         alpha[f] = __builtin_amdgcn_exp2f(mrow[f] - mnew);
         mrow[f] = mnew;
-        float ps = 0.f;
 #pragma unroll
         for (int fk = 0; fk < 4; ++fk)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[f][fk][v], sc, -mnew));
-            s[f][fk][v] = p;
-            ps += p;
-          }
-        lsum[f] = lsum[f] * alpha[f] + ps;
+          for (int v = 0; v < 4; ++v) s[f][fk][v] = __builtin_amdgcn_exp2f(fmaf(s[f][fk][v], sc, -mnew));
       }
-      // rescale the output only when some row's maximum moved
       if (!__all(alpha[0] == 1.0f && alpha[1] == 1.0f)) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < 2; ++f) {
 #pragma unroll
           for (int d = 0; d < FD; ++d)
 #pragma unroll
             for (int v = 0; v < 4; ++v) oacc[f][d][v] *= alpha[f];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) lacc[f][v] *= alpha[f];
+        }
       }
       // O^T += V^T P^T: lane holds O[q = qw + 16 f + lr][d = 16 fd + 4 lg + v]
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint4 pf0 = pack8(s[0][2 * j], s[0][2 * j + 1]);
         const uint4 pf1 = pack8(s[1][2 * j], s[1][2 * j + 1]);
+        Mfma<bf16>::run(lacc[0], ones, pf0);
+        Mfma<bf16>::run(lacc[1], ones, pf1);
 #pragma unroll
         for (int d = 0; d < FD; ++d) {
           const uint4 vf = frag_t<D>(Vc, vo[d], j);
@@ -303,9 +312,7 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
   bf16* obase = static_cast<bf16*>(a.out) + bs * a.ld_out + h * D;
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
-    float l = lsum[f];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = lacc[f][0];
     const int q = qw + f * 16 + lr;
     if (q < S) {
       const float inv = 1.0f / l;

@@ -32,12 +32,22 @@
 // back into their units, each upload overlapping the Adam of the next range,
 // and the next step's forward starts without waiting for them.
 //
-// Embedding and LM head (resident in HBM, updated by host Adam like a
-// layer): the LM-head and final-norm gradients leave right after the head
-// and are applied (and their parameters uploaded again) while the layer
-// backward runs; the embedding gradient leaves sparse -- only the rows of
-// ids present in the batch are nonzero -- and its dense Adam (every row:
-// moments decay) is pipelined with the upload of the updated rows.
+// Embedding and LM head (resident in HBM): by default a device Adam updates
+// them (fp32 master and moments in HBM), the LM head and final norm on a
+// side stream while the layer backward runs.  With SF_ENGINE_HEAD_HOST_ADAM
+// they take the host path like a layer: the LM-head and final-norm gradients
+// leave right after the head and are applied (and their parameters uploaded
+// again) while the layer backward runs; the embedding gradient leaves sparse
+// -- only the rows of ids present in the batch are nonzero -- and its dense
+// Adam (every row: moments decay) is pipelined with the upload of the
+// updated rows.
+//
+// Sliding activation checkpointing (de/es/fr §2B, SF_ENGINE_CKPT): layer
+// inputs leave for pinned host memory on the D2H stream as soon as they are
+// produced and the forward cycles through a ring of three input buffers; in
+// the backward the input of layer i-1 comes back into one of two slots while
+// layer i runs, and each layer first recomputes its forward (same kernels,
+// same inputs: the same bits) into a scratch output and saved set.
 #include <algorithm>
 #include <atomic>
 #include <chrono>

@@ -156,13 +156,14 @@ struct Loader {
   }
 };
 
-// Split-K factor for a grid of `tiles` output tiles: grids that cover most
-// CUs run unsplit; smaller ones double the split while the blocks still fit
-// one pass over the 256 CUs and every k-range stays at least 1024 deep
-// (measured: a split of short k-ranges costs more in partial-sum traffic and
-// the reduction than it gains).
+// Split-K factor for a grid of `tiles` output tiles: grids of at least half
+// the CUs' worth of tiles run unsplit; smaller ones double the split while
+// the blocks still fit one pass over the 256 CUs and every k-range stays at
+// least 1024 deep (measured: a split of short k-ranges, or of a grid that
+// already fills half the chip, costs more in partial-sum traffic and the
+// reduction than it gains).
 int splitk_factor(int tiles, int K) {
-  if (tiles >= 160) return 1;
+  if (tiles >= 128) return 1;
   int S = 1;
   while (S < 8 && tiles * S * 2 <= 256 && K / (S * 2) >= 1024) S *= 2;
   return S;
@@ -412,7 +413,14 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // [k][row] slot swizzle: 16 lanes of one transpose read cover 4 consecutive k
 // (the same two slots each); lanes 16 apart cover k 8 apart.  This map sends
 // those 8 k-rows to 8 distinct slot pairs.
-__device__ __forceinline__ int kswz(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+// Tiles of ROWS < 128 have fewer 16-byte slots per k-row (ROWS / 8); the map
+// keeps its low bits there, so a swizzled slot never leaves its k-row.
+template <int ROWS>
+__device__ __forceinline__ int kswz(int k) {
+  static_assert(ROWS >= 64, "at least 8 slots per k-row");
+  const int s = 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+  return ROWS >= 128 ? s : (s & (ROWS / 8 - 1));
+}
 // [row][k] slot swizzle
 __device__ __forceinline__ int rswz(int row) { return (row >> 1) & 7; }
 
@@ -443,7 +451,7 @@ struct Direct {
       } else {
         const int b = lane * 16;
         const int k = idx * KPI + b / ROWB;
-        const int ls = ((b % ROWB) / 16) ^ kswz(k);
+        const int ls = ((b % ROWB) / 16) ^ kswz<ROWS>(k);
         const int r = r0 + ls * 8;
         base[j] = r < rows ? static_cast<uint32_t>((static_cast<int64_t>(k) * ld + r) * 2) : kOOB;
         kl[j] = k;
@@ -478,7 +486,7 @@ __device__ __forceinline__ uint4 frag(const char* region, int rb, int ks, int lr
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int k = ks * 32 + 8 * lg + 4 * t + (lr >> 2);
-      const char* p = region + k * (ROWS * 2) + ((slot ^ kswz(k)) * 16) + half * 8;
+      const char* p = region + k * (ROWS * 2) + ((slot ^ kswz<ROWS>(k)) * 16) + half * 8;
       const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_v4i16*)(const_cast<char*>(p)));
       w[2 * t] = static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
@@ -527,7 +535,7 @@ struct DirectK {
       } else {
         const int b = lane * 16;
         const int k = idx * KPI + b / ROWB;
-        const int ls = ((b % ROWB) / 16) ^ kswz(k);
+        const int ls = ((b % ROWB) / 16) ^ kswz<ROWS>(k);
         const int r = r0 + ls * 8;
         base[j] = r < rows ? static_cast<uint32_t>((static_cast<int64_t>(k) * ld + r) * 2) : kOOB;
         kl[j] = k;
@@ -975,10 +983,14 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
       // ping-pong kernel (8 waves of 128x64, 4 stages of 32 k); smaller grids
       // take 128x128 tiles, 4 stages of 64 k with 8 waves of 32x64, or 2
       // stages when there are enough tiles to keep every CU busy without a
-      // deep pipeline.
+      // deep pipeline, or 128x64 tiles when even 128x128 ones would leave
+      // half the CUs idle.
       if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb);
       const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
       const long t128 = static_cast<long>((g.M + 127) / 128) * ((ncols + 127) / 128);
+      // at most half the CUs' worth of 128x128 tiles: 128x64 tiles (8 waves
+      // of 32x32) double the blocks instead of splitting K
+      if (t128 <= 128) return launch<T, 128, 64, 32, 32, LAY, E, 2, 64>(g, s, ws, wsb, ab, bb);
       if (t128 >= 320) {
         if constexpr (LAY == GemmLayout::TN) return launch<T, 128, 128, 64, 64, LAY, E, 2, 32>(g, s, ws, wsb, ab, bb);
         return launch<T, 128, 128, 32, 64, LAY, E, 1>(g, s, ws, wsb, ab, bb);
