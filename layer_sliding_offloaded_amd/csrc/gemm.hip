@@ -928,6 +928,9 @@ bool direct_ok(const GemmArgs& g, int64_t* a_bytes, int64_t* b_bytes) {
 template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, int KIND = 0, int BK = 64, int NS = 4>
 hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_bytes, int64_t a_bytes = 0,
                   int64_t b_bytes = 0) {
+  // the RoPE column map pairs columns i and i + head_dim/2 inside one tile
+  if constexpr (E == Epi::Rope)
+    if (g_in.head_dim <= 0 || BN % g_in.head_dim != 0) return hipErrorInvalidValue;
   const int ntm = (g_in.M + BM - 1) / BM;
   const int ncols = (E == Epi::SwigluFwd) ? 2 * g_in.ffn : g_in.N;
   const int ntn = (ncols + BN - 1) / BN;
@@ -989,8 +992,10 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
       const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
       const long t128 = static_cast<long>((g.M + 127) / 128) * ((ncols + 127) / 128);
       // at most half the CUs' worth of 128x128 tiles: 128x64 tiles (8 waves
-      // of 32x32) double the blocks instead of splitting K
-      if (t128 <= 128) return launch<T, 128, 64, 32, 32, LAY, E, 2, 64>(g, s, ws, wsb, ab, bb);
+      // of 32x32) double the blocks instead of splitting K (the RoPE
+      // epilogue needs whole heads in a tile: head_dim <= 64 there)
+      if (t128 <= 128 && (E != Epi::Rope || 64 % g.head_dim == 0))
+        return launch<T, 128, 64, 32, 32, LAY, E, 2, 64>(g, s, ws, wsb, ab, bb);
       if (t128 >= 320) {
         if constexpr (LAY == GemmLayout::TN) return launch<T, 128, 128, 64, 64, LAY, E, 2, 32>(g, s, ws, wsb, ab, bb);
         return launch<T, 128, 128, 32, 64, LAY, E, 1>(g, s, ws, wsb, ab, bb);
