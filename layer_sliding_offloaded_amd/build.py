@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# attention: MFMA accumulators in VGPRs (the softmax arithmetic reads them;
+# in AGPRs every tile paid a copy per accumulator register)
+HIP_EXTRA = {"attn_direct.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
 # -ffp-contract=off: host Adam rounds every operation exactly like the device kernel
 HOST_EXTRA = {"adam.cpp": ["-mavx2", "-mfma", "-fno-math-errno", "-ffp-contract=off"]}
@@ -45,7 +48,7 @@ def build(verbose=False, jobs=None):
     objs = []
     for s in HIP_SOURCES:
         o = os.path.join(BUILD, s + ".o")
-        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        cmds.append([hipcc, *HIPCC_FLAGS, *HIP_EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o])
         objs.append(o)
     for s in HOST_SOURCES:
         o = os.path.join(BUILD, s + ".o")

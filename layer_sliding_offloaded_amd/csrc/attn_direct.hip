@@ -683,14 +683,16 @@ hipError_t run_bwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
   const int64_t dout_bytes = ((T - 1) * a.ld_dout + static_cast<int64_t>(a.n_heads) * D) * 2;
   const int64_t stat_bytes = static_cast<int64_t>(a.batch) * a.n_heads * a.seq * 4;
   // Block shapes (measured; every shape gives the same bits): dK/dV with 4
-  // waves of 16 keys; dQ with 8 waves of 32 queries when that still makes
-  // two blocks per CU, else 8 waves of 16.
+  // waves of 16 keys; dQ with 4 waves of 32 queries when that still makes
+  // two blocks per CU, else 8 waves of 16.  (This file is compiled with the
+  // MFMA accumulators held in VGPRs, which made the 4-wave dQ the fastest:
+  // no AGPR-to-VGPR copies before the softmax arithmetic.)
   hipLaunchKernelGGL((attn_dkdv_direct<D, 1, 4>), dim3((a.seq + 63) / 64, a.n_kv, a.batch), dim3(256), 0, s, a,
                      static_cast<int>(qkv_bytes), static_cast<int>(dout_bytes), static_cast<int>(stat_bytes));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (static_cast<int64_t>((a.seq + 255) / 256) * a.n_heads * a.batch >= 512)
-    hipLaunchKernelGGL((attn_dq_direct<D, 2, 8>), dim3((a.seq + 255) / 256, a.n_heads, a.batch), dim3(512), 0, s, a,
+  if (static_cast<int64_t>((a.seq + 127) / 128) * a.n_heads * a.batch >= 512)
+    hipLaunchKernelGGL((attn_dq_direct<D, 2, 4>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(256), 0, s, a,
                        static_cast<int>(qkv_bytes));
   else
     hipLaunchKernelGGL((attn_dq_direct<D, 1, 8>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(512), 0, s, a,
