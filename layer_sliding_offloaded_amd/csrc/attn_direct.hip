@@ -22,6 +22,8 @@
 //    tile's loads are issued before the current tile's MFMAs.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attention.h"
 #include "common.h"
 
@@ -456,27 +458,32 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
             Mfma<bf16>::run(dp[fk][fq], da, vf[fk][c]);
           }
         }
-      // keys after a query, or queries past the end, only near the diagonal / tail
-      const bool masked = (kvw + KW - 1 > q0) || (q0 + BQ > S);
+      // P and dS; keys after a query, or queries past the end, exist only
+      // near the diagonal / tail, where the masked variant runs
+      auto probs = [&](auto mask) {
 #pragma unroll
-      for (int fq = 0; fq < 4; ++fq) {
-        const float4 lse4 = *reinterpret_cast<const float4*>(Lc + fq * 16 + lg * 4);
-        const float4 dsm4 = *reinterpret_cast<const float4*>(Lc + BQ + fq * 16 + lg * 4);
-        const float lse[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
-        const float dsm[4] = {dsm4.x, dsm4.y, dsm4.z, dsm4.w};
+        for (int fq = 0; fq < 4; ++fq) {
+          const float4 lse4 = *reinterpret_cast<const float4*>(Lc + fq * 16 + lg * 4);
+          const float4 dsm4 = *reinterpret_cast<const float4*>(Lc + BQ + fq * 16 + lg * 4);
+          const float lse[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
+          const float dsm[4] = {dsm4.x, dsm4.y, dsm4.z, dsm4.w};
 #pragma unroll
-        for (int fk = 0; fk < KF; ++fk) {
-          const int kv = kvw + fk * 16 + lr;
+          for (int fk = 0; fk < KF; ++fk) {
+            const int kv = kvw + fk * 16 + lr;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int q = q0 + fq * 16 + lg * 4 + v;
-            float pv = __builtin_amdgcn_exp2f(fmaf(p[fk][fq][v], sc, -lse[v]));
-            if (masked && (kv > q || q >= S)) pv = 0.f;
-            p[fk][fq][v] = pv;
-            dp[fk][fq][v] = pv * (dp[fk][fq][v] - dsm[v]);  // dS
+            for (int v = 0; v < 4; ++v) {
+              const int q = q0 + fq * 16 + lg * 4 + v;
+              float pv = __builtin_amdgcn_exp2f(fmaf(p[fk][fq][v], sc, -lse[v]));
+              if constexpr (decltype(mask)::value)
+                if (kv > q || q >= S) pv = 0.f;
+              p[fk][fq][v] = pv;
+              dp[fk][fq][v] = pv * (dp[fk][fq][v] - dsm[v]);  // dS
+            }
           }
         }
-      }
+      };
+      if ((kvw + KW - 1 > q0) || (q0 + BQ > S)) probs(std::true_type{});
+      else probs(std::false_type{});
       // dV^T += dO^T P, dK^T += Q^T dS: lane holds X[kv][d = 16 fd + 4 lg + v]
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -626,6 +633,8 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
             Mfma<bf16>::run(dp[f][fk], va, df[f][c]);
           }
         }
+      // (one predicated path: a separate unmasked copy of this loop pushes
+      // the 4-wave d = 128 kernel past 256 registers)
       const bool masked = (kv0 + BKV - 1 > qw) || (kv0 + BKV > S);
 #pragma unroll
       for (int f = 0; f < F; ++f) {
