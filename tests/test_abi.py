@@ -161,3 +161,17 @@ def test_host_adam_update_direction_matches_oracle(lib):
     w1, _, _ = oracle.adam_step(p0.astype(np.float64), 0, 0, g.astype(np.float64), 1, 1e-4, 0.9, 0.999, 1e-8)
     dref = w1 - p0.astype(np.float64)
     assert np.linalg.norm((p - p0) - dref) / np.linalg.norm(dref) <= 1e-3
+
+
+def test_engine_act_bytes_checkpointing(lib):
+    """With SF_ENGINE_CKPT the activation region no longer grows with the
+    layer count: six [T, H] buffers, two saved sets, the gradient buffer and
+    the loss."""
+    w = si.WORKLOADS["stack4-h1024-bf16"]
+    shape = rt.shape_from(w)
+    L = sf.sf_layer_layout(shape, 2048)
+    xb = (w.tokens * w.hidden * 2 + 255) // 256 * 256
+    for n in (1, 2, 4, 32):
+        got = sf.sf_engine_act_bytes_flags(shape, n, sf.SF_ENGINE_CKPT)
+        assert got == 6 * xb + 2 * L.saved_bytes + xb + 256, n
+    assert sf.sf_engine_act_bytes_flags(shape, 4, 0) == sf.sf_engine_act_bytes(shape, 4)
