@@ -401,7 +401,8 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
 //    the tile exactly as it lies in HBM, slots swizzled by k, read with the
 //    LDS transpose load (ds_read_b64_tr_b16), which hands each lane four
 //    consecutive k of one row -- the MFMA operand layout -- directly.
-// Two stages are double-buffered; one barrier per stage.
+// The 2-stage kernel below uses 64-k stages; the multi-stage and ping-pong
+// kernels use the k-depth-generic variants further down.
 namespace direct {
 
 constexpr int kBK = 64;              // k per stage
@@ -669,11 +670,11 @@ gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes)
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
-// Multi-stage variant: NS = 4 stages of BK k each, every stage in its own LDS
-// array (so the compiler can see that reading one stage does not alias the
-// loads into another) and the loop unrolled by 4.  The loads of stage kt + 3
-// are issued after the fragment reads of stage kt; the wait at the end of a
-// stage lets the two newer stages stay in flight.
+// Multi-stage variant: NS stages of BK k each (3 to 6; 4 in use), every
+// stage in its own LDS array and the loop unrolled by NS so that each stage's
+// address is a constant.  The loads of stage kt + NS - 1 are issued after the
+// fragment reads of stage kt; the wait at the end of a stage lets the NS - 2
+// newer stages stay in flight.
 template <int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E, int NS>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {

@@ -50,11 +50,15 @@ COPY_BYTES = 256 << 20
 
 
 def gemm_source_hash():
-    """sha256 of the GEMM kernel source: a stored traffic figure is valid only for it."""
+    """sha256 of the GEMM kernel source with comments and blank lines
+    removed: a stored traffic figure is valid only for that code."""
     h = hashlib.sha256()
     for f in ("gemm.hip", "gemm.h", "common.h"):
-        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(HERE, "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
