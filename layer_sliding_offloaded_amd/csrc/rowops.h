@@ -40,6 +40,6 @@ hipError_t ce_rows(int dtype, const float* logits, const int32_t* ids, void* dlo
 hipError_t loss_reduce(const float* loss_rows, float* loss, int rows, float inv_n, hipStream_t s);
 
 // Number of row chunks used for the gain-gradient partial sums.
-constexpr int kGainChunks = 128;
+constexpr int kGainChunks = 512;
 
 }  // namespace sf

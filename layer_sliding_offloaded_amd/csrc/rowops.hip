@@ -123,6 +123,88 @@ gain_partial_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const
   for (int e = 0; e < VE; e += 4) *reinterpret_cast<float4*>(p + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
 }
 
+// RMSNorm backward and gain-gradient partial sums in one pass over dout and
+// x: a block owns one chunk of rows (waves take every 4th row); a lane holds
+// NV 16-byte vectors of its row (columns (v * 64 + lane) * VE, so each wave
+// load is 1 KB contiguous) of dout and x in registers for both the row dot
+// and dx, and accumulates dout * x * r for its columns over the wave's rows.
+// The 4 waves' column sums are then added in wave order through LDS and
+// written as the chunk's partial row.  For H = NV * 64 * VE.
+template <typename T, int NV>
+__global__ void __launch_bounds__(256)
+rmsnorm_bwd_gain_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const float* __restrict__ r,
+                        const T* __restrict__ g, const T* __restrict__ resid, T* __restrict__ dx,
+                        float* __restrict__ partial, int rows, int H, int rows_per_chunk) {
+  constexpr int VE = 16 / sizeof(T);
+  __shared__ float colsum[NV * 64 * VE];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * rows_per_chunk, t1 = min(rows, t0 + rows_per_chunk);
+  // row data stays packed in the storage dtype (unpacked where used)
+  uint4 gq[NV];
+  float acc[NV][VE];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    gq[v] = *reinterpret_cast<const uint4*>(g + (v * 64 + lane) * VE);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[v][e] = 0.f;
+  }
+  for (int t = t0 + w; t < t1; t += 4) {
+    const int64_t base = static_cast<int64_t>(t) * H;
+    const float rr = r[t];
+    uint4 dq[NV], xq[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      dq[v] = *reinterpret_cast<const uint4*>(dout + base + (v * 64 + lane) * VE);
+      xq[v] = *reinterpret_cast<const uint4*>(xin + base + (v * 64 + lane) * VE);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      float d[VE], xv[VE], gg[VE];
+      Elem<T>::unpack(dq[v], d);
+      Elem<T>::unpack(xq[v], xv);
+      Elem<T>::unpack(gq[v], gg);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) dot += d[e] * gg[e] * xv[e];
+    }
+    dot = wave_sum(dot);
+    const float proj = dot * rr / H;  // mean(dn * n)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      float d[VE], xv[VE], gg[VE], o[VE];
+      Elem<T>::unpack(dq[v], d);
+      Elem<T>::unpack(xq[v], xv);
+      Elem<T>::unpack(gq[v], gg);
+      if (resid) load_vec<T>(resid + base + (v * 64 + lane) * VE, o);
+      else
+#pragma unroll
+        for (int e = 0; e < VE; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        o[e] += rr * (d[e] * gg[e] - xv[e] * rr * proj);
+        acc[v][e] += d[e] * xv[e] * rr;
+      }
+      store_vec<T>(dx + base + (v * 64 + lane) * VE, o);
+    }
+  }
+  // column sums of the chunk: waves 0, 1, 2, 3 in turn
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          float& c = colsum[(v * 64 + lane) * VE + e];
+          c = ww == 0 ? acc[v][e] : c + acc[v][e];
+        }
+    }
+    __syncthreads();
+  }
+  float* p = partial + static_cast<int64_t>(blockIdx.x) * H;
+  for (int j = threadIdx.x * 4; j < H; j += 256 * 4)
+    *reinterpret_cast<float4*>(p + j) = *reinterpret_cast<const float4*>(colsum + j);
+}
+
 // Gain gradient, stage 2: dg[j] = sum over the chunks of partial, in a fixed
 // order: four groups of consecutive chunks, each summed in order (loads
 // issued eight at a time), then the group sums in order.  Block = 64 columns
@@ -524,6 +606,31 @@ hipError_t rmsnorm_bwd(int dtype, const void* dout, const void* xin, const float
   if (rows <= 0) return hipSuccess;
   const int VE = dtype == 1 ? 8 : 4;
   const int rpc = (rows + nchunks - 1) / nchunks;
+  // one pass (rows held in registers) when H is 64 lanes x VE x NV with NV
+  // <= 4 (more would leave one wave per SIMD: the two-kernel path is then
+  // faster)
+  const int nv = H % (64 * VE) ? 0 : H / (64 * VE);
+  if (nv >= 1 && nv <= 4) {
+#define SF_NB(NV)                                                                                              \
+  case NV:                                                                                                     \
+    if (dtype == 1)                                                                                            \
+      hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<bf16, NV>), dim3(nchunks), dim3(256), 0, s,                  \
+                         static_cast<const bf16*>(dout), static_cast<const bf16*>(xin), r,                     \
+                         static_cast<const bf16*>(g), static_cast<const bf16*>(resid), static_cast<bf16*>(dx), \
+                         partial, rows, H, rpc);                                                               \
+    else                                                                                                       \
+      hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<float, NV>), dim3(nchunks), dim3(256), 0, s,                 \
+                         static_cast<const float*>(dout), static_cast<const float*>(xin), r,                   \
+                         static_cast<const float*>(g), static_cast<const float*>(resid),                       \
+                         static_cast<float*>(dx), partial, rows, H, rpc);                                      \
+    break;
+    switch (nv) {
+      SF_NB(1) SF_NB(2) SF_NB(3) SF_NB(4)
+    }
+#undef SF_NB
+    hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + 63) / 64), dim3(256), 0, s, partial, dg, nchunks, H);
+    return hipGetLastError();
+  }
   const dim3 pg((H / VE + 63) / 64, nchunks);
   if (dtype == 1) {
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s,
