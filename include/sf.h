@@ -115,6 +115,9 @@ typedef struct sf_ctx sf_ctx;
  * the context keeps the pointer and carves bwd temporaries and the RoPE
  * tables out of it (the tables are uploaded here, synchronously).  The
  * region must stay alive and untouched by the caller until sf_ctx_destroy.
+ * The context also owns a non-blocking HIP stream (default priority) on
+ * which sf_layer_bwd runs its weight-gradient GEMMs; with the environment
+ * variable SF_SERIAL_WGRAD=1 at creation they stay on the caller's stream.
  * Returns SF_ERR_NO_DEVICE when no gfx950 device is current.
  */
 sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_workspace,
@@ -141,7 +144,12 @@ sf_status sf_layer_fwd(sf_ctx* ctx, const void* d_w, const void* d_x, void* d_y,
  *   d_dw    : fp32 gradients in layout order (sf_layout.grad_off), overwritten
  *             (not accumulated).  Deterministic: no floating-point atomics.
  * Uses the context workspace for temporaries; calls on one context must be
- * serialised on one stream.
+ * serialised on one stream.  When the weight-gradient GEMMs are too small
+ * to fill the device (the [2F, H] one under 512 tiles of 256 x 256), they
+ * run on the context's side stream, forked from `stream` once their operands
+ * exist and joined back before the call's last operation: work queued on
+ * `stream` afterwards sees every output, and the results are the same bits
+ * as with all work on `stream`.
  */
 sf_status sf_layer_bwd(sf_ctx* ctx, const void* d_w, const void* d_x, const void* d_saved,
                        const void* d_dy, void* d_dx, float* d_dw, sf_stream stream);

@@ -12,6 +12,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -145,6 +146,11 @@ WorkLayout work_layout(const Dims& d, int head_chunk_rows) {
     }
     w.splitk = take(sk);
     w.splitk_bytes = sk;
+    // the weight-gradient GEMMs run beside the data-gradient chain: own scratch
+    sk = 0;
+    upd(d.H, d.F, Ti); upd(2 * d.F, d.H, Ti); upd(d.H, d.Nq, Ti); upd(d.Nqkv, d.H, Ti);
+    w.splitk_w = take(sk);
+    w.splitk_w_bytes = sk;
   }
   w.total = o;
   if (d.V > 0) {
@@ -185,6 +191,13 @@ inline const char* at(const void* base, size_t off) { return static_cast<const c
 }  // namespace sf
 
 using namespace sf;
+
+sf_ctx::~sf_ctx() {
+  if (side) (void)hipStreamSynchronize(side);
+  for (hipEvent_t ev : {ev_fork[0], ev_fork[1], ev_fork[2], ev_fork[3], ev_mlp_dw, ev_join})
+    if (ev) (void)hipEventDestroy(ev);
+  if (side) (void)hipStreamDestroy(side);
+}
 
 extern "C" {
 
@@ -257,6 +270,19 @@ sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_
   if (e1 != hipSuccess || e2 != hipSuccess) {
     delete c;
     return fail(SF_ERR_HIP, "uploading RoPE tables failed: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  }
+  // side stream for the weight-gradient GEMMs (default priority); the
+  // environment variable SF_SERIAL_WGRAD=1 keeps them on the caller's stream
+  const char* serial = std::getenv("SF_SERIAL_WGRAD");
+  if (!(serial && serial[0] == '1')) {
+    bool ok = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) == hipSuccess;
+    for (hipEvent_t* ev : {&c->ev_fork[0], &c->ev_fork[1], &c->ev_fork[2], &c->ev_fork[3], &c->ev_mlp_dw,
+                           &c->ev_join})
+      ok = ok && hipEventCreateWithFlags(ev, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      delete c;
+      return fail(SF_ERR_HIP, "creating the weight-gradient stream failed");
+    }
   }
   *out = c;
   return SF_OK;
@@ -360,6 +386,25 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
   float* const skw = reinterpret_cast<float*>(c->ws + c->work.splitk);
   const size_t skb = c->work.splitk_bytes;
   char* dw = reinterpret_cast<char*>(d_dw);
+  // The weight-gradient GEMMs depend on nothing the data-gradient chain
+  // computes after them, so they run on the side stream `sw`, each started
+  // once its operands exist (fork) and overlapping the rest of the chain;
+  // their inputs (dy, saved activations, dGU, dh, dqkv) stay untouched until
+  // the join at the end.  d_dx may alias d_dy, which the Wd gradient reads:
+  // the chain waits for the MLP weight gradients before writing d_dx.
+  // Where the largest of them ([2F, H]) covers two waves of 256 x 256 tiles
+  // on its own, running them beside the chain gains nothing: all stay on s.
+  const long dw_tiles = static_cast<long>((2 * d.F + 255) / 256) * ((d.H + 255) / 256);
+  const bool side = c->side != nullptr && dw_tiles < 512;
+  hipStream_t sw = side ? c->side : s;
+  float* const skw_w = side ? reinterpret_cast<float*>(c->ws + wl.splitk_w) : skw;
+  const size_t skb_w = side ? wl.splitk_w_bytes : skb;
+  auto fork = [&](int k) -> sf_status {
+    if (!side) return SF_OK;
+    SF_HIP(hipEventRecord(c->ev_fork[k], s));
+    SF_HIP(hipStreamWaitEvent(sw, c->ev_fork[k], 0));
+    return SF_OK;
+  };
 
   const void* xn = at(d_saved, sv.xn);
   const float* r1 = reinterpret_cast<const float*>(at(d_saved, sv.r1));
@@ -388,14 +433,18 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
   g.C = dGU; g.C2 = dGU + static_cast<size_t>(d.F) * d.e; g.ldc = 2 * d.F;
   g.R = G; g.R2 = U; g.ldr = d.F;
   g.M = T; g.N = d.F; g.K = d.H;
+  // dWd = dy^T a needs only dy and the saved a: it starts with the chain
+  if (sf_status st = fork(0)) return st;
   SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::SwigluBwd, g, s, skw, skb));
-  // dWd = dy^T a
-  g = GemmArgs();
-  g.A = d_dy; g.lda = d.H;
-  g.B = a; g.ldb = d.F;
-  g.C = dw + L.grad_off[SF_WD]; g.ldc = d.F;
-  g.M = d.H; g.N = d.F; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
+  {
+    GemmArgs gw;
+    gw.A = d_dy; gw.lda = d.H;
+    gw.B = a; gw.ldb = d.F;
+    gw.C = dw + L.grad_off[SF_WD]; gw.ldc = d.F;
+    gw.M = d.H; gw.N = d.F; gw.K = T;
+    SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, gw, sw, skw_w, skb_w));
+  }
+  if (sf_status st = fork(1)) return st;  // dGU exists
   // dhn = [dG | dU] [Wg; Wu]
   g = GemmArgs();
   g.A = dGU; g.lda = 2 * d.F;
@@ -409,12 +458,14 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
   g.B = hn; g.ldb = d.H;
   g.C = dw + L.grad_off[SF_WG]; g.ldc = d.H;
   g.M = 2 * d.F; g.N = d.H; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, sw, skw_w, skb_w));
   // the MLP weight gradients (Wg, Wu, Wd) are final from here on
-  if (ffn_done) SF_HIP(hipEventRecord(ffn_done, s));
+  if (ffn_done) SF_HIP(hipEventRecord(ffn_done, sw));
+  if (side) SF_HIP(hipEventRecord(c->ev_mlp_dw, sw));
   // RMSNorm-2 backward (+ residual dy) -> dh, dg2
   SF_HIP(rmsnorm_bwd(d.dtype, dhn, h, r2, at(d_w, L.off[SF_G2]), d_dy, dh, partial, kGainChunks,
                      reinterpret_cast<float*>(dw + L.grad_off[SF_G2]), T, d.H, s));
+  if (sf_status st = fork(2)) return st;  // dh exists
   // dA = dh Wo
   g = GemmArgs();
   g.A = dh; g.lda = d.H;
@@ -428,7 +479,7 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
   g.B = O; g.ldb = d.Nq;
   g.C = dw + L.grad_off[SF_WO]; g.ldc = d.Nq;
   g.M = d.H; g.N = d.Nq; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, sw, skw_w, skb_w));
   // attention backward (+ inverse RoPE) -> [dq | dk | dv]
   AttnArgs at_;
   at_.qkv = qkv; at_.ld_qkv = d.Nqkv;
@@ -441,6 +492,7 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
   at_.batch = d.B; at_.seq = d.S; at_.n_heads = d.nh; at_.n_kv = d.nkv; at_.head_dim = d.d;
   at_.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d)));
   SF_HIP(attention_bwd(d.dtype, at_, s));
+  if (sf_status st = fork(3)) return st;  // dqkv exists
   // dxn = [dq | dk | dv] Wqkv
   g = GemmArgs();
   g.A = dqkv; g.lda = d.Nqkv;
@@ -454,10 +506,15 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
   g.B = xn; g.ldb = d.H;
   g.C = dw + L.grad_off[SF_WQ]; g.ldc = d.H;
   g.M = d.Nqkv; g.N = d.H; g.K = T;
-  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, s, skw, skb));
-  // RMSNorm-1 backward (+ residual dh) -> dx, dg1
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, g, sw, skw_w, skb_w));
+  // RMSNorm-1 backward (+ residual dh) -> dx, dg1; d_dx may alias d_dy
+  if (side) SF_HIP(hipStreamWaitEvent(s, c->ev_mlp_dw, 0));
   SF_HIP(rmsnorm_bwd(d.dtype, dxn, d_x, r1, at(d_w, L.off[SF_G1]), dh, d_dx, partial, kGainChunks,
                      reinterpret_cast<float*>(dw + L.grad_off[SF_G1]), T, d.H, s));
+  if (side) {
+    SF_HIP(hipEventRecord(c->ev_join, sw));
+    SF_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
+  }
   return SF_OK;
 }
 

@@ -42,6 +42,7 @@ struct GemmArgs {
   // set by gemm(): k-range per grid row and split-K partial buffer
   int kchunk = 0;
   float* partial = nullptr;
+  int rows_epi = 0;  // set by gemm(): outputs take the 16-byte row epilogue
 };
 
 // dtype: 0 = fp32 storage, 1 = bf16 storage (inputs A, B and storage outputs).

@@ -169,7 +169,11 @@ int splitk_factor(int tiles, int K) {
   return S;
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// Logistic sigmoid with the hardware reciprocal (v_rcp_f32, 1 ulp) instead
+// of an IEEE division, which costs about ten instructions per element in
+// the SwiGLU epilogues; large |z| still give exactly 0 and 1.
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* v) {
@@ -198,6 +202,124 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int* tm, int* tn) 
   const int gsize = min(ntm - first_m, GM);
   *tm = first_m + (t % (GM * ntn)) % gsize;
   *tn = (t % (GM * ntn)) / gsize;
+}
+
+// Epilogues that take the row-contiguous path below (bf16 storage).
+// (pair epilogues need 64-column wave tiles: 32 output columns per plane)
+template <Epi E, int WN>
+constexpr bool kRowsEpi = E == Epi::Store || E == Epi::StoreF32 || E == Epi::Resid || E == Epi::SwigluBwd ||
+                          (E == Epi::SwigluFwd && WN >= 64);
+
+// LDS bytes of one wave's staging patch in the row epilogue: 16 rows of the
+// wave's output columns in fp32 (pair epilogues: gate and up planes of WN/2
+// columns each), rows padded by 4 floats.
+template <int WN, Epi E>
+constexpr int kPatchBytes = (E == Epi::SwigluFwd ? 2 * 16 * (WN / 2 + 4) : 16 * (WN + 4)) * 4;
+
+// Row-contiguous epilogue.  A wave's accumulators hold, per lane, 4 columns
+// of one row, so direct stores and operand loads touch 16 rows x 32 bytes
+// per instruction.  Here each 16-row slice of the wave tile goes through a
+// private LDS patch and comes back as 8 consecutive columns of one row per
+// lane: the residual, gate and up operands are read and the outputs written
+// as whole 16-byte vectors (one 64- or 128-byte row segment per 4 or 8
+// lanes), and the operands of the next slice are requested before the
+// current one is finished.  Same arithmetic as the fragment epilogue, so the
+// same bits.  Caller: every wave done with the main loop's LDS (barrier),
+// g.rows_epi set (16-byte aligned outputs and operands, ldc, ldr and the
+// column count multiples of 8, no split-K partials).
+template <int WM, int WN, int FM, int FN, Epi E>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&acc)[FM][FN], int m0, int n0,
+                                              int wm, int wn, int lane, float* patch) {
+  constexpr bool PAIR = E == Epi::SwigluFwd;
+  constexpr int WR = PAIR ? WN / 2 : WN;  // output columns of the wave
+  constexpr int LDW = WR + 4;
+  constexpr int LPR = WR / 8;   // lanes per row
+  constexpr int RPI = 64 / LPR;  // rows per pass
+  constexpr int NIT = 16 / RPI;  // passes per 16-row slice
+  constexpr int NOP = E == Epi::SwigluBwd ? 2 : (E == Epi::Resid ? 1 : 0);
+  static_assert(WR % 8 == 0 && 16 % RPI == 0, "wave tile width");
+  const int lr = lane % 16, lg = lane / 16;
+  const int rr = lane / LPR, cc = (lane % LPR) * 8;
+  // output column of this lane's 8 (gate/up index f for SwiGLU)
+  const int n = PAIR ? n0 / 2 + wn * WR + cc : n0 + wn * WN + cc;
+  const bool n_ok = n < (PAIR ? g.ffn : g.N);
+  const int mb = m0 + wm * WM + rr;
+  uint4 op[2][NIT][NOP > 0 ? NOP : 1];
+  auto fetch = [&](int i, uint4 (&dst)[NIT][NOP > 0 ? NOP : 1]) {
+    if constexpr (NOP > 0) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int m = mb + i * 16 + it * RPI;
+        const int64_t ro = static_cast<int64_t>(m) * g.ldr + n;
+        if (m < g.M && n_ok) {
+          dst[it][0] = *reinterpret_cast<const uint4*>(static_cast<const bf16*>(g.R) + ro);
+          if constexpr (NOP > 1) dst[it][1] = *reinterpret_cast<const uint4*>(static_cast<const bf16*>(g.R2) + ro);
+        }
+      }
+    }
+  };
+  fetch(0, op[0]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if (i + 1 < FM) fetch(i + 1, op[(i + 1) & 1]);
+    // lane (lr, lg) holds row lr, slots j*16 + 4*lg .. +3
+#pragma unroll
+    for (int j = 0; j < (PAIR ? FN / 2 : FN); ++j) {
+      *reinterpret_cast<f32x4*>(patch + lr * LDW + j * 16 + lg * 4) = acc[i][j];
+      if constexpr (PAIR)
+        *reinterpret_cast<f32x4*>(patch + 16 * LDW + lr * LDW + j * 16 + lg * 4) = acc[i][j + FN / 2];
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + rr;
+      const int m = mb + i * 16 + it * RPI;
+      float o[8];
+      {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(patch + r * LDW + cc);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(patch + r * LDW + cc + 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) { o[v] = lo[v]; o[4 + v] = hi[v]; }
+      }
+      if (m >= g.M || !n_ok) continue;
+      const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
+      if constexpr (E == Epi::Store) {
+        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(o);
+      } else if constexpr (E == Epi::StoreF32) {
+        float* c = static_cast<float*>(g.C) + off;
+        *reinterpret_cast<float4*>(c) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(c + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      } else if constexpr (E == Epi::Resid) {
+        float rv[8];
+        Elem<bf16>::unpack(op[i & 1][it][0], rv);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) o[v] += rv[v];
+        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(o);
+      } else if constexpr (E == Epi::SwigluBwd) {
+        float G[8], U[8], dG[8], dU[8];
+        Elem<bf16>::unpack(op[i & 1][it][0], G);
+        Elem<bf16>::unpack(op[i & 1][it][1], U);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float sg = sigmoid_f(G[v]);
+          dG[v] = o[v] * U[v] * sg * (1.0f + G[v] * (1.0f - sg));
+          dU[v] = o[v] * G[v] * sg;
+        }
+        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(dG);
+        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C2) + off) = Elem<bf16>::pack(dU);
+      } else {  // SwigluFwd: o = gate; up from the second plane
+        float u[8], a[8];
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(patch + 16 * LDW + r * LDW + cc);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(patch + 16 * LDW + r * LDW + cc + 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) { u[v] = lo[v]; u[4 + v] = hi[v]; }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) a[v] = silu_f(o[v]) * u[v];
+        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(o);
+        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C2) + off) = Elem<bf16>::pack(u);
+        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C3) + off) = Elem<bf16>::pack(a);
+      }
+    }
+  }
 }
 
 // Fused epilogue of one wave's WM x WN accumulator tile.
@@ -288,7 +410,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x4 (&acc)[F
           load4<T>(static_cast<const T*>(g.R2) + roff, U);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float sg = 1.0f / (1.0f + __expf(-G[v]));
+            const float sg = sigmoid_f(G[v]);
             dG[v] = o[v] * U[v] * sg * (1.0f + G[v] * (1.0f - sg));
             dU[v] = o[v] * G[v] * sg;
           }
@@ -383,6 +505,14 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
     __syncthreads();
   }
 
+  if constexpr (sizeof(T) == 2 && kRowsEpi<E, WN>) {
+    static_assert(NW * kPatchBytes<WN, E> <= sizeof(smem), "row epilogue patches");
+    if (g.rows_epi) {  // the loop ended with a barrier: the stages are free
+      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+                                       reinterpret_cast<float*>(&smem[0][0]) + w * (kPatchBytes<WN, E> / 4));
+      return;
+    }
+  }
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
@@ -667,6 +797,14 @@ gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes)
     __syncthreads();
   }
 
+  if constexpr (kRowsEpi<E, WN>) {
+    static_assert(NW * kPatchBytes<WN, E> <= sizeof(smem), "row epilogue patches");
+    if (g.rows_epi) {  // the loop ended with a barrier: the stages are free
+      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+                                       reinterpret_cast<float*>(smem) + w * (kPatchBytes<WN, E> / 4));
+      return;
+    }
+  }
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
@@ -767,6 +905,26 @@ gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
     direct::wait_vm<0>();  // no load into LDS outlives the block
   }
 
+  if constexpr (kRowsEpi<E, WN>) {
+    // patches fill stage arrays one after another, none straddling two
+    constexpr int PB = kPatchBytes<WN, E>, PER = STAGE / PB;
+    static_assert(PER >= 1 && NS * PER >= NW, "row epilogue patches");
+    if (g.rows_epi) {
+      __syncthreads();  // every wave is done with the stages
+      // (only the stage arrays that hold a patch are named)
+      constexpr int KMAX = (NW - 1) / PER;
+      const int k = w / PER;
+      char* base = S0;
+      if constexpr (KMAX >= 1) base = k == 1 ? S1 : base;
+      if constexpr (KMAX >= 2) base = k == 2 ? S2 : base;
+      if constexpr (KMAX >= 3) base = k == 3 ? S3 : base;
+      if constexpr (KMAX >= 4) base = k == 4 ? S4 : base;
+      if constexpr (KMAX >= 5) base = k == 5 ? S5 : base;
+      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+                                       reinterpret_cast<float*>(base + (w % PER) * PB));
+      return;
+    }
+  }
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
@@ -886,6 +1044,26 @@ gemm_pp_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
     direct::wait_vm<0>();  // no load into LDS outlives the block
   }
 
+  if constexpr (kRowsEpi<E, WN>) {
+    // patches fill stage arrays one after another, none straddling two
+    constexpr int PB = kPatchBytes<WN, E>, PER = STAGE / PB;
+    static_assert(PER >= 1 && NS * PER >= NW, "row epilogue patches");
+    if (g.rows_epi) {
+      __syncthreads();  // every wave is done with the stages
+      // (only the stage arrays that hold a patch are named)
+      constexpr int KMAX = (NW - 1) / PER;
+      const int k = w / PER;
+      char* base = S0;
+      if constexpr (KMAX >= 1) base = k == 1 ? S1 : base;
+      if constexpr (KMAX >= 2) base = k == 2 ? S2 : base;
+      if constexpr (KMAX >= 3) base = k == 3 ? S3 : base;
+      if constexpr (KMAX >= 4) base = k == 4 ? S4 : base;
+      if constexpr (KMAX >= 5) base = k == 5 ? S5 : base;
+      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+                                       reinterpret_cast<float*>(base + (w % PER) * PB));
+      return;
+    }
+  }
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
@@ -947,6 +1125,15 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
   if (S > 1) {
     S = (g.K + g.kchunk - 1) / g.kchunk;
     g.partial = ws;
+  }
+  if constexpr (sizeof(T) == 2 && kRowsEpi<E, WN>) {
+    // 16-byte row epilogue: every vector it touches must be whole and aligned
+    auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    bool ok = S == 1 && g.ldc % 8 == 0 && a16(g.C) && ((E == Epi::SwigluFwd ? g.ffn : g.N) % 8 == 0);
+    if constexpr (E == Epi::Resid || E == Epi::SwigluBwd) ok = ok && g.ldr % 8 == 0 && a16(g.R);
+    if constexpr (E == Epi::SwigluBwd) ok = ok && a16(g.R2) && a16(g.C2);
+    if constexpr (E == Epi::SwigluFwd) ok = ok && a16(g.C2) && a16(g.C3);
+    g.rows_epi = ok ? 1 : 0;
   }
   if constexpr (KIND == 3) {
     static_assert(sizeof(T) == 2, "direct loads are bf16 only");

@@ -34,7 +34,9 @@ struct SavedLayout {
 };
 // Offsets of the per-context workspace.
 struct WorkLayout {
-  size_t rope_cos, rope_sin, dGU, dhn, dh, dA, dsum, dqkv, dxn, gain_partial, splitk, splitk_bytes, total;
+  size_t rope_cos, rope_sin, dGU, dhn, dh, dA, dsum, dqkv, dxn, gain_partial, splitk, splitk_bytes;
+  size_t splitk_w, splitk_w_bytes;  // split-K scratch of the weight-gradient GEMMs (side stream)
+  size_t total;
   // head (appended when vocab > 0)
   size_t hf, rf, dhf, logits, dlogits, loss_rows, head_total;
 };
@@ -63,6 +65,12 @@ struct sf_ctx {
   char* ws = nullptr;  // caller-provided device workspace
   size_t ws_bytes = 0;
   int device = 0;
+  // Weight-gradient GEMMs of the backward run on `side` (null: on the
+  // caller's stream), forked and joined with the events below.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork[4] = {nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t ev_mlp_dw = nullptr, ev_join = nullptr;
+  ~sf_ctx();
 };
 
 #define SF_HIP(call)                                                                  \
