@@ -239,7 +239,18 @@ enum {
                                    the layer's backward, which first recomputes
                                    the layer's forward; the device keeps a
                                    fixed six [T, H] buffers and two saved sets
-                                   whatever n_layers is.  Same bits as without */
+                                   whatever n_layers is.  Same bits as without */,
+  SF_ENGINE_PIPELINE = 16       /* host Adam across the iteration boundary:
+                                   sf_slide_step returns once the device work
+                                   and the loss are done while Adam jobs still
+                                   run; the next step's forward waits, layer by
+                                   layer, only for the update of the layer it
+                                   is about to read, and the host applies
+                                   updates in ascending layer order (the order
+                                   the forward needs them).  Same bits as
+                                   without.  Not with SF_ENGINE_HEAD_HOST_ADAM
+                                   (SF_ERR_UNSUPPORTED).  Call sf_engine_sync
+                                   before reading host parameters or moments */
 };
 
 /*
@@ -350,12 +361,26 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
  *   d_in  : [T] int32 ids (SF_ENGINE_HEAD) or [T, H] layer-0 input.
  *   d_dy  : [T, H] upstream gradient of the last layer (no head), else NULL.
  *   h_loss: receives the loss (SF_ENGINE_HEAD), may be NULL.
- * Returns after the iteration's device work and Adam jobs are complete.
+ * Returns after the iteration's device work and Adam jobs are complete
+ * (with SF_ENGINE_PIPELINE: after its device work; *stats then holds only
+ * wall_ms and loss, and sf_engine_sync measures the steps as a whole).
+ * Host Adam takes the ranges whose copies have landed lowest layer first.
  * A HIP failure moves the engine to a sticky error state (SF_ERR_STATE on
  * later calls).
  */
 sf_status sf_slide_step(sf_engine* eng, const void* d_in, const void* d_dy, float* h_loss,
                         sf_step_stats* stats);
+
+/*
+ * Wait until every copy, kernel and host Adam job of the steps issued so far
+ * is complete (host parameters, masters and moments final, units 0 ..
+ * window-1 loaded for the next step).  stats (may be NULL) receives the
+ * measurements of all steps since the previous sync (pipelined), or of the
+ * last step (synchronous engine, where this only returns them again); the
+ * step trace then covers the same window.  An Adam failure surfaces here or
+ * at the next step and leaves the engine in the error state.
+ */
+sf_status sf_engine_sync(sf_engine* eng, sf_step_stats* stats);
 
 /* Device pointer of layer l's input activation from the last step (l = 0..
  * n_layers; l = n_layers is the last layer's output), and of the input

@@ -14,9 +14,9 @@
 //  - gradient buffers on the host are shared by all layers.
 //
 // Realisation here.  HIP streams: compute (the caller's), H2D (layer
-// prefetch), D2H (gradients) and a head-upload stream, all at default
-// priority and ordered only through events, so host-link copies in both
-// directions overlap kernels.  Unit u = layer mod window; each unit has
+// prefetch), D2H (gradients), the uploads Adam queues, and a head-upload
+// stream, all at default priority and ordered only through events, so
+// host-link copies in both directions overlap kernels.  Unit u = layer mod window; each unit has
 // separate "parameters free" and "gradients free" events, so a unit's
 // parameter slot can be refilled for L_{i-window+1} as soon as the backward
 // of L_i is done while its gradient slot is still draining.  A dispatcher
@@ -175,6 +175,8 @@ struct Job {
   size_t lo = 0, hi = 0;  // kLayer: byte range of the layer's fp32 gradients
   bool first = false;     // kLayer: the layer's first range
   bool last = false;      // kLayer: the layer's final range (frees the slot)
+  int64_t step = 0;       // the iteration whose gradients these are
+  AdamCoef coef{};        // that iteration's Adam coefficients
 };
 
 struct Interval {
@@ -234,6 +236,9 @@ struct sf_engine {
   size_t chunk_bytes = 0;  // gradient D2H / Adam / re-upload granularity
   bool preloaded = false;  // units 0..W-1 hold this step's layers 0..W-1 already
   hipStream_t s_comp = nullptr, s_h2d = nullptr, s_d2h = nullptr, s_head = nullptr;
+  // uploads of updated ranges that Adam queues (layers below the window):
+  // their own stream, so that they never wait behind the forward's prefetches
+  hipStream_t s_up = nullptr;
   std::vector<char*> uparam, ugrad, x, saved;
   char* dbuf = nullptr;
   // activation checkpointing: layer inputs ring (3), checkpoint slots for the
@@ -248,6 +253,8 @@ struct sf_engine {
              ev_cfree[2] = {nullptr, nullptr}, ev_ckpt_out = nullptr;
   float* d_loss = nullptr;
   std::vector<hipEvent_t> ev_param_ready, ev_param_free, ev_grad_free;
+  // the gradient region of a unit as a second parameter slot in the forward
+  std::vector<hipEvent_t> ev_gslot_ready, ev_gslot_free;
   // timing events and intervals (shared with the dispatcher thread)
   std::mutex tmu;
   std::vector<hipEvent_t> tev;
@@ -273,7 +280,19 @@ struct sf_engine {
   AdamCoef coef{};
   int n_threads = 1;  // Adam threads: the pool plus the dispatcher
   double adam_ms = 0;
-  double host_t0 = 0;                 // host clock at the step's first device event
+  // Cross-step pipelining (SF_ENGINE_PIPELINE): a step returns with its Adam
+  // jobs still running; adam_done[l] is the last step whose Adam of layer l
+  // is complete (its updated parameters written and, for layers below the
+  // window, their uploads queued), and the next forward waits on it per layer.
+  bool pipe = false;
+  std::vector<int64_t> adam_done;
+  hipEvent_t ev_head_done = nullptr;  // device Adam of the LM head and final gain
+  // Measurement window: one step (synchronous) or every step since the last
+  // sf_engine_sync (pipelined).
+  bool window_open = false;
+  hipEvent_t ev_origin = nullptr;
+  sf_step_stats last_stats{};
+  double host_t0 = 0;                 // host clock at the window's first device event
   std::vector<TraceRow> adam_rows;    // host Adam jobs of the current step (under mu)
   std::vector<TraceRow> trace;        // the last completed step
 };
@@ -314,8 +333,8 @@ struct Seg {
   size_t off, n, out_off;
 };
 
-void run_adam(sf_engine* e, float* p, float* m, float* v, const float* g, void* out, bool out_is_master,
-              const std::vector<Seg>& segs) {
+void run_adam(sf_engine* e, const AdamCoef& c, float* p, float* m, float* v, const float* g, void* out,
+              bool out_is_master, const std::vector<Seg>& segs) {
   // about four tasks per thread, each 16K .. 256K elements
   size_t total = 0;
   for (const Seg& s : segs) total += s.n;
@@ -325,7 +344,6 @@ void run_adam(sf_engine* e, float* p, float* m, float* v, const float* g, void* 
   for (const Seg& s : segs)
     for (size_t b = 0; b < s.n; b += chunk) tasks.push_back({s.off + b, std::min(chunk, s.n - b), s.out_off + b});
   const bool bf = e->d.dtype == SF_BF16;
-  const AdamCoef c = e->coef;
   e->pool->run(tasks.size(), [&](size_t i) {
     const Seg& t = tasks[i];
     if (bf) {
@@ -341,7 +359,7 @@ void run_adam(sf_engine* e, float* p, float* m, float* v, const float* g, void* 
 // take g = 0, exactly as a dense zero gradient would), in groups of rows;
 // each group's updated storage-dtype rows are uploaded on the head stream
 // while the next group is updated.
-sf_status run_embed_adam(sf_engine* e) {
+sf_status run_embed_adam(sf_engine* e, const AdamCoef& cf) {
   const sf_engine_cfg& c = e->cfg;
   const int H = e->d.H, V = e->d.V;
   const float* hg = c.h_head_grads;
@@ -356,7 +374,6 @@ sf_status run_embed_adam(sf_engine* e) {
   }
   const bool bf = e->d.dtype == SF_BF16;
   const bool out_is_master = c.h_head_params == static_cast<void*>(c.h_head_master);
-  const AdamCoef cf = e->coef;
   const int rows_per_task = std::max(1, (1 << 17) / H);
   const int groups = 8;
   const int rows_per_group = (V + groups - 1) / groups;
@@ -412,33 +429,33 @@ sf_status run_job(sf_engine* e, const Job& j) {
   const size_t VH = static_cast<size_t>(e->d.V) * e->d.H;
   if (j.kind == kLayer) {
     const ChunkMap cm = chunk_map(e->L, e->d.e, j.lo, j.hi);
-    run_adam(e, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot], c.h_params[j.layer],
-             c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), cm.segs);
+    run_adam(e, j.coef, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot],
+             c.h_params[j.layer], c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), cm.segs);
     // Layers 0 .. W-1 open the next step's forward and finish their backward
     // last: upload each updated range into the layer's unit right away, so
     // the upload of one range overlaps the Adam of the next.
     if (j.layer < e->W) {
       const int u = j.layer;
-      if (j.first) SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_param_free[u], 0));
+      if (j.first) SF_HIP(hipStreamWaitEvent(e->s_up, e->ev_param_free[u], 0));
       if (cm.phi > cm.plo) {
         if (sf_status rc = timed_h2d(e, e->uparam[u] + cm.plo, static_cast<const char*>(c.h_params[j.layer]) + cm.plo,
-                                     cm.phi - cm.plo, e->s_h2d))
+                                     cm.phi - cm.plo, e->s_up))
           return rc;
       }
-      if (j.last) SF_HIP(hipEventRecord(e->ev_param_ready[u], e->s_h2d));
+      if (j.last) SF_HIP(hipEventRecord(e->ev_param_ready[u], e->s_up));
     }
     return SF_OK;
   }
   if (j.kind == kHeadLm) {
     // final-norm gain and LM head: [VH, VH + H) and [VH + H, 2 VH + H)
-    run_adam(e, c.h_head_master, c.h_head_m, c.h_head_v, c.h_head_grads, c.h_head_params,
+    run_adam(e, j.coef, c.h_head_master, c.h_head_m, c.h_head_v, c.h_head_grads, c.h_head_params,
              c.h_head_params == static_cast<void*>(c.h_head_master), {{VH, VH + e->d.H, VH}});
     const char* hp = static_cast<const char*>(c.h_head_params);
     sf_status rc = timed_h2d(e, c.d_gf, hp + VH * e->d.e, e->d.H * e->d.e, e->s_head);
     if (rc) return rc;
     return timed_h2d(e, c.d_wlm, hp + (VH + e->d.H) * e->d.e, VH * e->d.e, e->s_head);
   }
-  return run_embed_adam(e);
+  return run_embed_adam(e, j.coef);
 }
 
 void dispatcher_loop(sf_engine* e) {
@@ -449,8 +466,26 @@ void dispatcher_loop(sf_engine* e) {
       std::unique_lock<std::mutex> lk(e->mu);
       e->cv.wait(lk, [&] { return e->stop || !e->jobs.empty(); });
       if (e->jobs.empty()) return;  // stop requested and nothing left
-      j = e->jobs.front();
-      e->jobs.pop_front();
+      // Among the ranges whose copies have landed, the lowest layer first
+      // (ranges of one layer in order): the next forward needs layer 0
+      // first, and layer 0's gradients arrive last.  With none landed, the
+      // oldest range (its copy was queued first).
+      size_t pick = 0;
+      int best = INT32_MAX;
+      for (size_t q = 0; q < e->jobs.size(); ++q) {
+        const Job& cand = e->jobs[q];
+        const int key = cand.kind == kLayer ? cand.layer : -1;
+        if (key >= best) continue;
+        bool earlier_same = false;  // keep a layer's ranges in order
+        for (size_t r = 0; r < q && !earlier_same; ++r)
+          earlier_same = e->jobs[r].kind == cand.kind && e->jobs[r].layer == cand.layer;
+        if (earlier_same) continue;
+        if (hipEventQuery(cand.ready) != hipSuccess) continue;
+        best = key;
+        pick = q;
+      }
+      j = e->jobs[pick];
+      e->jobs.erase(e->jobs.begin() + static_cast<std::ptrdiff_t>(pick));
     }
     std::string err;
     const hipError_t he = hipEventSynchronize(j.ready);
@@ -466,7 +501,10 @@ void dispatcher_loop(sf_engine* e) {
     if (!err.empty() && e->job_error.empty()) e->job_error = err;
     e->adam_ms += t1 - t0;
     e->adam_rows.push_back({3.0 + j.kind, t0 - e->host_t0, t1 - e->host_t0, static_cast<double>(j.layer)});
-    if (j.kind == kLayer && j.last) e->slot_free[j.slot] = true;
+    if (j.kind == kLayer && j.last) {
+      e->slot_free[j.slot] = true;
+      if (err.empty()) e->adam_done[j.layer] = j.step;
+    }
     --e->pending;
     e->cv.notify_all();
   }
@@ -542,7 +580,9 @@ sf_status wait_slot(sf_engine* e, int* slot) {
   return SF_OK;
 }
 
-void push_job(sf_engine* e, const Job& j) {
+void push_job(sf_engine* e, Job j) {
+  j.step = e->step;
+  j.coef = e->coef;
   std::lock_guard<std::mutex> lk(e->mu);
   e->jobs.push_back(j);
   ++e->pending;
@@ -567,6 +607,34 @@ sf_status timed_d2h(sf_engine* e, void* dst, const void* src, size_t bytes, hipE
   return record_interval(e, b0, b1, 2, static_cast<double>(bytes));
 }
 
+// Wait for every copy, kernel and Adam job, then measure the window (one
+// step, or all pipelined steps since the window opened) into *st.
+sf_status close_window(sf_engine* e, sf_step_stats* st) {
+  SF_HIP(hipStreamSynchronize(e->s_comp));
+  SF_HIP(hipStreamSynchronize(e->s_d2h));
+  drain(e);  // Adam jobs; they queue the re-upload of layers 0 .. W-1
+  SF_HIP(hipStreamSynchronize(e->s_h2d));
+  SF_HIP(hipStreamSynchronize(e->s_up));
+  SF_HIP(hipStreamSynchronize(e->s_head));
+  {
+    std::lock_guard<std::mutex> lk(e->mu);
+    if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
+  }
+  sf_step_stats local{};
+  if (!e->window_open) {
+    if (st) *st = e->last_stats;
+    return SF_OK;
+  }
+  if (sf_status rc = fill_stats(e, e->ev_origin, &local)) return rc;
+  std::lock_guard<std::mutex> lk(e->mu);
+  local.adam_ms = e->adam_ms;
+  e->trace.insert(e->trace.end(), e->adam_rows.begin(), e->adam_rows.end());
+  e->window_open = false;
+  e->last_stats = local;
+  if (st) *st = local;
+  return SF_OK;
+}
+
 sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_stats* st) {
   const Dims& d = e->d;
   const sf_engine_cfg& c = e->cfg;
@@ -576,28 +644,35 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   const int nl = e->nl, W = e->W;
   sf_ctx* ctx = e->ctx;
   {
+    // a failed Adam job of an earlier (pipelined) step
+    std::lock_guard<std::mutex> lk(e->mu);
+    if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
+  }
+  // a new measurement window: no Adam job is running (synchronous steps end
+  // with none; a pipelined window opens after sf_engine_sync drained them)
+  const bool new_window = !e->window_open;
+  if (new_window) {
     std::lock_guard<std::mutex> lk(e->tmu);
     e->tev_used = 0;
     e->iv.clear();
   }
   e->step += 1;
   e->coef = adam_coef(e->step, c.lr, c.b1, c.b2, c.eps);
-  {
-    std::lock_guard<std::mutex> lk(e->mu);
-    e->adam_ms = 0;
-    e->job_error.clear();
-  }
 
   hipEvent_t ev0 = timing_event(e);
   if (!ev0) return fail(SF_ERR_HIP, "event pool exhausted");
   SF_HIP(hipEventRecord(ev0, e->s_comp));
-  e->host_t0 = now_ms();
-  {
+  if (new_window) {
+    e->ev_origin = ev0;
+    e->host_t0 = now_ms();
+    e->window_open = true;
     std::lock_guard<std::mutex> lk(e->mu);
+    e->adam_ms = 0;
     e->adam_rows.clear();
   }
   // The side streams start after everything the caller queued before this call.
   SF_HIP(hipStreamWaitEvent(e->s_h2d, ev0, 0));
+  SF_HIP(hipStreamWaitEvent(e->s_up, ev0, 0));
   SF_HIP(hipStreamWaitEvent(e->s_d2h, ev0, 0));
   SF_HIP(hipStreamWaitEvent(e->s_head, ev0, 0));
 
@@ -648,20 +723,66 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
 
   // ---------------- forward: layer i in unit i % W, prefetch i + 1
   // (layers below W were uploaded at the end of the previous step, right
-  // after their Adam, when that step ran Adam)
-  auto fetch = [&](int j) { return (e->preloaded && j < W) ? SF_OK : prefetch(e, j); };
-  if ((rc = fetch(0))) return rc;
+  // after their Adam, when that step ran Adam).  Pipelined, the previous
+  // step's Adam of layer j may still be running: wait for it before its
+  // parameters are read (host copy) or its upload is waited on (units).
+  // A unit's gradient region is idle in the forward once the previous
+  // backward's gradients have left, and holds a layer's parameters twice
+  // over: layers with i mod 2W >= W run from there, so an upload waits for
+  // the layer 2W back instead of W back.  Of the last W layers, which stay
+  // for the backward, those in a gradient region move to their unit's
+  // parameter region by a device copy after their forward.  Uploads are
+  // queued in layer order as far ahead as the slots allow (2W - 1 layers);
+  // pipelined, one whose update is still running waits for a later turn
+  // unless the next forward needs it.
+  auto await_adam = [&](int j) -> sf_status {
+    if (!adam || !e->pipe) return SF_OK;
+    std::unique_lock<std::mutex> lk(e->mu);
+    e->cv.wait(lk, [&] { return e->adam_done[j] >= e->step - 1 || !e->job_error.empty(); });
+    if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
+    return SF_OK;
+  };
+  auto in_gslot = [&](int i) { return i % (2 * W) >= W; };
+  auto fetch = [&](int j) -> sf_status {
+    if (e->preloaded && j < W) return SF_OK;
+    if (sf_status r = await_adam(j)) return r;
+    if (!in_gslot(j)) return prefetch(e, j);
+    const int u = j % W;
+    SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_grad_free[u], 0));   // last gradients out
+    SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_gslot_free[u], 0));  // layer j - 2W's forward
+    if (sf_status r = timed_h2d(e, e->ugrad[u], c.h_params[j], e->L.param_bytes, e->s_h2d)) return r;
+    SF_HIP(hipEventRecord(e->ev_gslot_ready[u], e->s_h2d));
+    return SF_OK;
+  };
+  auto adam_ready = [&](int j) {
+    if (!adam || !e->pipe) return true;
+    std::lock_guard<std::mutex> lk(e->mu);
+    return e->adam_done[j] >= e->step - 1;
+  };
+  int next_fetch = 0;
+  auto advance = [&](int i) -> sf_status {  // before the forward of layer i
+    for (const int lim = std::min(nl, i + 2 * W); next_fetch < lim; ++next_fetch) {
+      const int j = next_fetch;
+      if (j > i && !adam_ready(j)) break;
+      if (sf_status r = fetch(j)) return r;
+    }
+    return SF_OK;
+  };
   for (int i = 0; i < nl; ++i) {
-    if (i + 1 < nl && (rc = fetch(i + 1))) return rc;
     const int u = i % W;
-    SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_param_ready[u], 0));
+    const bool gs = in_gslot(i);
+    if ((rc = advance(i))) return rc;
+    if (e->preloaded && i < W && (rc = await_adam(i))) return rc;
+    SF_HIP(hipStreamWaitEvent(e->s_comp, gs ? e->ev_gslot_ready[u] : e->ev_param_ready[u], 0));
     // the output slot held x_{i-2}: its copy to the host must be done
     if (ck && i >= 2) SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_xfree[(i + 1) % 3], 0));
     if ((rc = comp_begin(&a))) return rc;
     void* sv = ck ? e->sv[i == nl - 1 ? 1 : 0] : e->saved[i];
-    if ((rc = sf_layer_fwd(ctx, e->uparam[u], xin[i], xslot(i + 1), sv, e->s_comp))) return rc;
+    if ((rc = sf_layer_fwd(ctx, gs ? e->ugrad[u] : e->uparam[u], xin[i], xslot(i + 1), sv, e->s_comp))) return rc;
+    if (gs && i >= nl - W)  // stays for the backward: into the parameter region (layer i - W is done with it)
+      SF_HIP(hipMemcpyAsync(e->uparam[u], e->ugrad[u], e->L.param_bytes, hipMemcpyDeviceToDevice, e->s_comp));
     if ((rc = comp_end(a, &b))) return rc;
-    SF_HIP(hipEventRecord(e->ev_param_free[u], e->s_comp));
+    SF_HIP(hipEventRecord(gs ? e->ev_gslot_free[u] : e->ev_param_free[u], e->s_comp));
     if ((rc = ckpt_out(i + 1, b))) return rc;
   }
   if (ck && nl >= 2) SF_HIP(hipEventRecord(e->ev_ckpt_out, e->s_d2h));
@@ -692,6 +813,9 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     return SF_OK;
   };
   if (head) {
+    // the previous step's device Adam of the LM head (head stream) reads hg
+    // and writes d_gf / d_wlm
+    SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_head_done, 0));
     if ((rc = comp_begin(&a))) return rc;
     if ((rc = sf_head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
                               e->s_comp)))
@@ -707,6 +831,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
       if ((rc = dev_adam(VH, d.H, c.d_gf, e->s_head)) || (rc = dev_adam(VH + d.H, VH, c.d_wlm, e->s_head)))
         return rc;
       SF_HIP(hipEventRecord(hb, e->s_head));
+      SF_HIP(hipEventRecord(e->ev_head_done, e->s_head));
       if ((rc = record_interval(e, ha, hb, 0, 0))) return rc;
     }
     if (head_host) {
@@ -807,21 +932,15 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   }
 
   SF_HIP(hipStreamSynchronize(e->s_comp));
-  SF_HIP(hipStreamSynchronize(e->s_d2h));
-  drain(e);  // Adam jobs; they queue the re-upload of layers 0 .. W-1
-  SF_HIP(hipStreamSynchronize(e->s_h2d));
-  SF_HIP(hipStreamSynchronize(e->s_head));
-  {
+  e->preloaded = adam;
+  if (e->pipe) {
+    // Adam jobs (and the uploads they queue) go on; the next step waits for
+    // them layer by layer, sf_engine_sync for all of them
     std::lock_guard<std::mutex> lk(e->mu);
     if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
+    return SF_OK;
   }
-  e->preloaded = adam;
-  sf_step_stats local{};
-  if ((rc = fill_stats(e, ev0, st ? st : &local))) return rc;
-  std::lock_guard<std::mutex> lk(e->mu);
-  if (st) st->adam_ms = e->adam_ms;
-  e->trace.insert(e->trace.end(), e->adam_rows.begin(), e->adam_rows.end());
-  return SF_OK;
+  return close_window(e, st);
 }
 
 }  // namespace
@@ -895,6 +1014,9 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
     if (adam && !head_host && !c.d_head_state)
       return fail(SF_ERR_ARG, "SF_ENGINE_HEAD with SF_ENGINE_ADAM needs d_head_state (device Adam of the head)");
   }
+  const bool pipe = (c.flags & SF_ENGINE_PIPELINE) != 0;
+  if (pipe && head && head_host)
+    return fail(SF_ERR_UNSUPPORTED, "SF_ENGINE_PIPELINE does not combine with SF_ENGINE_HEAD_HOST_ADAM");
   if (head && head_host) {
     if (!c.h_head_grads) return fail(SF_ERR_ARG, "SF_ENGINE_HEAD_HOST_ADAM needs h_head_grads");
     if (!is_pinned(c.h_head_grads)) return fail(SF_ERR_NOT_PINNED, "h_head_grads is not pinned");
@@ -914,6 +1036,8 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   e->L = L;
   e->nl = c.n_layers;
   e->W = W;
+  e->pipe = pipe;
+  e->adam_done.assign(c.n_layers, 0);
   e->unit_bytes = unit;
   e->x_bytes = align256(static_cast<size_t>(d.T) * d.H * d.e);
   {
@@ -932,6 +1056,7 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
     return st;
   };
   if (hipStreamCreateWithFlags(&e->s_h2d, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&e->s_up, hipStreamNonBlocking) != hipSuccess ||
       hipStreamCreateWithFlags(&e->s_d2h, hipStreamNonBlocking) != hipSuccess ||
       hipStreamCreateWithFlags(&e->s_head, hipStreamNonBlocking) != hipSuccess)
     return cleanup(fail(SF_ERR_HIP, "stream creation failed"));
@@ -966,7 +1091,9 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
     }
     return true;
   };
-  if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_free))
+  if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_free) || !mk(e->ev_gslot_ready) ||
+      !mk(e->ev_gslot_free) ||
+      hipEventCreateWithFlags(&e->ev_head_done, hipEventDisableTiming) != hipSuccess)
     return cleanup(fail(SF_ERR_HIP, "event creation failed"));
   if (ckpt) {
     std::vector<hipEvent_t*> evs = {&e->ev_xfree[0], &e->ev_xfree[1], &e->ev_xfree[2], &e->ev_cready[0],
@@ -1007,6 +1134,7 @@ sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float*
     (void)hipStreamSynchronize(e->s_d2h);
     drain(e);
     (void)hipStreamSynchronize(e->s_h2d);
+    (void)hipStreamSynchronize(e->s_up);
     (void)hipStreamSynchronize(e->s_head);
     e->failed = true;
     return fail(rc, "%s", msg.c_str());
@@ -1022,6 +1150,16 @@ sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float*
   if (stats) {
     stats->wall_ms = now_ms() - t0;
     stats->loss = loss;
+  }
+  return SF_OK;
+}
+
+sf_status sf_engine_sync(sf_engine* e, sf_step_stats* stats) {
+  if (!e) return fail(SF_ERR_ARG, "engine is NULL");
+  if (e->failed) return fail(SF_ERR_STATE, "engine is in an error state after an earlier failure");
+  if (sf_status rc = close_window(e, stats)) {
+    e->failed = true;
+    return rc;
   }
   return SF_OK;
 }
@@ -1070,14 +1208,15 @@ sf_status sf_engine_destroy(sf_engine* e) {
     e->dispatcher.join();
   }
   e->pool.reset();
-  for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
+  for (hipStream_t s : {e->s_h2d, e->s_up, e->s_d2h, e->s_head})
     if (s) (void)hipStreamSynchronize(s);
-  for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_free, &e->tev})
+  for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_free, &e->ev_gslot_ready, &e->ev_gslot_free,
+                  &e->tev})
     for (hipEvent_t ev : *v) (void)hipEventDestroy(ev);
   for (hipEvent_t ev : {e->ev_xfree[0], e->ev_xfree[1], e->ev_xfree[2], e->ev_cready[0], e->ev_cready[1],
-                        e->ev_cfree[0], e->ev_cfree[1], e->ev_ckpt_out})
+                        e->ev_cfree[0], e->ev_cfree[1], e->ev_ckpt_out, e->ev_head_done})
     if (ev) (void)hipEventDestroy(ev);
-  for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
+  for (hipStream_t s : {e->s_h2d, e->s_up, e->s_d2h, e->s_head})
     if (s) (void)hipStreamDestroy(s);
   delete e;
   return SF_OK;

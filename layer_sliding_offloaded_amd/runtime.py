@@ -118,10 +118,12 @@ class Engine:
     head: None or dict with E [V, H], gf [H], Wlm [V, H] (float32 storage values).
     ckpt: sliding activation checkpointing (layer inputs kept in pinned host
     memory, each layer's forward recomputed before its backward).
+    pipeline: host Adam runs on across the step boundary (call sync() before
+    reading host parameters or moments).
     """
 
     def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
-                 adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False):
+                 adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False, pipeline=False):
         import ctypes
         hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
         self.w = w
@@ -138,6 +140,8 @@ class Engine:
             flags |= sf.SF_ENGINE_HEAD_HOST_ADAM
         if ckpt:
             flags |= sf.SF_ENGINE_CKPT
+        if pipeline:
+            flags |= sf.SF_ENGINE_PIPELINE
         act = sf.sf_engine_act_bytes_flags(shape, self.nl, flags)
         self.act = device_bytes(act)
         self.act_bytes = act
@@ -206,6 +210,11 @@ class Engine:
         """d_in: device int32 ids [T] (head) or storage-dtype x [T, H]; returns (loss, stats dict)."""
         loss, st = sf.sf_slide_step(self.eng, d_in.data_ptr(), None if d_dy is None else d_dy.data_ptr())
         return loss, st.as_dict()
+
+    def sync(self):
+        """Wait for every step's copies and Adam jobs; returns the stats dict of
+        the steps since the previous sync (pipelined) or of the last step."""
+        return sf.sf_engine_sync(self.eng).as_dict()
 
     def trace(self):
         """The last step's timeline: list of (kind name, start_ms, end_ms, info)."""

@@ -33,6 +33,7 @@ SF_ENGINE_ADAM = 1
 SF_ENGINE_HEAD = 2
 SF_ENGINE_HEAD_HOST_ADAM = 4
 SF_ENGINE_CKPT = 8
+SF_ENGINE_PIPELINE = 16
 
 _size_t = ctypes.c_size_t
 _vp = ctypes.c_void_p
@@ -85,7 +86,7 @@ class SfError(RuntimeError):
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
     "sf_gemm", "sf_gemm_workspace_bytes", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_act_bytes_flags", "sf_engine_create", "sf_slide_step",
-    "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_destroy", "sf_last_error",
+    "sf_engine_sync", "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_destroy", "sf_last_error",
 )
 
 _lib = None
@@ -119,6 +120,7 @@ def load():
         "sf_engine_act_bytes_flags": [ctypes.POINTER(SfShape), i32, i32, ctypes.POINTER(_size_t)],
         "sf_engine_create": [P, ctypes.POINTER(SfEngineCfg), ctypes.POINTER(P)],
         "sf_slide_step": [P, P, P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(SfStepStats)],
+        "sf_engine_sync": [P, ctypes.POINTER(SfStepStats)],
         "sf_engine_layer_input": [P, i32, ctypes.POINTER(P)],
         "sf_engine_dx0": [P, ctypes.POINTER(P)],
         "sf_engine_trace": [P, ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(i32)],
@@ -229,6 +231,14 @@ def sf_slide_step(eng, d_in, d_dy=None, want_stats=True):
     st = SfStepStats()
     _check(load().sf_slide_step(eng, d_in, d_dy, ctypes.byref(loss), ctypes.byref(st) if want_stats else None))
     return loss.value, st
+
+
+def sf_engine_sync(eng):
+    """Drain the engine (pipelined Adam included); returns the measurements of
+    the steps since the previous sync."""
+    st = SfStepStats()
+    _check(load().sf_engine_sync(eng, ctypes.byref(st)))
+    return st
 
 
 def sf_engine_layer_input(eng, layer):

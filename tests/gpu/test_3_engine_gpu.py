@@ -328,3 +328,78 @@ def test_engine_checkpointing_matches_plain_bitwise(head_adam, window, n_layers)
         assert b["st"]["h2d_bytes"] - a["st"]["h2d_bytes"] == n_ck * gi["x_bytes"], t
     if n_layers >= 4:
         assert gi["act_bytes"] < ri["act_bytes"]
+
+
+def _run_pipelined(w, layers, head, x, dy, steps, **kw):
+    """Steps a pipelined engine without draining in between (each forward
+    waits on the previous step's Adam in flight); returns the per-step losses
+    and, after one sync at the end, the final state as _run_engine does."""
+    eng = rt.Engine(w, layers, head, n_grad_slots=2, adam=True, chunk=96, adam_hp=si.ADAM, pipeline=True, **kw)
+    d_in = torch.from_numpy(x.reshape(-1)).cuda() if head is not None else rt.to_storage_tensor(x, w).cuda()
+    d_dy = None if head is not None else rt.to_storage_tensor(dy, w).cuda()
+    losses, walls = [], []
+    for _ in range(steps):
+        loss, st = eng.step(d_in, d_dy)
+        losses.append(loss)
+        walls.append(st["wall_ms"])
+    agg = eng.sync()
+    torch.cuda.synchronize()
+    n = w.tokens * w.hidden * 2
+    base = eng.act.data_ptr()
+    snap = dict(master=[m.copy() for m in eng.h_master], params=[p.numpy().view(np.uint16).copy() for p in eng.h_params])
+    if head is not None:
+        snap["head"] = [a.copy() for a in engine_head_state(eng)]
+    od = sf.sf_engine_dx0(eng.eng) - base
+    oy = sf.sf_engine_layer_input(eng.eng, w.n_layers) - base
+    snap["dx0"] = eng.act[od:od + n].cpu().numpy().copy()
+    snap["y"] = eng.act[oy:oy + n].cpu().numpy().copy()
+    trace = eng.trace()
+    eng.close()
+    return losses, snap, agg, trace
+
+
+@pytest.mark.parametrize("head_adam,window,n_layers,ckpt", [("device", 2, 4, False), (None, 2, 3, False),
+                                                            ("device", 3, 5, True), ("device", 2, 1, False)])
+def test_engine_pipelined_matches_synchronous_bitwise(head_adam, window, n_layers, ckpt):
+    """Running host Adam across the step boundary changes when updates are
+    applied, never what is computed: three pipelined steps give the same
+    losses and the same final parameters, moments, head state and outputs as
+    three synchronous ones, bit for bit."""
+    w = STACK.with_(n_layers=n_layers, vocab=STACK.vocab if head_adam else 0)
+    say("engine-pipelined", head_adam, window, n_layers, ckpt, w)
+    layers = [si.layer_params(w, l, gains="random") for l in range(n_layers)]
+    if head_adam:
+        head = dict(E=si.embedding(w), gf=si.final_gain(w, gains="random"), Wlm=si.lm_head(w))
+        x, dy = si.token_ids(w), None
+        kw = dict(head_adam=head_adam)
+    else:
+        head, x, dy, kw = None, si.layer_input(w), si.upstream_grad(w), {}
+    steps = 3
+    ref, _ = _run_engine(w, layers, head, x, dy, steps, window=window, ckpt=ckpt, **kw)
+    losses, got, agg, trace = _run_pipelined(w, layers, head, x, dy, steps, window=window, ckpt=ckpt, **kw)
+    if head is not None:
+        assert losses == [r["loss"] for r in ref]
+    last = ref[-1]
+    for i in range(n_layers):
+        assert np.array_equal(last["master"][i], got["master"][i]), i
+        assert np.array_equal(last["params"][i], got["params"][i]), i
+    if head is not None:
+        assert np.array_equal(last["head"][0], got["head"][0]) and np.array_equal(last["head"][1], got["head"][1])
+    else:
+        assert np.array_equal(last["dx0"], got["dx0"])
+    assert np.array_equal(last["y"], got["y"])
+    # the sync's window covers all three steps: every byte the synchronous
+    # steps moved, and one Adam pass per layer per step
+    assert agg["h2d_bytes"] == sum(r["st"]["h2d_bytes"] for r in ref)
+    assert agg["d2h_bytes"] == sum(r["st"]["d2h_bytes"] for r in ref)
+    assert 0.0 <= agg["overlap_pct"] <= 100.0 + 1e-6
+    assert {int(r[3]) for r in trace if r[0] == "adam"} == set(range(n_layers))
+
+
+def test_engine_pipelined_rejects_host_head_adam():
+    w = STACK.with_(n_layers=2)
+    layers = [si.layer_params(w, l) for l in range(2)]
+    head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
+    with pytest.raises(sf.SfError) as ei:
+        rt.Engine(w, layers, head, adam=True, chunk=96, head_adam="host", pipeline=True)
+    assert ei.value.code == sf.SF_ERR_UNSUPPORTED
