@@ -28,6 +28,8 @@
 // lane ends with 4 consecutive output columns of one row: 8-byte (bf16) or
 // 16-byte (fp32) stores, and the partner columns that RoPE (i, i + d/2) and
 // SwiGLU (gate j, up j) need sit in the same lane.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -166,6 +168,18 @@ int splitk_factor(int tiles, int K) {
   if (tiles >= 128) return 1;
   int S = 1;
   while (S < 8 && tiles * S * 2 <= 256 && K / (S * 2) >= 1024) S *= 2;
+  return S;
+}
+
+// Long-K products with few output tiles (the LM head's input gradient:
+// [T, H] from K = vocab): 256 x 256 ping-pong tiles, K split so that the
+// grid covers the CUs about once (2 to 8 ranges of >= 2048), then the
+// fixed-order reduction.  1: not such a product.
+int longk_split(int M, int N, int K) {
+  const long t256 = static_cast<long>((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 160 || K < 8192 || K < 4L * std::max(M, N)) return 1;
+  int S = static_cast<int>(std::min<long>(8, (256 + t256 - 1) / t256));
+  while (S > 1 && K / S < 2048) --S;
   return S;
 }
 
@@ -1104,9 +1118,11 @@ bool direct_ok(const GemmArgs& g, int64_t* a_bytes, int64_t* b_bytes) {
 
 // KIND 0: register-staged kernel; 1: direct loads, 2 stages of 64 k; 2: direct
 // loads, NS stages of BK k; 3: the same with two wave groups in ping-pong.
+// S_req > 0: split K into S_req ranges (Store / StoreF32, with enough scratch)
+// instead of the small-grid rule.
 template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, int KIND = 0, int BK = 64, int NS = 4>
 hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_bytes, int64_t a_bytes = 0,
-                  int64_t b_bytes = 0) {
+                  int64_t b_bytes = 0, int S_req = 0) {
   // the RoPE column map pairs columns i and i + head_dim/2 inside one tile
   if constexpr (E == Epi::Rope)
     if (g_in.head_dim <= 0 || BN % g_in.head_dim != 0) return hipErrorInvalidValue;
@@ -1118,7 +1134,7 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
   GemmArgs g = g_in;
   int S = 1;
   if constexpr (E == Epi::Store || E == Epi::StoreF32) {
-    S = splitk_factor(ntm * ntn, g.K);
+    S = S_req > 0 ? S_req : splitk_factor(ntm * ntn, g.K);
     if (S > 1 && (!ws || static_cast<size_t>(S) * g.M * g.N * 4 > ws_bytes)) S = 1;
   }
   g.kchunk = S > 1 ? ((g.K + S - 1) / S + 63) / 64 * 64 : g.K;
@@ -1177,6 +1193,11 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
       // deep pipeline, or 128x64 tiles when even 128x128 ones would leave
       // half the CUs idle.
       if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb);
+      if constexpr (E == Epi::Store || E == Epi::StoreF32) {
+        const int S = longk_split(g.M, g.N, g.K);
+        if (S > 1 && ws && static_cast<size_t>(S) * g.M * g.N * 4 <= wsb)
+          return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb, S);
+      }
       const int ncols = (E == Epi::SwigluFwd) ? 2 * g.ffn : g.N;
       const long t128 = static_cast<long>((g.M + 127) / 128) * ((ncols + 127) / 128);
       // at most half the CUs' worth of 128x128 tiles: 128x64 tiles (8 waves
@@ -1232,6 +1253,8 @@ int gemm_tile_config(int M, int N) {
 }
 
 size_t gemm_splitk_bytes(int M, int N, int K) {
+  const int SL = longk_split(M, N, K);
+  if (SL > 1) return static_cast<size_t>(SL) * M * N * 4;
   const int bm = gemm_tile_config(M, N) == 0 ? 256 : 128;
   const int tiles = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
   const int S = splitk_factor(tiles, K);
