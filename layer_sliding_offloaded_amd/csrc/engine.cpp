@@ -252,6 +252,10 @@ struct sf_engine {
   hipEvent_t ev_xfree[3] = {nullptr, nullptr, nullptr}, ev_cready[2] = {nullptr, nullptr},
              ev_cfree[2] = {nullptr, nullptr}, ev_ckpt_out = nullptr;
   float* d_loss = nullptr;
+  // the loss as the host reads it: one pinned word written by a kernel on
+  // the compute stream (a synchronous read-back would queue behind the
+  // uploads in flight on the copy engines and return milliseconds late)
+  float* h_loss = nullptr;
   std::vector<hipEvent_t> ev_param_ready, ev_param_free, ev_grad_free;
   // the gradient region of a unit as a second parameter slot in the forward
   std::vector<hipEvent_t> ev_gslot_ready, ev_gslot_free;
@@ -759,14 +763,53 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     std::lock_guard<std::mutex> lk(e->mu);
     return e->adam_done[j] >= e->step - 1;
   };
-  int next_fetch = 0;
-  auto advance = [&](int i) -> sf_status {  // before the forward of layer i
-    for (const int lim = std::min(nl, i + 2 * W); next_fetch < lim; ++next_fetch) {
+  // Uploads are queued in layer order, except the first window of layers
+  // that run from gradient regions (W .. 2W-1) after a preloaded start: those
+  // regions are freed by the previous backward from unit W-1 down to unit 0,
+  // so each of these layers is queued, highest first, as soon as its update
+  // is done rather than behind a lower one still waiting for its region.
+  std::vector<char> fetched(nl, 0);
+  int next_fetch = 0;  // every layer below it is fetched (or preloaded)
+  auto issue_ready = [&](int i, int lim) -> sf_status {
+    if (e->preloaded) {
+      for (int j = std::min(lim, 2 * W) - 1; j >= W; --j) {
+        if (fetched[j] || (j > i && !adam_ready(j))) continue;
+        if (sf_status r = fetch(j)) return r;
+        fetched[j] = 1;
+      }
+    }
+    for (; next_fetch < lim; ++next_fetch) {
       const int j = next_fetch;
+      if (fetched[j] || (e->preloaded && j < W)) continue;
       if (j > i && !adam_ready(j)) break;
       if (sf_status r = fetch(j)) return r;
+      fetched[j] = 1;
     }
     return SF_OK;
+  };
+  // Before the forward of layer i: queue the uploads of the next layers whose
+  // update is done.  While the update of a preloaded layer i (re-uploaded by
+  // its own Adam) is still running, wait for Adam progress and queue each
+  // later layer's upload as soon as its update finishes, so the copies run
+  // meanwhile instead of after it.
+  auto advance = [&](int i) -> sf_status {
+    const int lim = std::min(nl, i + 2 * W);
+    const bool wait_i = adam && e->pipe && e->preloaded && i < W;
+    for (;;) {
+      if (sf_status r = issue_ready(i, lim)) return r;
+      if (!wait_i) return SF_OK;
+      std::unique_lock<std::mutex> lk(e->mu);
+      if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
+      const int64_t want = e->step - 1;
+      if (e->adam_done[i] >= want) return SF_OK;
+      const int nf = next_fetch;
+      e->cv.wait(lk, [&] {
+        if (e->adam_done[i] >= want || !e->job_error.empty()) return true;
+        for (int j = nf; j < lim; ++j)
+          if (!fetched[j] && !(e->preloaded && j < W) && e->adam_done[j] >= want) return true;
+        return false;
+      });
+    }
   };
   for (int i = 0; i < nl; ++i) {
     const int u = i % W;
@@ -820,6 +863,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if ((rc = sf_head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
                               e->s_comp)))
       return rc;
+    SF_HIP(copy_f32(e->h_loss, e->d_loss, 1, e->s_comp));
     if ((rc = comp_end(a, &b))) return rc;
     if (adam && !head_host) {
       // LM head and final gain: updated on the head stream while the layer
@@ -1083,6 +1127,9 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   }
   e->dbuf = act_p;
   e->d_loss = reinterpret_cast<float*>(act_p + e->x_bytes);
+  if (hipHostMalloc(reinterpret_cast<void**>(&e->h_loss), 256, hipHostMallocDefault) != hipSuccess)
+    return cleanup(fail(SF_ERR_HIP, "pinned loss word allocation failed"));
+  *e->h_loss = 0.f;
   auto mk = [&](std::vector<hipEvent_t>& v) {
     for (int u = 0; u < W; ++u) {
       hipEvent_t ev;
@@ -1141,10 +1188,8 @@ sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float*
   }
   float loss = 0.f;
   if (head) {
-    if (hipMemcpy(&loss, e->d_loss, 4, hipMemcpyDeviceToHost) != hipSuccess) {
-      e->failed = true;
-      return fail(SF_ERR_HIP, "loss copy failed");
-    }
+    // written on the compute stream, which the step has synchronised
+    loss = *static_cast<volatile float*>(e->h_loss);
     if (h_loss) *h_loss = loss;
   }
   if (stats) {
@@ -1218,6 +1263,10 @@ sf_status sf_engine_destroy(sf_engine* e) {
     if (ev) (void)hipEventDestroy(ev);
   for (hipStream_t s : {e->s_h2d, e->s_up, e->s_d2h, e->s_head})
     if (s) (void)hipStreamDestroy(s);
+  if (e->h_loss) {
+    if (e->s_comp) (void)hipStreamSynchronize(e->s_comp);
+    (void)hipHostFree(e->h_loss);
+  }
   delete e;
   return SF_OK;
 }

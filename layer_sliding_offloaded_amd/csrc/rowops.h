@@ -21,6 +21,9 @@ hipError_t embed_fwd(int dtype, const void* E, const int32_t* ids, void* x0, int
 hipError_t embed_bwd(int dtype, const void* dx0, const int32_t* ids, float* dE, int rows, int H, int V,
                      hipStream_t s);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// dst[i] = src[i] for n fp32 words by plain vector stores (dst may be pinned
+// host memory: the words cross the host link without a copy engine).
+hipError_t copy_f32(float* dst, const float* src, int n, hipStream_t s);
 
 // Device Adam over n fp32 elements with precomputed coefficients
 // (o = 1 - b, ib = 1 / bias correction); out receives the storage-dtype copy.

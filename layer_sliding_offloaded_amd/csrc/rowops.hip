@@ -266,6 +266,10 @@ fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
   }
 }
 
+__global__ void __launch_bounds__(64) copy_f32_kernel(float* __restrict__ dst, const float* __restrict__ src, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
+}
+
 // dE[id] = sum over t with ids[t] == id of dx0[t], in increasing t.  The
 // wave of token t does the work only if t is the first occurrence of its id;
 // it then walks the later tokens with a ballot per 64 ids.
@@ -665,6 +669,12 @@ hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n / 4 + 255) / 256 + 1;
   hipLaunchKernelGGL(fill_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t copy_f32(float* dst, const float* src, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(1), dim3(64), 0, s, dst, src, n);
   return hipGetLastError();
 }
 

@@ -359,7 +359,8 @@ def _run_pipelined(w, layers, head, x, dy, steps, **kw):
 
 
 @pytest.mark.parametrize("head_adam,window,n_layers,ckpt", [("device", 2, 4, False), (None, 2, 3, False),
-                                                            ("device", 3, 5, True), ("device", 2, 1, False)])
+                                                            ("device", 3, 5, True), ("device", 2, 1, False),
+                                                            ("device", 2, 7, False), (None, 3, 8, False)])
 def test_engine_pipelined_matches_synchronous_bitwise(head_adam, window, n_layers, ckpt):
     """Running host Adam across the step boundary changes when updates are
     applied, never what is computed: three pipelined steps give the same
