@@ -151,11 +151,13 @@ rmsnorm_bwd_gain_kernel(const T* __restrict__ dout, const T* __restrict__ xin, c
   for (int t = t0 + w; t < t1; t += 4) {
     const int64_t base = static_cast<int64_t>(t) * H;
     const float rr = r[t];
-    uint4 dq[NV], xq[NV];
+    // the residual is requested with dout and x: one memory round trip per row
+    uint4 dq[NV], xq[NV], rq[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       dq[v] = *reinterpret_cast<const uint4*>(dout + base + (v * 64 + lane) * VE);
       xq[v] = *reinterpret_cast<const uint4*>(xin + base + (v * 64 + lane) * VE);
+      rq[v] = resid ? *reinterpret_cast<const uint4*>(resid + base + (v * 64 + lane) * VE) : make_uint4(0, 0, 0, 0);
     }
     float dot = 0.f;
 #pragma unroll
@@ -175,10 +177,7 @@ rmsnorm_bwd_gain_kernel(const T* __restrict__ dout, const T* __restrict__ xin, c
       Elem<T>::unpack(dq[v], d);
       Elem<T>::unpack(xq[v], xv);
       Elem<T>::unpack(gq[v], gg);
-      if (resid) load_vec<T>(resid + base + (v * 64 + lane) * VE, o);
-      else
-#pragma unroll
-        for (int e = 0; e < VE; ++e) o[e] = 0.f;
+      Elem<T>::unpack(rq[v], o);  // zeros (all bits clear) without a residual
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
         o[e] += rr * (d[e] * gg[e] - xv[e] * rr * proj);
@@ -206,31 +205,39 @@ rmsnorm_bwd_gain_kernel(const T* __restrict__ dout, const T* __restrict__ xin, c
 }
 
 // Gain gradient, stage 2: dg[j] = sum over the chunks of partial, in a fixed
-// order: four groups of consecutive chunks, each summed in order (loads
-// issued eight at a time), then the group sums in order.  Block = 64 columns
-// x 4 groups.
-__global__ void __launch_bounds__(256)
+// order: 32 groups of consecutive chunks, each summed in order (loads issued
+// sixteen at a time), then the group sums in order.  Block = 32 columns (one
+// 128-byte line of a partial row) x 32 groups: the sum of a column is
+// latency-bound, not bandwidth-bound (2 MB at hidden 1024), so every thread
+// waits for as few rounds of loads as possible and the blocks are many.
+constexpr int kReduceCols = 32, kReduceGroups = 32;
+__global__ void __launch_bounds__(kReduceCols * kReduceGroups)
 gain_reduce_kernel(const float* __restrict__ partial, float* __restrict__ dg, int nchunks, int H) {
-  __shared__ float part[4][64];
-  const int c64 = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + c64;
-  const int per = (nchunks + 3) / 4;
+  __shared__ float part[kReduceGroups][kReduceCols];
+  const int col = threadIdx.x % kReduceCols, grp = threadIdx.x / kReduceCols;
+  const int j = blockIdx.x * kReduceCols + col;
+  const int per = (nchunks + kReduceGroups - 1) / kReduceGroups;
   const int c0 = grp * per, c1 = min(nchunks, c0 + per);
   float s = 0.f;
   if (j < H) {
     int c = c0;
-    for (; c + 8 <= c1; c += 8) {
-      float v[8];
+    for (; c + 16 <= c1; c += 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = partial[static_cast<int64_t>(c + u) * H + j];
+      for (int u = 0; u < 16; ++u) v[u] = partial[static_cast<int64_t>(c + u) * H + j];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 16; ++u) s += v[u];
     }
     for (; c < c1; ++c) s += partial[static_cast<int64_t>(c) * H + j];
   }
-  part[grp][c64] = s;
+  part[grp][col] = s;
   __syncthreads();
-  if (grp == 0 && j < H) dg[j] = ((part[0][c64] + part[1][c64]) + part[2][c64]) + part[3][c64];
+  if (grp == 0 && j < H) {
+    float t = part[0][col];
+#pragma unroll
+    for (int k = 1; k < kReduceGroups; ++k) t += part[k][col];
+    dg[j] = t;
+  }
 }
 
 // x0[t] = E[ids[t]]; an id outside [0, V) yields a NaN row.
@@ -632,7 +639,8 @@ hipError_t rmsnorm_bwd(int dtype, const void* dout, const void* xin, const float
       SF_NB(1) SF_NB(2) SF_NB(3) SF_NB(4)
     }
 #undef SF_NB
-    hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + 63) / 64), dim3(256), 0, s, partial, dg, nchunks, H);
+    hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + kReduceCols - 1) / kReduceCols), dim3(kReduceCols * kReduceGroups),
+                     0, s, partial, dg, nchunks, H);
     return hipGetLastError();
   }
   const dim3 pg((H / VE + 63) / 64, nchunks);
@@ -649,7 +657,8 @@ hipError_t rmsnorm_bwd(int dtype, const void* dout, const void* xin, const float
     hipLaunchKernelGGL(gain_partial_kernel<float>, pg, dim3(64), 0, s, static_cast<const float*>(dout),
                        static_cast<const float*>(xin), r, partial, rows, H, rpc);
   }
-  hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + 63) / 64), dim3(256), 0, s, partial, dg, nchunks, H);
+  hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + kReduceCols - 1) / kReduceCols), dim3(kReduceCols * kReduceGroups),
+                     0, s, partial, dg, nchunks, H);
   return hipGetLastError();
 }
 

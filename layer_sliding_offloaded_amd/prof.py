@@ -265,6 +265,10 @@ def rowops(db_path, workload):
         ("rmsnorm_fwd_kernel", None, 2 * T * H * e + T * 4 + H * e, "x in, y out, r out"),
         ("rmsnorm_bwd_kernel", None, 4 * T * H * e + T * 4 + H * e, "dy, x, residual in; dx out"),
         ("gain_partial_kernel", None, 2 * T * H * e + T * 4 + 128 * H * 4, "dy, x in; 128 partial rows out"),
+        # fused RMSNorm backward + gain partial sums (hidden <= 2048): 512 row chunks
+        ("rmsnorm_bwd_gain_kernel", None, 4 * T * H * e + T * 4 + H * e + 512 * H * 4,
+         "dy, x, residual in; dx, 512 partial rows out"),
+        ("gain_reduce_kernel", None, 512 * H * 4 + H * 4, "512 partial rows in; gain gradient out"),
         ("attn_dot_kernel", None, 2 * T * nq * e + T * w.n_heads * 4, "dA, O in; row sums out"),
         ("ce_rows_reg_kernel", None, R * V * (4 + e) + R * 8, "fp32 logits in, dlogits out"),
         ("ce_rows_kernel", None, R * V * (4 + e) + R * 8, "fp32 logits in (twice), dlogits out"),
