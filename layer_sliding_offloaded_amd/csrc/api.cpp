@@ -520,10 +520,29 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
 
 }  // namespace sf
 
-extern "C" {
+namespace sf {
 
-sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
-                          float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream) {
+// The LM-head weight gradient of the last (or only) row chunk: dW_lm (=, or
+// += after earlier chunks) dlogits^T hf, from the head workspace the head
+// pass left.  No split-K workspace: it may run beside the layer backward.
+sf_status head_last_dw(sf_ctx* c, float* d_dwlm, sf_stream stream) {
+  const Dims& d = c->dims;
+  const WorkLayout& wl = c->work;
+  const int T = static_cast<int>(d.T);
+  const int R = c->head_chunk_rows;
+  const int r0 = ((T - 1) / R) * R;
+  GemmArgs g;
+  g.A = c->ws + wl.dlogits; g.lda = d.V;
+  g.B = c->ws + wl.hf + static_cast<size_t>(r0) * d.H * d.e; g.ldb = d.H;
+  g.C = d_dwlm; g.ldc = d.H;
+  g.M = d.V; g.N = d.H; g.K = T - r0;
+  SF_HIP(gemm(d.dtype, GemmLayout::TN, r0 == 0 ? Epi::StoreF32 : Epi::AccF32, g, static_cast<hipStream_t>(stream),
+              nullptr, 0));
+  return SF_OK;
+}
+
+sf_status head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
+                       float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream, bool defer_last_dw) {
   if (sf_status st = check_ctx(c)) return st;
   if (sf_status st = check_ptrs({d_gf, d_wlm, d_x, d_ids, d_dx, d_dgf, d_dwlm})) return st;
   if (!d_loss) return fail(SF_ERR_ARG, "d_loss is NULL");
@@ -563,6 +582,7 @@ sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const 
     g.C = dhf + static_cast<size_t>(r0) * d.H * d.e; g.ldc = d.H;
     g.M = rows; g.N = d.H; g.K = d.V;
     SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s, skw, skb));
+    if (defer_last_dw && r0 + R >= T) break;  // the caller runs head_last_dw later
     g = GemmArgs();
     g.A = dlogits; g.lda = d.V;
     g.B = hfc; g.ldb = d.H;
@@ -573,6 +593,15 @@ sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const 
   SF_HIP(loss_reduce(loss_rows, d_loss, T, inv_n, s));
   SF_HIP(rmsnorm_bwd(d.dtype, dhf, d_x, rf, d_gf, nullptr, d_dx, partial, kGainChunks, d_dgf, T, d.H, s));
   return SF_OK;
+}
+
+}  // namespace sf
+
+extern "C" {
+
+sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
+                          float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream) {
+  return sf::head_fwd_bwd(c, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream, false);
 }
 
 size_t sf_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {

@@ -237,8 +237,16 @@ struct sf_engine {
   bool preloaded = false;  // units 0..W-1 hold this step's layers 0..W-1 already
   hipStream_t s_comp = nullptr, s_h2d = nullptr, s_d2h = nullptr, s_head = nullptr;
   // uploads of updated ranges that Adam queues (layers below the window):
-  // their own stream, so that they never wait behind the forward's prefetches
+  // never behind the forward's prefetches or the gradient copies.  The device
+  // has few hardware queues (4 by default) and streams beyond them share one,
+  // where work waits for everything queued before it on any of its streams:
+  // a stream of their own shared a queue with the gradient copies.  So the
+  // uploads and the head's update (s_head) go on the context's side stream,
+  // which is idle at the end of the backward, where these uploads come, and
+  // the engine adds only the H2D and D2H streams to the caller's and the
+  // context's.
   hipStream_t s_up = nullptr;
+  bool own_head = false;  // s_head created here (the context has no side stream)
   std::vector<char*> uparam, ugrad, x, saved;
   char* dbuf = nullptr;
   // activation checkpointing: layer inputs ring (3), checkpoint slots for the
@@ -768,12 +776,20 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   // regions are freed by the previous backward from unit W-1 down to unit 0,
   // so each of these layers is queued, highest first, as soon as its update
   // is done rather than behind a lower one still waiting for its region.
+  // While the host can wait (the forward of a preloaded layer awaits its
+  // update), a first-window upload is queued only once its region is free on
+  // the device as well: queued earlier, its wait for the gradients to leave
+  // would hold up the work behind it on a hardware queue that the upload
+  // stream may share with the streams of Adam's uploads.
   std::vector<char> fetched(nl, 0);
   int next_fetch = 0;  // every layer below it is fetched (or preloaded)
-  auto issue_ready = [&](int i, int lim) -> sf_status {
+  auto region_free = [&](int j) {
+    return !(e->preloaded && j >= W && j < 2 * W) || hipEventQuery(e->ev_grad_free[j % W]) == hipSuccess;
+  };
+  auto issue_ready = [&](int i, int lim, bool can_wait) -> sf_status {
     if (e->preloaded) {
       for (int j = std::min(lim, 2 * W) - 1; j >= W; --j) {
-        if (fetched[j] || (j > i && !adam_ready(j))) continue;
+        if (fetched[j] || (j > i && (!adam_ready(j) || (can_wait && !region_free(j))))) continue;
         if (sf_status r = fetch(j)) return r;
         fetched[j] = 1;
       }
@@ -781,7 +797,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     for (; next_fetch < lim; ++next_fetch) {
       const int j = next_fetch;
       if (fetched[j] || (e->preloaded && j < W)) continue;
-      if (j > i && !adam_ready(j)) break;
+      if (j > i && (!adam_ready(j) || (can_wait && !region_free(j)))) break;
       if (sf_status r = fetch(j)) return r;
       fetched[j] = 1;
     }
@@ -796,19 +812,25 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     const int lim = std::min(nl, i + 2 * W);
     const bool wait_i = adam && e->pipe && e->preloaded && i < W;
     for (;;) {
-      if (sf_status r = issue_ready(i, lim)) return r;
+      if (sf_status r = issue_ready(i, lim, wait_i)) return r;
       if (!wait_i) return SF_OK;
+      // a first-window upload held back for its region: poll the device
+      bool held = false;
+      for (int j = next_fetch; j < lim && !held; ++j) held = j >= W && j < 2 * W && !fetched[j];
       std::unique_lock<std::mutex> lk(e->mu);
       if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
       const int64_t want = e->step - 1;
       if (e->adam_done[i] >= want) return SF_OK;
       const int nf = next_fetch;
-      e->cv.wait(lk, [&] {
+      auto progress = [&] {
         if (e->adam_done[i] >= want || !e->job_error.empty()) return true;
         for (int j = nf; j < lim; ++j)
-          if (!fetched[j] && !(e->preloaded && j < W) && e->adam_done[j] >= want) return true;
+          if (!fetched[j] && !(e->preloaded && j < W) && e->adam_done[j] >= want && !(j >= W && j < 2 * W))
+            return true;
         return false;
-      });
+      };
+      if (held) e->cv.wait_for(lk, std::chrono::microseconds(50), progress);
+      else e->cv.wait(lk, progress);
     }
   };
   for (int i = 0; i < nl; ++i) {
@@ -855,29 +877,37 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
                        k.b1, k.b2, k.one_b1, k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, st_));
     return SF_OK;
   };
+  // With the device Adam of the LM head, the head's last W_lm gradient GEMM
+  // and that Adam run on the head stream once the last layer's MLP weight
+  // gradients are final: nothing in the step reads them, and beside the
+  // start of the backward they would delay the first gradient range, which
+  // host Adam waits for.
+  const bool head_dev_adam = head && adam && !head_host;
+  hipEvent_t head_end = nullptr;
+  auto head_update = [&](hipEvent_t mlp_done) -> sf_status {
+    hipEvent_t ha = timing_event(e), hb = timing_event(e);
+    if (!ha || !hb) return fail(SF_ERR_HIP, "event pool exhausted");
+    SF_HIP(hipStreamWaitEvent(e->s_head, head_end, 0));
+    SF_HIP(hipStreamWaitEvent(e->s_head, mlp_done, 0));
+    SF_HIP(hipEventRecord(ha, e->s_head));
+    if (sf_status r = head_last_dw(ctx, hg + VH + d.H, e->s_head)) return r;
+    if (sf_status r = dev_adam(VH, d.H, c.d_gf, e->s_head)) return r;
+    if (sf_status r = dev_adam(VH + d.H, VH, c.d_wlm, e->s_head)) return r;
+    SF_HIP(hipEventRecord(hb, e->s_head));
+    SF_HIP(hipEventRecord(e->ev_head_done, e->s_head));
+    return record_interval(e, ha, hb, 0, 0);
+  };
   if (head) {
     // the previous step's device Adam of the LM head (head stream) reads hg
     // and writes d_gf / d_wlm
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_head_done, 0));
     if ((rc = comp_begin(&a))) return rc;
-    if ((rc = sf_head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
-                              e->s_comp)))
+    if ((rc = head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
+                           e->s_comp, head_dev_adam)))
       return rc;
     SF_HIP(copy_f32(e->h_loss, e->d_loss, 1, e->s_comp));
     if ((rc = comp_end(a, &b))) return rc;
-    if (adam && !head_host) {
-      // LM head and final gain: updated on the head stream while the layer
-      // backward runs (nothing later in the step reads them)
-      hipEvent_t ha = timing_event(e), hb = timing_event(e);
-      if (!ha || !hb) return fail(SF_ERR_HIP, "event pool exhausted");
-      SF_HIP(hipStreamWaitEvent(e->s_head, b, 0));
-      SF_HIP(hipEventRecord(ha, e->s_head));
-      if ((rc = dev_adam(VH, d.H, c.d_gf, e->s_head)) || (rc = dev_adam(VH + d.H, VH, c.d_wlm, e->s_head)))
-        return rc;
-      SF_HIP(hipEventRecord(hb, e->s_head));
-      SF_HIP(hipEventRecord(e->ev_head_done, e->s_head));
-      if ((rc = record_interval(e, ha, hb, 0, 0))) return rc;
-    }
+    head_end = b;
     if (head_host) {
       hipEvent_t done;
       if ((rc = timed_d2h(e, c.h_head_grads + VH, hg + VH, (VH + d.H) * 4, b, &done))) return rc;
@@ -917,6 +947,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if ((rc = layer_bwd(ctx, e->uparam[u], xi, sv, dy, e->dbuf, reinterpret_cast<float*>(e->ugrad[u]), e->s_comp,
                         ffn)))
       return rc;
+    if (head_dev_adam && i == nl - 1 && (rc = head_update(ffn))) return rc;
     if (ck && i < nl - 1) SF_HIP(hipEventRecord(e->ev_cfree[i % 2], e->s_comp));
     if ((rc = comp_end(a, &b))) return rc;
     dy = e->dbuf;
@@ -1100,10 +1131,16 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
     return st;
   };
   if (hipStreamCreateWithFlags(&e->s_h2d, hipStreamNonBlocking) != hipSuccess ||
-      hipStreamCreateWithFlags(&e->s_up, hipStreamNonBlocking) != hipSuccess ||
-      hipStreamCreateWithFlags(&e->s_d2h, hipStreamNonBlocking) != hipSuccess ||
-      hipStreamCreateWithFlags(&e->s_head, hipStreamNonBlocking) != hipSuccess)
+      hipStreamCreateWithFlags(&e->s_d2h, hipStreamNonBlocking) != hipSuccess)
     return cleanup(fail(SF_ERR_HIP, "stream creation failed"));
+  if (ctx->side) {
+    e->s_head = ctx->side;
+  } else {
+    if (hipStreamCreateWithFlags(&e->s_head, hipStreamNonBlocking) != hipSuccess)
+      return cleanup(fail(SF_ERR_HIP, "stream creation failed"));
+    e->own_head = true;
+  }
+  e->s_up = e->s_head;
   char* pool = static_cast<char*>(c.d_pool);
   for (int u = 0; u < W; ++u) {
     e->uparam.push_back(pool + u * unit);
@@ -1253,7 +1290,7 @@ sf_status sf_engine_destroy(sf_engine* e) {
     e->dispatcher.join();
   }
   e->pool.reset();
-  for (hipStream_t s : {e->s_h2d, e->s_up, e->s_d2h, e->s_head})
+  for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
     if (s) (void)hipStreamSynchronize(s);
   for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_free, &e->ev_gslot_ready, &e->ev_gslot_free,
                   &e->tev})
@@ -1261,7 +1298,7 @@ sf_status sf_engine_destroy(sf_engine* e) {
   for (hipEvent_t ev : {e->ev_xfree[0], e->ev_xfree[1], e->ev_xfree[2], e->ev_cready[0], e->ev_cready[1],
                         e->ev_cfree[0], e->ev_cfree[1], e->ev_ckpt_out, e->ev_head_done})
     if (ev) (void)hipEventDestroy(ev);
-  for (hipStream_t s : {e->s_h2d, e->s_up, e->s_d2h, e->s_head})
+  for (hipStream_t s : {e->s_h2d, e->s_d2h, e->own_head ? e->s_head : nullptr})
     if (s) (void)hipStreamDestroy(s);
   if (e->h_loss) {
     if (e->s_comp) (void)hipStreamSynchronize(e->s_comp);

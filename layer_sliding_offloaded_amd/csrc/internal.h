@@ -54,6 +54,12 @@ namespace sf {
 // weight gradients (Wg, Wu, Wd) are complete, before the attention half.
 sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy, void* d_dx,
                     float* d_dw, sf_stream stream, hipEvent_t ffn_done);
+// sf_head_fwd_bwd; with defer_last_dw the LM-head weight gradient of the last
+// row chunk is left to head_last_dw, which reads the head workspace (dlogits,
+// hf) and must run before the context's next head pass.
+sf_status head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
+                       float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream, bool defer_last_dw);
+sf_status head_last_dw(sf_ctx* c, float* d_dwlm, sf_stream stream);
 }  // namespace sf
 
 struct sf_ctx {
