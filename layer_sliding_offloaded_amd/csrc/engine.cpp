@@ -478,15 +478,22 @@ void dispatcher_loop(sf_engine* e) {
       std::unique_lock<std::mutex> lk(e->mu);
       e->cv.wait(lk, [&] { return e->stop || !e->jobs.empty(); });
       if (e->jobs.empty()) return;  // stop requested and nothing left
-      // Among the ranges whose copies have landed, the lowest layer first
-      // (ranges of one layer in order): the next forward needs layer 0
-      // first, and layer 0's gradients arrive last.  With none landed, the
-      // oldest range (its copy was queued first).
+      // Among the ranges whose copies have landed (ranges of one layer in
+      // order): first the layers above the window in the order they arrived
+      // (highest first), since a layer frees its gradient slot, which a later
+      // layer's copies wait for, only when all its ranges are done; then the
+      // window's layers lowest first, as the next forward needs layer 0 first
+      // and layer 0's gradients arrive last.  A layer's last range (its gains,
+      // a few KB) goes before all others.  With none landed, the oldest range
+      // (its copy was queued first).
       size_t pick = 0;
       int best = INT32_MAX;
       for (size_t q = 0; q < e->jobs.size(); ++q) {
         const Job& cand = e->jobs[q];
-        const int key = cand.kind == kLayer ? cand.layer : -1;
+        const int key = cand.kind != kLayer ? -1
+                        : cand.last         ? -2
+                        : cand.layer >= e->W ? e->nl - cand.layer
+                                             : e->nl + cand.layer;
         if (key >= best) continue;
         bool earlier_same = false;  // keep a layer's ranges in order
         for (size_t r = 0; r < q && !earlier_same; ++r)
