@@ -264,7 +264,7 @@ def rowops(db_path, workload):
     spec = [
         ("rmsnorm_fwd_kernel", None, 2 * T * H * e + T * 4 + H * e, "x in, y out, r out"),
         ("rmsnorm_bwd_kernel", None, 4 * T * H * e + T * 4 + H * e, "dy, x, residual in; dx out"),
-        ("gain_partial_kernel", None, 2 * T * H * e + T * 4 + 128 * H * 4, "dy, x in; 128 partial rows out"),
+        ("gain_partial_kernel", None, 2 * T * H * e + T * 4 + 512 * H * 4, "dy, x in; 512 partial rows out"),
         # fused RMSNorm backward + gain partial sums (hidden <= 2048): 512 row chunks
         ("rmsnorm_bwd_gain_kernel", None, 4 * T * H * e + T * 4 + H * e + 512 * H * 4,
          "dy, x, residual in; dx, 512 partial rows out"),
