@@ -991,10 +991,27 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   }
 
   // ---------------- embedding backward (+ its device Adam)
+  // With Adam, the gradient stays sparse: the summed rows of the ids present
+  // (embed_bwd_sparse, in the dense gradient's region, which is then unused)
+  // and a row map feed the device Adam, which gives rows no token touched a
+  // zero gradient -- the same bits as Adam over the dense gradient, without
+  // clearing, scattering and re-reading V x H fp32 values.
+  const bool sparse_embed = adam && e->sp.total + static_cast<size_t>(d.V) <= VH;
   if (head && !head_host) {
     if ((rc = comp_begin(&a))) return rc;
-    if ((rc = sf_embed_bwd(ctx, e->dbuf, ids, hg, e->s_comp))) return rc;
-    if (adam && (rc = dev_adam(0, VH, c.d_E, e->s_comp))) return rc;
+    if (sparse_embed) {
+      int32_t* hgi = reinterpret_cast<int32_t*>(hg);
+      SF_HIP(embed_bwd_sparse(d.dtype, e->dbuf, ids, hgi + e->sp.ids, hg + e->sp.rows, hgi, hgi + e->sp.scratch,
+                              static_cast<int>(d.T), d.H, d.V, e->s_comp));
+      float* st = c.d_head_state;
+      const AdamCoef& k = e->coef;
+      SF_HIP(embed_adam_sparse(d.dtype, st, st + NH, st + 2 * NH, hg + e->sp.rows, hgi + e->sp.ids, hgi,
+                               hgi + e->sp.total, static_cast<int>(d.T), c.d_E, d.V, d.H, k.b1, k.b2, k.one_b1,
+                               k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, e->s_comp));
+    } else {
+      if ((rc = sf_embed_bwd(ctx, e->dbuf, ids, hg, e->s_comp))) return rc;
+      if (adam && (rc = dev_adam(0, VH, c.d_E, e->s_comp))) return rc;
+    }
     if ((rc = comp_end(a, nullptr))) return rc;
   }
   // ---------------- embedding backward on the host path: sparse rows of the ids present

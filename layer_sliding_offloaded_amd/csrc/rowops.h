@@ -38,6 +38,14 @@ hipError_t adam_device(int dtype, float* p, float* m, float* v, const float* g, 
 hipError_t embed_bwd_sparse(int dtype, const void* dx0, const int32_t* ids, int32_t* out_ids, float* out_rows,
                             int32_t* count, int32_t* scratch, int rows, int H, int V, hipStream_t s);
 
+// Device Adam of an embedding [V, H] from its sparse gradient (as produced by
+// embed_bwd_sparse: out_ids / rows for the first *count slots, at most
+// max_rows): map (V int32 of scratch) is rebuilt, rows no token touched take
+// a zero gradient.  Bitwise equal to adam_device over the dense gradient.
+hipError_t embed_adam_sparse(int dtype, float* p, float* m, float* v, const float* rows, const int32_t* out_ids,
+                             const int32_t* count, int32_t* map, int max_rows, void* out, int V, int H, float b1,
+                             float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s);
+
 hipError_t ce_rows(int dtype, const float* logits, const int32_t* ids, void* dlogits, float* loss_rows, int t0,
                    int R, int V, int S, float inv_n, hipStream_t s);
 hipError_t loss_reduce(const float* loss_rows, float* loss, int rows, float inv_n, hipStream_t s);

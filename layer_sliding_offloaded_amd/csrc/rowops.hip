@@ -438,7 +438,44 @@ adam_device_kernel(float* __restrict__ p, float* __restrict__ m, float* __restri
   // for fp32), so every operation rounds exactly as the host loop's
 #pragma clang fp contract(off)
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
+  // 4 elements a thread when every operand is 16-byte aligned (8 for a bf16
+  // copy) while whole vectors remain, then one a thread for the tail (and for
+  // unaligned operands)
+  constexpr bool kOut4 = sizeof(TO) == 2;
+  const bool vec = ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(v) |
+                     reinterpret_cast<uintptr_t>(g)) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(out) & (kOut4 ? 7u : 15u)) == 0;
+  int64_t done = 0;
+  if (vec) {
+    const int64_t n4 = n / 4;
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < n4; q += stride) {
+      const int64_t i = q * 4;
+      const float4 g4 = *reinterpret_cast<const float4*>(g + i);
+      const float4 p4 = *reinterpret_cast<const float4*>(p + i);
+      const float4 m4 = *reinterpret_cast<const float4*>(m + i);
+      const float4 v4 = *reinterpret_cast<const float4*>(v + i);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
+      const float mm[4] = {m4.x, m4.y, m4.z, m4.w}, vv[4] = {v4.x, v4.y, v4.z, v4.w};
+      float po[4], mo[4], vo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float gi = gg[k];
+        const float mi = b1 * mm[k] + o1 * gi;
+        const float vi = b2 * vv[k] + o2 * gi * gi;
+        mo[k] = mi;
+        vo[k] = vi;
+        const float den = sqrtf(vi * ib2) + eps;
+        po[k] = pp[k] - lr * (mi * ib1) / den;
+      }
+      *reinterpret_cast<float4*>(p + i) = make_float4(po[0], po[1], po[2], po[3]);
+      *reinterpret_cast<float4*>(m + i) = make_float4(mo[0], mo[1], mo[2], mo[3]);
+      *reinterpret_cast<float4*>(v + i) = make_float4(vo[0], vo[1], vo[2], vo[3]);
+      if constexpr (kOut4) *reinterpret_cast<uint2*>(out + i) = make_uint2(pack2(po[0], po[1]), pack2(po[2], po[3]));
+      else *reinterpret_cast<float4*>(out + i) = make_float4(po[0], po[1], po[2], po[3]);
+    }
+    done = n4 * 4;
+  }
+  for (int64_t i = done + static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
     const float gi = g[i];
     const float mi = b1 * m[i] + o1 * gi;
     const float vi = b2 * v[i] + o2 * gi * gi;
@@ -449,6 +486,68 @@ adam_device_kernel(float* __restrict__ p, float* __restrict__ m, float* __restri
     p[i] = pi;
     if constexpr (sizeof(TO) == 2) out[i].u = f2bf(pi);
     else out[i] = pi;
+  }
+}
+
+// Row map of a sparse embedding gradient: map[r] = the slot of row r among
+// the n distinct rows (out_ids), -1 for rows no token uses.
+__global__ void __launch_bounds__(256) row_map_clear_kernel(int32_t* __restrict__ map, int V) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r < V) map[r] = -1;
+}
+__global__ void __launch_bounds__(256)
+row_map_set_kernel(const int32_t* __restrict__ out_ids, const int32_t* __restrict__ count, int32_t* __restrict__ map,
+                   int max_rows, int V) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s < max_rows && s < *count) {
+    const int r = out_ids[s];
+    if (r >= 0 && r < V) map[r] = s;
+  }
+}
+
+// Device Adam over a [V, H] tensor whose gradient is sparse: row r's
+// gradient is rows[map[r]] when map[r] >= 0 and zero otherwise (rows no token
+// touched still decay their moments).  The same operations per element as
+// adam_device_kernel, so the bits equal those of Adam on the dense gradient.
+// Block = one row at a time, 4 consecutive elements a thread (H % 4 == 0).
+template <typename TO>
+__global__ void __launch_bounds__(256)
+adam_rows_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
+                 const float* __restrict__ rows, const int32_t* __restrict__ map, TO* __restrict__ out, int V, int H,
+                 float b1, float b2, float o1, float o2, float ib1, float ib2, float lr, float eps) {
+#pragma clang fp contract(off)
+  for (int r = blockIdx.x; r < V; r += gridDim.x) {
+    const int sl = map[r];
+    const int64_t base = static_cast<int64_t>(r) * H;
+    for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
+      const int64_t i = base + c;
+      const float4 g4 = sl >= 0 ? *reinterpret_cast<const float4*>(rows + static_cast<int64_t>(sl) * H + c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 p4 = *reinterpret_cast<const float4*>(p + i);
+      const float4 m4 = *reinterpret_cast<const float4*>(m + i);
+      const float4 v4 = *reinterpret_cast<const float4*>(v + i);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
+      const float mm[4] = {m4.x, m4.y, m4.z, m4.w}, vv[4] = {v4.x, v4.y, v4.z, v4.w};
+      float po[4], mo[4], vo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float gi = gg[k];
+        const float mi = b1 * mm[k] + o1 * gi;
+        const float vi = b2 * vv[k] + o2 * gi * gi;
+        mo[k] = mi;
+        vo[k] = vi;
+        const float den = sqrtf(vi * ib2) + eps;
+        po[k] = pp[k] - lr * (mi * ib1) / den;
+      }
+      *reinterpret_cast<float4*>(p + i) = make_float4(po[0], po[1], po[2], po[3]);
+      *reinterpret_cast<float4*>(m + i) = make_float4(mo[0], mo[1], mo[2], mo[3]);
+      *reinterpret_cast<float4*>(v + i) = make_float4(vo[0], vo[1], vo[2], vo[3]);
+      if constexpr (sizeof(TO) == 2) {
+        *reinterpret_cast<uint2*>(out + i) = make_uint2(pack2(po[0], po[1]), pack2(po[2], po[3]));
+      } else {
+        *reinterpret_cast<float4*>(out + i) = make_float4(po[0], po[1], po[2], po[3]);
+      }
+    }
   }
 }
 
@@ -727,6 +826,25 @@ hipError_t adam_device(int dtype, float* p, float* m, float* v, const float* g, 
   else
     hipLaunchKernelGGL(adam_device_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, m, v, g,
                        static_cast<float*>(out), n, b1, b2, o1, o2, ib1, ib2, lr, eps);
+  return hipGetLastError();
+}
+
+hipError_t embed_adam_sparse(int dtype, float* p, float* m, float* v, const float* rows, const int32_t* out_ids,
+                             const int32_t* count, int32_t* map, int max_rows, void* out, int V, int H, float b1,
+                             float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s) {
+  if (V <= 0 || H <= 0) return hipSuccess;
+  if (H % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_map_clear_kernel, dim3((V + 255) / 256), dim3(256), 0, s, map, V);
+  if (max_rows > 0)
+    hipLaunchKernelGGL(row_map_set_kernel, dim3((max_rows + 255) / 256), dim3(256), 0, s, out_ids, count, map,
+                       max_rows, V);
+  const dim3 grid(static_cast<unsigned>(std::min(V, 8192)));
+  if (dtype == 1)
+    hipLaunchKernelGGL(adam_rows_kernel<bf16>, grid, dim3(256), 0, s, p, m, v, rows, map, static_cast<bf16*>(out), V,
+                       H, b1, b2, o1, o2, ib1, ib2, lr, eps);
+  else
+    hipLaunchKernelGGL(adam_rows_kernel<float>, grid, dim3(256), 0, s, p, m, v, rows, map, static_cast<float*>(out),
+                       V, H, b1, b2, o1, o2, ib1, ib2, lr, eps);
   return hipGetLastError();
 }
 
