@@ -14,9 +14,13 @@
 //  - gradient buffers on the host are shared by all layers.
 //
 // Realisation here.  HIP streams: compute (the caller's), H2D (layer
-// prefetch), D2H (gradients), the uploads Adam queues, and a head-upload
-// stream, all at default priority and ordered only through events, so
-// host-link copies in both directions overlap kernels.  Unit u = layer mod window; each unit has
+// prefetch), D2H (gradients) and the context's side stream, which besides
+// the layer backward's weight-gradient GEMMs carries the LM head's update and
+// the uploads Adam queues; all at default priority and ordered only through
+// events, so host-link copies in both directions overlap kernels.  Four
+// streams in all: the device has four hardware queues by default, and a
+// stream beyond them shares a queue, where its work waits behind everything
+// queued before it on the other streams of that queue.  Unit u = layer mod window; each unit has
 // separate "parameters free" and "gradients free" events, so a unit's
 // parameter slot can be refilled for L_{i-window+1} as soon as the backward
 // of L_i is done while its gradient slot is still draining.  A dispatcher
@@ -33,8 +37,10 @@
 // and the next step's forward starts without waiting for them.
 //
 // Embedding and LM head (resident in HBM): by default a device Adam updates
-// them (fp32 master and moments in HBM), the LM head and final norm on a
-// side stream while the layer backward runs.  With SF_ENGINE_HEAD_HOST_ADAM
+// them (fp32 master and moments in HBM), the LM head and final norm on the
+// side stream once the last layer's MLP weight gradients are final, the
+// embedding from its sparse gradient (distinct rows and a row map) at the
+// end of the backward.  With SF_ENGINE_HEAD_HOST_ADAM
 // they take the host path like a layer: the LM-head and final-norm gradients
 // leave right after the head and are applied (and their parameters uploaded
 // again) while the layer backward runs; the embedding gradient leaves sparse
