@@ -100,6 +100,48 @@ def stored_traffic(workload, role):
     return table[role]
 
 
+def link_probe(torch, nbytes=256 << 20, reps=4):
+    """Pinned host <-> device copy rates (GB/s) measured with hipMemcpyAsync
+    (torch copies of pinned buffers): each direction alone, then both at once
+    on two streams of default priority."""
+    h_src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h_dst = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d_dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d_src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s_up, s_down = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn, stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        return e0, e1
+
+    def rate(e):
+        return nbytes * reps / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9
+
+    up = lambda: [d_dst.copy_(h_src, non_blocking=True) for _ in range(reps)]
+    down = lambda: [h_dst.copy_(d_src, non_blocking=True) for _ in range(reps)]
+    with torch.cuda.stream(s_up):
+        up()  # warm-up
+        eu = timed(up, s_up)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s_down):
+        down()
+        ed = timed(down, s_down)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s_up):
+        bu = timed(up, s_up)
+    with torch.cuda.stream(s_down):
+        bd = timed(down, s_down)
+    torch.cuda.synchronize()
+    out = {"h2d_gbps": round(rate(eu), 2), "d2h_gbps": round(rate(ed), 2),
+           "bidir_h2d_gbps": round(rate(bu), 2), "bidir_d2h_gbps": round(rate(bd), 2),
+           "probe": f"{reps} x {nbytes >> 20} MiB pinned copies per direction"}
+    del h_src, h_dst, d_dst, d_src
+    return out
+
+
 def cpu_baseline(w, target_s=12.0):
     """The fp64 oracle, as it stands, on one layer fwd+bwd of a bounded slice
     (batch 1) of the workload, repeated until about target_s of CPU work."""
@@ -321,6 +363,14 @@ def main():
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": stored_traffic(w.name, dom_name)},
     }
+    # host-link roofline: the step's bytes each way at the probe's
+    # bidirectional rates (both directions run at once in the step)
+    link = link_probe(torch)
+    t_link = max(med["h2d_bytes"] / (link["bidir_h2d_gbps"] * 1e9), med["d2h_bytes"] / (link["bidir_d2h_gbps"] * 1e9))
+    link_tok = T * w.n_layers / t_link if t_link > 0 else None
+    out["host_link"] = dict(link, step_h2d_gbps=round(med["h2d_gbps"], 2), step_d2h_gbps=round(med["d2h_gbps"], 2),
+                            link_bound_tokens_per_s_per_layer=round(link_tok, 1) if link_tok else None,
+                            frac=round(value / link_tok, 4) if link_tok else None)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
