@@ -365,7 +365,7 @@ sf_status sf_layer_fwd(sf_ctx* c, const void* d_w, const void* d_x, void* d_y, v
 
 sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy,
                        void* d_dx, float* d_dw, sf_stream stream) {
-  return sf::layer_bwd(c, d_w, d_x, d_saved, d_dy, d_dx, d_dw, stream, nullptr);
+  return sf::layer_bwd(c, d_w, d_x, d_saved, d_dy, d_dx, d_dw, stream, nullptr, nullptr);
 }
 
 }  // extern "C"
@@ -373,7 +373,7 @@ sf_status sf_layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* 
 namespace sf {
 
 sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy, void* d_dx,
-                    float* d_dw, sf_stream stream, hipEvent_t ffn_done) {
+                    float* d_dw, sf_stream stream, hipEvent_t ffn_done, hipEvent_t wd_done) {
   if (sf_status st = check_ctx(c)) return st;
   if (sf_status st = check_ptrs({d_w, d_x, d_saved, d_dy, d_dx, d_dw})) return st;
   const Dims& d = c->dims;
@@ -443,6 +443,7 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
     gw.C = dw + L.grad_off[SF_WD]; gw.ldc = d.F;
     gw.M = d.H; gw.N = d.F; gw.K = T;
     SF_HIP(gemm(d.dtype, GemmLayout::TN, Epi::StoreF32, gw, sw, skw_w, skb_w));
+    if (wd_done) SF_HIP(hipEventRecord(wd_done, sw));
   }
   if (sf_status st = fork(1)) return st;  // dGU exists
   // dhn = [dG | dU] [Wg; Wu]

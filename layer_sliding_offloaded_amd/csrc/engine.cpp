@@ -955,10 +955,10 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
       sv = e->sv[0];
       if ((rc = sf_layer_fwd(ctx, e->uparam[u], xi, e->ys, sv, e->s_comp))) return rc;
     }
-    hipEvent_t ffn = timing_event(e);
-    if (!ffn) return fail(SF_ERR_HIP, "event pool exhausted");
+    hipEvent_t ffn = timing_event(e), wd = timing_event(e);
+    if (!ffn || !wd) return fail(SF_ERR_HIP, "event pool exhausted");
     if ((rc = layer_bwd(ctx, e->uparam[u], xi, sv, dy, e->dbuf, reinterpret_cast<float*>(e->ugrad[u]), e->s_comp,
-                        ffn)))
+                        ffn, wd)))
       return rc;
     if (head_dev_adam && i == nl - 1 && (rc = head_update(ffn))) return rc;
     if (ck && i < nl - 1) SF_HIP(hipEventRecord(e->ev_cfree[i % 2], e->s_comp));
@@ -968,14 +968,16 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     int k = 0;
     if ((rc = wait_slot(e, &k))) return rc;
     // Gradients leave in ranges and Adam of a range starts as soon as it
-    // lands; the MLP weights' gradients (most of a layer) go first, right
+    // lands; the MLP weights' gradients (most of a layer) go first: Wd's
+    // right after the backward's first weight-gradient GEMM, Wg and Wu's
     // after the MLP half of the backward.
     const size_t gb = e->L.grad_bytes;
-    const size_t f0 = e->L.grad_off[SF_WG], f1 = e->L.grad_off[SF_WD] + e->L.grad_bytes_t[SF_WD];
+    const size_t f0 = e->L.grad_off[SF_WG], fd = e->L.grad_off[SF_WD];
+    const size_t f1 = fd + e->L.grad_bytes_t[SF_WD];
     const struct {
       size_t lo, hi;
       hipEvent_t after;
-    } parts[3] = {{f0, f1, ffn}, {0, f0, b}, {f1, gb, b}};
+    } parts[4] = {{fd, f1, wd}, {f0, fd, ffn}, {0, f0, b}, {f1, gb, b}};
     std::vector<Job> rj;
     for (const auto& pt : parts) {
       for (size_t lo = pt.lo; lo < pt.hi; lo += e->chunk_bytes) {
@@ -1216,7 +1218,7 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
       if (hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess)
         return cleanup(fail(SF_ERR_HIP, "event creation failed"));
   }
-  for (int i = 0; i < 24 * e->nl + 64; ++i) {
+  for (int i = 0; i < 32 * e->nl + 64; ++i) {
     hipEvent_t ev;
     if (hipEventCreate(&ev) != hipSuccess) return cleanup(fail(SF_ERR_HIP, "event creation failed"));
     e->tev.push_back(ev);

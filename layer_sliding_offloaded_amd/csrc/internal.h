@@ -50,10 +50,11 @@ WorkLayout work_layout(const Dims& d, int head_chunk_rows);
 
 struct sf_ctx;
 namespace sf {
-// sf_layer_bwd with an optional event recorded on the stream once the MLP
-// weight gradients (Wg, Wu, Wd) are complete, before the attention half.
+// sf_layer_bwd with optional events recorded once the MLP weight gradients
+// (Wg, Wu, Wd) are complete, before the attention half (ffn_done), and once
+// the Wd gradient alone is (wd_done: the first weight-gradient GEMM).
 sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_saved, const void* d_dy, void* d_dx,
-                    float* d_dw, sf_stream stream, hipEvent_t ffn_done);
+                    float* d_dw, sf_stream stream, hipEvent_t ffn_done, hipEvent_t wd_done);
 // sf_head_fwd_bwd; with defer_last_dw the LM-head weight gradient of the last
 // row chunk is left to head_last_dw, which reads the head workspace (dlogits,
 // hf) and must run before the context's next head pass.
