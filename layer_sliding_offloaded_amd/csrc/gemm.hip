@@ -222,13 +222,13 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int* tm, int* tn) 
 // (pair epilogues need 64-column wave tiles: 32 output columns per plane)
 template <Epi E, int WN>
 constexpr bool kRowsEpi = E == Epi::Store || E == Epi::StoreF32 || E == Epi::Resid || E == Epi::SwigluBwd ||
-                          (E == Epi::SwigluFwd && WN >= 64);
+                          ((E == Epi::SwigluFwd || E == Epi::Rope) && WN >= 64);
 
 // LDS bytes of one wave's staging patch in the row epilogue: 16 rows of the
 // wave's output columns in fp32 (pair epilogues: gate and up planes of WN/2
 // columns each), rows padded by 4 floats.
 template <int WN, Epi E>
-constexpr int kPatchBytes = (E == Epi::SwigluFwd ? 2 * 16 * (WN / 2 + 4) : 16 * (WN + 4)) * 4;
+constexpr int kPatchBytes = (E == Epi::SwigluFwd || E == Epi::Rope ? 2 * 16 * (WN / 2 + 4) : 16 * (WN + 4)) * 4;
 
 // Row-contiguous epilogue.  A wave's accumulators hold, per lane, 4 columns
 // of one row, so direct stores and operand loads touch 16 rows x 32 bytes
@@ -244,8 +244,8 @@ constexpr int kPatchBytes = (E == Epi::SwigluFwd ? 2 * 16 * (WN / 2 + 4) : 16 * 
 template <int WM, int WN, int FM, int FN, Epi E>
 __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&acc)[FM][FN], int m0, int n0,
                                               int wm, int wn, int lane, float* patch) {
-  constexpr bool PAIR = E == Epi::SwigluFwd;
-  constexpr int WR = PAIR ? WN / 2 : WN;  // output columns of the wave
+  constexpr bool PAIR = E == Epi::SwigluFwd || E == Epi::Rope;
+  constexpr int WR = PAIR ? WN / 2 : WN;  // output columns of the wave (pairs: first members)
   constexpr int LDW = WR + 4;
   constexpr int LPR = WR / 8;   // lanes per row
   constexpr int RPI = 64 / LPR;  // rows per pass
@@ -254,9 +254,17 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&a
   static_assert(WR % 8 == 0 && 16 % RPI == 0, "wave tile width");
   const int lr = lane % 16, lg = lane / 16;
   const int rr = lane / LPR, cc = (lane % LPR) * 8;
-  // output column of this lane's 8 (gate/up index f for SwiGLU)
-  const int n = PAIR ? n0 / 2 + wn * WR + cc : n0 + wn * WN + cc;
-  const bool n_ok = n < (PAIR ? g.ffn : g.N);
+  // output column of this lane's 8 (gate/up index f for SwiGLU; for RoPE the
+  // first column of the 8 pairs (c, c + head_dim/2), whose 8 first members
+  // share one head since head_dim/2 is a multiple of 8)
+  int n;
+  if constexpr (E == Epi::Rope) {
+    const int pp = wn * WR + cc, hd2 = g.head_dim / 2;
+    n = n0 + (pp / hd2) * g.head_dim + (pp % hd2);
+  } else {
+    n = PAIR ? n0 / 2 + wn * WR + cc : n0 + wn * WN + cc;
+  }
+  const bool n_ok = n < (E == Epi::SwigluFwd ? g.ffn : g.N);
   const int mb = m0 + wm * WM + rr;
   uint4 op[2][NIT][NOP > 0 ? NOP : 1];
   auto fetch = [&](int i, uint4 (&dst)[NIT][NOP > 0 ? NOP : 1]) {
@@ -320,6 +328,35 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&a
         }
         *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(dG);
         *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C2) + off) = Elem<bf16>::pack(dU);
+      } else if constexpr (E == Epi::Rope) {
+        // o: first members (columns n ..), u: partners (columns n + head_dim/2 ..)
+        float u[8];
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(patch + 16 * LDW + r * LDW + cc);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(patch + 16 * LDW + r * LDW + cc + 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) { u[v] = lo[v]; u[4 + v] = hi[v]; }
+        float o1[8], o2[8];
+        if (n < g.rope_cols) {
+          const int hd2 = g.head_dim / 2;
+          const int64_t t = static_cast<int64_t>(m % g.seq) * hd2 + n % g.head_dim;
+          const float4 c0 = *reinterpret_cast<const float4*>(g.rope_cos + t);
+          const float4 c1 = *reinterpret_cast<const float4*>(g.rope_cos + t + 4);
+          const float4 s0 = *reinterpret_cast<const float4*>(g.rope_sin + t);
+          const float4 s1 = *reinterpret_cast<const float4*>(g.rope_sin + t + 4);
+          const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            o1[v] = o[v] * cs[v] - u[v] * sn[v];
+            o2[v] = u[v] * cs[v] + o[v] * sn[v];
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 8; ++v) { o1[v] = o[v]; o2[v] = u[v]; }
+        }
+        bf16* c = static_cast<bf16*>(g.C) + off;
+        *reinterpret_cast<uint4*>(c) = Elem<bf16>::pack(o1);
+        *reinterpret_cast<uint4*>(c + g.head_dim / 2) = Elem<bf16>::pack(o2);
       } else {  // SwigluFwd: o = gate; up from the second plane
         float u[8], a[8];
         const f32x4 lo = *reinterpret_cast<const f32x4*>(patch + 16 * LDW + r * LDW + cc);
@@ -1149,6 +1186,9 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
     if constexpr (E == Epi::Resid || E == Epi::SwigluBwd) ok = ok && g.ldr % 8 == 0 && a16(g.R);
     if constexpr (E == Epi::SwigluBwd) ok = ok && a16(g.R2) && a16(g.C2);
     if constexpr (E == Epi::SwigluFwd) ok = ok && a16(g.C2) && a16(g.C3);
+    // RoPE: 8 pair members inside one head half, whole rotated heads, float4 table reads
+    if constexpr (E == Epi::Rope)
+      ok = ok && g.head_dim % 16 == 0 && g.rope_cols % g.head_dim == 0 && a16(g.rope_cos) && a16(g.rope_sin);
     g.rows_epi = ok ? 1 : 0;
   }
   if constexpr (KIND == 3) {
