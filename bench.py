@@ -168,7 +168,7 @@ def cpu_baseline(w, target_s=12.0):
         oracle.layer_bwd(p, cache, dy, sh)
         n += 1
         el = time.perf_counter() - t0
-        if el >= target_s or n >= 50:
+        if el >= target_s or n >= 1000:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(n * ws.tokens / el, 2), "unit": "tokens/s per layer (fwd+bwd)", "cores": threads,
