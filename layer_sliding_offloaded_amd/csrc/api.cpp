@@ -276,8 +276,13 @@ sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_
   const char* serial = std::getenv("SF_SERIAL_WGRAD");
   if (!(serial && serial[0] == '1')) {
     bool ok = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) == hipSuccess;
-    for (hipEvent_t* ev : {&c->ev_fork[0], &c->ev_fork[1], &c->ev_fork[2], &c->ev_fork[3], &c->ev_mlp_dw,
-                           &c->ev_join})
+    // The fork events hand data from the caller's stream to kernels on the
+    // side stream of the same device only: no system-scope fence (which
+    // writes caches back for the host) on the compute chain.  The join keeps
+    // it, since the caller may copy the results out by DMA after it.
+    for (hipEvent_t* ev : {&c->ev_fork[0], &c->ev_fork[1], &c->ev_fork[2], &c->ev_fork[3]})
+      ok = ok && hipEventCreateWithFlags(ev, hipEventDisableTiming | hipEventDisableSystemFence) == hipSuccess;
+    for (hipEvent_t* ev : {&c->ev_mlp_dw, &c->ev_join})
       ok = ok && hipEventCreateWithFlags(ev, hipEventDisableTiming) == hipSuccess;
     if (!ok) {
       delete c;
