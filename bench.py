@@ -363,10 +363,11 @@ def main():
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": stored_traffic(w.name, dom_name)},
     }
-    # host-link roofline: the step's bytes each way at the probe's
-    # bidirectional rates (both directions run at once in the step)
+    # host-link roofline: the step's bytes each way at the probe's rate for
+    # that direction alone (the link is full duplex; the probe's rates with
+    # both directions at once are reported too, but steps have exceeded them)
     link = link_probe(torch)
-    t_link = max(med["h2d_bytes"] / (link["bidir_h2d_gbps"] * 1e9), med["d2h_bytes"] / (link["bidir_d2h_gbps"] * 1e9))
+    t_link = max(med["h2d_bytes"] / (link["h2d_gbps"] * 1e9), med["d2h_bytes"] / (link["d2h_gbps"] * 1e9))
     link_tok = T * w.n_layers / t_link if t_link > 0 else None
     out["host_link"] = dict(link, step_h2d_gbps=round(med["h2d_gbps"], 2), step_d2h_gbps=round(med["d2h_gbps"], 2),
                             link_bound_tokens_per_s_per_layer=round(link_tok, 1) if link_tok else None,
