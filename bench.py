@@ -265,7 +265,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1000.0 * elapsed / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, loss {loss:.4f}", file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step"
+          + (f", loss {loss:.4f}" if head is not None else " (no head: no loss)"), file=sys.stderr, flush=True)
     if pipeline:
         # one measurement window over the timed steps: per-step means of times
         # and bytes; rates and the overlap share over the whole window
