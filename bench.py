@@ -204,7 +204,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the layer-sliding step is a "
-              "single-GPU method and this build has no multi-GPU path.", file=sys.stderr)
+              "single-GPU method and this library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
