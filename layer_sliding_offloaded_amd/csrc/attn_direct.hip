@@ -214,102 +214,119 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
 #pragma unroll
   for (int d = 0; d < FD; ++d) vo[d] = ofs_t<D>(d * 16, lr, lg);
 
-  lk.issue(rs, K0, w, S, 0);
-  lv.issue(rs, V0, w, S, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  auto tile = [&](int kt, const char* Kc, const char* Vc, char* Kn, char* Vn) {
-    const int kv0 = kt * BKV;
-    if (kt + 1 < nkv) {
-      const uint32_t adv = static_cast<uint32_t>((kv0 + BKV) * ld * 2);
-      lk.issue(rs, Kn, w, S - kv0 - BKV, adv);
-      lv.issue(rs, Vn, w, S - kv0 - BKV, adv);
-    }
-    if (kv0 <= qw + 31) {
-      // S^T: lane holds S[q = qw + 16 f + lr][kv = kv0 + 16 fk + 4 lg + v]
-      f32x4 s[2][4];
+  // Software pipeline over key tiles: iteration kt computes the scores of
+  // tile kt + 1 (MFMA) while the softmax of tile kt runs (VALU), then P.V of
+  // tile kt.  K(kt + 1) and V(kt) were loaded during iteration kt - 1; the
+  // loads of K(kt + 2) and V(kt + 1) go into the buffers that tiles kt and
+  // kt - 1 used, which every wave has finished reading at the barrier that
+  // opens the iteration.
+  auto scores = [&](const char* Kc, f32x4 (&sv)[2][4]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int fk = 0; fk < 4; ++fk) sv[f][fk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      uint4 kf[4];
+#pragma unroll
+      for (int fk = 0; fk < 4; ++fk) kf[fk] = lds16(Kc, ko[c] + fk * 16 * 128);
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int fk = 0; fk < 4; ++fk) s[f][fk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        uint4 kf[4];
-#pragma unroll
-        for (int fk = 0; fk < 4; ++fk) kf[fk] = lds16(Kc, ko[c] + fk * 16 * 128);
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int fk = 0; fk < 4; ++fk) Mfma<bf16>::run(s[f][fk], kf[fk], qf[f][c]);
-      }
-      // raw scores are scaled inside the exponent: p = 2^(s sc - m), with the
-      // running maximum m kept in scaled units (sc > 0)
-      if (kv0 + BKV - 1 > qw) {  // diagonal tile: mask keys after the row
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int fk = 0; fk < 4; ++fk)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (kv0 + fk * 16 + lg * 4 + v > qw + f * 16 + lr) s[f][fk][v] = -INFINITY;
-      }
-      // The shift m of a row moves only when the tile's maximum exceeds it
-      // by more than kLazy (log2 units): probabilities stay <= 2^kLazy, and
-      // the output and row sum, which carry the same shift, are rescaled
-      // only then (softmax is invariant to a common shift of the exponents).
-      float alpha[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int fk = 0; fk < 4; ++fk)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[f][fk][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float ms = mx * sc;
-        const float mnew = ms > mrow[f] + kLazy ? ms : mrow[f];
-        alpha[f] = __builtin_amdgcn_exp2f(mrow[f] - mnew);
-        mrow[f] = mnew;
-#pragma unroll
-        for (int fk = 0; fk < 4; ++fk)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) s[f][fk][v] = __builtin_amdgcn_exp2f(fmaf(s[f][fk][v], sc, -mnew));
-      }
-      if (!__all(alpha[0] == 1.0f && alpha[1] == 1.0f)) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-#pragma unroll
-          for (int d = 0; d < FD; ++d)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) oacc[f][d][v] *= alpha[f];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) lacc[f][v] *= alpha[f];
-        }
-      }
-      // O^T += V^T P^T: lane holds O[q = qw + 16 f + lr][d = 16 fd + 4 lg + v]
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint4 pf0 = pack8(s[0][2 * j], s[0][2 * j + 1]);
-        const uint4 pf1 = pack8(s[1][2 * j], s[1][2 * j + 1]);
-        Mfma<bf16>::run(lacc[0], ones, pf0);
-        Mfma<bf16>::run(lacc[1], ones, pf1);
-#pragma unroll
-        for (int d = 0; d < FD; ++d) {
-          const uint4 vf = frag_t<D>(Vc, vo[d], j);
-          Mfma<bf16>::run(oacc[0][d], vf, pf0);
-          Mfma<bf16>::run(oacc[1][d], vf, pf1);
-        }
-      }
+        for (int fk = 0; fk < 4; ++fk) Mfma<bf16>::run(sv[f][fk], kf[fk], qf[f][c]);
     }
+  };
+  auto active = [&](int kt) { return kt < nkv && kt * BKV <= qw + 31; };
+
+  lk.issue(rs, K0, w, S, 0);
+  lv.issue(rs, V0, w, S, 0);
+  if (nkv > 1) lk.issue(rs, K1, w, S - BKV, static_cast<uint32_t>(BKV * ld * 2));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x4 s[2][4];
+  if (active(0)) scores(K0, s);
+
+  auto tile = [&](int kt, const char* Vc, char* Vn, const char* Knext, char* Kfree) {
+    // this wave's loads of K(kt + 1) and V(kt) have landed; the barrier
+    // covers the other waves' loads and their reads of iteration kt - 1 (for
+    // kt = 0: of K0 by the scores computed before the loop)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    const int kv0 = kt * BKV;
+    if (kt + 2 < nkv) lk.issue(rs, Kfree, w, S - kv0 - 2 * BKV, static_cast<uint32_t>((kv0 + 2 * BKV) * ld * 2));
+    if (kt + 1 < nkv) lv.issue(rs, Vn, w, S - kv0 - BKV, static_cast<uint32_t>((kv0 + BKV) * ld * 2));
+    if (!active(kt)) return;
+    f32x4 sn[2][4];
+    if (active(kt + 1)) scores(Knext, sn);
+    // raw scores are scaled inside the exponent: p = 2^(s sc - m), with the
+    // running maximum m kept in scaled units (sc > 0)
+    if (kv0 + BKV - 1 > qw) {  // diagonal tile: mask keys after the row
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int fk = 0; fk < 4; ++fk)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (kv0 + fk * 16 + lg * 4 + v > qw + f * 16 + lr) s[f][fk][v] = -INFINITY;
+    }
+    // The shift m of a row moves only when the tile's maximum exceeds it
+    // by more than kLazy (log2 units): probabilities stay <= 2^kLazy, and
+    // the output and row sum, which carry the same shift, are rescaled
+    // only then (softmax is invariant to a common shift of the exponents).
+    float alpha[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int fk = 0; fk < 4; ++fk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[f][fk][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float ms = mx * sc;
+      const float mnew = ms > mrow[f] + kLazy ? ms : mrow[f];
+      alpha[f] = __builtin_amdgcn_exp2f(mrow[f] - mnew);
+      mrow[f] = mnew;
+#pragma unroll
+      for (int fk = 0; fk < 4; ++fk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[f][fk][v] = __builtin_amdgcn_exp2f(fmaf(s[f][fk][v], sc, -mnew));
+    }
+    if (!__all(alpha[0] == 1.0f && alpha[1] == 1.0f)) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+#pragma unroll
+        for (int d = 0; d < FD; ++d)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) oacc[f][d][v] *= alpha[f];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lacc[f][v] *= alpha[f];
+      }
+    }
+    // O^T += V^T P^T: lane holds O[q = qw + 16 f + lr][d = 16 fd + 4 lg + v]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4 pf0 = pack8(s[0][2 * j], s[0][2 * j + 1]);
+      const uint4 pf1 = pack8(s[1][2 * j], s[1][2 * j + 1]);
+      Mfma<bf16>::run(lacc[0], ones, pf0);
+      Mfma<bf16>::run(lacc[1], ones, pf1);
+#pragma unroll
+      for (int d = 0; d < FD; ++d) {
+        const uint4 vf = frag_t<D>(Vc, vo[d], j);
+        Mfma<bf16>::run(oacc[0][d], vf, pf0);
+        Mfma<bf16>::run(oacc[1][d], vf, pf1);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int fk = 0; fk < 4; ++fk) s[f][fk] = sn[f][fk];
   };
   for (int kt = 0; kt < nkv; kt += 2) {
-    tile(kt, K0, V0, K1, V1);
-    if (kt + 1 < nkv) tile(kt + 1, K1, V1, K0, V0);
+    tile(kt, V0, V1, K1, K0);
+    if (kt + 1 < nkv) tile(kt + 1, V1, V0, K0, K1);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS outlives the block
 
   bf16* obase = static_cast<bf16*>(a.out) + bs * a.ld_out + h * D;
 #pragma unroll
