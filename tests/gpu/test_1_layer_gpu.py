@@ -31,6 +31,10 @@ CASES = {
     "bf16-mqa-d64-s130": (BASE.with_(dtype="bf16", hidden=512, n_heads=8, n_kv_heads=1, head_dim=64, ffn=1024,
                                      batch=1, seq=130), 2e-2, 0.05),
     "bf16-seq1": (BASE.with_(dtype="bf16", batch=3, seq=1), 2e-2, 0.05),
+    # attention tile edges: one key tile exactly, a second tile of one row, tile-aligned rows
+    "bf16-s64": (BASE.with_(dtype="bf16", batch=2, seq=64), 2e-2, 0.05),
+    "bf16-gqa-d128-s65": (BASE.with_(dtype="bf16", batch=1, seq=65, **GQA128), 2e-2, 0.05),
+    "bf16-s128": (BASE.with_(dtype="bf16", batch=2, seq=128), 2e-2, 0.05),
     # one layer of the 4-layer h1024 stack at its full size (T = 2048), standard inputs
     "bf16-stack4-h1024-full": (W["stack4-h1024-bf16"], 2e-2, 1.0),
 }
