@@ -28,3 +28,34 @@ def test_stored_traffic_requires_matching_source(tmp_path, monkeypatch):
     path.write_text("gemm_source_sha256: 0000\ntraffic_bytes: " + json.dumps(table) + "\n")
     assert bench.stored_traffic("w", "gu_dw") is None
 
+
+
+def test_layer_gemms_cover_the_projection_flops():
+    """The 12 GEMMs timed one by one are exactly the dense part of a layer's
+    forward + backward: forward, dX and dW each multiply the T tokens by every
+    projection weight once (2 T P flops apiece), so their sum is 6 T P_lin --
+    the non-attention term of layer_flops.  Checked on shapes with GQA and
+    with n_heads * head_dim != hidden, where a transposed or dropped GEMM
+    changes the sum."""
+    import seeded_inputs as si
+    for name, w in si.WORKLOADS.items():
+        gemm = sum(2.0 * M * N * K for _, _, M, N, K in bench.layer_gemms(w))
+        attn = 6.0 * w.batch * w.n_heads * w.seq * w.seq * w.head_dim
+        assert gemm + attn == bench.layer_flops(w), name
+    w = si.WORKLOADS["stack4-h1024-bf16"].with_(n_heads=6, n_kv_heads=2, head_dim=96, hidden=512, ffn=768)
+    T, H = w.tokens, w.hidden
+    p_lin = H * 96 * (6 + 2 + 2) + 6 * 96 * H + 3 * 768 * H
+    gemm = sum(2.0 * M * N * K for _, _, M, N, K in bench.layer_gemms(w))
+    assert gemm == 6.0 * T * p_lin
+    # every GEMM's reduction length is one of the layer's own widths
+    for _, lay, M, N, K in bench.layer_gemms(w):
+        assert K in (H, 6 * 96, 2 * 768, 768, (6 + 4) * 96, T)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
