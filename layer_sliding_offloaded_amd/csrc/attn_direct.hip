@@ -47,15 +47,16 @@ __device__ __forceinline__ int rswz(int row) { return (row >> 1) & 7; }
 // [row][d] tiles with whole D*2-byte rows, read two ways: 16-byte chunks of
 // 16 consecutive rows (A operand along d), and transposed, where a 16-lane
 // group reads 32 bytes of each of 4 consecutive rows and two groups cover 8
-// consecutive rows.  The 16-byte slot XOR below keeps both patterns on
-// distinct banks: 256-byte rows (d = 128) all start at bank 0, so the 16 rows
-// need 16 distinct slots and any 8 aligned rows 8 distinct slot pairs;
-// 128-byte rows (d = 64) alternate bank halves, so the even and the odd rows
-// each need distinct slots (pairs).
+// consecutive rows.  The 16-byte slot XOR below is the one, among a dozen
+// row masks measured with the LDS bank-conflict counter, under which both
+// patterns run conflict-free on gfx950: XOR the slot with row mod 8 (d = 64)
+// or twice that (d = 128).  An earlier mask that also folded in row bit 3
+// gave every along-d read a two-way conflict (8 LDS cycles per 16-byte read
+// instead of 4), although 16 consecutive lanes then hit 16 distinct slots.
 template <int D>
 __device__ __forceinline__ int tswz(int r) {
-  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  if constexpr (D == 128) return (r & 7) << 1;
+  else return r & 7;
 }
 
 __device__ __forceinline__ uint4 pack8(const f32x4& a, const f32x4& b) {
