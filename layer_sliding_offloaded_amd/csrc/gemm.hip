@@ -595,15 +595,18 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // [k][row] slot swizzle: 16 lanes of one transpose read cover 4 consecutive k
-// (the same two slots each); lanes 16 apart cover k 8 apart.  This map sends
-// those 8 k-rows to 8 distinct slot pairs.
-// Tiles of ROWS < 128 have fewer 16-byte slots per k-row (ROWS / 8); the map
-// keeps its low bits there, so a swizzled slot never leaves its k-row.
+// (the same two slots each); lanes 16 apart cover k 8 apart, and the 32 lanes
+// of a pass must hit distinct banks.  256-byte k-rows (ROWS = 128) all start
+// at bank 0: the map sends those 8 k-rows to 8 distinct slot pairs.  128-byte
+// k-rows (ROWS = 64) alternate bank halves by k's parity: the 4 k-rows of
+// each parity need distinct pairs among the 4 of a half, from k bits 1 and 3
+// (the low bits of the 256-byte map, k & 3, repeat for k and k + 8: a two-way
+// conflict on every transpose read, measured at 0.5 per access).
 template <int ROWS>
 __device__ __forceinline__ int kswz(int k) {
-  static_assert(ROWS >= 64, "at least 8 slots per k-row");
-  const int s = 2 * ((k & 3) | (((k >> 3) & 1) << 2));
-  return ROWS >= 128 ? s : (s & (ROWS / 8 - 1));
+  static_assert(ROWS == 64 || ROWS >= 128, "8 or at least 16 slots per k-row");
+  if constexpr (ROWS >= 128) return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+  else return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1));
 }
 // [row][k] slot swizzle
 __device__ __forceinline__ int rswz(int row) { return (row >> 1) & 7; }
