@@ -408,6 +408,24 @@ sf_status sf_engine_dx0(sf_engine* eng, void** d_dx0);
  */
 sf_status sf_engine_trace(sf_engine* eng, double* out, int32_t capacity, int32_t* n_rows);
 
+/*
+ * Bookkeeping of the engine's timing, for tests and inspection.  Writes
+ * min(n, 5) values to out (host): [0] timing events the engine owns (all
+ * created by sf_engine_create; steps never create more), [1] of them free,
+ * [2] timed intervals still in flight, [3] completed intervals of the
+ * current measurement window held on the host (32 bytes each, until the
+ * window closes: every synchronous step, or sf_engine_sync when pipelined),
+ * [4] times the host waited for an interval to complete because every
+ * timing event was in use.
+ *
+ * Failure injection for tests of the error path: with the environment
+ * variable SF_FAULT_ADAM_JOB=k set at sf_engine_create, the engine's k-th
+ * host Adam job (counted from 0 over the engine's life) reports a failure
+ * instead of running; the step or sync that observes it returns SF_ERR_HIP
+ * and the engine is then in the sticky error state.
+ */
+sf_status sf_engine_counters(sf_engine* eng, int64_t* out, int32_t n);
+
 sf_status sf_engine_destroy(sf_engine* eng);
 
 const char* sf_last_error(void);

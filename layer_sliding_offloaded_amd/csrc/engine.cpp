@@ -59,6 +59,7 @@
 #include <chrono>
 #include <condition_variable>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <deque>
 #include <functional>
@@ -189,7 +190,13 @@ struct Interval {
   hipEvent_t a, b;
   int kind;  // 0 compute, 1 H2D, 2 D2H
   double bytes;
+  int64_t seq;  // issue order (the oldest live interval is waited for first)
 };
+
+// Streams whose timed intervals complete in issue order: the compute
+// stream, the H2D stream, the D2H stream and the context's side stream
+// (head update and the uploads Adam queues).
+enum { kStComp = 0, kStH2d = 1, kStD2h = 2, kStSide = 3, kNumStreams = 4 };
 
 // One row of the step trace: what, when (ms after the step's first device
 // event), and its bytes (copies) or layer (Adam jobs).
@@ -273,11 +280,23 @@ struct sf_engine {
   std::vector<hipEvent_t> ev_param_ready, ev_param_free, ev_grad_free;
   // the gradient region of a unit as a second parameter slot in the forward
   std::vector<hipEvent_t> ev_gslot_ready, ev_gslot_free;
-  // timing events and intervals (shared with the dispatcher thread)
+  // Timing events: a fixed pool created with the engine.  An interval's two
+  // events go back to the pool once its end event has completed and its
+  // times (ms after the window's origin) are in `rows`; when the pool is
+  // empty, the host waits for the oldest live interval.  Shared with the
+  // dispatcher thread (under tmu).
   std::mutex tmu;
-  std::vector<hipEvent_t> tev;
-  size_t tev_used = 0;
-  std::vector<Interval> iv;
+  std::vector<hipEvent_t> tev_all, tev_free;
+  std::deque<Interval> live[kNumStreams];
+  std::vector<TraceRow> rows;  // completed intervals of the measurement window
+  int64_t seq = 0;
+  int64_t blocked_waits = 0;
+  // markers inside a layer's backward (MLP weight gradients final, Wd's
+  // final), one pair per unit, re-recorded for every layer of the unit
+  std::vector<hipEvent_t> ev_ffn, ev_wd;
+  // test hook: the Adam job with this index (counted from engine creation)
+  // reports a failure instead of running (environment SF_FAULT_ADAM_JOB)
+  int64_t fault_adam_job = -1, adam_jobs_seen = 0;
   int64_t step = 0;
   bool failed = false;
   // embedding sparse gradients
@@ -308,7 +327,8 @@ struct sf_engine {
   // Measurement window: one step (synchronous) or every step since the last
   // sf_engine_sync (pipelined).
   bool window_open = false;
-  hipEvent_t ev_origin = nullptr;
+  hipEvent_t ev_origin = nullptr;  // recorded when a window opens (timing)
+  hipEvent_t ev_start = nullptr;   // each later step's start (side streams wait on it)
   sf_step_stats last_stats{};
   double host_t0 = 0;                 // host clock at the window's first device event
   std::vector<TraceRow> adam_rows;    // host Adam jobs of the current step (under mu)
@@ -318,31 +338,64 @@ struct sf_engine {
 namespace sf {
 namespace {
 
-hipEvent_t timing_event(sf_engine* e) {
-  std::lock_guard<std::mutex> lk(e->tmu);
-  if (e->tev_used >= e->tev.size()) {
-    hipEvent_t ev;
-    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
-    e->tev.push_back(ev);
+// Move every completed interval at the head of a stream's queue into
+// `rows` and its events back to the pool; returns how many.  Under tmu.
+size_t reclaim_locked(sf_engine* e) {
+  size_t n = 0;
+  for (auto& q : e->live) {
+    while (!q.empty() && hipEventQuery(q.front().b) == hipSuccess) {
+      const Interval& x = q.front();
+      float a = 0, b = 0;
+      (void)hipEventElapsedTime(&a, e->ev_origin, x.a);
+      (void)hipEventElapsedTime(&b, e->ev_origin, x.b);
+      e->rows.push_back({static_cast<double>(x.kind), a, b, x.bytes});
+      e->tev_free.push_back(x.a);
+      e->tev_free.push_back(x.b);
+      q.pop_front();
+      ++n;
+    }
   }
-  return e->tev[e->tev_used++];
+  return n;
 }
 
-sf_status record_interval(sf_engine* e, hipEvent_t a, hipEvent_t b, int kind, double bytes) {
+// A free timing event from the pool; waits for the oldest live interval
+// when none is free.  nullptr only if the pool is empty with nothing live.
+hipEvent_t timing_event(sf_engine* e) {
+  std::unique_lock<std::mutex> lk(e->tmu);
+  for (;;) {
+    if (!e->tev_free.empty()) {
+      hipEvent_t ev = e->tev_free.back();
+      e->tev_free.pop_back();
+      return ev;
+    }
+    if (reclaim_locked(e) > 0) continue;
+    const Interval* oldest = nullptr;
+    for (auto& q : e->live)
+      if (!q.empty() && (!oldest || q.front().seq < oldest->seq)) oldest = &q.front();
+    if (!oldest) return nullptr;
+    hipEvent_t wait = oldest->b;
+    ++e->blocked_waits;
+    lk.unlock();
+    (void)hipEventSynchronize(wait);
+    lk.lock();
+  }
+}
+
+sf_status record_interval(sf_engine* e, hipEvent_t a, hipEvent_t b, int kind, double bytes, int stream) {
   if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
   std::lock_guard<std::mutex> lk(e->tmu);
-  e->iv.push_back({a, b, kind, bytes});
+  e->live[stream].push_back({a, b, kind, bytes, e->seq++});
   return SF_OK;
 }
 
-// One H2D copy on stream s with a timed interval.
+// One H2D copy on stream s (the H2D stream or the side stream) with a timed interval.
 sf_status timed_h2d(sf_engine* e, void* dst, const void* src, size_t bytes, hipStream_t s) {
   hipEvent_t a = timing_event(e), b = timing_event(e);
   if (!a || !b) return fail(SF_ERR_HIP, "event pool exhausted");
   SF_HIP(hipEventRecord(a, s));
   SF_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s));
   SF_HIP(hipEventRecord(b, s));
-  return record_interval(e, a, b, 1, static_cast<double>(bytes));
+  return record_interval(e, a, b, 1, static_cast<double>(bytes), s == e->s_h2d ? kStH2d : kStSide);
 }
 
 // Adam over segments (fp32 offset in master/m/v/grad, count, element offset
@@ -515,8 +568,11 @@ void dispatcher_loop(sf_engine* e) {
     std::string err;
     const hipError_t he = hipEventSynchronize(j.ready);
     const double t0 = now_ms();
+    const bool fault = e->fault_adam_job >= 0 && e->adam_jobs_seen++ == e->fault_adam_job;
     if (he != hipSuccess) {
       err = std::string("gradient copy failed: ") + hipGetErrorString(he);
+    } else if (fault) {
+      err = "injected failure of Adam job " + std::to_string(e->fault_adam_job) + " (SF_FAULT_ADAM_JOB)";
     } else {
       const sf_status rc = run_job(e, j);
       if (rc != SF_OK) err = sf_last_error();
@@ -560,21 +616,27 @@ double union_ms(std::vector<std::pair<double, double>> v) {
   return tot;
 }
 
-sf_status fill_stats(sf_engine* e, hipEvent_t ev0, sf_step_stats* st) {
+sf_status fill_stats(sf_engine* e, sf_step_stats* st) {
   std::vector<std::pair<double, double>> comp, copy, h2d, d2h;
   double lo = 1e300, hi = -1e300, hb = 0, db = 0;
+  {
+    // every stream has been synchronised: all live intervals are complete
+    std::lock_guard<std::mutex> lk(e->tmu);
+    reclaim_locked(e);
+    for (auto& q : e->live)
+      if (!q.empty()) return fail(SF_ERR_HIP, "a timed interval did not complete");
+  }
   e->trace.clear();
-  for (const Interval& x : e->iv) {
-    float a = 0, b = 0;
-    SF_HIP(hipEventElapsedTime(&a, ev0, x.a));
-    SF_HIP(hipEventElapsedTime(&b, ev0, x.b));
-    e->trace.push_back({static_cast<double>(x.kind), a, b, x.bytes});
-    lo = std::min(lo, static_cast<double>(a));
-    hi = std::max(hi, static_cast<double>(b));
-    if (x.kind == 0) comp.push_back({a, b});
+  for (const TraceRow& x : e->rows) {
+    const double a = x.start, b = x.end;
+    const int kind = static_cast<int>(x.kind);
+    e->trace.push_back(x);
+    lo = std::min(lo, a);
+    hi = std::max(hi, b);
+    if (kind == 0) comp.push_back({a, b});
     else copy.push_back({a, b});
-    if (x.kind == 1) { h2d.push_back({a, b}); hb += x.bytes; }
-    if (x.kind == 2) { d2h.push_back({a, b}); db += x.bytes; }
+    if (kind == 1) { h2d.push_back({a, b}); hb += x.info; }
+    if (kind == 2) { d2h.push_back({a, b}); db += x.info; }
   }
   st->compute_ms = union_ms(comp);
   st->copy_ms = union_ms(copy);
@@ -629,7 +691,7 @@ sf_status timed_d2h(sf_engine* e, void* dst, const void* src, size_t bytes, hipE
   SF_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, e->s_d2h));
   SF_HIP(hipEventRecord(b1, e->s_d2h));
   *done = b1;
-  return record_interval(e, b0, b1, 2, static_cast<double>(bytes));
+  return record_interval(e, b0, b1, 2, static_cast<double>(bytes), kStD2h);
 }
 
 // Wait for every copy, kernel and Adam job, then measure the window (one
@@ -650,7 +712,7 @@ sf_status close_window(sf_engine* e, sf_step_stats* st) {
     if (st) *st = e->last_stats;
     return SF_OK;
   }
-  if (sf_status rc = fill_stats(e, e->ev_origin, &local)) return rc;
+  if (sf_status rc = fill_stats(e, &local)) return rc;
   std::lock_guard<std::mutex> lk(e->mu);
   local.adam_ms = e->adam_ms;
   e->trace.insert(e->trace.end(), e->adam_rows.begin(), e->adam_rows.end());
@@ -678,17 +740,14 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   const bool new_window = !e->window_open;
   if (new_window) {
     std::lock_guard<std::mutex> lk(e->tmu);
-    e->tev_used = 0;
-    e->iv.clear();
+    e->rows.clear();
   }
   e->step += 1;
   e->coef = adam_coef(e->step, c.lr, c.b1, c.b2, c.eps);
 
-  hipEvent_t ev0 = timing_event(e);
-  if (!ev0) return fail(SF_ERR_HIP, "event pool exhausted");
+  hipEvent_t ev0 = new_window ? e->ev_origin : e->ev_start;
   SF_HIP(hipEventRecord(ev0, e->s_comp));
   if (new_window) {
-    e->ev_origin = ev0;
     e->host_t0 = now_ms();
     e->window_open = true;
     std::lock_guard<std::mutex> lk(e->mu);
@@ -712,7 +771,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if (!b) return fail(SF_ERR_HIP, "event pool exhausted");
     SF_HIP(hipEventRecord(b, e->s_comp));
     if (b_out) *b_out = b;
-    return record_interval(e, a, b, 0, 0);
+    return record_interval(e, a, b, 0, 0, kStComp);
   };
   sf_status rc;
   hipEvent_t a, b;
@@ -908,7 +967,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if (sf_status r = dev_adam(VH + d.H, VH, c.d_wlm, e->s_head)) return r;
     SF_HIP(hipEventRecord(hb, e->s_head));
     SF_HIP(hipEventRecord(e->ev_head_done, e->s_head));
-    return record_interval(e, ha, hb, 0, 0);
+    return record_interval(e, ha, hb, 0, 0, kStSide);
   };
   if (head) {
     // the previous step's device Adam of the LM head (head stream) reads hg
@@ -955,8 +1014,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
       sv = e->sv[0];
       if ((rc = sf_layer_fwd(ctx, e->uparam[u], xi, e->ys, sv, e->s_comp))) return rc;
     }
-    hipEvent_t ffn = timing_event(e), wd = timing_event(e);
-    if (!ffn || !wd) return fail(SF_ERR_HIP, "event pool exhausted");
+    hipEvent_t ffn = e->ev_ffn[u], wd = e->ev_wd[u];
     if ((rc = layer_bwd(ctx, e->uparam[u], xi, sv, dy, e->dbuf, reinterpret_cast<float*>(e->ugrad[u]), e->s_comp,
                         ffn, wd)))
       return rc;
@@ -1208,8 +1266,10 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
     return true;
   };
   if (!mk(e->ev_param_ready) || !mk(e->ev_param_free) || !mk(e->ev_grad_free) || !mk(e->ev_gslot_ready) ||
-      !mk(e->ev_gslot_free) ||
-      hipEventCreateWithFlags(&e->ev_head_done, hipEventDisableTiming) != hipSuccess)
+      !mk(e->ev_gslot_free) || !mk(e->ev_ffn) || !mk(e->ev_wd) ||
+      hipEventCreateWithFlags(&e->ev_head_done, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&e->ev_start, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreate(&e->ev_origin) != hipSuccess)
     return cleanup(fail(SF_ERR_HIP, "event creation failed"));
   if (ckpt) {
     std::vector<hipEvent_t*> evs = {&e->ev_xfree[0], &e->ev_xfree[1], &e->ev_xfree[2], &e->ev_cready[0],
@@ -1218,11 +1278,16 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
       if (hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess)
         return cleanup(fail(SF_ERR_HIP, "event creation failed"));
   }
-  for (int i = 0; i < 32 * e->nl + 64; ++i) {
+  // about two steps' worth of timed intervals (a step records at most ~14
+  // per layer, two events each): pipelined steps then rarely wait for one
+  for (int i = 0; i < 64 * e->nl + 128; ++i) {
     hipEvent_t ev;
     if (hipEventCreate(&ev) != hipSuccess) return cleanup(fail(SF_ERR_HIP, "event creation failed"));
-    e->tev.push_back(ev);
+    e->tev_all.push_back(ev);
   }
+  e->tev_free = e->tev_all;
+  e->rows.reserve(e->tev_all.size());
+  if (const char* f = std::getenv("SF_FAULT_ADAM_JOB")) e->fault_adam_job = std::atoll(f);
   e->slot_free.assign(c.n_grad_slots, true);
   // default: every available core but two (the thread that queues device
   // work and the HIP runtime's own), so a preempted Adam worker does not
@@ -1311,6 +1376,23 @@ sf_status sf_engine_trace(sf_engine* e, double* out, int32_t capacity, int32_t* 
   return SF_OK;
 }
 
+sf_status sf_engine_counters(sf_engine* e, int64_t* out, int32_t n) {
+  if (!e || !out || n < 0) return fail(SF_ERR_ARG, "bad argument");
+  int64_t v[5];
+  {
+    std::lock_guard<std::mutex> lk(e->tmu);
+    size_t live = 0;
+    for (auto& q : e->live) live += q.size();
+    v[0] = static_cast<int64_t>(e->tev_all.size());
+    v[1] = static_cast<int64_t>(e->tev_free.size());
+    v[2] = static_cast<int64_t>(live);
+    v[3] = static_cast<int64_t>(e->rows.size());
+    v[4] = e->blocked_waits;
+  }
+  for (int32_t i = 0; i < n && i < 5; ++i) out[i] = v[i];
+  return SF_OK;
+}
+
 sf_status sf_engine_destroy(sf_engine* e) {
   if (!e) return SF_OK;
   if (e->dispatcher.joinable()) {
@@ -1325,10 +1407,10 @@ sf_status sf_engine_destroy(sf_engine* e) {
   for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
     if (s) (void)hipStreamSynchronize(s);
   for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_free, &e->ev_gslot_ready, &e->ev_gslot_free,
-                  &e->tev})
+                  &e->ev_ffn, &e->ev_wd, &e->tev_all})
     for (hipEvent_t ev : *v) (void)hipEventDestroy(ev);
   for (hipEvent_t ev : {e->ev_xfree[0], e->ev_xfree[1], e->ev_xfree[2], e->ev_cready[0], e->ev_cready[1],
-                        e->ev_cfree[0], e->ev_cfree[1], e->ev_ckpt_out, e->ev_head_done})
+                        e->ev_cfree[0], e->ev_cfree[1], e->ev_ckpt_out, e->ev_head_done, e->ev_start, e->ev_origin})
     if (ev) (void)hipEventDestroy(ev);
   for (hipStream_t s : {e->s_h2d, e->s_d2h, e->own_head ? e->s_head : nullptr})
     if (s) (void)hipStreamDestroy(s);

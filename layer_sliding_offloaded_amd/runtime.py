@@ -149,7 +149,8 @@ class Engine:
         self.x_bytes = (shape.batch * shape.seq * shape.hidden * ebytes + 255) // 256 * 256
         self.h_ckpt = pinned_bytes(max(self.nl - 1, 1) * self.x_bytes) if ckpt else None
         self.h_params = [pack_params(L, p, w, pinned_bytes(L.param_bytes)) for p in layers]
-        self.h_master = [master_from_params(L, p) for p in layers]
+        # fp32 master weights and Adam moments (host, pageable): only with Adam
+        self.h_master = [master_from_params(L, p) for p in layers] if adam else []
         self.h_m = [np.zeros_like(m) for m in self.h_master]
         self.h_v = [np.zeros_like(m) for m in self.h_master]
         self.h_slots = [pinned_bytes(L.grad_bytes) for _ in range(n_grad_slots)]
@@ -169,9 +170,10 @@ class Engine:
         cfg.d_pool, cfg.pool_bytes = self.pool.data_ptr(), self.pool.numel()
         cfg.d_act, cfg.act_bytes = self.act.data_ptr(), self.act.numel()
         cfg.h_params = parr([t.data_ptr() for t in self.h_params])
-        cfg.h_master = parr([m.ctypes.data for m in self.h_master])
-        cfg.h_m = parr([m.ctypes.data for m in self.h_m])
-        cfg.h_v = parr([m.ctypes.data for m in self.h_v])
+        if adam:
+            cfg.h_master = parr([m.ctypes.data for m in self.h_master])
+            cfg.h_m = parr([m.ctypes.data for m in self.h_m])
+            cfg.h_v = parr([m.ctypes.data for m in self.h_v])
         cfg.h_grad_slots = parr([t.data_ptr() for t in self.h_slots])
         cfg.compute_stream = self.stream.cuda_stream
         if ckpt:
@@ -215,6 +217,10 @@ class Engine:
         """Wait for every step's copies and Adam jobs; returns the stats dict of
         the steps since the previous sync (pipelined) or of the last step."""
         return sf.sf_engine_sync(self.eng).as_dict()
+
+    def counters(self):
+        """The engine's timing bookkeeping (sf_engine_counters)."""
+        return sf.sf_engine_counters(self.eng)
 
     def trace(self):
         """The last step's timeline: list of (kind name, start_ms, end_ms, info)."""

@@ -86,7 +86,8 @@ class SfError(RuntimeError):
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
     "sf_gemm", "sf_gemm_workspace_bytes", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_act_bytes_flags", "sf_engine_create", "sf_slide_step",
-    "sf_engine_sync", "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_destroy", "sf_last_error",
+    "sf_engine_sync", "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_counters",
+    "sf_engine_destroy", "sf_last_error",
 )
 
 _lib = None
@@ -124,6 +125,7 @@ def load():
         "sf_engine_layer_input": [P, i32, ctypes.POINTER(P)],
         "sf_engine_dx0": [P, ctypes.POINTER(P)],
         "sf_engine_trace": [P, ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(i32)],
+        "sf_engine_counters": [P, ctypes.POINTER(ctypes.c_int64), i32],
         "sf_engine_destroy": [P],
     }
     for name, args in sig.items():
@@ -264,6 +266,16 @@ def sf_engine_trace(eng):
     _check(load().sf_engine_trace(eng, buf, n.value, ctypes.byref(n)))
     rows = [tuple(buf[4 * i:4 * i + 4]) for i in range(n.value)]
     return sorted(rows, key=lambda r: (r[1], r[0]))
+
+
+COUNTER_NAMES = ("events", "events_free", "live_intervals", "window_rows", "blocked_waits")
+
+
+def sf_engine_counters(eng):
+    """The engine's timing bookkeeping as a dict (see COUNTER_NAMES)."""
+    buf = (ctypes.c_int64 * len(COUNTER_NAMES))()
+    _check(load().sf_engine_counters(eng, buf, len(COUNTER_NAMES)))
+    return dict(zip(COUNTER_NAMES, list(buf)))
 
 
 def sf_engine_destroy(eng):

@@ -132,3 +132,31 @@ def test_stack_step_matches_finite_differences():
     assert rel_l2(dgf, fd_grad(f, gf)) <= 1e-6
     for name in ("Wq", "Wd", "g1"):
         assert rel_l2(lg[0][name], fd_grad(f, layers[0][name])) <= 1e-6, name
+
+
+def test_adam_all_matches_torch_over_a_dict():
+    """The per-tensor Adam of a whole layer dict against torch.optim.Adam
+    (float64) over three steps: updated weights and both moments of every
+    tensor, so swapped moments, a wrong step index or a dropped state write
+    show up."""
+    from oracle.model import adam_all
+    rng = np.random.default_rng(8)
+    shapes = dict(Wq=(6, 4), Wd=(4, 5), g1=(4,))
+    w0 = {k: rng.normal(size=s) for k, s in shapes.items()}
+    hp = dict(lr=1e-3, b1=0.9, b2=0.999, eps=1e-8)
+    tp = {k: torch.nn.Parameter(torch.tensor(v)) for k, v in w0.items()}
+    opt = torch.optim.Adam(list(tp.values()), lr=hp["lr"], betas=(hp["b1"], hp["b2"]), eps=hp["eps"])
+    params = {k: v.copy() for k, v in w0.items()}
+    states = {k: (np.zeros(s), np.zeros(s)) for k, s in shapes.items()}
+    for t in (1, 2, 3):
+        grads = {k: rng.normal(size=s) * 10 ** rng.uniform(-4, 0, s) for k, s in shapes.items()}
+        params = adam_all(params, grads, states, t, hp["lr"], hp["b1"], hp["b2"], hp["eps"])
+        for k in shapes:
+            tp[k].grad = torch.tensor(grads[k])
+        opt.step()
+        for k in shapes:
+            ref = tp[k].detach().numpy()
+            assert rel_l2(params[k] - w0[k], ref - w0[k]) <= 1e-12, (t, k)
+            st = opt.state[tp[k]]
+            assert rel_l2(states[k][0], st["exp_avg"].numpy()) <= 1e-13, (t, k)
+            assert rel_l2(states[k][1], st["exp_avg_sq"].numpy()) <= 1e-13, (t, k)
