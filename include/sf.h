@@ -191,6 +191,26 @@ sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int
 /* Workspace bytes sf_gemm can use for split-K at these sizes (0 = none). */
 size_t sf_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
+/*
+ * sf_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same product, kernels and bits as sf_gemm given a workspace of at least
+ * sf_gemm_workspace_bytes(M, N, K), but with no workspace argument.  The
+ * split-K partial sums go to a static device buffer of
+ * SF_GEMM_STATIC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends; no call allocates or frees anything.
+ * Every partial sum is written before it is read, so the buffer needs no
+ * clearing and keeps the last call's contents.  All calls on one device
+ * share the buffer: calls that overlap in time (other streams, other host
+ * threads) race and must be serialised by the caller.
+ * Errors: those of sf_gemm, and SF_ERR_POOL (before any device work) when
+ * sf_gemm_workspace_bytes(M, N, K) > SF_GEMM_STATIC_SCRATCH_BYTES.
+ */
+#define SF_GEMM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+sf_status sf_gemm_noalloc(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K,
+                          const void* d_A, int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc,
+                          sf_stream stream);
+
 /* x0[t] = E[ids[t]] for t < T.  E [V, H] storage dtype, x0 [T, H]. */
 sf_status sf_embed_fwd(sf_ctx* ctx, const void* d_E, const int32_t* d_ids, void* d_x0, sf_stream stream);
 

@@ -615,13 +615,22 @@ size_t sf_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   return gemm_splitk_bytes(M, N, K);
 }
 
-sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* d_A,
-                  int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc, void* d_workspace,
-                  size_t workspace_bytes, sf_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by sf_gemm and sf_gemm_noalloc; fills *g.  *empty: nothing
+// to compute (M or N is 0).
+sf_status gemm_args(int32_t dtype, int32_t layout, int32_t M, int32_t N, int32_t K, const void* d_A, int64_t lda,
+                    const void* d_B, int64_t ldb, void* d_C, int64_t ldc, GemmArgs* g, bool* empty) {
+  *empty = false;
   if (dtype != SF_F32 && dtype != SF_BF16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
   if (layout < 0 || layout > 2) return fail(SF_ERR_ARG, "bad layout %d", layout);
   if (M < 0 || N < 0 || K < 0) return fail(SF_ERR_ARG, "negative size");
-  if (M == 0 || N == 0) return SF_OK;
+  if (M == 0 || N == 0) {
+    *empty = true;
+    return SF_OK;
+  }
   if (sf_status st = check_ptrs({d_A, d_B, d_C})) return st;
   // contiguous dimensions of A, B, C and N itself in multiples of 8 elements
   const int64_t a_contig = layout == 2 ? M : K;
@@ -629,15 +638,46 @@ sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int
   if (a_contig % 8 || b_contig % 8 || N % 8 || lda % 8 || ldb % 8 || ldc % 8)
     return fail(SF_ERR_UNSUPPORTED, "contiguous dimensions and leading dimensions must be multiples of 8");
   if (lda < a_contig || ldb < b_contig || ldc < N) return fail(SF_ERR_ARG, "leading dimension too small");
+  g->A = d_A; g->lda = lda;
+  g->B = d_B; g->ldb = ldb;
+  g->C = d_C; g->ldc = ldc;
+  g->M = M; g->N = N; g->K = K;
+  return SF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sf_status sf_gemm(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* d_A,
+                  int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc, void* d_workspace,
+                  size_t workspace_bytes, sf_stream stream) {
   GemmArgs g;
-  g.A = d_A; g.lda = lda;
-  g.B = d_B; g.ldb = ldb;
-  g.C = d_C; g.ldc = ldc;
-  g.M = M; g.N = N; g.K = K;
+  bool empty = false;
+  if (sf_status st = gemm_args(dtype, layout, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, &g, &empty)) return st;
+  if (empty) return SF_OK;
   if (d_workspace && !aligned16(d_workspace)) return fail(SF_ERR_ALIGN, "workspace is not 16-byte aligned");
   SF_HIP(gemm(dtype, static_cast<GemmLayout>(layout), out_f32 ? Epi::StoreF32 : Epi::Store, g,
               static_cast<hipStream_t>(stream), static_cast<float*>(d_workspace),
               d_workspace ? workspace_bytes : 0));
+  return SF_OK;
+}
+
+sf_status sf_gemm_noalloc(int32_t dtype, int32_t layout, int32_t out_f32, int32_t M, int32_t N, int32_t K,
+                          const void* d_A, int64_t lda, const void* d_B, int64_t ldb, void* d_C, int64_t ldc,
+                          sf_stream stream) {
+  GemmArgs g;
+  bool empty = false;
+  if (sf_status st = gemm_args(dtype, layout, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, &g, &empty)) return st;
+  if (empty) return SF_OK;
+  const size_t need = K > 0 ? gemm_splitk_bytes(M, N, K) : 0;
+  if (need > kGemmStaticScratchBytes)
+    return fail(SF_ERR_POOL, "this product splits K into partial sums of %zu bytes; the static scratch holds %zu",
+                need, kGemmStaticScratchBytes);
+  float* ws = nullptr;
+  SF_HIP(gemm_static_scratch(&ws));
+  SF_HIP(gemm(dtype, static_cast<GemmLayout>(layout), out_f32 ? Epi::StoreF32 : Epi::Store, g,
+              static_cast<hipStream_t>(stream), ws, kGemmStaticScratchBytes));
   return SF_OK;
 }
 

@@ -58,4 +58,10 @@ size_t gemm_splitk_bytes(int M, int N, int K);
 // Which tile configuration gemm() picks for (M, N); for measurement.
 int gemm_tile_config(int M, int N);
 
+// Bytes of the static split-K scratch (64 MiB) and its device address on the
+// current device (looked up once per device).  Shared by every call on that
+// device: calls that overlap in time race on it.
+constexpr size_t kGemmStaticScratchBytes = size_t{64} << 20;
+hipError_t gemm_static_scratch(float** ptr);
+
 }  // namespace sf

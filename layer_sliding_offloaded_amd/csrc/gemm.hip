@@ -29,6 +29,7 @@
 // 16-byte (fp32) stores, and the partner columns that RoPE (i, i + d/2) and
 // SwiGLU (gate j, up j) need sit in the same lane.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "gemm.h"
@@ -1291,6 +1292,33 @@ hipError_t dispatch(GemmLayout lay, Epi epi, const GemmArgs& g, hipStream_t s, f
 }
 
 }  // namespace
+
+// Split-K scratch of sf_gemm_noalloc: a file-scope device array, so callers
+// that cannot allocate (graph capture, serving loops) need no workspace.
+// Each device holds its own copy from the library's load until the process
+// ends.  Host code never uses the name itself (on the host it is only a
+// stand-in): the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kGemmStaticScratchBytes];
+
+hipError_t gemm_static_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<float*>(addr[dev]);
+  return hipSuccess;
+}
 
 int gemm_tile_config(int M, int N) {
   const long big = static_cast<long>((M + 255) / 256) * ((N + 255) / 256);

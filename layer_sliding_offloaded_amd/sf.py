@@ -85,7 +85,7 @@ class SfError(RuntimeError):
 
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
-    "sf_gemm", "sf_gemm_workspace_bytes", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_act_bytes_flags", "sf_engine_create", "sf_slide_step",
+    "sf_gemm", "sf_gemm_workspace_bytes", "sf_gemm_noalloc", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_act_bytes_flags", "sf_engine_create", "sf_slide_step",
     "sf_engine_sync", "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_counters",
     "sf_engine_destroy", "sf_last_error",
 )
@@ -111,6 +111,8 @@ def load():
         "sf_head_fwd_bwd": [P, P, P, P, P, P, P, P, P, P],
         "sf_gemm": [i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int64,
                     P, _size_t, P],
+        "sf_gemm_noalloc": [i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, ctypes.c_int64, P,
+                            ctypes.c_int64, P],
         "sf_embed_fwd": [P, P, P, P, P],
         "sf_embed_bwd": [P, P, P, P, P],
         "sf_adam_host": [P, P, P, P, P, _size_t, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
@@ -185,6 +187,13 @@ def sf_head_fwd_bwd(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, s
 
 def sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream, d_ws=None, ws_bytes=0):
     _check(load().sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, d_ws, ws_bytes, stream))
+
+
+GEMM_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def sf_gemm_noalloc(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream):
+    _check(load().sf_gemm_noalloc(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream))
 
 
 def sf_gemm_workspace_bytes(M, N, K):
