@@ -1,12 +1,16 @@
 """Benchmark of the layer-sliding training step on one MI355X.
 
-One "step" is one sf_slide_step over a batch of synthetic tokens: forward
+One "step" is one sf_slide_step over a batch of synthetic inputs: forward
 through every layer with the next layer's bf16 weights streamed in from
-pinned host memory, the fused LinearCrossEntropy head, the backward in
-reverse order with each layer's fp32 gradients streamed out, and host Adam
-on every layer (window of 2 layers resident).  The default workload is the
-4-layer stack with hidden 1024, 16 heads x 64, ffn 2816, vocab 32000,
-batch 4 x seq 512.
+pinned host memory, the backward in reverse order with each layer's fp32
+gradients streamed out to pinned host slots (window of 2 layers resident).
+The default workload is the largest one a single GPU runs: a slice of eight
+~123B-shaped layers (hidden 12288, 96 query heads x 128 with 8 KV heads,
+ffn 28672, batch 1 x seq 4096) cycled through the window, x and dy ~ N(0, 1)
+in, no head; its host optimizer is off (fp32 master weights and moments of
+the eight layers would take 133 GB of host memory), gradients still leave
+every layer.  Smaller workloads (``--workload``) add the embedding, the fused
+LinearCrossEntropy head and host Adam on every layer.
 
 Printed (one JSON line): tokens/s per layer fwd+bwd of the sliding step
 (value), MFMA utilisation of the resident layer kernels, copy/compute
@@ -29,33 +33,13 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBPS = 8000.0
 
 
-def layer_flops(w):
-    """Algorithmic FLOPs of one layer forward + backward: 6 T P_lin + 6 B n_h S^2 d (causal half)."""
-    T = w.tokens
-    p_lin = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim * w.hidden + w.hidden * w.n_heads * w.head_dim \
-        + 3 * w.ffn * w.hidden
-    attn = 6.0 * w.batch * w.n_heads * w.seq * w.seq * w.head_dim  # (2 fwd + 4 bwd) x 2 x S^2 d / 2
-    return 6.0 * T * p_lin + attn
-
-
-def layer_gemms(w):
-    """The 12 GEMMs of one layer's forward + backward: (name, layout, M, N, K)."""
-    T, H, F = w.tokens, w.hidden, w.ffn
-    Nq = w.n_heads * w.head_dim
-    Nqkv = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim
-    return [
-        ("qkv_fwd", 0, T, Nqkv, H), ("o_fwd", 0, T, H, Nq), ("gu_fwd", 0, T, 2 * F, H), ("down_fwd", 0, T, H, F),
-        ("down_dx", 1, T, F, H), ("down_dw", 2, H, F, T), ("gu_dx", 1, T, H, 2 * F), ("gu_dw", 2, 2 * F, H, T),
-        ("o_dx", 1, T, Nq, H), ("o_dw", 2, H, Nq, T), ("qkv_dx", 1, T, H, Nqkv), ("qkv_dw", 2, Nqkv, H, T),
-    ]
-
-
 def time_gemms(w, sf, torch, reps=20):
     """Average duration (ms) of each layer GEMM, launched alone on the current stream."""
     dt = sf.SF_BF16 if w.dtype == "bf16" else sf.SF_F32
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     s = torch.cuda.current_stream()
     out = {}
+    from layer_sliding_offloaded_amd.prof import layer_gemms
     for name, lay, M, N, K in layer_gemms(w):
         a_shape = (K, M) if lay == 2 else (M, K)
         b_shape = (N, K) if lay == 0 else (K, N)
@@ -180,11 +164,10 @@ def cpu_baseline(w, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # 50 steps: the pipelined schedule's last Adam tail (drained inside the
-    # timed region) is then a small part of the measurement
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="stack4-h1024-bf16")
+    # default 20 steps at the 123B-shaped slice (~25 s timed), 50 elsewhere
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="slice123b-gqa-bf16")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adam-threads", type=int, default=0)
@@ -214,26 +197,41 @@ def main():
     from layer_sliding_offloaded_amd import runtime as rt
     from layer_sliding_offloaded_amd import sf
 
+    from layer_sliding_offloaded_amd.prof import layer_flops
+
     sf.load()
     torch.cuda.set_device(0)
     w = si.WORKLOADS[args.workload]
     if args.layers:
         w = w.with_(n_layers=args.layers)
+    big = w.name == "slice123b-gqa-bf16"
+    if args.steps is None:
+        args.steps = 20 if big else 50
+    if args.warmup is None:
+        args.warmup = 2 if big else 5
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
 
-    adam = not args.no_adam and w.name != "slice123b-gqa-bf16"
+    adam = not args.no_adam and not big
     t_setup = time.perf_counter()
-    layers = []
-    for l in range(w.n_layers):
-        layers.append(si.layer_params(w, l))
+    kept = {}
+
+    def draw(l):
+        p = si.layer_params(w, l)
+        if l == 0:
+            kept[0] = p  # for the resident-layer measurement
         print(f"[bench] layer {l} parameters drawn ({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr,
               flush=True)
+        return p
+
     head = None
     if w.vocab:
         head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
     pipeline = adam and not args.sync_adam
-    eng = rt.Engine(w, layers, head, window=w.window, n_grad_slots=args.grad_slots, adam=adam, chunk=2048,
-                    adam_threads=args.adam_threads, ckpt=args.ckpt, pipeline=pipeline)
+    # draws run on a few host threads (each layer has its own seed)
+    ncpu = len(os.sched_getaffinity(0))
+    eng = rt.Engine(w, draw, head, window=w.window, n_grad_slots=args.grad_slots, adam=adam, chunk=2048,
+                    adam_threads=args.adam_threads, ckpt=args.ckpt, pipeline=pipeline,
+                    draw_threads=max(1, min(8, ncpu // 2)))
     hbm = {"unit_pool_bytes": eng.pool.numel(), "activation_bytes": eng.act_bytes}
     # host memory the engine holds for the layers (pinned: bf16 params, fp32
     # gradient slots, checkpoints; pageable: fp32 master weights and moments)
@@ -286,7 +284,7 @@ def main():
     del eng
 
     # resident layer kernels: one layer fwd + bwd with weights in HBM
-    p = layers[0]
+    p = kept.pop(0)
     c = rt.Context(w, 2048)
     L = c.layout
     dw = rt.pack_params(L, p, w).cuda()

@@ -24,6 +24,15 @@ Modes:
   bytes per launch for the workload, achieved GB/s and the fraction of the
   8 TB/s HBM peak.  The median is taken over all launches; most of them are
   bench.py's resident-layer loop, where nothing else runs.
+* ``layer-probe``: the ``probe`` sequence (calibration copy, then the 12
+  layer GEMMs through ``sf_gemm``) followed by one resident decoder layer
+  forward + backward (``sf_layer_fwd`` / ``sf_layer_bwd``) at the workload's
+  shape, each after a warm-up run.  Meant to run under ``rocprofv3 --pmc
+  MfmaUtil MfmaFlopsBF16``.
+* ``mfma``: from that counter CSV, per GEMM role and per kernel of the layer:
+  MFMA busy share (``MfmaUtil``: SQ_VALU_MFMA_BUSY_CYCLES over active cycles
+  of all SIMDs) and the bf16 MFMA FLOPs the hardware executed
+  (``MfmaFlopsBF16``) against the algorithmic FLOPs.
 * ``head-study``: the chunked LM head + cross-entropy (``sf_head_fwd_bwd``)
   at one shape for several chunk sizes, the largest being the whole token
   count (every logit materialised at once): device bytes of the head's
@@ -62,11 +71,31 @@ def gemm_source_hash():
     return h.hexdigest()
 
 
+def layer_flops(w):
+    """Algorithmic FLOPs of one layer forward + backward: 6 T P_lin + 6 B n_h S^2 d (causal half)."""
+    T = w.tokens
+    p_lin = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim * w.hidden + w.hidden * w.n_heads * w.head_dim \
+        + 3 * w.ffn * w.hidden
+    attn = 6.0 * w.batch * w.n_heads * w.seq * w.seq * w.head_dim  # (2 fwd + 4 bwd) x 2 x S^2 d / 2
+    return 6.0 * T * p_lin + attn
+
+
+def layer_gemms(w):
+    """The 12 GEMMs of one layer's forward + backward: (name, layout, M, N, K)."""
+    T, H, F = w.tokens, w.hidden, w.ffn
+    Nq = w.n_heads * w.head_dim
+    Nqkv = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim
+    return [
+        ("qkv_fwd", 0, T, Nqkv, H), ("o_fwd", 0, T, H, Nq), ("gu_fwd", 0, T, 2 * F, H), ("down_fwd", 0, T, H, F),
+        ("down_dx", 1, T, F, H), ("down_dw", 2, H, F, T), ("gu_dx", 1, T, H, 2 * F), ("gu_dw", 2, 2 * F, H, T),
+        ("o_dx", 1, T, Nq, H), ("o_dw", 2, H, Nq, T), ("qkv_dx", 1, T, H, Nqkv), ("qkv_dw", 2, Nqkv, H, T),
+    ]
+
+
 def _gemms(workload):
     sys.path.insert(0, os.path.dirname(HERE))
-    import bench
     import seeded_inputs as si
-    return bench.layer_gemms(si.WORKLOADS[workload])
+    return layer_gemms(si.WORKLOADS[workload])
 
 
 def probe(workload):
@@ -102,6 +131,97 @@ def probe(workload):
         print("probe:", name, flush=True)
         f()
         torch.cuda.synchronize()
+
+
+def layer_probe(workload):
+    """Calibration copy + the 12 layer GEMMs, then one resident layer
+    forward + backward (each sequence after a warm-up run)."""
+    import torch
+
+    sys.path.insert(0, os.path.dirname(HERE))
+    import seeded_inputs as si
+    from layer_sliding_offloaded_amd import runtime as rt
+    from layer_sliding_offloaded_amd import sf
+    sf.load()
+    w = si.WORKLOADS[workload]
+    c = rt.Context(w, 2048)
+    L = c.layout
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dw = torch.empty(L.param_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    dw.normal_(0.0, 0.02, generator=gen)
+    for k in (7, 8):  # gains 1
+        dw[L.off[k] // 2:(L.off[k] + L.bytes[k]) // 2] = 1.0
+    x = torch.randn(w.tokens, w.hidden, generator=gen, device="cuda").to(torch.bfloat16)
+    dy = torch.randn(w.tokens, w.hidden, generator=gen, device="cuda").to(torch.bfloat16)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    saved = rt.device_bytes(L.saved_bytes)
+    g = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+
+    def layer():
+        sf.sf_layer_fwd(c.ctx, dw.data_ptr(), x.data_ptr(), y.data_ptr(), saved.data_ptr(), s)
+        sf.sf_layer_bwd(c.ctx, dw.data_ptr(), x.data_ptr(), saved.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                        g.data_ptr(), s)
+
+    layer()
+    torch.cuda.synchronize()
+    probe(workload)
+    print("probe: layer", flush=True)
+    layer()
+    torch.cuda.synchronize()
+    c.close()
+
+
+def _counter_rows(path):
+    """{dispatch id: (kernel name, {counter: value})} in dispatch order."""
+    acc = {}
+    for r in _rows(path):
+        k = int(r["Dispatch_Id"])
+        name, cs = acc.setdefault(k, (r["Kernel_Name"], {}))
+        cs[r["Counter_Name"]] = cs.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [acc[k] for k in sorted(acc)]
+
+
+def mfma(csv_path, workload):
+    """MFMA busy share and hardware vs algorithmic FLOPs (see the module docstring)."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    import seeded_inputs as si
+    w = si.WORKLOADS[workload]
+    d = _counter_rows(csv_path)
+    # the last calibration copy splits the warm-up from the measured sequence
+    idx = max(i for i, (n, _) in enumerate(d) if "copyBuffer" in n)
+    rest = d[idx + 1:]
+    gemms = layer_gemms(w)
+    print("| GEMM | M x N x K | MfmaUtil % | MFMA FLOPs (bf16, hardware) | algorithmic 2MNK | ratio |")
+    print("|---|---|---:|---:|---:|---:|")
+    i = 0
+    for name, lay, M, N, K in gemms:
+        util, fl = 0.0, 0.0
+        kname, cs = rest[i]
+        i += 1
+        util = cs.get("MfmaUtil", 0.0)
+        fl = cs.get("MfmaFlopsBF16", 0.0)
+        while i < len(rest) and "splitk_reduce" in rest[i][0]:
+            i += 1
+        alg = 2.0 * M * N * K
+        print(f"| {name} | {M} x {N} x {K} | {util:.1f} | {fl / 1e9:.2f} G | {alg / 1e9:.2f} G | {fl / alg:.3f} |")
+    layer = rest[i:]
+    T, S, B = w.tokens, w.seq, w.batch
+    attn_fwd = 4.0 * B * w.n_heads * S * S * w.head_dim / 2
+    print()
+    print("Kernels of one resident layer forward + backward, in launch order:")
+    print()
+    print("| # | kernel | MfmaUtil % | MFMA FLOPs (bf16, hardware) |")
+    print("|---:|---|---:|---:|")
+    tot = 0.0
+    for j, (kname, cs) in enumerate(layer):
+        fl = cs.get("MfmaFlopsBF16", 0.0)
+        tot += fl
+        print(f"| {j} | `{short_name(kname)[:90]}` | {cs.get('MfmaUtil', 0.0):.1f} | {fl / 1e9:.2f} G |")
+    print()
+    print(f"Layer total: {tot / 1e12:.3f} TFLOP of bf16 MFMA work executed; algorithmic "
+          f"{layer_flops(w) / 1e12:.3f} TFLOP (6 T P_lin + 6 B n_h S^2 d); attention forward alone is "
+          f"{attn_fwd / 1e9:.1f} GFLOP algorithmic (causal half).")
 
 
 def _rows(path):
@@ -360,7 +480,8 @@ def head_study(hidden, vocab, batch, seq, chunks, reps=5):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs", "rowops", "head-study"])
+    ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs", "rowops", "head-study",
+                                     "layer-probe", "mfma"])
     ap.add_argument("files", nargs="*")
     ap.add_argument("--workload", default="stack4-h1024-bf16")
     ap.add_argument("--top", type=int, default=30)
@@ -372,6 +493,10 @@ def main():
     a = ap.parse_args()
     if a.mode == "probe":
         probe(a.workload)
+    elif a.mode == "layer-probe":
+        layer_probe(a.workload)
+    elif a.mode == "mfma":
+        mfma(a.files[0], a.workload)
     elif a.mode == "summarize":
         summarize(a.files[0], a.files[1], a.workload)
     elif a.mode == "gemm-runs":

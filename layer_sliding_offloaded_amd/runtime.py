@@ -114,7 +114,10 @@ class Engine:
     master weights and Adam moments, and (with a head) the resident
     embedding / LM-head tensors.
 
-    layers: list of per-layer parameter dicts (float32 storage values).
+    layers: list of per-layer parameter dicts (float32 storage values), or a
+    callable l -> such a dict for l in range(w.n_layers); a callable's layers
+    are drawn on `draw_threads` threads and packed into pinned memory one by
+    one, so only a few of them exist unpacked at once.
     head: None or dict with E [V, H], gf [H], Wlm [V, H] (float32 storage values).
     ckpt: sliding activation checkpointing (layer inputs kept in pinned host
     memory, each layer's forward recomputed before its backward).
@@ -123,11 +126,16 @@ class Engine:
     """
 
     def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
-                 adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False, pipeline=False):
+                 adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False, pipeline=False,
+                 draw_threads=1):
         import ctypes
+        from concurrent.futures import ThreadPoolExecutor
         hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
         self.w = w
-        self.nl = len(layers)
+        if callable(layers):
+            layer_fn, self.nl = layers, w.n_layers
+        else:
+            layer_fn, self.nl = (lambda l: layers[l]), len(layers)
         self.ctx = Context(w, chunk)
         L = self.ctx.layout
         self.layout = L
@@ -148,9 +156,16 @@ class Engine:
         ebytes = 2 if w.dtype == "bf16" else 4
         self.x_bytes = (shape.batch * shape.seq * shape.hidden * ebytes + 255) // 256 * 256
         self.h_ckpt = pinned_bytes(max(self.nl - 1, 1) * self.x_bytes) if ckpt else None
-        self.h_params = [pack_params(L, p, w, pinned_bytes(L.param_bytes)) for p in layers]
-        # fp32 master weights and Adam moments (host, pageable): only with Adam
-        self.h_master = [master_from_params(L, p) for p in layers] if adam else []
+        def stage(l):
+            p = layer_fn(l)
+            # fp32 master weights (host, pageable): only with Adam
+            return pack_params(L, p, w, pinned_bytes(L.param_bytes)), (master_from_params(L, p) if adam else None)
+
+        with ThreadPoolExecutor(max(1, min(draw_threads, self.nl))) as ex:
+            staged = list(ex.map(stage, range(self.nl)))
+        self.h_params = [a for a, _ in staged]
+        self.h_master = [m for _, m in staged] if adam else []
+        del staged
         self.h_m = [np.zeros_like(m) for m in self.h_master]
         self.h_v = [np.zeros_like(m) for m in self.h_master]
         self.h_slots = [pinned_bytes(L.grad_bytes) for _ in range(n_grad_slots)]

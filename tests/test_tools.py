@@ -39,16 +39,16 @@ def test_layer_gemms_cover_the_projection_flops():
     changes the sum."""
     import seeded_inputs as si
     for name, w in si.WORKLOADS.items():
-        gemm = sum(2.0 * M * N * K for _, _, M, N, K in bench.layer_gemms(w))
+        gemm = sum(2.0 * M * N * K for _, _, M, N, K in prof.layer_gemms(w))
         attn = 6.0 * w.batch * w.n_heads * w.seq * w.seq * w.head_dim
-        assert gemm + attn == bench.layer_flops(w), name
+        assert gemm + attn == prof.layer_flops(w), name
     w = si.WORKLOADS["stack4-h1024-bf16"].with_(n_heads=6, n_kv_heads=2, head_dim=96, hidden=512, ffn=768)
     T, H = w.tokens, w.hidden
     p_lin = H * 96 * (6 + 2 + 2) + 6 * 96 * H + 3 * 768 * H
-    gemm = sum(2.0 * M * N * K for _, _, M, N, K in bench.layer_gemms(w))
+    gemm = sum(2.0 * M * N * K for _, _, M, N, K in prof.layer_gemms(w))
     assert gemm == 6.0 * T * p_lin
     # every GEMM's reduction length is one of the layer's own widths
-    for _, lay, M, N, K in bench.layer_gemms(w):
+    for _, lay, M, N, K in prof.layer_gemms(w):
         assert K in (H, 6 * 96, 2 * 768, 768, (6 + 4) * 96, T)
 
 
