@@ -179,8 +179,12 @@ def main():
     ap.add_argument("--grad-slots", type=int, default=2,
                     help="pinned fp32 gradient slots shared by all layers (a ring; n_layers = one buffer per layer)")
     ap.add_argument("--sync-adam", action="store_true",
-                    help="every step waits for its own host Adam before returning (default: Adam runs on into the "
-                         "next step, whose forward waits per layer for the update it reads)")
+                    help="every step waits for its own host Adam and copies before returning (default: Adam, or "
+                         "without Adam the last gradient copies, run on into the next step, whose forward waits per "
+                         "layer for the update it reads)")
+    ap.add_argument("--no-keep", action="store_true",
+                    help="without Adam, upload layers 0..window-1 again in every forward (default: they stay in "
+                         "their units from the previous backward)")
     ap.add_argument("--ckpt", action="store_true",
                     help="sliding activation checkpointing: layer inputs wait in pinned host memory and each "
                          "layer's forward is recomputed before its backward")
@@ -226,11 +230,17 @@ def main():
     head = None
     if w.vocab:
         head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
+    # pipelined: host Adam runs on into the next step.  Without Adam the
+    # parameters never change, so the layers that end the backward in their
+    # units open the next forward; those steps stay synchronous (a step's
+    # last gradient copies overlapping the next step's uploads ran at a
+    # quarter of the link rate on this machine)
     pipeline = adam and not args.sync_adam
+    keep = not adam and not args.no_keep
     # draws run on a few host threads (each layer has its own seed)
     ncpu = len(os.sched_getaffinity(0))
     eng = rt.Engine(w, draw, head, window=w.window, n_grad_slots=args.grad_slots, adam=adam, chunk=2048,
-                    adam_threads=args.adam_threads, ckpt=args.ckpt, pipeline=pipeline,
+                    adam_threads=args.adam_threads, ckpt=args.ckpt, pipeline=pipeline, keep_turnaround=keep,
                     draw_threads=max(1, min(8, ncpu // 2)))
     hbm = {"unit_pool_bytes": eng.pool.numel(), "activation_bytes": eng.act_bytes}
     # host memory the engine holds for the layers (pinned: bf16 params, fp32
@@ -348,6 +358,8 @@ def main():
                    "activation_checkpointing": args.ckpt,
                    "adam_schedule": ("pipelined across steps" if pipeline else "synchronous per step") if adam
                    else "off",
+                   "step_schedule": "pipelined across steps" if pipeline else "synchronous per step",
+                   "turnaround_layers_kept": keep,
                    "parallelism": "none (1 GPU)"},
         "engine_hbm": hbm,
         "engine_host_bytes": host,

@@ -270,7 +270,19 @@ enum {
                                    the forward needs them).  Same bits as
                                    without.  Not with SF_ENGINE_HEAD_HOST_ADAM
                                    (SF_ERR_UNSUPPORTED).  Call sf_engine_sync
-                                   before reading host parameters or moments */
+                                   before reading host parameters or moments.
+                                   Without SF_ENGINE_ADAM the step returns
+                                   once its kernels are done while the last
+                                   gradient copies still run (the next step's
+                                   uploads overlap them); sf_engine_sync
+                                   before reading h_grad_slots */,
+  SF_ENGINE_KEEP_TURNAROUND = 32 /* without SF_ENGINE_ADAM: the caller keeps
+                                   h_params unchanged between steps, so layers
+                                   0 .. window-1, which end the backward in
+                                   their units, open the next forward without
+                                   being uploaded again (with SF_ENGINE_ADAM
+                                   they always are: Adam re-uploads them).
+                                   Same bits as without */
 };
 
 /*

@@ -1097,7 +1097,10 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   }
 
   SF_HIP(hipStreamSynchronize(e->s_comp));
-  e->preloaded = adam;
+  // the units of layers 0 .. W-1 hold what the next forward reads first:
+  // their updated parameters (Adam re-uploads them) or, with the
+  // parameters fixed between steps, the ones the backward just used
+  e->preloaded = adam || (c.flags & SF_ENGINE_KEEP_TURNAROUND) != 0;
   if (e->pipe) {
     // Adam jobs (and the uploads they queue) go on; the next step waits for
     // them layer by layer, sf_engine_sync for all of them

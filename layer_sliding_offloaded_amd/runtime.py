@@ -121,13 +121,16 @@ class Engine:
     head: None or dict with E [V, H], gf [H], Wlm [V, H] (float32 storage values).
     ckpt: sliding activation checkpointing (layer inputs kept in pinned host
     memory, each layer's forward recomputed before its backward).
-    pipeline: host Adam runs on across the step boundary (call sync() before
-    reading host parameters or moments).
+    pipeline: host Adam (or, without Adam, the last gradient copies) runs on
+    across the step boundary (call sync() before reading host parameters,
+    moments or gradient slots).
+    keep_turnaround: without Adam, layers 0..window-1 stay in their units from
+    one step's backward to the next step's forward (h_params unchanged).
     """
 
     def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
                  adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False, pipeline=False,
-                 draw_threads=1):
+                 draw_threads=1, keep_turnaround=False):
         import ctypes
         from concurrent.futures import ThreadPoolExecutor
         hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
@@ -150,6 +153,8 @@ class Engine:
             flags |= sf.SF_ENGINE_CKPT
         if pipeline:
             flags |= sf.SF_ENGINE_PIPELINE
+        if keep_turnaround:
+            flags |= sf.SF_ENGINE_KEEP_TURNAROUND
         act = sf.sf_engine_act_bytes_flags(shape, self.nl, flags)
         self.act = device_bytes(act)
         self.act_bytes = act

@@ -34,6 +34,7 @@ SF_ENGINE_HEAD = 2
 SF_ENGINE_HEAD_HOST_ADAM = 4
 SF_ENGINE_CKPT = 8
 SF_ENGINE_PIPELINE = 16
+SF_ENGINE_KEEP_TURNAROUND = 32
 
 _size_t = ctypes.c_size_t
 _vp = ctypes.c_void_p

@@ -134,6 +134,41 @@ def test_engine_c2_gradients_match_oracle_adam_off(c2_case):
     _fail(errs)
 
 
+def test_engine_c2_keep_turnaround_pipelined_matches_oracle(c2_case):
+    """Without Adam, with the parameters fixed between steps: the layers that
+    end the backward in their units open the next forward without an upload,
+    and steps return while the last gradient copies still run.  Two such
+    steps give the same gradients, bit for bit, as one plain step, the
+    oracle's gradients within the bf16 tolerance, and move W layers' worth
+    of parameters less over the host link in the second step."""
+    layers, head, ids, traj = c2_case
+    w = C2
+    nl = w.n_layers
+    say("engine-c2-keep-turnaround", w)
+    d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
+    ref = rt.Engine(w, layers, head, window=2, n_grad_slots=nl, adam=False, chunk=2048)
+    loss0, st0 = ref.step(d_ids)
+    ref.sync()
+    ref_slots = [t.numpy().copy() for t in ref.h_slots]
+    ref.close()
+    eng = rt.Engine(w, layers, head, window=2, n_grad_slots=nl, adam=False, chunk=2048, pipeline=True,
+                    keep_turnaround=True)
+    losses = [eng.step(d_ids)[0] for _ in range(2)]
+    agg = eng.sync()
+    torch.cuda.synchronize()
+    assert losses == [loss0, loss0]
+    for k in range(nl):
+        assert np.array_equal(eng.h_slots[k].numpy(), ref_slots[k]), k
+    assert agg["h2d_bytes"] == 2 * st0["h2d_bytes"] - 2 * eng.layout.param_bytes
+    assert agg["d2h_bytes"] == 2 * st0["d2h_bytes"]
+    shapes = {k: v.shape for k, v in layers[0].items()}
+    errs = {"loss": (abs(losses[-1] - traj[0]["loss"]) / traj[0]["loss"], BF16_TOL)}
+    for i in range(nl):
+        _check_grads(errs, _slot_grads(eng, nl - 1 - i, shapes), traj[0]["layers"][i], f"L{i}", BF16_TOL)
+    eng.close()
+    _fail(errs)
+
+
 def _adam_chain(w0, grads, steps_from=1):
     """fp64 Adam over a list of gradient arrays, starting from zero moments."""
     w, m, v = w0.astype(np.float64), np.zeros(w0.shape), np.zeros(w0.shape)
