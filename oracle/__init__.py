@@ -18,8 +18,9 @@ What the oracle computes and why that is the right thing:
   the fused ops (RoPE, RMSNorm, SwiGLU, LinearCrossEntropy: de §2C, es §2C,
   fr §2C) but print no layer equations.  The oracle is therefore the plain
   definition of a pre-norm Llama decoder block (``layer.py``), its
-  hand-derived backward, the next-token cross-entropy head (``head.py``) and
-  plain Adam (``adam.py``).
+  hand-derived backward, the next-token cross-entropy head (``head.py``),
+  plain Adam (``adam.py``) and fp16's dynamic loss scaling
+  (``loss_scale.py``).
 * Layer sliding moves tensors between host and device and overlaps the host
   optimizer with the device backward (de §2A, es §2A, fr §2A); it changes
   where values live, not what is computed.  The oracle computes the plain,
@@ -53,5 +54,6 @@ from .layer import (  # noqa: F401
     layer_bwd,
 )
 from .head import embed_fwd, embed_bwd, head_fwd_bwd  # noqa: F401
-from .adam import adam_step, round_bf16  # noqa: F401
+from .adam import adam_step, round_bf16, round_f16  # noqa: F401
+from .loss_scale import adam_with_skip, applied_updates, update_scale  # noqa: F401
 from .model import stack_step  # noqa: F401

@@ -38,3 +38,18 @@ def round_bf16(x):
     """
     f, e = np.frexp(np.asarray(x, dtype=np.float64))
     return np.ldexp(np.round(f * 256.0) / 256.0, e)
+
+
+def round_f16(x):
+    """Round float64 values to the nearest IEEE binary16 value (ties to even).
+
+    binary16 keeps 11 significant bits for normal numbers (|x| >= 2^-14);
+    below that the spacing is fixed at 2^-24 (subnormals).  The quantum of x
+    is therefore 2^(max(e, -14) - 11) with x = f 2^e, 0.5 <= |f| < 1 from
+    frexp, i.e. 2^(e-1) <= |x| < 2^e; numpy's round() breaks ties to even.
+    Inputs are finite and below the largest binary16 value (65504).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.ldexp(1.0, np.maximum(e - 1, -14) - 10)
+    return np.round(x / q) * q
