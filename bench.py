@@ -35,8 +35,8 @@ PEAK_HBM_GBPS = 8000.0
 
 def time_gemms(w, sf, torch, reps=20):
     """Average duration (ms) of each layer GEMM, launched alone on the current stream."""
-    dt = sf.SF_BF16 if w.dtype == "bf16" else sf.SF_F32
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    from layer_sliding_offloaded_amd import runtime as rt
+    dt, tdt = rt.sf_dtype(w), rt.storage_dtype(w)
     s = torch.cuda.current_stream()
     out = {}
     from layer_sliding_offloaded_amd.prof import layer_gemms
@@ -169,6 +169,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="slice123b-gqa-bf16")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default=None,
+                    help="16-bit storage type (default: the workload's); f16 runs with dynamic loss scaling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adam-threads", type=int, default=0)
     ap.add_argument("--trace", default=None,
@@ -209,6 +211,10 @@ def main():
     if args.layers:
         w = w.with_(n_layers=args.layers)
     big = w.name == "slice123b-gqa-bf16"
+    if args.dtype and args.dtype != w.dtype:
+        if w.dtype == "f32":
+            sys.exit(f"--dtype: {w.name} is an fp32 workload")
+        w = w.with_(dtype=args.dtype, name=w.name.rsplit("-", 1)[0] + "-" + args.dtype)
     if args.steps is None:
         args.steps = 20 if big else 50
     if args.warmup is None:
@@ -322,7 +328,7 @@ def main():
     torch.cuda.synchronize()
     layer_ms = e0.elapsed_time(e1) / reps
     fl = layer_flops(w)
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS  # fp16 MFMA: the bf16 rate
     layer_tflops = fl / (layer_ms * 1e-3) / 1e12
     c.close()
     del dw, x, dy, y, dx, saved, g

@@ -28,9 +28,11 @@
  *     stream.  Device work is enqueued asynchronously on that stream unless
  *     the entry point says otherwise.
  *   - Device pointers must be 16-byte aligned.  Row-major layouts throughout.
- *   - Storage dtype: SF_F32 (everything fp32) or SF_BF16 (parameters and
- *     activations bf16, accumulation and statistics fp32).  Weight gradients
- *     are always fp32.
+ *   - Storage dtype: SF_F32 (everything fp32), SF_BF16 (parameters and
+ *     activations bf16, accumulation and statistics fp32) or SF_F16 (the same
+ *     with IEEE fp16, whose narrow range the sliding engine covers with
+ *     dynamic loss scaling; de/es/fr §2B name the FP32 -> BF16/FP16
+ *     conversion).  Weight gradients are always fp32.
  */
 #ifndef SF_H
 #define SF_H
@@ -55,7 +57,7 @@ enum {
   SF_ERR_NO_DEVICE = -8     /* no usable gfx950 device                       */
 };
 
-typedef enum { SF_F32 = 0, SF_BF16 = 1 } sf_dtype;
+typedef enum { SF_F32 = 0, SF_BF16 = 1, SF_F16 = 2 } sf_dtype;
 
 typedef void* sf_stream; /* hipStream_t */
 
@@ -171,6 +173,17 @@ sf_status sf_head_fwd_bwd(sf_ctx* ctx, const void* d_gf, const void* d_wlm, cons
                           float* d_dwlm, sf_stream stream);
 
 /*
+ * sf_head_fwd_bwd with the gradients multiplied by grad_scale (> 0, finite;
+ * a power of two keeps the scaling exact): dlogits, and through them d_dx,
+ * d_dgf and d_dwlm, carry the factor; the loss does not.  This is how loss
+ * scaling enters the backward: with SF_F16 storage the unscaled dlogits of
+ * a large vocabulary (about 1/N per entry) would mostly be fp16 subnormals.
+ */
+sf_status sf_head_fwd_bwd_scaled(sf_ctx* ctx, const void* d_gf, const void* d_wlm, const void* d_x,
+                                 const int32_t* d_ids, float* d_loss, void* d_dx, float* d_dgf,
+                                 float* d_dwlm, float grad_scale, sf_stream stream);
+
+/*
  * One dense projection with the block's MFMA GEMM -- the primitive behind
  * every projection above (exposed for measurement and testing):
  *   layout 0 (NT): C[M, N] = A[M, K] B[N, K]^T   (forward  y = x W^T)
@@ -242,6 +255,20 @@ sf_status sf_adam_host(float* p, float* m, float* v, const float* g, uint16_t* p
  */
 sf_status sf_adam_device(int32_t dtype, float* d_p, float* d_m, float* d_v, const float* d_g, void* d_out, size_t n,
                          int64_t step, float lr, float b1, float b2, float eps, sf_stream stream);
+
+/*
+ * The host and device Adam steps for any storage dtype, with the gradient
+ * taken as g * grad_scale (the inverse of a loss scale; 1 leaves it exact,
+ * and a power of two keeps it exact): the same operations, rounded the same
+ * way, on both sides.  p_out / d_out receive the storage copy (SF_BF16 or
+ * SF_F16: round to nearest even; SF_F32: NULL or p itself).
+ */
+sf_status sf_adam_host_ex(int32_t dtype, float* p, float* m, float* v, const float* g, void* p_out, size_t n,
+                          int64_t step, float lr, float b1, float b2, float eps, float grad_scale,
+                          int32_t n_threads);
+sf_status sf_adam_device_ex(int32_t dtype, float* d_p, float* d_m, float* d_v, const float* d_g, void* d_out,
+                            size_t n, int64_t step, float lr, float b1, float b2, float eps, float grad_scale,
+                            sf_stream stream);
 
 /* ------------------------------------------------------------------ engine */
 
@@ -357,6 +384,19 @@ typedef struct {
   float* h_head_grads;
   float* d_head_state;
   void* h_ckpt;
+  /* Dynamic loss scaling (SF_F16 storage only; ignored otherwise).  The
+   * backward starts from the loss gradient times S (dlogits, or the given
+   * d_dy without a head); weight gradients leave scaled and Adam takes them
+   * times 1/S.  After each layer's backward the device checks its fp32
+   * gradients for infinities and NaNs: a layer is updated only if its
+   * gradients and all computed before it in the backward (the head's, the
+   * layers above) are finite, the embedding only if the whole step is; a
+   * skipped update leaves the tensor, its moments and its Adam step count
+   * as they were.  Then S halves (not below 1) after a step with a
+   * non-finite gradient and doubles after scale_window consecutive finite
+   * steps.  Host Adam of a layer starts once that layer's check is done. */
+  float loss_scale;        /* initial S; 0 = 65536                              */
+  int32_t scale_window;    /* 0 = 2000                                           */
 } sf_engine_cfg;
 
 /* Per-step measurements (host wall clock and device events). */
@@ -374,6 +414,11 @@ typedef struct {
   double h2d_bytes, d2h_bytes;
   double h2d_gbps, d2h_gbps;
   float loss;
+  float loss_scale;        /* S this step used (1 without loss scaling)            */
+  int32_t skipped;         /* updates this step skipped for non-finite gradients:
+                              layers, plus one for the LM head and final gain and
+                              one for the embedding (SF_F16; pipelined: the last
+                              step's)                                               */
 } sf_step_stats;
 
 /* Device bytes the engine needs in d_act for `shape`, n_layers and the
@@ -454,7 +499,10 @@ sf_status sf_engine_trace(sf_engine* eng, double* out, int32_t capacity, int32_t
  * variable SF_FAULT_ADAM_JOB=k set at sf_engine_create, the engine's k-th
  * host Adam job (counted from 0 over the engine's life) reports a failure
  * instead of running; the step or sync that observes it returns SF_ERR_HIP
- * and the engine is then in the sticky error state.
+ * and the engine is then in the sticky error state.  With
+ * SF_FAULT_NONFINITE_LAYER=i (fp16 engines), layer i's non-finite flag is
+ * raised in every step as if its gradients had overflowed, which exercises
+ * the layer-wise skip rule of sf_engine_cfg.loss_scale without an overflow.
  */
 sf_status sf_engine_counters(sf_engine* eng, int64_t* out, int32_t n);
 

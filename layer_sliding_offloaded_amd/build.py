@@ -28,7 +28,7 @@ HIPCC_FLAGS = [
 HIP_EXTRA = {"attn_direct.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
 # -ffp-contract=off: host Adam rounds every operation exactly like the device kernel
-HOST_EXTRA = {"adam.cpp": ["-mavx2", "-mfma", "-fno-math-errno", "-ffp-contract=off"]}
+HOST_EXTRA = {"adam.cpp": ["-mavx2", "-mfma", "-mf16c", "-fno-math-errno", "-ffp-contract=off"]}
 
 
 def _run(cmd):

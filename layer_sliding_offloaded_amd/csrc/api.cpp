@@ -49,7 +49,8 @@ sf_status fail(sf_status code, const char* fmt, ...) {
 
 sf_status check_shape(const sf_shape* s, Dims* out) {
   if (!s) return fail(SF_ERR_ARG, "shape is NULL");
-  if (s->dtype != SF_F32 && s->dtype != SF_BF16) return fail(SF_ERR_ARG, "dtype %d is not SF_F32/SF_BF16", s->dtype);
+  if (s->dtype != SF_F32 && s->dtype != SF_BF16 && s->dtype != SF_F16)
+    return fail(SF_ERR_ARG, "dtype %d is not SF_F32/SF_BF16/SF_F16", s->dtype);
   if (s->hidden <= 0 || s->n_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 || s->ffn <= 0 ||
       s->batch <= 0 || s->seq <= 0 || s->vocab < 0)
     return fail(SF_ERR_ARG, "non-positive size in shape");
@@ -67,7 +68,7 @@ sf_status check_shape(const sf_shape* s, Dims* out) {
   d.H = s->hidden; d.nh = s->n_heads; d.nkv = s->n_kv_heads; d.d = s->head_dim; d.F = s->ffn;
   d.V = s->vocab; d.B = s->batch; d.S = s->seq; d.T = T;
   d.Nq = d.nh * d.d; d.Nkv = d.nkv * d.d; d.Nqkv = d.Nq + 2 * d.Nkv;
-  d.dtype = s->dtype; d.e = s->dtype == SF_BF16 ? 2 : 4;
+  d.dtype = s->dtype; d.e = s->dtype == SF_F32 ? 4 : 2;
   d.eps = s->rms_eps; d.rope_base = s->rope_base;
   if (out) *out = d;
   return SF_OK;
@@ -548,8 +549,10 @@ sf_status head_last_dw(sf_ctx* c, float* d_dwlm, sf_stream stream) {
 }
 
 sf_status head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
-                       float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream, bool defer_last_dw) {
+                       float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream, bool defer_last_dw,
+                       float grad_scale) {
   if (sf_status st = check_ctx(c)) return st;
+  if (!(grad_scale > 0.f) || !std::isfinite(grad_scale)) return fail(SF_ERR_ARG, "grad_scale must be finite and > 0");
   if (sf_status st = check_ptrs({d_gf, d_wlm, d_x, d_ids, d_dx, d_dgf, d_dwlm})) return st;
   if (!d_loss) return fail(SF_ERR_ARG, "d_loss is NULL");
   const Dims& d = c->dims;
@@ -581,7 +584,7 @@ sf_status head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const voi
     g.C = logits; g.ldc = d.V;
     g.M = rows; g.N = d.V; g.K = d.H;
     SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::StoreF32, g, s, skw, skb));
-    SF_HIP(ce_rows(d.dtype, logits, d_ids, dlogits, loss_rows, r0, rows, d.V, d.S, inv_n, s));
+    SF_HIP(ce_rows(d.dtype, logits, d_ids, dlogits, loss_rows, r0, rows, d.V, d.S, inv_n * grad_scale, s));
     g = GemmArgs();
     g.A = dlogits; g.lda = d.V;
     g.B = d_wlm; g.ldb = d.H;
@@ -610,6 +613,12 @@ sf_status sf_head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const 
   return sf::head_fwd_bwd(c, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream, false);
 }
 
+sf_status sf_head_fwd_bwd_scaled(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x,
+                                 const int32_t* d_ids, float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm,
+                                 float grad_scale, sf_stream stream) {
+  return sf::head_fwd_bwd(c, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream, false, grad_scale);
+}
+
 size_t sf_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   return gemm_splitk_bytes(M, N, K);
@@ -624,7 +633,7 @@ namespace {
 sf_status gemm_args(int32_t dtype, int32_t layout, int32_t M, int32_t N, int32_t K, const void* d_A, int64_t lda,
                     const void* d_B, int64_t ldb, void* d_C, int64_t ldc, GemmArgs* g, bool* empty) {
   *empty = false;
-  if (dtype != SF_F32 && dtype != SF_BF16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
+  if (dtype != SF_F32 && dtype != SF_BF16 && dtype != SF_F16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
   if (layout < 0 || layout > 2) return fail(SF_ERR_ARG, "bad layout %d", layout);
   if (M < 0 || N < 0 || K < 0) return fail(SF_ERR_ARG, "negative size");
   if (M == 0 || N == 0) {
@@ -681,19 +690,26 @@ sf_status sf_gemm_noalloc(int32_t dtype, int32_t layout, int32_t out_f32, int32_
   return SF_OK;
 }
 
-sf_status sf_adam_device(int32_t dtype, float* d_p, float* d_m, float* d_v, const float* d_g, void* d_out, size_t n,
-                         int64_t step, float lr, float b1, float b2, float eps, sf_stream stream) {
-  if (dtype != SF_F32 && dtype != SF_BF16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
+sf_status sf_adam_device_ex(int32_t dtype, float* d_p, float* d_m, float* d_v, const float* d_g, void* d_out,
+                            size_t n, int64_t step, float lr, float b1, float b2, float eps, float grad_scale,
+                            sf_stream stream) {
+  if (dtype != SF_F32 && dtype != SF_BF16 && dtype != SF_F16) return fail(SF_ERR_ARG, "bad dtype %d", dtype);
+  if (!(grad_scale > 0.f) || !std::isfinite(grad_scale)) return fail(SF_ERR_ARG, "grad_scale must be finite and > 0");
   if (n == 0) return SF_OK;
   if (!d_p || !d_m || !d_v || !d_g) return fail(SF_ERR_ARG, "NULL array");
   if (step < 1) return fail(SF_ERR_ARG, "step must be >= 1");
   const AdamCoef c = adam_coef(step, lr, b1, b2, eps);
   // without a storage copy the kernel writes the copy over the master (same value)
   void* out = d_out ? d_out : (dtype == SF_F32 ? static_cast<void*>(d_p) : nullptr);
-  if (!out) return fail(SF_ERR_ARG, "bf16 storage copy needs d_out");
+  if (!out) return fail(SF_ERR_ARG, "16-bit storage copy needs d_out");
   SF_HIP(adam_device(dtype, d_p, d_m, d_v, d_g, out, static_cast<int64_t>(n), c.b1, c.b2, c.one_b1, c.one_b2,
-                     c.inv_bc1, c.inv_bc2, c.lr, c.eps, static_cast<hipStream_t>(stream)));
+                     c.inv_bc1, c.inv_bc2, c.lr, c.eps, static_cast<hipStream_t>(stream), grad_scale));
   return SF_OK;
+}
+
+sf_status sf_adam_device(int32_t dtype, float* d_p, float* d_m, float* d_v, const float* d_g, void* d_out, size_t n,
+                         int64_t step, float lr, float b1, float b2, float eps, sf_stream stream) {
+  return sf_adam_device_ex(dtype, d_p, d_m, d_v, d_g, d_out, n, step, lr, b1, b2, eps, 1.0f, stream);
 }
 
 sf_status sf_embed_fwd(sf_ctx* c, const void* d_E, const int32_t* d_ids, void* d_x0, sf_stream stream) {

@@ -26,12 +26,12 @@ struct AttnArgs {
 hipError_t attention_fwd(int dtype, const AttnArgs& a, hipStream_t s);
 hipError_t attention_bwd(int dtype, const AttnArgs& a, hipStream_t s);
 
-// bf16 kernels with direct global -> LDS loads (attn_direct.hip).  ok():
-// d in {64, 128}, 16-byte aligned rows, q'k'v buffer under 2 GiB (its byte
-// extent is returned for the buffer-load bounds).
+// 16-bit (bf16 or fp16, dtype 1 or 2) kernels with direct global -> LDS
+// loads (attn_direct.hip).  ok(): d in {64, 128}, 16-byte aligned rows, q'k'v
+// buffer under 2 GiB (its byte extent is returned for the buffer-load bounds).
 bool attention_direct_ok(const AttnArgs& a, int64_t* qkv_bytes);
-hipError_t attention_fwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s);
+hipError_t attention_fwd_direct(int dtype, const AttnArgs& a, int64_t qkv_bytes, hipStream_t s);
 // dK/dV and dQ; needs dsum (rowsum(dA * A)) already computed
-hipError_t attention_bwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s);
+hipError_t attention_bwd_direct(int dtype, const AttnArgs& a, int64_t qkv_bytes, hipStream_t s);
 
 }  // namespace sf

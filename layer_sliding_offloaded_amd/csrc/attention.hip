@@ -31,9 +31,12 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 
-// Pack 8 fp32 (bf16) or take 4 fp32 as the 16-byte B-operand chunk.
-__device__ __forceinline__ uint4 pack_chunk_bf16(const f32x4& a, const f32x4& b) {
-  return make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3]));
+// Pack 8 fp32 into a 16-bit type (bf16 or fp16) or take 4 fp32 as the
+// 16-byte B-operand chunk.
+template <typename T>
+__device__ __forceinline__ uint4 pack_chunk16(const f32x4& a, const f32x4& b) {
+  return make_uint4(pack_pair<T>(a[0], a[1]), pack_pair<T>(a[2], a[3]), pack_pair<T>(b[0], b[1]),
+                    pack_pair<T>(b[2], b[3]));
 }
 __device__ __forceinline__ uint4 pack_chunk_f32(const f32x4& a) {
   return make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
@@ -103,8 +106,8 @@ __device__ __forceinline__ void tile_rows_t(T* lds, int lrow, const T* __restric
 }
 
 // A-operand chunk from a transposed LDS tile [rows][LROW] for the product
-// with register-resident probabilities: bf16 takes keys {32j + 4g .. +3} and
-// {32j + 16 + 4g .. +3} (matching pack_chunk_bf16 of fragments 2j, 2j+1);
+// with register-resident probabilities: 16-bit types take keys {32j + 4g .. +3} and
+// {32j + 16 + 4g .. +3} (matching pack_chunk16 of fragments 2j, 2j+1);
 // fp32 takes keys {16j + 4g .. +3}.
 template <typename T>
 __device__ __forceinline__ uint4 tchunk(const T* lds, int lrow, int row, int j, int g) {
@@ -239,7 +242,7 @@ attn_fwd_kernel(const AttnArgs a) {
         uint4 pf[2];
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          if constexpr (sizeof(T) == 2) pf[f] = pack_chunk_bf16(s[f][2 * j], s[f][2 * j + 1]);
+          if constexpr (sizeof(T) == 2) pf[f] = pack_chunk16<T>(s[f][2 * j], s[f][2 * j + 1]);
           else pf[f] = pack_chunk_f32(s[f][j]);
         }
 #pragma unroll
@@ -412,8 +415,8 @@ attn_bwd_dkdv_kernel(const AttnArgs a) {
       for (int j = 0; j < PJ; ++j) {
         uint4 pb, sb;
         if constexpr (sizeof(T) == 2) {
-          pb = pack_chunk_bf16(p[2 * j], p[2 * j + 1]);
-          sb = pack_chunk_bf16(ds[2 * j], ds[2 * j + 1]);
+          pb = pack_chunk16<T>(p[2 * j], p[2 * j + 1]);
+          sb = pack_chunk16<T>(ds[2 * j], ds[2 * j + 1]);
         } else {
           pb = pack_chunk_f32(p[j]);
           sb = pack_chunk_f32(ds[j]);
@@ -530,7 +533,7 @@ attn_bwd_dq_kernel(const AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < PJ; ++j) {
       uint4 sb;
-      if constexpr (sizeof(T) == 2) sb = pack_chunk_bf16(s[2 * j], s[2 * j + 1]);
+      if constexpr (sizeof(T) == 2) sb = pack_chunk16<T>(s[2 * j], s[2 * j + 1]);
       else sb = pack_chunk_f32(s[j]);
 #pragma unroll
       for (int d = 0; d < FD; ++d) Mfma<T>::run(dq[d], tchunk<T>(Kt, TROW, d * 16 + lr, j, lg), sb);
@@ -576,26 +579,33 @@ hipError_t run_bwd(const AttnArgs& a, hipStream_t s) {
 
 hipError_t attention_fwd(int dtype, const AttnArgs& a, hipStream_t s) {
   int64_t qkv_bytes = 0;
-  if (dtype == 1 && attention_direct_ok(a, &qkv_bytes)) return attention_fwd_direct(a, qkv_bytes, s);
-  if (dtype == 1) return a.head_dim == 64 ? run_fwd<bf16, 64>(a, s) : run_fwd<bf16, 128>(a, s);
-  return a.head_dim == 64 ? run_fwd<float, 64>(a, s) : run_fwd<float, 128>(a, s);
+  if (dtype != 0 && attention_direct_ok(a, &qkv_bytes)) return attention_fwd_direct(dtype, a, qkv_bytes, s);
+  return with_storage(dtype, [&](auto tag) {
+    using T = typename decltype(tag)::type;
+    return a.head_dim == 64 ? run_fwd<T, 64>(a, s) : run_fwd<T, 128>(a, s);
+  });
 }
 
 hipError_t attention_bwd(int dtype, const AttnArgs& a, hipStream_t s) {
   int64_t qkv_bytes = 0;
-  if (dtype == 1 && attention_direct_ok(a, &qkv_bytes) && a.ld_dout % 8 == 0 &&
+  if (dtype != 0 && attention_direct_ok(a, &qkv_bytes) && a.ld_dout % 8 == 0 &&
       !(reinterpret_cast<uintptr_t>(a.dout) & 15u)) {
     const int64_t rows = static_cast<int64_t>(a.batch) * a.seq * a.n_heads;
-    if (a.head_dim == 64)
-      hipLaunchKernelGGL((attn_dot_kernel<bf16, 64>), dim3((rows + 255) / 256), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_dot_kernel<bf16, 128>), dim3((rows + 255) / 256), dim3(256), 0, s, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = with_storage(dtype, [&](auto tag) {
+      using T = typename decltype(tag)::type;
+      if (a.head_dim == 64)
+        hipLaunchKernelGGL((attn_dot_kernel<T, 64>), dim3((rows + 255) / 256), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_dot_kernel<T, 128>), dim3((rows + 255) / 256), dim3(256), 0, s, a);
+      return hipGetLastError();
+    });
     if (e != hipSuccess) return e;
-    return attention_bwd_direct(a, qkv_bytes, s);
+    return attention_bwd_direct(dtype, a, qkv_bytes, s);
   }
-  if (dtype == 1) return a.head_dim == 64 ? run_bwd<bf16, 64>(a, s) : run_bwd<bf16, 128>(a, s);
-  return a.head_dim == 64 ? run_bwd<float, 64>(a, s) : run_bwd<float, 128>(a, s);
+  return with_storage(dtype, [&](auto tag) {
+    using T = typename decltype(tag)::type;
+    return a.head_dim == 64 ? run_bwd<T, 64>(a, s) : run_bwd<T, 128>(a, s);
+  });
 }
 
 }  // namespace sf

@@ -1,4 +1,4 @@
-// Causal flash attention, bf16, with global -> LDS direct loads (gfx950).
+// Causal flash attention, bf16 or fp16 storage, with global -> LDS direct loads (gfx950).
 //
 // Same mathematics and data layout as the register-staged kernels (online
 // softmax in base 2 over key tiles, log-sum-exp saved per (b, h, s),
@@ -59,8 +59,10 @@ __device__ __forceinline__ int tswz(int r) {
   else return r & 7;
 }
 
+template <typename T>
 __device__ __forceinline__ uint4 pack8(const f32x4& a, const f32x4& b) {
-  return make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3]));
+  return make_uint4(pack_pair<T>(a[0], a[1]), pack_pair<T>(a[2], a[3]), pack_pair<T>(b[0], b[1]),
+                    pack_pair<T>(b[2], b[3]));
 }
 
 // ---- loads of one 64-row x D tile into LDS --------------------------------
@@ -155,7 +157,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t by
 
 // ------------------------------------------------------------------ forward
 // Block: 4 waves x 32 query rows of one (b, h); key tiles of 64.
-template <int D>
+template <typename T, int D>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
   constexpr int BQ = 128, BKV = 64, NW = 4;
@@ -187,7 +189,7 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
   lv.init(w, lane, (bs * ld + (a.n_heads + a.n_kv + kvh) * D) * 2, ld);
 
   // Q fragments (B operand): lane supplies row lr, d-chunk lg of each 32
-  const bf16* qbase = static_cast<const bf16*>(a.qkv) + bs * ld + h * D;
+  const T* qbase = static_cast<const T*>(a.qkv) + bs * ld + h * D;
   uint4 qf[2][DC];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
@@ -203,10 +205,11 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
 #pragma unroll
     for (int d = 0; d < FD; ++d) oacc[f][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrow[2] = {-INFINITY, -INFINITY};
-  // row sums of the (bf16) probabilities, accumulated by MFMA against a
+  // row sums of the (16-bit) probabilities, accumulated by MFMA against a
   // fragment of ones: every element of lacc[f] holds the sum for row lr
   f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+  constexpr uint32_t kOnes = One16<T>::kBits | (One16<T>::kBits << 16);
+  const uint4 ones = make_uint4(kOnes, kOnes, kOnes, kOnes);
   const float sc = a.scale * kLog2e;
   const int nkv = (min(q0 + BQ, S) - 1) / BKV + 1;
   int ko[DC], vo[FD];
@@ -234,7 +237,7 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int fk = 0; fk < 4; ++fk) Mfma<bf16>::run(sv[f][fk], kf[fk], qf[f][c]);
+        for (int fk = 0; fk < 4; ++fk) Mfma<T>::run(sv[f][fk], kf[fk], qf[f][c]);
     }
   };
   auto active = [&](int kt) { return kt < nkv && kt * BKV <= qw + 31; };
@@ -307,15 +310,15 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
     // O^T += V^T P^T: lane holds O[q = qw + 16 f + lr][d = 16 fd + 4 lg + v]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint4 pf0 = pack8(s[0][2 * j], s[0][2 * j + 1]);
-      const uint4 pf1 = pack8(s[1][2 * j], s[1][2 * j + 1]);
-      Mfma<bf16>::run(lacc[0], ones, pf0);
-      Mfma<bf16>::run(lacc[1], ones, pf1);
+      const uint4 pf0 = pack8<T>(s[0][2 * j], s[0][2 * j + 1]);
+      const uint4 pf1 = pack8<T>(s[1][2 * j], s[1][2 * j + 1]);
+      Mfma<T>::run(lacc[0], ones, pf0);
+      Mfma<T>::run(lacc[1], ones, pf1);
 #pragma unroll
       for (int d = 0; d < FD; ++d) {
         const uint4 vf = frag_t<D>(Vc, vo[d], j);
-        Mfma<bf16>::run(oacc[0][d], vf, pf0);
-        Mfma<bf16>::run(oacc[1][d], vf, pf1);
+        Mfma<T>::run(oacc[0][d], vf, pf0);
+        Mfma<T>::run(oacc[1][d], vf, pf1);
       }
     }
 #pragma unroll
@@ -329,7 +332,7 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS outlives the block
 
-  bf16* obase = static_cast<bf16*>(a.out) + bs * a.ld_out + h * D;
+  T* obase = static_cast<T*>(a.out) + bs * a.ld_out + h * D;
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const float l = lacc[f][0];
@@ -340,7 +343,7 @@ attn_fwd_direct(const AttnArgs a, int qkv_bytes) {
       for (int d = 0; d < FD; ++d) {
         const f32x4 o = oacc[f][d];
         *reinterpret_cast<uint2*>(obase + static_cast<int64_t>(q) * a.ld_out + d * 16 + lg * 4) =
-            make_uint2(pack2(o[0] * inv, o[1] * inv), pack2(o[2] * inv, o[3] * inv));
+            make_uint2(pack_pair<T>(o[0] * inv, o[1] * inv), pack_pair<T>(o[2] * inv, o[3] * inv));
       }
       if (lg == 0) a.lse[(static_cast<int64_t>(b) * a.n_heads + h) * S + q] = mrow[f] + log2f(l);
     }
@@ -365,8 +368,9 @@ __device__ __forceinline__ void rope_inv(f32x4 (&x)[D / 16], const AttnArgs& a, 
     }
 }
 
-__device__ __forceinline__ void store4bf(bf16* p, const f32x4& v) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+template <typename T>
+__device__ __forceinline__ void store4v(T* p, const f32x4& v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_pair<T>(v[0], v[1]), pack_pair<T>(v[2], v[3]));
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -375,7 +379,7 @@ __device__ __forceinline__ void store4bf(bf16* p, const f32x4& v) {
 // tiles (kind 1) serve both the score recompute (along d) and the dK / dV
 // products (transposed, along the queries); log-sum-exp and D of the tile's
 // queries are staged next to them.
-template <int D, int KF, int NWV>
+template <typename T, int D, int KF, int NWV>
 __global__ void __launch_bounds__(NWV * 64)
 attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes) {
   constexpr int KW = 16 * KF, BKV = NWV * KW, BQ = 64, NW = NWV;
@@ -406,13 +410,13 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
   const __amdgpu_buffer_rsrc_t rd = rsrc(a.dsum, stat_bytes);
 
   // K, V fragments (B operand): lane supplies row kvw + 16 fk + lr, d-chunk lg
-  const bf16* qkv = static_cast<const bf16*>(a.qkv);
+  const T* qkv = static_cast<const T*>(a.qkv);
   uint4 kf[KF][DC], vf[KF][DC];
 #pragma unroll
   for (int fk = 0; fk < KF; ++fk) {
     const int kv = kvw + fk * 16 + lr;
-    const bf16* kr = qkv + (bs + kv) * ld + (a.n_heads + kvh) * D;
-    const bf16* vr = qkv + (bs + kv) * ld + (a.n_heads + a.n_kv + kvh) * D;
+    const T* kr = qkv + (bs + kv) * ld + (a.n_heads + kvh) * D;
+    const T* vr = qkv + (bs + kv) * ld + (a.n_heads + a.n_kv + kvh) * D;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       kf[fk][c] = kv < S ? *reinterpret_cast<const uint4*>(kr + c * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
@@ -472,8 +476,8 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
           const uint4 da = lds16(Oc, dof[c] + fq * 16 * (D * 2));
 #pragma unroll
           for (int fk = 0; fk < KF; ++fk) {
-            Mfma<bf16>::run(p[fk][fq], qa, kf[fk][c]);
-            Mfma<bf16>::run(dp[fk][fq], da, vf[fk][c]);
+            Mfma<T>::run(p[fk][fq], qa, kf[fk][c]);
+            Mfma<T>::run(dp[fk][fq], da, vf[fk][c]);
           }
         }
       // P and dS; keys after a query, or queries past the end, exist only
@@ -508,8 +512,8 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
         uint4 pb[KF], sb[KF];
 #pragma unroll
         for (int fk = 0; fk < KF; ++fk) {
-          pb[fk] = pack8(p[fk][2 * j], p[fk][2 * j + 1]);
-          sb[fk] = pack8(dp[fk][2 * j], dp[fk][2 * j + 1]);
+          pb[fk] = pack8<T>(p[fk][2 * j], p[fk][2 * j + 1]);
+          sb[fk] = pack8<T>(dp[fk][2 * j], dp[fk][2 * j + 1]);
         }
 #pragma unroll
         for (int d = 0; d < FD; ++d) {
@@ -517,8 +521,8 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
           const uint4 qa = frag_t<D>(Qc, tof[d], j);
 #pragma unroll
           for (int fk = 0; fk < KF; ++fk) {
-            Mfma<bf16>::run(dv[fk][d], oa, pb[fk]);
-            Mfma<bf16>::run(dk[fk][d], qa, sb[fk]);
+            Mfma<T>::run(dv[fk][d], oa, pb[fk]);
+            Mfma<T>::run(dk[fk][d], qa, sb[fk]);
           }
         }
       }
@@ -544,12 +548,12 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
 #pragma unroll
       for (int v = 0; v < 4; ++v) dk[fk][d][v] *= a.scale;
     rope_inv<D>(dk[fk], a, kv, lg);
-    bf16* dkp = static_cast<bf16*>(a.dqkv) + (bs + kv) * a.ld_dqkv + (a.n_heads + kvh) * D;
-    bf16* dvp = static_cast<bf16*>(a.dqkv) + (bs + kv) * a.ld_dqkv + (a.n_heads + a.n_kv + kvh) * D;
+    T* dkp = static_cast<T*>(a.dqkv) + (bs + kv) * a.ld_dqkv + (a.n_heads + kvh) * D;
+    T* dvp = static_cast<T*>(a.dqkv) + (bs + kv) * a.ld_dqkv + (a.n_heads + a.n_kv + kvh) * D;
 #pragma unroll
     for (int d = 0; d < FD; ++d) {
-      store4bf(dkp + d * 16 + lg * 4, dk[fk][d]);
-      store4bf(dvp + d * 16 + lg * 4, dv[fk][d]);
+      store4v<T>(dkp + d * 16 + lg * 4, dk[fk][d]);
+      store4v<T>(dvp + d * 16 + lg * 4, dv[fk][d]);
     }
   }
 }
@@ -557,7 +561,7 @@ attn_dkdv_direct(const AttnArgs a, int qkv_bytes, int dout_bytes, int stat_bytes
 // -------------------------------------------------------------------- dQ
 // Block: NWV waves x 16 F queries of one (b, h); key tiles of 64 (kind 1: the
 // score recompute reads K and V along d, the dQ product reads K transposed).
-template <int D, int F, int NWV>
+template <typename T, int D, int F, int NWV>
 __global__ void __launch_bounds__(NWV * 64)
 attn_dq_direct(const AttnArgs a, int qkv_bytes) {
   constexpr int QW = 16 * F, BQ = NWV * QW, BKV = 64, NW = NWV;
@@ -588,8 +592,8 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
   lv.init(w, lane, (bs * ld + (a.n_heads + a.n_kv + kvh) * D) * 2, ld);
 
   // Q, dO fragments (B operand) and the rows' statistics
-  const bf16* qbase = static_cast<const bf16*>(a.qkv) + bs * ld + h * D;
-  const bf16* dbase = static_cast<const bf16*>(a.dout) + bs * a.ld_dout + h * D;
+  const T* qbase = static_cast<const T*>(a.qkv) + bs * ld + h * D;
+  const T* dbase = static_cast<const T*>(a.dout) + bs * a.ld_dout + h * D;
   uint4 qf[F][DC], df[F][DC];
   float lse[F], dsm[F];
   const int64_t srow = (static_cast<int64_t>(b) * a.n_heads + h) * S;
@@ -647,8 +651,8 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
           const uint4 va = lds16(Vc, dof[c] + fk * 16 * (D * 2));
 #pragma unroll
           for (int f = 0; f < F; ++f) {
-            Mfma<bf16>::run(s[f][fk], ka, qf[f][c]);
-            Mfma<bf16>::run(dp[f][fk], va, df[f][c]);
+            Mfma<T>::run(s[f][fk], ka, qf[f][c]);
+            Mfma<T>::run(dp[f][fk], va, df[f][c]);
           }
         }
       // (one predicated path: a separate unmasked copy of this loop pushes
@@ -672,12 +676,12 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
       for (int j = 0; j < 2; ++j) {
         uint4 sb[F];
 #pragma unroll
-        for (int f = 0; f < F; ++f) sb[f] = pack8(s[f][2 * j], s[f][2 * j + 1]);
+        for (int f = 0; f < F; ++f) sb[f] = pack8<T>(s[f][2 * j], s[f][2 * j + 1]);
 #pragma unroll
         for (int d = 0; d < FD; ++d) {
           const uint4 ka = frag_t<D>(Kc, tof[d], j);
 #pragma unroll
-          for (int f = 0; f < F; ++f) Mfma<bf16>::run(dq[f][d], ka, sb[f]);
+          for (int f = 0; f < F; ++f) Mfma<T>::run(dq[f][d], ka, sb[f]);
         }
       }
     }
@@ -698,39 +702,39 @@ attn_dq_direct(const AttnArgs a, int qkv_bytes) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) dq[f][d][v] *= a.scale;
     rope_inv<D>(dq[f], a, q, lg);
-    bf16* dqp = static_cast<bf16*>(a.dqkv) + (bs + q) * a.ld_dqkv + h * D;
+    T* dqp = static_cast<T*>(a.dqkv) + (bs + q) * a.ld_dqkv + h * D;
 #pragma unroll
-    for (int d = 0; d < FD; ++d) store4bf(dqp + d * 16 + lg * 4, dq[f][d]);
+    for (int d = 0; d < FD; ++d) store4v<T>(dqp + d * 16 + lg * 4, dq[f][d]);
   }
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t run_bwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
-  const int64_t T = static_cast<int64_t>(a.batch) * a.seq;
-  const int64_t dout_bytes = ((T - 1) * a.ld_dout + static_cast<int64_t>(a.n_heads) * D) * 2;
+  const int64_t nt = static_cast<int64_t>(a.batch) * a.seq;
+  const int64_t dout_bytes = ((nt - 1) * a.ld_dout + static_cast<int64_t>(a.n_heads) * D) * 2;
   const int64_t stat_bytes = static_cast<int64_t>(a.batch) * a.n_heads * a.seq * 4;
   // Block shapes (measured; every shape gives the same bits): dK/dV with 4
   // waves of 16 keys; dQ with 4 waves of 32 queries when that still makes
   // two blocks per CU, else 8 waves of 16.  (This file is compiled with the
   // MFMA accumulators held in VGPRs, which made the 4-wave dQ the fastest:
   // no AGPR-to-VGPR copies before the softmax arithmetic.)
-  hipLaunchKernelGGL((attn_dkdv_direct<D, 1, 4>), dim3((a.seq + 63) / 64, a.n_kv, a.batch), dim3(256), 0, s, a,
+  hipLaunchKernelGGL((attn_dkdv_direct<T, D, 1, 4>), dim3((a.seq + 63) / 64, a.n_kv, a.batch), dim3(256), 0, s, a,
                      static_cast<int>(qkv_bytes), static_cast<int>(dout_bytes), static_cast<int>(stat_bytes));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (static_cast<int64_t>((a.seq + 127) / 128) * a.n_heads * a.batch >= 512)
-    hipLaunchKernelGGL((attn_dq_direct<D, 2, 4>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(256), 0, s, a,
-                       static_cast<int>(qkv_bytes));
+    hipLaunchKernelGGL((attn_dq_direct<T, D, 2, 4>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(256), 0, s,
+                       a, static_cast<int>(qkv_bytes));
   else
-    hipLaunchKernelGGL((attn_dq_direct<D, 1, 8>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(512), 0, s, a,
-                       static_cast<int>(qkv_bytes));
+    hipLaunchKernelGGL((attn_dq_direct<T, D, 1, 8>), dim3((a.seq + 127) / 128, a.n_heads, a.batch), dim3(512), 0, s,
+                       a, static_cast<int>(qkv_bytes));
   return hipGetLastError();
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t run_fwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
   dim3 grid((a.seq + 127) / 128, a.n_heads, a.batch);
-  hipLaunchKernelGGL((attn_fwd_direct<D>), grid, dim3(256), 0, s, a, static_cast<int>(qkv_bytes));
+  hipLaunchKernelGGL((attn_fwd_direct<T, D>), grid, dim3(256), 0, s, a, static_cast<int>(qkv_bytes));
   return hipGetLastError();
 }
 
@@ -744,12 +748,16 @@ bool attention_direct_ok(const AttnArgs& a, int64_t* qkv_bytes) {
   return *qkv_bytes < (int64_t{1} << 31) - 1024;
 }
 
-hipError_t attention_fwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
-  return a.head_dim == 64 ? run_fwd_direct<64>(a, qkv_bytes, s) : run_fwd_direct<128>(a, qkv_bytes, s);
+hipError_t attention_fwd_direct(int dtype, const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
+  if (dtype == 2)
+    return a.head_dim == 64 ? run_fwd_direct<f16, 64>(a, qkv_bytes, s) : run_fwd_direct<f16, 128>(a, qkv_bytes, s);
+  return a.head_dim == 64 ? run_fwd_direct<bf16, 64>(a, qkv_bytes, s) : run_fwd_direct<bf16, 128>(a, qkv_bytes, s);
 }
 
-hipError_t attention_bwd_direct(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
-  return a.head_dim == 64 ? run_bwd_direct<64>(a, qkv_bytes, s) : run_bwd_direct<128>(a, qkv_bytes, s);
+hipError_t attention_bwd_direct(int dtype, const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
+  if (dtype == 2)
+    return a.head_dim == 64 ? run_bwd_direct<f16, 64>(a, qkv_bytes, s) : run_bwd_direct<f16, 128>(a, qkv_bytes, s);
+  return a.head_dim == 64 ? run_bwd_direct<bf16, 64>(a, qkv_bytes, s) : run_bwd_direct<bf16, 128>(a, qkv_bytes, s);
 }
 
 }  // namespace sf

@@ -1,4 +1,4 @@
-// Device helpers shared by the HIP kernels: bf16 storage, 16-byte vectors,
+// Device helpers shared by the HIP kernels: bf16 and fp16 storage, 16-byte vectors,
 // wavefront reductions and the gfx950 MFMA wrappers.
 #pragma once
 
@@ -23,6 +23,27 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ uint16_t f2bf(float f) { return static_cast<uint16_t>(pack2(f, 0.0f)); }
+
+// ----------------------------------------------------------------- fp16
+// IEEE binary16 storage (SF_F16), also raw uint16_t.  Conversion to fp32 is
+// exact; from fp32 it rounds to nearest even (v_cvt_f16_f32 in the default
+// round mode), and magnitudes past 65504 become infinities, which the
+// engine's loss scaling detects in the weight gradients.
+struct f16 { uint16_t u; };
+
+typedef __attribute__((ext_vector_type(2))) _Float16 hw_f16x2;
+
+__device__ __forceinline__ float h2f(uint16_t u) { return static_cast<float>(__builtin_bit_cast(_Float16, u)); }
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  const hw_f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
+
+// Two values of a 16-bit storage type packed into one word (low = first).
+template <typename T> __device__ __forceinline__ uint32_t pack_pair(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack_pair<bf16>(float lo, float hi) { return pack2(lo, hi); }
+template <> __device__ __forceinline__ uint32_t pack_pair<f16>(float lo, float hi) { return pack2h(lo, hi); }
 
 // Element traits: the storage type of activations and weights.
 template <typename T> struct Elem;
@@ -57,6 +78,39 @@ template <> struct Elem<bf16> {
   }
 };
 
+template <> struct Elem<f16> {
+  static constexpr int kPerVec = 8;
+  static __device__ __forceinline__ float load(const f16* p, size_t i) { return h2f(p[i].u); }
+  static __device__ __forceinline__ void store(f16* p, size_t i, float v) { p[i].u = f2h(v); }
+  static __device__ __forceinline__ void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
+      f[2 * i + 1] = h2f(static_cast<uint16_t>(w[i] >> 16));
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(pack2h(f[0], f[1]), pack2h(f[2], f[3]), pack2h(f[4], f[5]), pack2h(f[6], f[7]));
+  }
+};
+
+// The bit pattern of 1.0 in a 16-bit storage type.
+template <typename T> struct One16;
+template <> struct One16<bf16> { static constexpr uint32_t kBits = 0x3F80u; };
+template <> struct One16<f16> { static constexpr uint32_t kBits = 0x3C00u; };
+
+// Storage dtype code (0 fp32, 1 bf16, 2 fp16) -> type, for host dispatch:
+// f(Tag<T>{}) with T = float, bf16 or f16.
+template <typename T> struct Tag { using type = T; };
+template <typename F>
+hipError_t with_storage(int dtype, F&& f) {
+  if (dtype == 1) return f(Tag<bf16>{});
+  if (dtype == 2) return f(Tag<f16>{});
+  if (dtype == 0) return f(Tag<float>{});
+  return hipErrorInvalidValue;
+}
+
 // ----------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -76,6 +130,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // 8 bf16 (one 16x16x32 MFMA) or 4 fp32 (four 16x16x4 MFMAs, one per
 // element, so that 16 consecutive k are covered either way per 4 chunks).
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 template <typename T> struct Mfma;
@@ -84,6 +139,13 @@ template <> struct Mfma<bf16> {
   static __device__ __forceinline__ void run(f32x4& acc, const uint4& a, const uint4& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+};
+template <> struct Mfma<f16> {
+  static constexpr int kChunkK = 8;
+  static __device__ __forceinline__ void run(f32x4& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                 acc, 0, 0, 0);
   }
 };
 template <> struct Mfma<float> {
@@ -130,6 +192,10 @@ template <> struct Transpose<bf16> {
   static constexpr int N = 8;
   static __device__ __forceinline__ void run(const uint4* v, uint4* o) { transpose8x8_b16(v, o); }
 };
+template <> struct Transpose<f16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void run(const uint4* v, uint4* o) { transpose8x8_b16(v, o); }
+};
 template <> struct Transpose<float> {
   static constexpr int N = 4;
   static __device__ __forceinline__ void run(const uint4* v, uint4* o) { transpose4x4_b32(v, o); }
@@ -139,7 +205,7 @@ template <> struct Transpose<float> {
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float* v) {
   if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_pair<T>(v[0], v[1]), pack_pair<T>(v[2], v[3]));
   } else {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }

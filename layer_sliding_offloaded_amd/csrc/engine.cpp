@@ -57,6 +57,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cmath>
 #include <condition_variable>
 #include <cstdint>
 #include <cstdlib>
@@ -180,6 +181,7 @@ struct Job {
   int slot;   // host gradient slot (kLayer)
   hipEvent_t ready;
   size_t lo = 0, hi = 0;  // kLayer: byte range of the layer's fp32 gradients
+  hipEvent_t verdict = nullptr;  // loss scaling: the layer's gradients have been checked
   bool first = false;     // kLayer: the layer's first range
   bool last = false;      // kLayer: the layer's final range (frees the slot)
   int64_t step = 0;       // the iteration whose gradients these are
@@ -297,6 +299,29 @@ struct sf_engine {
   // test hook: the Adam job with this index (counted from engine creation)
   // reports a failure instead of running (environment SF_FAULT_ADAM_JOB)
   int64_t fault_adam_job = -1, adam_jobs_seen = 0;
+  // Dynamic loss scaling (SF_F16 storage).  d_ovf: running OR of non-finite
+  // gradients of the step's backward (device, in the activation region's
+  // tail); d_ovf_head: its value right after the head (the head's device
+  // Adam reads it); h_ovf: pinned verdicts [2 steps by parity][n_layers + 2]
+  // (layer i, n_layers: head, n_layers + 1: whole step) that the compute
+  // stream publishes; ev_verdict[i]: layer i's verdict is published.
+  bool lscale = false;
+  float scale = 1.f;
+  int32_t scale_window = 2000;
+  int64_t good_steps = 0;
+  int32_t* d_ovf = nullptr;
+  int32_t* d_ovf_head = nullptr;
+  int32_t* h_ovf = nullptr;
+  std::vector<hipEvent_t> ev_verdict;
+  // Adam steps applied so far per layer, LM head and embedding (a skipped
+  // update does not count) and this step's coefficients from them
+  std::vector<int64_t> adam_t;
+  int64_t head_t = 0, embed_t = 0;
+  std::vector<AdamCoef> lcoef;
+  AdamCoef hcoef{}, ecoef{};
+  float last_scale = 1.f;
+  int32_t last_skipped = 0;
+  int fault_nonfinite_layer = -1;  // test hook (environment SF_FAULT_NONFINITE_LAYER)
   int64_t step = 0;
   bool failed = false;
   // embedding sparse gradients
@@ -414,11 +439,12 @@ void run_adam(sf_engine* e, const AdamCoef& c, float* p, float* m, float* v, con
   std::vector<Seg> tasks;
   for (const Seg& s : segs)
     for (size_t b = 0; b < s.n; b += chunk) tasks.push_back({s.off + b, std::min(chunk, s.n - b), s.out_off + b});
-  const bool bf = e->d.dtype == SF_BF16;
+  const bool half = e->d.dtype != SF_F32;
+  const int out16 = e->d.dtype == SF_F16 ? 2 : 1;
   e->pool->run(tasks.size(), [&](size_t i) {
     const Seg& t = tasks[i];
-    if (bf) {
-      adam_range(p + t.off, m + t.off, v + t.off, g + t.off, static_cast<uint16_t*>(out) + t.out_off, t.n, c);
+    if (half) {
+      adam_range(p + t.off, m + t.off, v + t.off, g + t.off, static_cast<uint16_t*>(out) + t.out_off, t.n, c, out16);
     } else {
       adam_range(p + t.off, m + t.off, v + t.off, g + t.off, nullptr, t.n, c);
       if (!out_is_master) std::memcpy(static_cast<float*>(out) + t.out_off, p + t.off, t.n * 4);
@@ -443,7 +469,8 @@ sf_status run_embed_adam(sf_engine* e, const AdamCoef& cf) {
     if (id < 0 || id >= V) return fail(SF_ERR_HIP, "corrupt sparse embedding gradient id %d", id);
     e->slot_of_row[id] = s;
   }
-  const bool bf = e->d.dtype == SF_BF16;
+  const bool bf = e->d.dtype != SF_F32;
+  const int out16 = e->d.dtype == SF_F16 ? 2 : 1;
   const bool out_is_master = c.h_head_params == static_cast<void*>(c.h_head_master);
   const int rows_per_task = std::max(1, (1 << 17) / H);
   const int groups = 8;
@@ -460,7 +487,7 @@ sf_status run_embed_adam(sf_engine* e, const AdamCoef& cf) {
         const size_t o = static_cast<size_t>(r) * H;
         if (bf) {
           adam_range(c.h_head_master + o, c.h_head_m + o, c.h_head_v + o, gr,
-                     static_cast<uint16_t*>(c.h_head_params) + o, H, cf);
+                     static_cast<uint16_t*>(c.h_head_params) + o, H, cf, out16);
         } else {
           adam_range(c.h_head_master + o, c.h_head_m + o, c.h_head_v + o, gr, nullptr, H, cf);
           if (!out_is_master) std::memcpy(static_cast<float*>(c.h_head_params) + o, c.h_head_master + o, H * 4);
@@ -500,15 +527,19 @@ sf_status run_job(sf_engine* e, const Job& j) {
   const size_t VH = static_cast<size_t>(e->d.V) * e->d.H;
   if (j.kind == kLayer) {
     const ChunkMap cm = chunk_map(e->L, e->d.e, j.lo, j.hi);
-    run_adam(e, j.coef, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot],
-             c.h_params[j.layer], c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), cm.segs);
+    // loss scaling: a non-finite gradient in this layer or before it in the
+    // backward leaves the layer as it is (its unit still holds it)
+    const bool skip = e->lscale && e->h_ovf[(j.step & 1) * (e->nl + 2) + j.layer] != 0;
+    if (!skip)
+      run_adam(e, j.coef, c.h_master[j.layer], c.h_m[j.layer], c.h_v[j.layer], c.h_grad_slots[j.slot],
+               c.h_params[j.layer], c.h_params[j.layer] == static_cast<void*>(c.h_master[j.layer]), cm.segs);
     // Layers 0 .. W-1 open the next step's forward and finish their backward
     // last: upload each updated range into the layer's unit right away, so
     // the upload of one range overlaps the Adam of the next.
     if (j.layer < e->W) {
       const int u = j.layer;
       if (j.first) SF_HIP(hipStreamWaitEvent(e->s_up, e->ev_param_free[u], 0));
-      if (cm.phi > cm.plo) {
+      if (!skip && cm.phi > cm.plo) {
         if (sf_status rc = timed_h2d(e, e->uparam[u] + cm.plo, static_cast<const char*>(c.h_params[j.layer]) + cm.plo,
                                      cm.phi - cm.plo, e->s_up))
           return rc;
@@ -566,7 +597,8 @@ void dispatcher_loop(sf_engine* e) {
       e->jobs.erase(e->jobs.begin() + static_cast<std::ptrdiff_t>(pick));
     }
     std::string err;
-    const hipError_t he = hipEventSynchronize(j.ready);
+    hipError_t he = hipEventSynchronize(j.ready);
+    if (he == hipSuccess && j.verdict) he = hipEventSynchronize(j.verdict);
     const double t0 = now_ms();
     const bool fault = e->fault_adam_job >= 0 && e->adam_jobs_seen++ == e->fault_adam_job;
     if (he != hipSuccess) {
@@ -669,7 +701,7 @@ sf_status wait_slot(sf_engine* e, int* slot) {
 
 void push_job(sf_engine* e, Job j) {
   j.step = e->step;
-  j.coef = e->coef;
+  j.coef = j.kind == kLayer ? e->lcoef[j.layer] : e->coef;
   std::lock_guard<std::mutex> lk(e->mu);
   e->jobs.push_back(j);
   ++e->pending;
@@ -715,6 +747,9 @@ sf_status close_window(sf_engine* e, sf_step_stats* st) {
   if (sf_status rc = fill_stats(e, &local)) return rc;
   std::lock_guard<std::mutex> lk(e->mu);
   local.adam_ms = e->adam_ms;
+  // the loss scale and skips of the window's last step
+  local.loss_scale = e->last_scale;
+  local.skipped = e->last_skipped;
   e->trace.insert(e->trace.end(), e->adam_rows.begin(), e->adam_rows.end());
   e->window_open = false;
   e->last_stats = local;
@@ -743,10 +778,27 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     e->rows.clear();
   }
   e->step += 1;
+  // Adam coefficients of this step: the step number of each tensor counts
+  // its applied updates (all of them without loss scaling); gradients enter
+  // times 1 / S
+  const float gscale = 1.0f / e->scale;
   e->coef = adam_coef(e->step, c.lr, c.b1, c.b2, c.eps);
+  e->coef.gscale = gscale;
+  for (int l = 0; l < nl; ++l) {
+    e->lcoef[l] = adam_coef(e->adam_t[l] + 1, c.lr, c.b1, c.b2, c.eps);
+    e->lcoef[l].gscale = gscale;
+  }
+  e->hcoef = adam_coef(e->head_t + 1, c.lr, c.b1, c.b2, c.eps);
+  e->ecoef = adam_coef(e->embed_t + 1, c.lr, c.b1, c.b2, c.eps);
+  e->hcoef.gscale = e->ecoef.gscale = gscale;
+  // this step's verdicts (the slots of step - 2, long complete)
+  int32_t* hv = e->lscale ? e->h_ovf + (e->step & 1) * (nl + 2) : nullptr;
+  if (hv)
+    for (int k = 0; k < nl + 2; ++k) hv[k] = 0;
 
   hipEvent_t ev0 = new_window ? e->ev_origin : e->ev_start;
   SF_HIP(hipEventRecord(ev0, e->s_comp));
+  if (e->lscale) SF_HIP(set_word(e->d_ovf, 0, e->s_comp));
   if (new_window) {
     e->host_t0 = now_ms();
     e->window_open = true;
@@ -942,11 +994,11 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   // device Adam of a resident head tensor: master/m/v at element offset `off`
   // of d_head_state's three regions, gradient at the same offset of hg
   const size_t NH = 2 * VH + d.H;
-  auto dev_adam = [&](size_t off, size_t n, void* out, hipStream_t st_) -> sf_status {
+  auto dev_adam = [&](size_t off, size_t n, void* out, hipStream_t st_, const AdamCoef& k,
+                      const int32_t* skip) -> sf_status {
     float* st = c.d_head_state;
-    const AdamCoef& k = e->coef;
     SF_HIP(adam_device(d.dtype, st + off, st + NH + off, st + 2 * NH + off, hg + off, out, static_cast<int64_t>(n),
-                       k.b1, k.b2, k.one_b1, k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, st_));
+                       k.b1, k.b2, k.one_b1, k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, st_, k.gscale, skip));
     return SF_OK;
   };
   // With the device Adam of the LM head, the head's last W_lm gradient GEMM
@@ -955,6 +1007,9 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   // start of the backward they would delay the first gradient range, which
   // host Adam waits for.
   const bool head_dev_adam = head && adam && !head_host;
+  // with loss scaling the head computes its whole W_lm gradient itself, so
+  // that it is checked before any layer's
+  const bool defer_dw = head_dev_adam && !e->lscale;
   hipEvent_t head_end = nullptr;
   auto head_update = [&](hipEvent_t mlp_done) -> sf_status {
     hipEvent_t ha = timing_event(e), hb = timing_event(e);
@@ -962,9 +1017,11 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     SF_HIP(hipStreamWaitEvent(e->s_head, head_end, 0));
     SF_HIP(hipStreamWaitEvent(e->s_head, mlp_done, 0));
     SF_HIP(hipEventRecord(ha, e->s_head));
-    if (sf_status r = head_last_dw(ctx, hg + VH + d.H, e->s_head)) return r;
-    if (sf_status r = dev_adam(VH, d.H, c.d_gf, e->s_head)) return r;
-    if (sf_status r = dev_adam(VH + d.H, VH, c.d_wlm, e->s_head)) return r;
+    if (defer_dw)
+      if (sf_status r = head_last_dw(ctx, hg + VH + d.H, e->s_head)) return r;
+    const int32_t* skip = e->lscale ? e->d_ovf_head : nullptr;
+    if (sf_status r = dev_adam(VH, d.H, c.d_gf, e->s_head, e->hcoef, skip)) return r;
+    if (sf_status r = dev_adam(VH + d.H, VH, c.d_wlm, e->s_head, e->hcoef, skip)) return r;
     SF_HIP(hipEventRecord(hb, e->s_head));
     SF_HIP(hipEventRecord(e->ev_head_done, e->s_head));
     return record_interval(e, ha, hb, 0, 0, kStSide);
@@ -975,9 +1032,18 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_head_done, 0));
     if ((rc = comp_begin(&a))) return rc;
     if ((rc = head_fwd_bwd(ctx, c.d_gf, c.d_wlm, xin[nl], ids, e->d_loss, e->dbuf, hg + VH, hg + VH + d.H,
-                           e->s_comp, head_dev_adam)))
+                           e->s_comp, defer_dw, e->scale)))
       return rc;
     SF_HIP(copy_f32(e->h_loss, e->d_loss, 1, e->s_comp));
+    if (e->lscale) {
+      // the head's gradients (final gain and LM head, contiguous) decide its
+      // own update and are the first part of every layer's verdict
+      SF_HIP(nonfinite_flag(hg + VH, static_cast<int64_t>(VH) + d.H, e->d_ovf, e->s_comp));
+      SF_HIP(copy_words(reinterpret_cast<uint32_t*>(e->d_ovf_head), reinterpret_cast<const uint32_t*>(e->d_ovf), 1,
+                        e->s_comp));
+      SF_HIP(copy_words(reinterpret_cast<uint32_t*>(hv + nl), reinterpret_cast<const uint32_t*>(e->d_ovf), 1,
+                        e->s_comp));
+    }
     if ((rc = comp_end(a, &b))) return rc;
     head_end = b;
     if (head_host) {
@@ -990,7 +1056,19 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
       }
     }
     dy = e->dbuf;
+  } else if (e->lscale) {
+    // the caller's upstream gradient times S seeds the backward
+    SF_HIP(scale_storage(d.dtype, d_dy, e->dbuf, static_cast<int64_t>(d.T) * d.H, e->scale, e->s_comp));
+    dy = e->dbuf;
   }
+  // loss scaling: each layer's fp32 gradient tensors (not the padding
+  // between them) are checked after its backward
+  FloatSegs gsegs{};
+  for (int t = 0; t < SF_NTENSORS; ++t) {
+    gsegs.off[t] = static_cast<int64_t>(e->L.grad_off[t] / 4);
+    gsegs.n[t] = static_cast<int64_t>(e->L.grad_bytes_t[t] / 4);
+  }
+  gsegs.count = SF_NTENSORS;
 
   // ---------------- backward: layer i in unit i % W, prefetch i - W + 1
   // (checkpointing: the input of layer i - 1 comes back meanwhile, and every
@@ -1019,6 +1097,13 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
                         ffn, wd)))
       return rc;
     if (head_dev_adam && i == nl - 1 && (rc = head_update(ffn))) return rc;
+    if (e->lscale) {
+      if (i == e->fault_nonfinite_layer) SF_HIP(set_word(e->d_ovf, 1, e->s_comp));
+      SF_HIP(nonfinite_flag_segs(reinterpret_cast<const float*>(e->ugrad[u]), gsegs, e->d_ovf, e->s_comp));
+      SF_HIP(copy_words(reinterpret_cast<uint32_t*>(hv + i), reinterpret_cast<const uint32_t*>(e->d_ovf), 1,
+                        e->s_comp));
+      SF_HIP(hipEventRecord(e->ev_verdict[i], e->s_comp));
+    }
     if (ck && i < nl - 1) SF_HIP(hipEventRecord(e->ev_cfree[i % 2], e->s_comp));
     if ((rc = comp_end(a, &b))) return rc;
     dy = e->dbuf;
@@ -1040,6 +1125,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     for (const auto& pt : parts) {
       for (size_t lo = pt.lo; lo < pt.hi; lo += e->chunk_bytes) {
         Job jb{kLayer, i, k, nullptr};
+        jb.verdict = e->lscale ? e->ev_verdict[i] : nullptr;
         jb.lo = lo;
         jb.hi = std::min(pt.hi, lo + e->chunk_bytes);
         if ((rc = timed_d2h(e, reinterpret_cast<char*>(c.h_grad_slots[k]) + lo, e->ugrad[u] + lo, jb.hi - lo,
@@ -1063,6 +1149,14 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   // zero gradient -- the same bits as Adam over the dense gradient, without
   // clearing, scattering and re-reading V x H fp32 values.
   const bool sparse_embed = adam && e->sp.total + static_cast<size_t>(d.V) <= VH;
+  // loss scaling: the embedding's gradient rows are sums of dx_0, so dx_0
+  // decides; the whole step's verdict is then final
+  if (e->lscale) {
+    if (head) SF_HIP(nonfinite_storage(d.dtype, e->dbuf, static_cast<int64_t>(d.T) * d.H, e->d_ovf, e->s_comp));
+    SF_HIP(copy_words(reinterpret_cast<uint32_t*>(hv + nl + 1), reinterpret_cast<const uint32_t*>(e->d_ovf), 1,
+                      e->s_comp));
+  }
+  const int32_t* embed_skip = e->lscale ? e->d_ovf : nullptr;
   if (head && !head_host) {
     if ((rc = comp_begin(&a))) return rc;
     if (sparse_embed) {
@@ -1070,13 +1164,13 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
       SF_HIP(embed_bwd_sparse(d.dtype, e->dbuf, ids, hgi + e->sp.ids, hg + e->sp.rows, hgi, hgi + e->sp.scratch,
                               static_cast<int>(d.T), d.H, d.V, e->s_comp));
       float* st = c.d_head_state;
-      const AdamCoef& k = e->coef;
+      const AdamCoef& k = e->ecoef;
       SF_HIP(embed_adam_sparse(d.dtype, st, st + NH, st + 2 * NH, hg + e->sp.rows, hgi + e->sp.ids, hgi,
                                hgi + e->sp.total, static_cast<int>(d.T), c.d_E, d.V, d.H, k.b1, k.b2, k.one_b1,
-                               k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, e->s_comp));
+                               k.one_b2, k.inv_bc1, k.inv_bc2, k.lr, k.eps, e->s_comp, k.gscale, embed_skip));
     } else {
       if ((rc = sf_embed_bwd(ctx, e->dbuf, ids, hg, e->s_comp))) return rc;
-      if (adam && (rc = dev_adam(0, VH, c.d_E, e->s_comp))) return rc;
+      if (adam && (rc = dev_adam(0, VH, c.d_E, e->s_comp, e->ecoef, embed_skip))) return rc;
     }
     if ((rc = comp_end(a, nullptr))) return rc;
   }
@@ -1097,6 +1191,32 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   }
 
   SF_HIP(hipStreamSynchronize(e->s_comp));
+  // The verdicts are published: count the updates each tensor applied (all
+  // of them without loss scaling) and move the loss scale for the next step.
+  e->last_scale = e->scale;
+  e->last_skipped = 0;
+  if (adam) {
+    for (int l = 0; l < nl; ++l) {
+      const bool skip = hv && hv[l] != 0;
+      e->adam_t[l] += skip ? 0 : 1;
+      e->last_skipped += skip ? 1 : 0;
+    }
+    if (head) {
+      const bool hs = hv && hv[nl] != 0, es = hv && hv[nl + 1] != 0;
+      e->head_t += hs ? 0 : 1;
+      e->embed_t += es ? 0 : 1;
+      e->last_skipped += (hs ? 1 : 0) + (es ? 1 : 0);
+    }
+  }
+  if (hv) {
+    if (hv[nl + 1] != 0) {
+      e->scale = std::max(1.0f, e->scale * 0.5f);
+      e->good_steps = 0;
+    } else if (++e->good_steps >= e->scale_window) {
+      if (std::isfinite(e->scale * 2.0f)) e->scale *= 2.0f;
+      e->good_steps = 0;
+    }
+  }
   // the units of layers 0 .. W-1 hold what the next forward reads first:
   // their updated parameters (Adam re-uploads them) or, with the
   // parameters fixed between steps, the ones the backward just used
@@ -1185,6 +1305,12 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   const bool pipe = (c.flags & SF_ENGINE_PIPELINE) != 0;
   if (pipe && head && head_host)
     return fail(SF_ERR_UNSUPPORTED, "SF_ENGINE_PIPELINE does not combine with SF_ENGINE_HEAD_HOST_ADAM");
+  const bool lscale = d.dtype == SF_F16;
+  if (lscale && head && head_host)
+    return fail(SF_ERR_UNSUPPORTED, "SF_F16 loss scaling does not combine with SF_ENGINE_HEAD_HOST_ADAM");
+  if (lscale && !(c.loss_scale >= 0.f && std::isfinite(c.loss_scale)))
+    return fail(SF_ERR_ARG, "loss_scale must be finite and >= 0 (0: the default)");
+  if (lscale && c.scale_window < 0) return fail(SF_ERR_ARG, "scale_window must be >= 0 (0: the default)");
   if (head && head_host) {
     if (!c.h_head_grads) return fail(SF_ERR_ARG, "SF_ENGINE_HEAD_HOST_ADAM needs h_head_grads");
     if (!is_pinned(c.h_head_grads)) return fail(SF_ERR_NOT_PINNED, "h_head_grads is not pinned");
@@ -1257,6 +1383,28 @@ sf_status sf_engine_create(sf_ctx* ctx, const sf_engine_cfg* cfg, sf_engine** ou
   }
   e->dbuf = act_p;
   e->d_loss = reinterpret_cast<float*>(act_p + e->x_bytes);
+  // the loss word's 256-byte tail also holds the loss-scaling flags
+  e->d_ovf = reinterpret_cast<int32_t*>(act_p + e->x_bytes + 64);
+  e->d_ovf_head = reinterpret_cast<int32_t*>(act_p + e->x_bytes + 128);
+  e->lscale = lscale;
+  e->scale = lscale ? (c.loss_scale > 0.f ? c.loss_scale : 65536.0f) : 1.0f;
+  e->scale_window = lscale && c.scale_window > 0 ? c.scale_window : 2000;
+  e->last_scale = e->scale;
+  e->adam_t.assign(c.n_layers, 0);
+  e->lcoef.assign(c.n_layers, AdamCoef{});
+  if (lscale) {
+    if (hipHostMalloc(reinterpret_cast<void**>(&e->h_ovf), 2 * (c.n_layers + 2) * sizeof(int32_t),
+                      hipHostMallocDefault) != hipSuccess)
+      return cleanup(fail(SF_ERR_HIP, "pinned loss-scaling flags allocation failed"));
+    std::memset(e->h_ovf, 0, 2 * (c.n_layers + 2) * sizeof(int32_t));
+    for (int l = 0; l < c.n_layers; ++l) {
+      hipEvent_t ev;
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+        return cleanup(fail(SF_ERR_HIP, "event creation failed"));
+      e->ev_verdict.push_back(ev);
+    }
+    if (const char* f = std::getenv("SF_FAULT_NONFINITE_LAYER")) e->fault_nonfinite_layer = std::atoi(f);
+  }
   if (hipHostMalloc(reinterpret_cast<void**>(&e->h_loss), 256, hipHostMallocDefault) != hipSuccess)
     return cleanup(fail(SF_ERR_HIP, "pinned loss word allocation failed"));
   *e->h_loss = 0.f;
@@ -1332,6 +1480,8 @@ sf_status sf_slide_step(sf_engine* e, const void* d_in, const void* d_dy, float*
   if (stats) {
     stats->wall_ms = now_ms() - t0;
     stats->loss = loss;
+    stats->loss_scale = e->last_scale;
+    stats->skipped = e->last_skipped;
   }
   return SF_OK;
 }
@@ -1410,16 +1560,17 @@ sf_status sf_engine_destroy(sf_engine* e) {
   for (hipStream_t s : {e->s_h2d, e->s_d2h, e->s_head})
     if (s) (void)hipStreamSynchronize(s);
   for (auto* v : {&e->ev_param_ready, &e->ev_param_free, &e->ev_grad_free, &e->ev_gslot_ready, &e->ev_gslot_free,
-                  &e->ev_ffn, &e->ev_wd, &e->tev_all})
+                  &e->ev_ffn, &e->ev_wd, &e->tev_all, &e->ev_verdict})
     for (hipEvent_t ev : *v) (void)hipEventDestroy(ev);
   for (hipEvent_t ev : {e->ev_xfree[0], e->ev_xfree[1], e->ev_xfree[2], e->ev_cready[0], e->ev_cready[1],
                         e->ev_cfree[0], e->ev_cfree[1], e->ev_ckpt_out, e->ev_head_done, e->ev_start, e->ev_origin})
     if (ev) (void)hipEventDestroy(ev);
   for (hipStream_t s : {e->s_h2d, e->s_d2h, e->own_head ? e->s_head : nullptr})
     if (s) (void)hipStreamDestroy(s);
-  if (e->h_loss) {
+  if (e->h_loss || e->h_ovf) {
     if (e->s_comp) (void)hipStreamSynchronize(e->s_comp);
-    (void)hipHostFree(e->h_loss);
+    if (e->h_loss) (void)hipHostFree(e->h_loss);
+    if (e->h_ovf) (void)hipHostFree(e->h_ovf);
   }
   delete e;
   return SF_OK;

@@ -194,8 +194,10 @@ template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* v) {
   if constexpr (sizeof(T) == 2) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    const uint4 w = make_uint4(u.x, u.y, 0u, 0u);
+    float f[8];
+    Elem<T>::unpack(w, f);
+    v[0] = f[0]; v[1] = f[1]; v[2] = f[2]; v[3] = f[3];
   } else {
     const float4 f = *reinterpret_cast<const float4*>(p);
     v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
@@ -244,7 +246,7 @@ constexpr int kPatchBytes = (E == Epi::SwigluFwd || E == Epi::Rope ? 2 * 16 * (W
 // same bits.  Caller: every wave done with the main loop's LDS (barrier),
 // g.rows_epi set (16-byte aligned outputs and operands, ldc, ldr and the
 // column count multiples of 8, no split-K partials).
-template <int WM, int WN, int FM, int FN, Epi E>
+template <typename T, int WM, int WN, int FM, int FN, Epi E>
 __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&acc)[FM][FN], int m0, int n0,
                                               int wm, int wn, int lane, float* patch) {
   constexpr bool PAIR = E == Epi::SwigluFwd || E == Epi::Rope;
@@ -277,8 +279,8 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&a
         const int m = mb + i * 16 + it * RPI;
         const int64_t ro = static_cast<int64_t>(m) * g.ldr + n;
         if (m < g.M && n_ok) {
-          dst[it][0] = *reinterpret_cast<const uint4*>(static_cast<const bf16*>(g.R) + ro);
-          if constexpr (NOP > 1) dst[it][1] = *reinterpret_cast<const uint4*>(static_cast<const bf16*>(g.R2) + ro);
+          dst[it][0] = *reinterpret_cast<const uint4*>(static_cast<const T*>(g.R) + ro);
+          if constexpr (NOP > 1) dst[it][1] = *reinterpret_cast<const uint4*>(static_cast<const T*>(g.R2) + ro);
         }
       }
     }
@@ -308,29 +310,29 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&a
       if (m >= g.M || !n_ok) continue;
       const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
       if constexpr (E == Epi::Store) {
-        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(o);
+        *reinterpret_cast<uint4*>(static_cast<T*>(g.C) + off) = Elem<T>::pack(o);
       } else if constexpr (E == Epi::StoreF32) {
         float* c = static_cast<float*>(g.C) + off;
         *reinterpret_cast<float4*>(c) = make_float4(o[0], o[1], o[2], o[3]);
         *reinterpret_cast<float4*>(c + 4) = make_float4(o[4], o[5], o[6], o[7]);
       } else if constexpr (E == Epi::Resid) {
         float rv[8];
-        Elem<bf16>::unpack(op[i & 1][it][0], rv);
+        Elem<T>::unpack(op[i & 1][it][0], rv);
 #pragma unroll
         for (int v = 0; v < 8; ++v) o[v] += rv[v];
-        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(o);
+        *reinterpret_cast<uint4*>(static_cast<T*>(g.C) + off) = Elem<T>::pack(o);
       } else if constexpr (E == Epi::SwigluBwd) {
         float G[8], U[8], dG[8], dU[8];
-        Elem<bf16>::unpack(op[i & 1][it][0], G);
-        Elem<bf16>::unpack(op[i & 1][it][1], U);
+        Elem<T>::unpack(op[i & 1][it][0], G);
+        Elem<T>::unpack(op[i & 1][it][1], U);
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           const float sg = sigmoid_f(G[v]);
           dG[v] = o[v] * U[v] * sg * (1.0f + G[v] * (1.0f - sg));
           dU[v] = o[v] * G[v] * sg;
         }
-        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(dG);
-        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C2) + off) = Elem<bf16>::pack(dU);
+        *reinterpret_cast<uint4*>(static_cast<T*>(g.C) + off) = Elem<T>::pack(dG);
+        *reinterpret_cast<uint4*>(static_cast<T*>(g.C2) + off) = Elem<T>::pack(dU);
       } else if constexpr (E == Epi::Rope) {
         // o: first members (columns n ..), u: partners (columns n + head_dim/2 ..)
         float u[8];
@@ -357,9 +359,9 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&a
 #pragma unroll
           for (int v = 0; v < 8; ++v) { o1[v] = o[v]; o2[v] = u[v]; }
         }
-        bf16* c = static_cast<bf16*>(g.C) + off;
-        *reinterpret_cast<uint4*>(c) = Elem<bf16>::pack(o1);
-        *reinterpret_cast<uint4*>(c + g.head_dim / 2) = Elem<bf16>::pack(o2);
+        T* c = static_cast<T*>(g.C) + off;
+        *reinterpret_cast<uint4*>(c) = Elem<T>::pack(o1);
+        *reinterpret_cast<uint4*>(c + g.head_dim / 2) = Elem<T>::pack(o2);
       } else {  // SwigluFwd: o = gate; up from the second plane
         float u[8], a[8];
         const f32x4 lo = *reinterpret_cast<const f32x4*>(patch + 16 * LDW + r * LDW + cc);
@@ -368,9 +370,9 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, const f32x4 (&a
         for (int v = 0; v < 4; ++v) { u[v] = lo[v]; u[4 + v] = hi[v]; }
 #pragma unroll
         for (int v = 0; v < 8; ++v) a[v] = silu_f(o[v]) * u[v];
-        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C) + off) = Elem<bf16>::pack(o);
-        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C2) + off) = Elem<bf16>::pack(u);
-        *reinterpret_cast<uint4*>(static_cast<bf16*>(g.C3) + off) = Elem<bf16>::pack(a);
+        *reinterpret_cast<uint4*>(static_cast<T*>(g.C) + off) = Elem<T>::pack(o);
+        *reinterpret_cast<uint4*>(static_cast<T*>(g.C2) + off) = Elem<T>::pack(u);
+        *reinterpret_cast<uint4*>(static_cast<T*>(g.C3) + off) = Elem<T>::pack(a);
       }
     }
   }
@@ -562,7 +564,7 @@ gemm_kernel(const GemmArgs g, int ntm, int ntn) {
   if constexpr (sizeof(T) == 2 && kRowsEpi<E, WN>) {
     static_assert(NW * kPatchBytes<WN, E> <= sizeof(smem), "row epilogue patches");
     if (g.rows_epi) {  // the loop ended with a barrier: the stages are free
-      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+      epilogue_rows<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
                                        reinterpret_cast<float*>(&smem[0][0]) + w * (kPatchBytes<WN, E> / 4));
       return;
     }
@@ -777,10 +779,10 @@ inline int64_t extent(int64_t rows, int64_t cols, int64_t ld) { return ((rows - 
 
 }  // namespace direct
 
-template <int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
+template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
-  using T = bf16;
+  static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
   constexpr bool AKC = (LAY != GemmLayout::TN);
   constexpr bool BKC = (LAY == GemmLayout::NT);
   constexpr int NW = (BM / WM) * (BN / WN);
@@ -857,7 +859,7 @@ gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes)
   if constexpr (kRowsEpi<E, WN>) {
     static_assert(NW * kPatchBytes<WN, E> <= sizeof(smem), "row epilogue patches");
     if (g.rows_epi) {  // the loop ended with a barrier: the stages are free
-      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+      epilogue_rows<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
                                        reinterpret_cast<float*>(smem) + w * (kPatchBytes<WN, E> / 4));
       return;
     }
@@ -870,10 +872,10 @@ gemm_direct_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes)
 // address is a constant.  The loads of stage kt + NS - 1 are issued after the
 // fragment reads of stage kt; the wait at the end of a stage lets the NS - 2
 // newer stages stay in flight.
-template <int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E, int NS>
+template <typename T, int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E, int NS>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
-  using T = bf16;
+  static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
   static_assert(NS >= 3 && NS <= 6, "3 to 6 stages");
   constexpr bool AKC = (LAY != GemmLayout::TN);
   constexpr bool BKC = (LAY == GemmLayout::NT);
@@ -977,7 +979,7 @@ gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
       if constexpr (KMAX >= 3) base = k == 3 ? S3 : base;
       if constexpr (KMAX >= 4) base = k == 4 ? S4 : base;
       if constexpr (KMAX >= 5) base = k == 5 ? S5 : base;
-      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+      epilogue_rows<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
                                        reinterpret_cast<float*>(base + (w % PER) * PB));
       return;
     }
@@ -992,10 +994,10 @@ gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
 // one wave feeding it while the other waits on memory.  A barrier separates
 // the phases; group 1 runs one phase behind group 0.  One fragment set per
 // wave suffices because a wave's own phases alternate.
-template <int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E, int NS>
+template <typename T, int BM, int BN, int WM, int WN, int BK, GemmLayout LAY, Epi E, int NS>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_pp_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
-  using T = bf16;
+  static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
   static_assert(NS >= 3 && NS <= 6, "3 to 6 stages");
   constexpr bool AKC = (LAY != GemmLayout::TN);
   constexpr bool BKC = (LAY == GemmLayout::NT);
@@ -1116,7 +1118,7 @@ gemm_pp_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
       if constexpr (KMAX >= 3) base = k == 3 ? S3 : base;
       if constexpr (KMAX >= 4) base = k == 4 ? S4 : base;
       if constexpr (KMAX >= 5) base = k == 5 ? S5 : base;
-      epilogue_rows<WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
+      epilogue_rows<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
                                        reinterpret_cast<float*>(base + (w % PER) * PB));
       return;
     }
@@ -1198,16 +1200,16 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
     g.rows_epi = ok ? 1 : 0;
   }
   if constexpr (KIND == 3) {
-    static_assert(sizeof(T) == 2, "direct loads are bf16 only");
-    hipLaunchKernelGGL((gemm_pp_kernel<BM, BN, WM, WN, BK, LAY, E, NS>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
-                       ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
+    static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
+    hipLaunchKernelGGL((gemm_pp_kernel<T, BM, BN, WM, WN, BK, LAY, E, NS>), dim3(ntm * ntn, S), dim3(NT), 0, s, g,
+                       ntm, ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
   } else if constexpr (KIND == 2) {
-    static_assert(sizeof(T) == 2, "direct loads are bf16 only");
-    hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, WM, WN, BK, LAY, E, NS>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
-                       ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
+    static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
+    hipLaunchKernelGGL((gemm_pipe_kernel<T, BM, BN, WM, WN, BK, LAY, E, NS>), dim3(ntm * ntn, S), dim3(NT), 0, s, g,
+                       ntm, ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
   } else if constexpr (KIND == 1) {
-    static_assert(sizeof(T) == 2, "direct loads are bf16 only");
-    hipLaunchKernelGGL((gemm_direct_kernel<BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
+    static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
+    hipLaunchKernelGGL((gemm_direct_kernel<T, BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm,
                        ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
   } else {
     hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm, ntn);
@@ -1336,8 +1338,9 @@ size_t gemm_splitk_bytes(int M, int N, int K) {
 
 hipError_t gemm(int dtype, GemmLayout layout, Epi epi, const GemmArgs& g, hipStream_t stream, float* ws,
                 size_t ws_bytes) {
-  if (dtype == 1) return dispatch<bf16>(layout, epi, g, stream, ws, ws_bytes);
-  return dispatch<float>(layout, epi, g, stream, ws, ws_bytes);
+  return with_storage(dtype, [&](auto tag) {
+    return dispatch<typename decltype(tag)::type>(layout, epi, g, stream, ws, ws_bytes);
+  });
 }
 
 }  // namespace sf

@@ -58,8 +58,10 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
 // sf_head_fwd_bwd; with defer_last_dw the LM-head weight gradient of the last
 // row chunk is left to head_last_dw, which reads the head workspace (dlogits,
 // hf) and must run before the context's next head pass.
+// grad_scale multiplies dlogits (and so every gradient of the head), not the loss.
 sf_status head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const void* d_x, const int32_t* d_ids,
-                       float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream, bool defer_last_dw);
+                       float* d_loss, void* d_dx, float* d_dgf, float* d_dwlm, sf_stream stream, bool defer_last_dw,
+                       float grad_scale = 1.0f);
 sf_status head_last_dw(sf_ctx* c, float* d_dwlm, sf_stream stream);
 }  // namespace sf
 

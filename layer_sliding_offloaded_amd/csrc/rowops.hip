@@ -8,6 +8,8 @@
 // floating-point atomics, so results are bitwise reproducible.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "rowops.h"
 
@@ -277,6 +279,75 @@ __global__ void __launch_bounds__(64) copy_f32_kernel(float* __restrict__ dst, c
   for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
 }
 
+__global__ void __launch_bounds__(64) copy_words_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                                       int n) {
+  for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
+}
+
+__global__ void __launch_bounds__(64) set_word_kernel(int32_t* __restrict__ p, int32_t v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
+// *flag = 1 when any of g[0 .. n) is an infinity or a NaN (an fp32 whose
+// exponent bits are all ones); it is never cleared here.  Only the value 1
+// is ever written, so the blocks' racing writes leave the same word.
+__global__ void __launch_bounds__(256)
+nonfinite_kernel(const float* __restrict__ g, int64_t n, int32_t* __restrict__ flag) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  bool bad = false;
+  const int64_t n4 = n / 4;
+  const uint4* g4 = reinterpret_cast<const uint4*>(g);
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < n4; q += stride) {
+    const uint4 w = g4[q];
+    const uint32_t e = 0x7F800000u;
+    bad |= ((w.x & e) == e) | ((w.y & e) == e) | ((w.z & e) == e) | ((w.w & e) == e);
+  }
+  for (int64_t i = n4 * 4 + static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride)
+    bad |= (__float_as_uint(g[i]) & 0x7F800000u) == 0x7F800000u;
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) *flag = 1;
+}
+
+// The same over up to kMaxSegs fp32 ranges of one buffer (blockIdx.y = range).
+__global__ void __launch_bounds__(256)
+nonfinite_segs_kernel(const float* __restrict__ base, FloatSegs segs, int32_t* __restrict__ flag) {
+  const int k = blockIdx.y;
+  const float* g = base + segs.off[k];
+  const int64_t n = segs.n[k];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  bool bad = false;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride)
+    bad |= (__float_as_uint(g[i]) & 0x7F800000u) == 0x7F800000u;
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) *flag = 1;
+}
+
+// *flag = 1 when any of n values of a 16-bit storage type is non-finite
+// (bf16: exponent bits 0x7F80 all ones; fp16: 0x7C00).
+template <typename T>
+__global__ void __launch_bounds__(256)
+nonfinite16_kernel(const uint16_t* __restrict__ x, int64_t n, int32_t* __restrict__ flag) {
+  constexpr uint32_t e = sizeof(T) == 2 && One16<T>::kBits == 0x3C00u ? 0x7C00u : 0x7F80u;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  bool bad = false;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride)
+    bad |= (static_cast<uint32_t>(x[i]) & e) == e;
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) *flag = 1;
+}
+
+// y = s x in the storage dtype (rounded once), n a multiple of 8.
+template <typename T>
+__global__ void __launch_bounds__(256)
+scale_kernel(const T* __restrict__ x, T* __restrict__ y, int64_t n, float sc) {
+  constexpr int VE = 16 / sizeof(T);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256 * VE;
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * VE; i < n; i += stride) {
+    float f[VE];
+    load_vec<T>(x + i, f);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) f[e] *= sc;
+    store_vec<T>(y + i, f);
+  }
+}
+
 // dE[id] = sum over t with ids[t] == id of dx0[t], in increasing t.  The
 // wave of token t does the work only if t is the first occurrence of its id;
 // it then walks the later tokens with a ballot per 64 ids.
@@ -433,10 +504,11 @@ template <typename TO>
 __global__ void __launch_bounds__(256)
 adam_device_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v, const float* __restrict__ g,
                    TO* __restrict__ out, int64_t n, float b1, float b2, float o1, float o2, float ib1, float ib2,
-                   float lr, float eps) {
+                   float lr, float eps, float gs, const int32_t* __restrict__ skip) {
   // no fused multiply-add; sqrtf and '/' are correctly rounded (HIP's default
   // for fp32), so every operation rounds exactly as the host loop's
 #pragma clang fp contract(off)
+  if (skip && *skip) return;  // loss scaling found a non-finite gradient: no update
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   // 4 elements a thread when every operand is 16-byte aligned (8 for a bf16
   // copy) while whole vectors remain, then one a thread for the tail (and for
@@ -459,7 +531,7 @@ adam_device_kernel(float* __restrict__ p, float* __restrict__ m, float* __restri
       float po[4], mo[4], vo[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float gi = gg[k];
+        const float gi = gg[k] * gs;
         const float mi = b1 * mm[k] + o1 * gi;
         const float vi = b2 * vv[k] + o2 * gi * gi;
         mo[k] = mi;
@@ -470,13 +542,12 @@ adam_device_kernel(float* __restrict__ p, float* __restrict__ m, float* __restri
       *reinterpret_cast<float4*>(p + i) = make_float4(po[0], po[1], po[2], po[3]);
       *reinterpret_cast<float4*>(m + i) = make_float4(mo[0], mo[1], mo[2], mo[3]);
       *reinterpret_cast<float4*>(v + i) = make_float4(vo[0], vo[1], vo[2], vo[3]);
-      if constexpr (kOut4) *reinterpret_cast<uint2*>(out + i) = make_uint2(pack2(po[0], po[1]), pack2(po[2], po[3]));
-      else *reinterpret_cast<float4*>(out + i) = make_float4(po[0], po[1], po[2], po[3]);
+      store4<TO>(out + i, po);
     }
     done = n4 * 4;
   }
   for (int64_t i = done + static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
-    const float gi = g[i];
+    const float gi = g[i] * gs;
     const float mi = b1 * m[i] + o1 * gi;
     const float vi = b2 * v[i] + o2 * gi * gi;
     m[i] = mi;
@@ -484,8 +555,7 @@ adam_device_kernel(float* __restrict__ p, float* __restrict__ m, float* __restri
     const float den = sqrtf(vi * ib2) + eps;
     const float pi = p[i] - lr * (mi * ib1) / den;
     p[i] = pi;
-    if constexpr (sizeof(TO) == 2) out[i].u = f2bf(pi);
-    else out[i] = pi;
+    Elem<TO>::store(out, i, pi);
   }
 }
 
@@ -514,8 +584,10 @@ template <typename TO>
 __global__ void __launch_bounds__(256)
 adam_rows_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
                  const float* __restrict__ rows, const int32_t* __restrict__ map, TO* __restrict__ out, int V, int H,
-                 float b1, float b2, float o1, float o2, float ib1, float ib2, float lr, float eps) {
+                 float b1, float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, float gs,
+                 const int32_t* __restrict__ skip) {
 #pragma clang fp contract(off)
+  if (skip && *skip) return;
   for (int r = blockIdx.x; r < V; r += gridDim.x) {
     const int sl = map[r];
     const int64_t base = static_cast<int64_t>(r) * H;
@@ -531,7 +603,7 @@ adam_rows_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict
       float po[4], mo[4], vo[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float gi = gg[k];
+        const float gi = gg[k] * gs;
         const float mi = b1 * mm[k] + o1 * gi;
         const float vi = b2 * vv[k] + o2 * gi * gi;
         mo[k] = mi;
@@ -542,11 +614,7 @@ adam_rows_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict
       *reinterpret_cast<float4*>(p + i) = make_float4(po[0], po[1], po[2], po[3]);
       *reinterpret_cast<float4*>(m + i) = make_float4(mo[0], mo[1], mo[2], mo[3]);
       *reinterpret_cast<float4*>(v + i) = make_float4(vo[0], vo[1], vo[2], vo[3]);
-      if constexpr (sizeof(TO) == 2) {
-        *reinterpret_cast<uint2*>(out + i) = make_uint2(pack2(po[0], po[1]), pack2(po[2], po[3]));
-      } else {
-        *reinterpret_cast<float4*>(out + i) = make_float4(po[0], po[1], po[2], po[3]);
-      }
+      store4<TO>(out + i, po);
     }
   }
 }
@@ -692,85 +760,68 @@ loss_reduce_kernel(const float* __restrict__ loss_rows, float* __restrict__ loss
 
 }  // namespace
 
-#define SF_DISPATCH(dtype, KERNEL, grid, block, stream, ...)                                          \
-  do {                                                                                                \
-    if ((dtype) == 1) hipLaunchKernelGGL(KERNEL<bf16>, grid, block, 0, stream, __VA_ARGS__);          \
-    else hipLaunchKernelGGL(KERNEL<float>, grid, block, 0, stream, __VA_ARGS__);                      \
-  } while (0)
+// Host dispatch: every row kernel exists for fp32, bf16 and fp16 storage.
+#define SF_T typename decltype(tag)::type
 
 hipError_t rmsnorm_fwd(int dtype, const void* x, const void* g, void* y, float* r, int rows, int H,
                        float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (dtype == 1)
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s,
-                       static_cast<const bf16*>(x), static_cast<const bf16*>(g), static_cast<bf16*>(y), r, rows, H, eps);
-  else
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s,
-                       static_cast<const float*>(x), static_cast<const float*>(g), static_cast<float*>(y), r, rows, H, eps);
-  return hipGetLastError();
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const T*>(x),
+                       static_cast<const T*>(g), static_cast<T*>(y), r, rows, H, eps);
+    return hipGetLastError();
+  });
 }
 
 hipError_t rmsnorm_bwd(int dtype, const void* dout, const void* xin, const float* r, const void* g,
                        const void* resid, void* dx, float* partial, int nchunks, float* dg, int rows, int H,
                        hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const int VE = dtype == 1 ? 8 : 4;
-  const int rpc = (rows + nchunks - 1) / nchunks;
-  // one pass (rows held in registers) when H is 64 lanes x VE x NV with NV
-  // <= 4 (more would leave one wave per SIMD: the two-kernel path is then
-  // faster)
-  const int nv = H % (64 * VE) ? 0 : H / (64 * VE);
-  if (nv >= 1 && nv <= 4) {
-#define SF_NB(NV)                                                                                              \
-  case NV:                                                                                                     \
-    if (dtype == 1)                                                                                            \
-      hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<bf16, NV>), dim3(nchunks), dim3(256), 0, s,                  \
-                         static_cast<const bf16*>(dout), static_cast<const bf16*>(xin), r,                     \
-                         static_cast<const bf16*>(g), static_cast<const bf16*>(resid), static_cast<bf16*>(dx), \
-                         partial, rows, H, rpc);                                                               \
-    else                                                                                                       \
-      hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<float, NV>), dim3(nchunks), dim3(256), 0, s,                 \
-                         static_cast<const float*>(dout), static_cast<const float*>(xin), r,                   \
-                         static_cast<const float*>(g), static_cast<const float*>(resid),                       \
-                         static_cast<float*>(dx), partial, rows, H, rpc);                                      \
-    break;
-    switch (nv) {
-      SF_NB(1) SF_NB(2) SF_NB(3) SF_NB(4)
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    constexpr int VE = 16 / sizeof(T);
+    const int rpc = (rows + nchunks - 1) / nchunks;
+    const T* d = static_cast<const T*>(dout);
+    const T* xi = static_cast<const T*>(xin);
+    const T* gg = static_cast<const T*>(g);
+    const T* rs = static_cast<const T*>(resid);
+    T* o = static_cast<T*>(dx);
+    // one pass (rows held in registers) when H is 64 lanes x VE x NV with NV
+    // <= 4 (more would leave one wave per SIMD: the two-kernel path is then
+    // faster)
+    const int nv = H % (64 * VE) ? 0 : H / (64 * VE);
+    if (nv >= 1 && nv <= 4) {
+      switch (nv) {
+        case 1: hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<T, 1>), dim3(nchunks), dim3(256), 0, s, d, xi, r, gg, rs, o,
+                                   partial, rows, H, rpc); break;
+        case 2: hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<T, 2>), dim3(nchunks), dim3(256), 0, s, d, xi, r, gg, rs, o,
+                                   partial, rows, H, rpc); break;
+        case 3: hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<T, 3>), dim3(nchunks), dim3(256), 0, s, d, xi, r, gg, rs, o,
+                                   partial, rows, H, rpc); break;
+        default: hipLaunchKernelGGL((rmsnorm_bwd_gain_kernel<T, 4>), dim3(nchunks), dim3(256), 0, s, d, xi, r, gg, rs,
+                                    o, partial, rows, H, rpc); break;
+      }
+    } else {
+      const dim3 pg((H / VE + 63) / 64, nchunks);
+      hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, d, xi, r, gg, rs, o, rows, H);
+      hipLaunchKernelGGL(gain_partial_kernel<T>, pg, dim3(64), 0, s, d, xi, r, partial, rows, H, rpc);
     }
-#undef SF_NB
-    hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + kReduceCols - 1) / kReduceCols), dim3(kReduceCols * kReduceGroups),
-                     0, s, partial, dg, nchunks, H);
+    hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + kReduceCols - 1) / kReduceCols),
+                       dim3(kReduceCols * kReduceGroups), 0, s, partial, dg, nchunks, H);
     return hipGetLastError();
-  }
-  const dim3 pg((H / VE + 63) / 64, nchunks);
-  if (dtype == 1) {
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s,
-                       static_cast<const bf16*>(dout), static_cast<const bf16*>(xin), r, static_cast<const bf16*>(g),
-                       static_cast<const bf16*>(resid), static_cast<bf16*>(dx), rows, H);
-    hipLaunchKernelGGL(gain_partial_kernel<bf16>, pg, dim3(64), 0, s, static_cast<const bf16*>(dout),
-                       static_cast<const bf16*>(xin), r, partial, rows, H, rpc);
-  } else {
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s,
-                       static_cast<const float*>(dout), static_cast<const float*>(xin), r, static_cast<const float*>(g),
-                       static_cast<const float*>(resid), static_cast<float*>(dx), rows, H);
-    hipLaunchKernelGGL(gain_partial_kernel<float>, pg, dim3(64), 0, s, static_cast<const float*>(dout),
-                       static_cast<const float*>(xin), r, partial, rows, H, rpc);
-  }
-  hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + kReduceCols - 1) / kReduceCols), dim3(kReduceCols * kReduceGroups),
-                     0, s, partial, dg, nchunks, H);
-  return hipGetLastError();
+  });
 }
 
 hipError_t embed_fwd(int dtype, const void* E, const int32_t* ids, void* x0, int rows, int H, int V,
                      hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (dtype == 1)
-    hipLaunchKernelGGL(embed_fwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const bf16*>(E),
-                       ids, static_cast<bf16*>(x0), rows, H, V);
-  else
-    hipLaunchKernelGGL(embed_fwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const float*>(E),
-                       ids, static_cast<float*>(x0), rows, H, V);
-  return hipGetLastError();
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    hipLaunchKernelGGL(embed_fwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const T*>(E), ids,
+                       static_cast<T*>(x0), rows, H, V);
+    return hipGetLastError();
+  });
 }
 
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
@@ -790,13 +841,12 @@ hipError_t embed_bwd(int dtype, const void* dx0, const int32_t* ids, float* dE, 
                      hipStream_t s) {
   hipError_t e = fill_f32(dE, static_cast<int64_t>(V) * H, 0.f, s);
   if (e != hipSuccess || rows <= 0) return e;
-  if (dtype == 1)
-    hipLaunchKernelGGL(embed_bwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const bf16*>(dx0),
-                       ids, dE, rows, H, V);
-  else
-    hipLaunchKernelGGL(embed_bwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const float*>(dx0),
-                       ids, dE, rows, H, V);
-  return hipGetLastError();
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    hipLaunchKernelGGL(embed_bwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const T*>(dx0), ids,
+                       dE, rows, H, V);
+    return hipGetLastError();
+  });
 }
 
 hipError_t embed_bwd_sparse(int dtype, const void* dx0, const int32_t* ids, int32_t* out_ids, float* out_rows,
@@ -807,31 +857,31 @@ hipError_t embed_bwd_sparse(int dtype, const void* dx0, const int32_t* ids, int3
   const dim3 g((rows + 3) / 4);
   hipLaunchKernelGGL(embed_first_kernel, g, dim3(256), 0, s, ids, first, rows, V);
   hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, first, slot, count, rows);
-  if (dtype == 1)
-    hipLaunchKernelGGL(embed_rows_kernel<bf16>, g, dim3(256), 0, s, static_cast<const bf16*>(dx0), ids, first, slot,
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    hipLaunchKernelGGL(embed_rows_kernel<T>, g, dim3(256), 0, s, static_cast<const T*>(dx0), ids, first, slot,
                        out_ids, out_rows, rows, H);
-  else
-    hipLaunchKernelGGL(embed_rows_kernel<float>, g, dim3(256), 0, s, static_cast<const float*>(dx0), ids, first,
-                       slot, out_ids, out_rows, rows, H);
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 hipError_t adam_device(int dtype, float* p, float* m, float* v, const float* g, void* out, int64_t n, float b1,
-                       float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s) {
+                       float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s,
+                       float gscale, const int32_t* skip) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 32);
-  if (dtype == 1)
-    hipLaunchKernelGGL(adam_device_kernel<bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, m, v, g,
-                       static_cast<bf16*>(out), n, b1, b2, o1, o2, ib1, ib2, lr, eps);
-  else
-    hipLaunchKernelGGL(adam_device_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, m, v, g,
-                       static_cast<float*>(out), n, b1, b2, o1, o2, ib1, ib2, lr, eps);
-  return hipGetLastError();
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    hipLaunchKernelGGL(adam_device_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, m, v, g,
+                       static_cast<T*>(out), n, b1, b2, o1, o2, ib1, ib2, lr, eps, gscale, skip);
+    return hipGetLastError();
+  });
 }
 
 hipError_t embed_adam_sparse(int dtype, float* p, float* m, float* v, const float* rows, const int32_t* out_ids,
                              const int32_t* count, int32_t* map, int max_rows, void* out, int V, int H, float b1,
-                             float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s) {
+                             float b2, float o1, float o2, float ib1, float ib2, float lr, float eps, hipStream_t s,
+                             float gscale, const int32_t* skip) {
   if (V <= 0 || H <= 0) return hipSuccess;
   if (H % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(row_map_clear_kernel, dim3((V + 255) / 256), dim3(256), 0, s, map, V);
@@ -839,47 +889,95 @@ hipError_t embed_adam_sparse(int dtype, float* p, float* m, float* v, const floa
     hipLaunchKernelGGL(row_map_set_kernel, dim3((max_rows + 255) / 256), dim3(256), 0, s, out_ids, count, map,
                        max_rows, V);
   const dim3 grid(static_cast<unsigned>(std::min(V, 8192)));
-  if (dtype == 1)
-    hipLaunchKernelGGL(adam_rows_kernel<bf16>, grid, dim3(256), 0, s, p, m, v, rows, map, static_cast<bf16*>(out), V,
-                       H, b1, b2, o1, o2, ib1, ib2, lr, eps);
-  else
-    hipLaunchKernelGGL(adam_rows_kernel<float>, grid, dim3(256), 0, s, p, m, v, rows, map, static_cast<float*>(out),
-                       V, H, b1, b2, o1, o2, ib1, ib2, lr, eps);
-  return hipGetLastError();
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    hipLaunchKernelGGL(adam_rows_kernel<T>, grid, dim3(256), 0, s, p, m, v, rows, map, static_cast<T*>(out), V, H, b1,
+                       b2, o1, o2, ib1, ib2, lr, eps, gscale, skip);
+    return hipGetLastError();
+  });
 }
 
 hipError_t ce_rows(int dtype, const float* logits, const int32_t* ids, void* dlogits, float* loss_rows, int t0,
                    int R, int V, int S, float inv_n, hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  // whole row in registers when V fits 1024 threads x NV 16-byte vectors
-  const int nv = V % 4 ? 0 : (V + 4095) / 4096;
-#define SF_CE_REG(NV)                                                                                          \
-  if (nv <= NV) {                                                                                              \
-    if (dtype == 1)                                                                                            \
-      hipLaunchKernelGGL((ce_rows_reg_kernel<bf16, NV>), dim3(R), dim3(1024), 0, s, logits, ids,              \
-                         static_cast<bf16*>(dlogits), loss_rows, t0, V, S, inv_n);                             \
-    else                                                                                                       \
-      hipLaunchKernelGGL((ce_rows_reg_kernel<float, NV>), dim3(R), dim3(1024), 0, s, logits, ids,             \
-                         static_cast<float*>(dlogits), loss_rows, t0, V, S, inv_n);                            \
-    return hipGetLastError();                                                                                  \
-  }
-  if (nv > 0) {
-    SF_CE_REG(8)
-    SF_CE_REG(16)
-  }
-#undef SF_CE_REG
-  if (dtype == 1)
-    hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(R), dim3(256), 0, s, logits, ids, static_cast<bf16*>(dlogits),
-                       loss_rows, t0, R, V, S, inv_n);
-  else
-    hipLaunchKernelGGL(ce_rows_kernel<float>, dim3(R), dim3(256), 0, s, logits, ids, static_cast<float*>(dlogits),
-                       loss_rows, t0, R, V, S, inv_n);
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    T* dl = static_cast<T*>(dlogits);
+    // whole row in registers when V fits 1024 threads x NV 16-byte vectors
+    const int nv = V % 4 ? 0 : (V + 4095) / 4096;
+    if (nv > 0 && nv <= 8)
+      hipLaunchKernelGGL((ce_rows_reg_kernel<T, 8>), dim3(R), dim3(1024), 0, s, logits, ids, dl, loss_rows, t0, V, S,
+                         inv_n);
+    else if (nv > 0 && nv <= 16)
+      hipLaunchKernelGGL((ce_rows_reg_kernel<T, 16>), dim3(R), dim3(1024), 0, s, logits, ids, dl, loss_rows, t0, V,
+                         S, inv_n);
+    else
+      hipLaunchKernelGGL(ce_rows_kernel<T>, dim3(R), dim3(256), 0, s, logits, ids, dl, loss_rows, t0, R, V, S, inv_n);
+    return hipGetLastError();
+  });
+}
+
+hipError_t copy_words(uint32_t* dst, const uint32_t* src, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_words_kernel, dim3(1), dim3(64), 0, s, dst, src, n);
   return hipGetLastError();
+}
+
+hipError_t set_word(int32_t* p, int32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, s, p, v);
+  return hipGetLastError();
+}
+
+hipError_t nonfinite_flag(const float* g, int64_t n, int32_t* flag, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (reinterpret_cast<uintptr_t>(g) & 15u) return hipErrorInvalidValue;
+  const int64_t blocks = std::min<int64_t>((n / 4 + 255) / 256 + 1, 256 * 8);
+  hipLaunchKernelGGL(nonfinite_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g, n, flag);
+  return hipGetLastError();
+}
+
+hipError_t nonfinite_flag_segs(const float* base, const FloatSegs& segs, int32_t* flag, hipStream_t s) {
+  if (segs.count <= 0 || segs.count > kMaxSegs) return segs.count == 0 ? hipSuccess : hipErrorInvalidValue;
+  int64_t nmax = 0;
+  for (int k = 0; k < segs.count; ++k) nmax = std::max(nmax, segs.n[k]);
+  if (nmax <= 0) return hipSuccess;
+  const int64_t bx = std::min<int64_t>((nmax + 255) / 256, 512);
+  hipLaunchKernelGGL(nonfinite_segs_kernel, dim3(static_cast<unsigned>(bx), segs.count), dim3(256), 0, s, base, segs,
+                     flag);
+  return hipGetLastError();
+}
+
+hipError_t nonfinite_storage(int dtype, const void* x, int64_t n, int32_t* flag, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == 0) return nonfinite_flag(static_cast<const float*>(x), n, flag, s);
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 8);
+  if (dtype == 2)
+    hipLaunchKernelGGL(nonfinite16_kernel<f16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(x), n, flag);
+  else
+    hipLaunchKernelGGL(nonfinite16_kernel<bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(x), n, flag);
+  return hipGetLastError();
+}
+
+hipError_t scale_storage(int dtype, const void* x, void* y, int64_t n, float sc, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  return with_storage(dtype, [&](auto tag) {
+    using T = SF_T;
+    constexpr int VE = 16 / sizeof(T);
+    const int64_t blocks = std::min<int64_t>((n / VE + 255) / 256, 256 * 16);
+    hipLaunchKernelGGL(scale_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, static_cast<const T*>(x),
+                       static_cast<T*>(y), n, sc);
+    return hipGetLastError();
+  });
 }
 
 hipError_t loss_reduce(const float* loss_rows, float* loss, int rows, float inv_n, hipStream_t s) {
   hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, loss_rows, loss, rows, inv_n);
   return hipGetLastError();
 }
+
+#undef SF_T
 
 }  // namespace sf

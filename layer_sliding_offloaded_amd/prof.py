@@ -372,7 +372,7 @@ def rowops(db_path, workload):
     sys.path.insert(0, os.path.dirname(HERE))
     import seeded_inputs as si
     w = si.WORKLOADS[workload]
-    e = 2 if w.dtype == "bf16" else 4
+    e = 4 if w.dtype == "f32" else 2
     T, H, V = w.tokens, w.hidden, w.vocab
     nq = w.n_heads * w.head_dim
     R = min(T, 2048)  # head chunk rows bench.py uses

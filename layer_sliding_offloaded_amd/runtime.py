@@ -15,11 +15,18 @@ def shape_from(w, batch=None, seq=None):
     """sf_shape for a workload-like object (fields of seeded_inputs.Workload)."""
     return sf.make_shape(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn, w.vocab,
                          batch if batch is not None else w.batch, seq if seq is not None else w.seq,
-                         w.eps, w.rope_base, sf.SF_BF16 if w.dtype == "bf16" else sf.SF_F32)
+                         w.eps, w.rope_base, sf_dtype(w))
+
+
+DTYPES = {"f32": (sf.SF_F32, torch.float32), "bf16": (sf.SF_BF16, torch.bfloat16), "f16": (sf.SF_F16, torch.float16)}
+
+
+def sf_dtype(w):
+    return DTYPES[w.dtype][0]
 
 
 def storage_dtype(w):
-    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return DTYPES[w.dtype][1]
 
 
 def device_bytes(n, device="cuda"):
@@ -71,7 +78,6 @@ def unpack_params(layout, flat_bytes, shapes, w):
     """Storage-dtype flat parameter buffer (CPU uint8 tensor) -> dict of float32 arrays."""
     out = {}
     dt = storage_dtype(w)
-    es = 2 if w.dtype == "bf16" else 4
     for i, name in enumerate(TENSORS):
         o, nb = layout.off[i], layout.bytes[i]
         t = flat_bytes[o:o + nb].view(dt).to(torch.float32)
@@ -126,11 +132,13 @@ class Engine:
     moments or gradient slots).
     keep_turnaround: without Adam, layers 0..window-1 stay in their units from
     one step's backward to the next step's forward (h_params unchanged).
+    loss_scale, scale_window: fp16 storage's dynamic loss scaling (initial
+    scale and growth window; 0 takes the library's defaults).
     """
 
     def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
                  adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False, pipeline=False,
-                 draw_threads=1, keep_turnaround=False):
+                 draw_threads=1, keep_turnaround=False, loss_scale=0.0, scale_window=0):
         import ctypes
         from concurrent.futures import ThreadPoolExecutor
         hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
@@ -158,7 +166,7 @@ class Engine:
         act = sf.sf_engine_act_bytes_flags(shape, self.nl, flags)
         self.act = device_bytes(act)
         self.act_bytes = act
-        ebytes = 2 if w.dtype == "bf16" else 4
+        ebytes = 4 if w.dtype == "f32" else 2
         self.x_bytes = (shape.batch * shape.seq * shape.hidden * ebytes + 255) // 256 * 256
         self.h_ckpt = pinned_bytes(max(self.nl - 1, 1) * self.x_bytes) if ckpt else None
         def stage(l):
@@ -196,6 +204,7 @@ class Engine:
             cfg.h_v = parr([m.ctypes.data for m in self.h_v])
         cfg.h_grad_slots = parr([t.data_ptr() for t in self.h_slots])
         cfg.compute_stream = self.stream.cuda_stream
+        cfg.loss_scale, cfg.scale_window = loss_scale, scale_window
         if ckpt:
             cfg.h_ckpt = self.h_ckpt.data_ptr()
         if head is not None:

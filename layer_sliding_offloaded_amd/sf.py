@@ -25,6 +25,7 @@ SF_ERR_NO_DEVICE = -8
 
 SF_F32 = 0
 SF_BF16 = 1
+SF_F16 = 2
 
 SF_WQ, SF_WK, SF_WV, SF_WO, SF_WG, SF_WU, SF_WD, SF_G1, SF_G2 = range(9)
 TENSOR_NAMES = ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd", "g1", "g2")
@@ -64,7 +65,8 @@ class SfEngineCfg(ctypes.Structure):
                 ("h_grad_slots", ctypes.POINTER(_vp)), ("compute_stream", _vp),
                 ("d_E", _vp), ("d_gf", _vp), ("d_wlm", _vp), ("d_head_grads", _vp),
                 ("h_head_params", _vp), ("h_head_master", _vp), ("h_head_m", _vp), ("h_head_v", _vp),
-                ("h_head_grads", _vp), ("d_head_state", _vp), ("h_ckpt", _vp)]
+                ("h_head_grads", _vp), ("d_head_state", _vp), ("h_ckpt", _vp),
+                ("loss_scale", ctypes.c_float), ("scale_window", ctypes.c_int32)]
 
 
 class SfStepStats(ctypes.Structure):
@@ -72,7 +74,7 @@ class SfStepStats(ctypes.Structure):
                 ("h2d_ms", ctypes.c_double), ("d2h_ms", ctypes.c_double), ("overlap_pct", ctypes.c_double),
                 ("busy_ms", ctypes.c_double), ("span_ms", ctypes.c_double), ("adam_ms", ctypes.c_double), ("h2d_bytes", ctypes.c_double),
                 ("d2h_bytes", ctypes.c_double), ("h2d_gbps", ctypes.c_double), ("d2h_gbps", ctypes.c_double),
-                ("loss", ctypes.c_float)]
+                ("loss", ctypes.c_float), ("loss_scale", ctypes.c_float), ("skipped", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -86,6 +88,7 @@ class SfError(RuntimeError):
 
 EXPORTS = (
     "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
+    "sf_head_fwd_bwd_scaled", "sf_adam_host_ex", "sf_adam_device_ex",
     "sf_gemm", "sf_gemm_workspace_bytes", "sf_gemm_noalloc", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_act_bytes_flags", "sf_engine_create", "sf_slide_step",
     "sf_engine_sync", "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_counters",
     "sf_engine_destroy", "sf_last_error",
@@ -110,6 +113,11 @@ def load():
         "sf_layer_fwd": [P, P, P, P, P, P],
         "sf_layer_bwd": [P, P, P, P, P, P, P, P],
         "sf_head_fwd_bwd": [P, P, P, P, P, P, P, P, P, P],
+        "sf_head_fwd_bwd_scaled": [P, P, P, P, P, P, P, P, P, ctypes.c_float, P],
+        "sf_adam_host_ex": [i32, P, P, P, P, P, _size_t, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                            ctypes.c_float, ctypes.c_float, ctypes.c_float, i32],
+        "sf_adam_device_ex": [i32, P, P, P, P, P, _size_t, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                              ctypes.c_float, ctypes.c_float, ctypes.c_float, P],
         "sf_gemm": [i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int64,
                     P, _size_t, P],
         "sf_gemm_noalloc": [i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, ctypes.c_int64, P,
@@ -184,6 +192,20 @@ def sf_layer_bwd(ctx, d_w, d_x, d_saved, d_dy, d_dx, d_dw, stream):
 
 def sf_head_fwd_bwd(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream):
     _check(load().sf_head_fwd_bwd(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, stream))
+
+
+def sf_head_fwd_bwd_scaled(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, grad_scale, stream):
+    _check(load().sf_head_fwd_bwd_scaled(ctx, d_gf, d_wlm, d_x, d_ids, d_loss, d_dx, d_dgf, d_dwlm, grad_scale,
+                                         stream))
+
+
+def sf_adam_host_ex(dtype, p, m, v, g, p_out, n, step, lr, b1, b2, eps, grad_scale=1.0, n_threads=0):
+    """Host pointers (ints); p_out (storage copy) may be None for fp32."""
+    _check(load().sf_adam_host_ex(dtype, p, m, v, g, p_out, n, step, lr, b1, b2, eps, grad_scale, n_threads))
+
+
+def sf_adam_device_ex(dtype, d_p, d_m, d_v, d_g, d_out, n, step, lr, b1, b2, eps, grad_scale, stream):
+    _check(load().sf_adam_device_ex(dtype, d_p, d_m, d_v, d_g, d_out, n, step, lr, b1, b2, eps, grad_scale, stream))
 
 
 def sf_gemm(dtype, layout, out_f32, M, N, K, d_A, lda, d_B, ldb, d_C, ldc, stream, d_ws=None, ws_bytes=0):

@@ -34,7 +34,7 @@ class Workload:
     batch: int
     seq: int
     n_layers: int
-    dtype: str          # "f32" or "bf16"
+    dtype: str          # "f32", "bf16" or "f16"
     window: int = 2
     eps: float = 1e-6
     rope_base: float = 10000.0
@@ -96,6 +96,8 @@ def to_storage(a, dtype):
         return a
     if dtype == "bf16":
         return bf16_bits_to_f32(f32_to_bf16_bits(a))
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float32)   # IEEE round to nearest even
     raise ValueError(dtype)
 
 

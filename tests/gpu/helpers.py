@@ -76,12 +76,14 @@ def layer_errors(w, p, x, dy, y, dx, g):
     for k in go:
         errs["d" + k] = rel(g[k], go[k])
     # The residual stream is stored in the storage dtype twice per layer (h
-    # and y; dh and dx), each rounding within 2^-9 relative, so a delta can
-    # be no more precise than 2^-8 |y| in bf16: the delta checks get that
-    # floor, expressed relative to the delta's own norm.
-    if w.dtype == "bf16":
-        errs["floor:y-x"] = 2.0 ** -8 * np.linalg.norm(yo) / np.linalg.norm(yo - x)
-        errs["floor:dx-dy"] = 2.0 ** -8 * np.linalg.norm(dxo) / np.linalg.norm(dxo - dy)
+    # and y; dh and dx), each rounding within half an ulp (2^-9 relative in
+    # bf16, 2^-12 in fp16), so a delta can be no more precise than 2^-8 |y|
+    # in bf16 (2^-11 |y| in fp16): the delta checks get that floor, expressed
+    # relative to the delta's own norm.
+    ulp = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}.get(w.dtype)
+    if ulp:
+        errs["floor:y-x"] = ulp * np.linalg.norm(yo) / np.linalg.norm(yo - x)
+        errs["floor:dx-dy"] = ulp * np.linalg.norm(dxo) / np.linalg.norm(dxo - dy)
     if w.seq == 1:
         # one key per query: softmax is constant, dq and dk vanish exactly;
         # bound their gradients against the scale of dWv instead
@@ -112,3 +114,80 @@ def make_layer_case(w, seed_layer=0, gains="random", scale=1.0):
     x = si.layer_input(w, scale=scale)
     dy = si.upstream_grad(w, scale=scale)
     return p, x, dy
+
+
+def stack_inputs(w):
+    """Seeded layers (random gains), embedding / final gain / LM head and ids of a stack."""
+    layers = [si.layer_params(w, l, gains="random") for l in range(w.n_layers)]
+    head = dict(E=si.embedding(w), gf=si.final_gain(w, gains="random"), Wlm=si.lm_head(w))
+    return layers, head, si.token_ids(w)
+
+
+def oracle_trajectory(w, layers, head, ids, steps, hp, rnd):
+    """`steps` oracle iterations of a stack: stack_step at the current
+    (storage-rounded) weights, fp64 Adam on every tensor, then the next
+    step's weights as rnd() of the fp64 masters (round_bf16 / round_f16).
+    Returns per step: loss, layer and head gradients, masters after Adam."""
+    sh = oracle_shape(w)
+    lay = [f64(p) for p in layers]
+    hd = f64(head)
+    mlay = [{k: v.copy() for k, v in p.items()} for p in lay]
+    mhd = {k: v.copy() for k, v in hd.items()}
+    st_l = [{k: (np.zeros_like(v), np.zeros_like(v)) for k, v in p.items()} for p in lay]
+    st_h = {k: (np.zeros_like(v), np.zeros_like(v)) for k, v in hd.items()}
+    out = []
+    for t in range(1, steps + 1):
+        say("oracle step", t)
+        loss, lg, dE, dgf, dWlm = oracle.stack_step(lay, hd["E"], hd["gf"], hd["Wlm"], ids, sh)
+        out.append(dict(loss=loss, layers=lg, head=dict(E=dE, gf=dgf, Wlm=dWlm)))
+        for i in range(len(lay)):
+            mlay[i] = oracle.model.adam_all(mlay[i], lg[i], st_l[i], t, hp["lr"], hp["b1"], hp["b2"], hp["eps"])
+            lay[i] = {k: rnd(v) for k, v in mlay[i].items()}
+        mhd = oracle.model.adam_all(mhd, dict(E=dE, gf=dgf, Wlm=dWlm), st_h, t, hp["lr"], hp["b1"], hp["b2"],
+                                    hp["eps"])
+        hd = {k: rnd(v) for k, v in mhd.items()}
+        out[-1]["master_layers"] = [{k: v.copy() for k, v in p.items()} for p in mlay]
+        out[-1]["master_head"] = {k: v.copy() for k, v in mhd.items()}
+    return out
+
+
+def oracle_trajectory_skips(w, layers, head, ids, steps, hp, rnd, nonfinite):
+    """Like oracle_trajectory, with fp16's loss-scaling skip rule: at step t,
+    nonfinite(t) -> (head_bad, [layer_bad for layer 0 .. L-1]) says where a
+    non-finite gradient appeared; oracle.applied_updates decides which groups
+    update (oracle.adam_with_skip: a skipped group keeps tensor, moments and
+    step count).  Returns per step: loss, gradients, masters after the step
+    and the applied groups."""
+    sh = oracle_shape(w)
+    lay = [f64(p) for p in layers]
+    hd = f64(head)
+    mlay = [{k: v.copy() for k, v in p.items()} for p in lay]
+    mhd = {k: v.copy() for k, v in hd.items()}
+    st_l = [{k: [np.zeros_like(v), np.zeros_like(v), 0] for k, v in p.items()} for p in lay]
+    st_h = {k: [np.zeros_like(v), np.zeros_like(v), 0] for k, v in hd.items()}
+    a = (hp["lr"], hp["b1"], hp["b2"], hp["eps"])
+
+    def upd(master, st, grads, apply):
+        for k in master:
+            m, v, t = st[k]
+            master[k], st[k][0], st[k][1], st[k][2] = oracle.adam_with_skip(master[k], m, v, t, grads[k], apply, *a)
+
+    out = []
+    for t in range(1, steps + 1):
+        say("oracle step", t)
+        loss, lg, dE, dgf, dWlm = oracle.stack_step(lay, hd["E"], hd["gf"], hd["Wlm"], ids, sh)
+        head_bad, layer_bad = nonfinite(t)
+        ah, al, ae = oracle.applied_updates(head_bad, layer_bad)
+        for i in range(len(lay)):
+            upd(mlay[i], st_l[i], lg[i], al[i])
+            lay[i] = {k: rnd(v) for k, v in mlay[i].items()}
+        # the head's groups: final gain and LM head (ah), embedding (ae)
+        hg = dict(E=dE, gf=dgf, Wlm=dWlm)
+        for k, ok in (("gf", ah), ("Wlm", ah), ("E", ae)):
+            m, v, tk = st_h[k]
+            mhd[k], st_h[k][0], st_h[k][1], st_h[k][2] = oracle.adam_with_skip(mhd[k], m, v, tk, hg[k], ok, *a)
+        hd = {k: rnd(v) for k, v in mhd.items()}
+        out.append(dict(loss=loss, layers=lg, head=dict(E=dE, gf=dgf, Wlm=dWlm),
+                        master_layers=[{k: v.copy() for k, v in p.items()} for p in mlay],
+                        master_head={k: v.copy() for k, v in mhd.items()}, applied=(ah, al, ae)))
+    return out

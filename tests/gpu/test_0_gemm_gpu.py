@@ -20,18 +20,25 @@ SHAPES = [(128, 256, 64), (200, 688, 256), (1000, 520, 1376), (37, 8, 8), (4096,
 
 
 @pytest.mark.parametrize("layout", [0, 1, 2], ids=["NT", "NN", "TN"])
-@pytest.mark.parametrize("dtype", [sf.SF_F32, sf.SF_BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", [sf.SF_F32, sf.SF_BF16, sf.SF_F16], ids=["f32", "bf16", "f16"])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_gemm_parity(layout, dtype, M, N, K):
-    if layout == 2 and M % 8:
-        pytest.skip("TN needs M % 8 == 0 (M is A's contiguous dimension)")
-    if layout == 0 and K % 8 or layout == 1 and K % 8:
-        pytest.skip("A's contiguous dimension K must be a multiple of 8")
     say("gemm", layout, dtype, M, N, K)
     rng = np.random.default_rng(M * 7 + N * 3 + K)
-    tdt = torch.bfloat16 if dtype == sf.SF_BF16 else torch.float32
+    tdt = {sf.SF_F32: torch.float32, sf.SF_BF16: torch.bfloat16, sf.SF_F16: torch.float16}[dtype]
     a_shape = (K, M) if layout == 2 else (M, K)
     b_shape = (N, K) if layout == 0 else (K, N)
+    if a_shape[1] % 8:
+        # out of contract (A's contiguous dimension: M for TN, K otherwise):
+        # refused on the host before any device work
+        dA = torch.zeros(a_shape, dtype=tdt, device="cuda")
+        dB = torch.zeros(b_shape, dtype=tdt, device="cuda")
+        C = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+        with pytest.raises(sf.SfError) as e:
+            sf.sf_gemm(dtype, layout, 1, M, N, K, dA.data_ptr(), a_shape[1], dB.data_ptr(), b_shape[1],
+                       C.data_ptr(), N, rt.stream_handle(), None, 0)
+        assert e.value.code == sf.SF_ERR_UNSUPPORTED
+        return
     A = torch.from_numpy(rng.standard_normal(a_shape, dtype=np.float32)).to(tdt)
     B = torch.from_numpy(rng.standard_normal(b_shape, dtype=np.float32)).to(tdt)
     a64 = A.double().numpy()
@@ -51,6 +58,7 @@ def test_gemm_parity(layout, dtype, M, N, K):
         # fp32 accumulation over K terms: relative error ~ sqrt(K) 2^-24 (1e-5 at K = 32000)
         tol = 1e-5
         assert rel(out[split, 1], ref) <= tol, (split, rel(out[split, 1], ref))
-        # storage-dtype output: one more rounding of the fp32 result (bf16: 2^-9)
-        tol_s = 1e-5 if dtype == sf.SF_F32 else 4e-3
+        # storage-dtype output: one more rounding of the fp32 result (bf16:
+        # 2^-9, fp16: 2^-12 relative at most)
+        tol_s = {sf.SF_F32: 1e-5, sf.SF_BF16: 4e-3, sf.SF_F16: 5e-4}[dtype]
         assert rel(out[split, 0], ref) <= tol_s

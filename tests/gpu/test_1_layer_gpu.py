@@ -2,7 +2,9 @@
 against the fp64 oracle, element by element on the same seeded inputs.
 
 Tolerances (relative L2 per tensor): 1e-4 for fp32 storage, 2e-2 for bf16
-storage; also on the residual-free deltas y - x and dx - dy.
+storage; also on the residual-free deltas y - x and dx - dy.  fp16 storage
+gets the same multiple of its unit roundoff as bf16: 2e-2 is 5.1 x 2^-8, so
+5.1 x 2^-11 = 2.5e-3.
 """
 
 import numpy as np
@@ -18,6 +20,7 @@ W = si.WORKLOADS
 BASE = W["layer-h256-fp32"]
 
 GQA128 = dict(hidden=512, n_heads=4, n_kv_heads=2, head_dim=128, ffn=1376)
+F16_TOL = 2.5e-3
 # name: (workload, tolerance, input scale)
 CASES = {
     # the fp32 single-layer workload at its full size
@@ -37,6 +40,13 @@ CASES = {
     "bf16-s128": (BASE.with_(dtype="bf16", batch=2, seq=128), 2e-2, 0.05),
     # one layer of the 4-layer h1024 stack at its full size (T = 2048), standard inputs
     "bf16-stack4-h1024-full": (W["stack4-h1024-bf16"], 2e-2, 1.0),
+    # fp16 storage: the same kernels with IEEE half operands
+    "f16-h256-b2-s160": (BASE.with_(dtype="f16", batch=2, seq=160), F16_TOL, 0.05),
+    "f16-h256-b2-s160-x1": (BASE.with_(dtype="f16", batch=2, seq=160), F16_TOL, 1.0),
+    "f16-gqa-d128-b2-s200": (BASE.with_(dtype="f16", batch=2, seq=200, **GQA128), F16_TOL, 0.05),
+    "f16-s65-seq-edge": (BASE.with_(dtype="f16", batch=2, seq=65), F16_TOL, 0.05),
+    "f16-seq1": (BASE.with_(dtype="f16", batch=3, seq=1), F16_TOL, 0.05),
+    "f16-stack4-h1024-full": (W["stack4-h1024-bf16"].with_(dtype="f16"), F16_TOL, 1.0),
 }
 
 

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 BASE = si.WORKLOADS["layer-h256-fp32"].with_(vocab=1000, batch=2, seq=96)
 
 
-def run_head(w, chunk, gf, Wlm, x, ids):
+def run_head(w, chunk, gf, Wlm, x, ids, grad_scale=None):
     c = rt.Context(w, head_chunk_rows=chunk)
     d_gf = rt.to_storage_tensor(gf, w).cuda()
     d_wlm = rt.to_storage_tensor(Wlm, w).cuda()
@@ -26,8 +26,13 @@ def run_head(w, chunk, gf, Wlm, x, ids):
     dx = torch.empty_like(d_x)
     dgf = torch.empty(w.hidden, dtype=torch.float32, device="cuda")
     dwlm = torch.empty(w.vocab, w.hidden, dtype=torch.float32, device="cuda")
-    sf.sf_head_fwd_bwd(c.ctx, d_gf.data_ptr(), d_wlm.data_ptr(), d_x.data_ptr(), d_ids.data_ptr(), loss.data_ptr(),
-                       dx.data_ptr(), dgf.data_ptr(), dwlm.data_ptr(), rt.stream_handle())
+    if grad_scale is None:
+        sf.sf_head_fwd_bwd(c.ctx, d_gf.data_ptr(), d_wlm.data_ptr(), d_x.data_ptr(), d_ids.data_ptr(),
+                           loss.data_ptr(), dx.data_ptr(), dgf.data_ptr(), dwlm.data_ptr(), rt.stream_handle())
+    else:
+        sf.sf_head_fwd_bwd_scaled(c.ctx, d_gf.data_ptr(), d_wlm.data_ptr(), d_x.data_ptr(), d_ids.data_ptr(),
+                                  loss.data_ptr(), dx.data_ptr(), dgf.data_ptr(), dwlm.data_ptr(), grad_scale,
+                                  rt.stream_handle())
     torch.cuda.synchronize()
     out = (loss.item(), dx.float().cpu().numpy(), dgf.cpu().numpy(), dwlm.cpu().numpy())
     c.close()
@@ -67,6 +72,41 @@ def test_head_parity_vocab_paths(dtype, tol, vocab):
     errs = {"loss": abs(loss - lo) / abs(lo), "dx": rel(dx, dxo), "dgf": rel(dgf, dgfo), "dWlm": rel(dwlm, dwo)}
     print({k: f"{v:.2e}" for k, v in errs.items()})
     assert all(v <= tol for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("vocab,chunk,scale", [(1000, 64, 1024.0), (32000, 96, 65536.0)])
+def test_head_parity_f16_scaled(vocab, chunk, scale):
+    """fp16 storage with the gradients scaled by S (the loss-scaling seed):
+    dx, dg_f and dW_lm divided by S against the oracle at the fp16 bound
+    (2.5e-3: the bf16 bound's multiple of the unit roundoff), the loss
+    unscaled."""
+    w = BASE.with_(dtype="f16", vocab=vocab)
+    say("head-f16", vocab, chunk, scale, w)
+    gf = si.final_gain(w, gains="random")
+    Wlm = si.lm_head(w)
+    x = si.layer_input(w)
+    ids = si.token_ids(w)
+    loss, dx, dgf, dwlm = run_head(w, chunk, gf, Wlm, x, ids, grad_scale=scale)
+    lo, dxo, dgfo, dwo = oracle.head_fwd_bwd(gf.astype(np.float64), Wlm.astype(np.float64), x.astype(np.float64),
+                                             ids, w.eps)
+    errs = {"loss": abs(loss - lo) / abs(lo), "dx": rel(dx / scale, dxo), "dgf": rel(dgf / scale, dgfo),
+            "dWlm": rel(dwlm / scale, dwo)}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(v <= 2.5e-3 for v in errs.values()), errs
+
+
+def test_head_scaled_is_exact_power_of_two_multiple():
+    """A power-of-two gradient scale multiplies every gradient of the head
+    exactly: bf16 outputs with S = 256 are the unscaled ones times 256, bit
+    for bit, and the loss is unchanged."""
+    w = BASE.with_(dtype="bf16")
+    say("head-scaled-exact", w)
+    gf = si.final_gain(w, gains="random")
+    args = (gf, si.lm_head(w), si.layer_input(w), si.token_ids(w))
+    l1, dx1, dgf1, dw1 = run_head(w, 64, *args)
+    l2, dx2, dgf2, dw2 = run_head(w, 64, *args, grad_scale=256.0)
+    assert l1 == l2
+    assert np.array_equal(dx1 * 256.0, dx2) and np.array_equal(dgf1 * 256.0, dgf2) and np.array_equal(dw1 * 256.0, dw2)
 
 
 def test_head_zero_weight_loss_is_ln_v():
