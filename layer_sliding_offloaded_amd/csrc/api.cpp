@@ -133,6 +133,9 @@ WorkLayout work_layout(const Dims& d, int head_chunk_rows) {
   w.dqkv = take(T * d.Nqkv * e);
   w.dxn = take(T * d.H * e);
   w.gain_partial = take(static_cast<size_t>(kGainChunks) * d.H * 4);
+  // the 16-bit attention backward may split a GQA group's query heads
+  w.kv_split = d.dtype != SF_F32 ? attn_kv_split(d.B, d.S, d.nh, d.nkv) : 1;
+  w.dkv_partial = take(static_cast<size_t>(attn_kv_partial_bytes(w.kv_split, d.B, d.S, d.nkv, d.d)));
   // split-K scratch: the largest any projection of the layer or head asks for
   {
     const int Ti = static_cast<int>(d.T);
@@ -498,6 +501,8 @@ sf_status layer_bwd(sf_ctx* c, const void* d_w, const void* d_x, const void* d_s
   at_.rope_sin = reinterpret_cast<const float*>(ws + wl.rope_sin);
   at_.batch = d.B; at_.seq = d.S; at_.n_heads = d.nh; at_.n_kv = d.nkv; at_.head_dim = d.d;
   at_.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d)));
+  at_.kv_split = wl.kv_split;
+  at_.dkv_partial = reinterpret_cast<float*>(ws + wl.dkv_partial);
   SF_HIP(attention_bwd(d.dtype, at_, s));
   if (sf_status st = fork(3)) return st;  // dqkv exists
   // dxn = [dq | dk | dv] Wqkv

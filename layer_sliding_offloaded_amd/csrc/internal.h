@@ -36,6 +36,8 @@ struct SavedLayout {
 struct WorkLayout {
   size_t rope_cos, rope_sin, dGU, dhn, dh, dA, dsum, dqkv, dxn, gain_partial, splitk, splitk_bytes;
   size_t splitk_w, splitk_w_bytes;  // split-K scratch of the weight-gradient GEMMs (side stream)
+  size_t dkv_partial;               // fp32 partial dK/dV sums of the attention head shares (16-bit storage)
+  int kv_split;
   size_t total;
   // head (appended when vocab > 0)
   size_t hf, rf, dhf, logits, dlogits, loss_rows, head_total;
