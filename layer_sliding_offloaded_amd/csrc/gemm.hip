@@ -987,6 +987,11 @@ gemm_pipe_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
+template <int STAGE, int NS>
+struct PPStages {
+  __attribute__((aligned(1024))) char s[NS][STAGE];
+};
+
 // Ping-pong variant: the 8 waves form two groups of four (one wave per SIMD
 // in each), and the groups alternate between a memory phase (fragment reads
 // of the next stage from LDS, loads of a later stage into LDS) and a compute
@@ -1003,19 +1008,16 @@ gemm_pp_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
   constexpr bool BKC = (LAY == GemmLayout::NT);
   constexpr int NW = (BM / WM) * (BN / WN);
   static_assert(NW == 8, "two groups of four waves");
+  static_assert(NS * (BM + BN) * BK * 2 <= 160 * 1024, "stages within the 160 KB of LDS");
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int WGM = BM / WM;
   constexpr int KS = BK / 32;
   constexpr int ABYTES = BM * BK * 2;
   constexpr int STAGE = (BM + BN) * BK * 2;
   static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
-  __shared__ __attribute__((aligned(1024))) char S0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char S1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char S2[STAGE];
-  __shared__ __attribute__((aligned(1024))) char S3[NS > 3 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char S4[NS > 4 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char S5[NS > 5 ? STAGE : 16];
-  char* const stage[6] = {S0, S1, S2, S3, S4, S5};
+  // exactly NS stages (at 256 x 256 x 32, five fill the 160 KB of LDS)
+  __shared__ PPStages<STAGE, NS> smem;
+  char* const stage[6] = {smem.s[0], smem.s[1], smem.s[2 % NS], smem.s[3 % NS], smem.s[4 % NS], smem.s[5 % NS]};
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1112,12 +1114,8 @@ gemm_pp_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
       // (only the stage arrays that hold a patch are named)
       constexpr int KMAX = (NW - 1) / PER;
       const int k = w / PER;
-      char* base = S0;
-      if constexpr (KMAX >= 1) base = k == 1 ? S1 : base;
-      if constexpr (KMAX >= 2) base = k == 2 ? S2 : base;
-      if constexpr (KMAX >= 3) base = k == 3 ? S3 : base;
-      if constexpr (KMAX >= 4) base = k == 4 ? S4 : base;
-      if constexpr (KMAX >= 5) base = k == 5 ? S5 : base;
+      static_assert(KMAX < NS, "patches inside the stages");
+      char* base = smem.s[0] + k * STAGE;
       epilogue_rows<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lane,
                                        reinterpret_cast<float*>(base + (w % PER) * PB));
       return;
@@ -1240,7 +1238,16 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
       // stages when there are enough tiles to keep every CU busy without a
       // deep pipeline, or 128x64 tiles when even 128x128 ones would leave
       // half the CUs idle.
-      if (cfg == 0) return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb);
+      // Five stages (the whole 160 KB of LDS) give the loads a fifth more
+      // lead: 7-9 % on the forward products with 3-3.5 rounds of tiles over
+      // the CUs at the 123B-shaped layer, 0-5 % on the input-gradient ones.
+      // The weight-gradient kernel (both operands read transposed) already
+      // needs 256 VGPRs at four stages and spills in its loop at five
+      // (3.5x slower): four there.
+      if (cfg == 0) {
+        if constexpr (LAY == GemmLayout::TN) return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb);
+        return launch<T, 256, 256, 128, 64, LAY, E, 3, 32, 5>(g, s, ws, wsb, ab, bb);
+      }
       if constexpr (E == Epi::Store || E == Epi::StoreF32) {
         const int S = longk_split(g.M, g.N, g.K);
         if (S > 1 && ws && static_cast<size_t>(S) * g.M * g.N * 4 <= wsb)
