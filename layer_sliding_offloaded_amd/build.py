@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libsf.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["gemm.hip", "attention.hip", "attn_direct.hip", "rowops.hip"]
-HOST_SOURCES = ["api.cpp", "engine.cpp", "adam.cpp"]
+HOST_SOURCES = ["api.cpp", "layout.cpp", "engine.cpp", "adam.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
