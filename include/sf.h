@@ -109,6 +109,23 @@ typedef struct {
  */
 sf_status sf_layer_layout(const sf_shape* shape, int32_t head_chunk_rows, sf_layout* out);
 
+/*
+ * sf_layer_layout with the rows of dlogits the head keeps for one LM-head
+ * weight-gradient product.  The fused head (de §2C "Fused
+ * LinearCrossEntropy") computes logits, loss and dlogits in chunks of
+ * head_chunk_rows rows; each chunk's dW_lm contribution, added to the fp32
+ * dW_lm, reads and writes all of V x H fp32 (4.2 GB at V 128256, H 4096),
+ * so small chunks pay that once per chunk.  With head_dw_rows > head_chunk_rows
+ * (rounded up to a multiple of it, at most all rows) the bf16 dlogits of
+ * that many rows stay in the workspace and dW_lm takes one product per
+ * group: head_workspace_bytes grows by (head_dw_rows - head_chunk_rows) V e,
+ * the fp32 logits stay chunked.  0 (or <= head_chunk_rows): one product per
+ * chunk, as sf_layer_layout.  The sums of dW_lm then run in another order
+ * (same values up to fp32 rounding).
+ */
+sf_status sf_layer_layout_ex(const sf_shape* shape, int32_t head_chunk_rows, int32_t head_dw_rows,
+                             sf_layout* out);
+
 typedef struct sf_ctx sf_ctx;
 
 /*
@@ -124,6 +141,9 @@ typedef struct sf_ctx sf_ctx;
  */
 sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_workspace,
                         size_t workspace_bytes, sf_ctx** out);
+/* sf_ctx_create with the head's dW_lm grouping of sf_layer_layout_ex. */
+sf_status sf_ctx_create_ex(const sf_shape* shape, int32_t head_chunk_rows, int32_t head_dw_rows,
+                           void* d_workspace, size_t workspace_bytes, sf_ctx** out);
 sf_status sf_ctx_destroy(sf_ctx* ctx);
 
 /*

@@ -60,13 +60,18 @@ extern "C" {
 
 sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_workspace, size_t workspace_bytes,
                         sf_ctx** out) {
+  return sf_ctx_create_ex(shape, head_chunk_rows, 0, d_workspace, workspace_bytes, out);
+}
+
+sf_status sf_ctx_create_ex(const sf_shape* shape, int32_t head_chunk_rows, int32_t head_dw_rows, void* d_workspace,
+                           size_t workspace_bytes, sf_ctx** out) {
   Dims d;
   sf_status st = check_shape(shape, &d);
   if (st) return st;
   if (!out) return fail(SF_ERR_ARG, "out is NULL");
   *out = nullptr;
   sf_layout L;
-  st = sf_layer_layout(shape, head_chunk_rows, &L);
+  st = sf_layer_layout_ex(shape, head_chunk_rows, head_dw_rows, &L);
   if (st) return st;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(SF_ERR_NO_DEVICE, "no HIP device");
@@ -85,8 +90,9 @@ sf_status sf_ctx_create(const sf_shape* shape, int32_t head_chunk_rows, void* d_
   c->dims = d;
   c->layout = L;
   c->saved = saved_layout(d);
-  c->work = work_layout(d, head_chunk_rows);
+  c->work = work_layout(d, head_chunk_rows, head_dw_rows);
   c->head_chunk_rows = head_chunk_rows;
+  c->head_dw_rows = head_dw_rows_eff(d.T, head_chunk_rows, head_dw_rows);
   c->ws = static_cast<char*>(d_workspace);
   c->ws_bytes = workspace_bytes;
   c->device = dev;
@@ -372,8 +378,8 @@ sf_status head_last_dw(sf_ctx* c, float* d_dwlm, sf_stream stream) {
   const Dims& d = c->dims;
   const WorkLayout& wl = c->work;
   const int T = static_cast<int>(d.T);
-  const int R = c->head_chunk_rows;
-  const int r0 = ((T - 1) / R) * R;
+  const int D = c->head_dw_rows;  // the last group of dlogits rows
+  const int r0 = ((T - 1) / D) * D;
   GemmArgs g;
   g.A = c->ws + wl.dlogits; g.lda = d.V;
   g.B = c->ws + wl.hf + static_cast<size_t>(r0) * d.H * d.e; g.ldb = d.H;
@@ -410,9 +416,15 @@ sf_status head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const voi
   const float inv_n = 1.0f / (static_cast<float>(d.B) * static_cast<float>(d.S - 1));
 
   SF_HIP(rmsnorm_fwd(d.dtype, d_x, d_gf, hf, rf, T, d.H, d.eps, s));
-  const int R = c->head_chunk_rows;
+  // Row chunks of R: logits, cross entropy and dlogits, dx.  dlogits of a
+  // group of D rows (D a multiple of R) stay in the workspace, and each
+  // group adds its dW_lm = dlogits^T hf in one product: the fp32 dW_lm is
+  // read and written once per group rather than once per chunk.
+  const int R = c->head_chunk_rows, D = c->head_dw_rows;
   for (int r0 = 0; r0 < T; r0 += R) {
     const int rows = std::min(R, T - r0);
+    const int g0 = r0 / D * D;  // first row of this chunk's group
+    char* dlc = static_cast<char*>(dlogits) + static_cast<size_t>(r0 - g0) * d.V * d.e;
     const char* hfc = static_cast<const char*>(hf) + static_cast<size_t>(r0) * d.H * d.e;
     GemmArgs g;
     g.A = hfc; g.lda = d.H;
@@ -420,20 +432,22 @@ sf_status head_fwd_bwd(sf_ctx* c, const void* d_gf, const void* d_wlm, const voi
     g.C = logits; g.ldc = d.V;
     g.M = rows; g.N = d.V; g.K = d.H;
     SF_HIP(gemm(d.dtype, GemmLayout::NT, Epi::StoreF32, g, s, skw, skb));
-    SF_HIP(ce_rows(d.dtype, logits, d_ids, dlogits, loss_rows, r0, rows, d.V, d.S, inv_n * grad_scale, s));
+    SF_HIP(ce_rows(d.dtype, logits, d_ids, dlc, loss_rows, r0, rows, d.V, d.S, inv_n * grad_scale, s));
     g = GemmArgs();
-    g.A = dlogits; g.lda = d.V;
+    g.A = dlc; g.lda = d.V;
     g.B = d_wlm; g.ldb = d.H;
     g.C = dhf + static_cast<size_t>(r0) * d.H * d.e; g.ldc = d.H;
     g.M = rows; g.N = d.H; g.K = d.V;
     SF_HIP(gemm(d.dtype, GemmLayout::NN, Epi::Store, g, s, skw, skb));
-    if (defer_last_dw && r0 + R >= T) break;  // the caller runs head_last_dw later
+    const int end = r0 + rows;
+    if (end % D != 0 && end < T) continue;  // the group goes on
+    if (defer_last_dw && end >= T) break;   // the caller runs head_last_dw later
     g = GemmArgs();
     g.A = dlogits; g.lda = d.V;
-    g.B = hfc; g.ldb = d.H;
+    g.B = static_cast<const char*>(hf) + static_cast<size_t>(g0) * d.H * d.e; g.ldb = d.H;
     g.C = d_dwlm; g.ldc = d.H;
-    g.M = d.V; g.N = d.H; g.K = rows;
-    SF_HIP(gemm(d.dtype, GemmLayout::TN, r0 == 0 ? Epi::StoreF32 : Epi::AccF32, g, s, skw, skb));
+    g.M = d.V; g.N = d.H; g.K = end - g0;
+    SF_HIP(gemm(d.dtype, GemmLayout::TN, g0 == 0 ? Epi::StoreF32 : Epi::AccF32, g, s, skw, skb));
   }
   SF_HIP(loss_reduce(loss_rows, d_loss, T, inv_n, s));
   SF_HIP(rmsnorm_bwd(d.dtype, dhf, d_x, rf, d_gf, nullptr, d_dx, partial, kGainChunks, d_dgf, T, d.H, s));

@@ -46,7 +46,10 @@ struct WorkLayout {
 sf_status check_shape(const sf_shape* s, Dims* out);
 void param_layout(const Dims& d, size_t elem, size_t* off, size_t* bytes, size_t* total);
 SavedLayout saved_layout(const Dims& d);
-WorkLayout work_layout(const Dims& d, int head_chunk_rows);
+// head_dw_rows: rows of dlogits kept for one LM-head weight-gradient product
+// (head_dw_rows_eff); 0 = the chunk rows.
+int head_dw_rows_eff(int64_t T, int head_chunk_rows, int head_dw_rows);
+WorkLayout work_layout(const Dims& d, int head_chunk_rows, int head_dw_rows = 0);
 
 }  // namespace sf
 
@@ -73,6 +76,7 @@ struct sf_ctx {
   sf::SavedLayout saved;
   sf::WorkLayout work;
   int head_chunk_rows = 0;
+  int head_dw_rows = 0;  // effective (a multiple of the chunk rows)
   char* ws = nullptr;  // caller-provided device workspace
   size_t ws_bytes = 0;
   int device = 0;

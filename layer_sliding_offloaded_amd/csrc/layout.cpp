@@ -1,6 +1,7 @@
 // Shape validation, buffer layouts and the thread-local error text of the C
 // ABI: host code only (no device calls), shared by the library and the CPU
 // build of the sliding engine's host logic.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -106,7 +107,14 @@ SavedLayout saved_layout(const Dims& d) {
   return s;
 }
 
-WorkLayout work_layout(const Dims& d, int head_chunk_rows) {
+int head_dw_rows_eff(int64_t T, int head_chunk_rows, int head_dw_rows) {
+  const int64_t R = head_chunk_rows > 0 ? head_chunk_rows : 1;
+  if (head_dw_rows <= R) return static_cast<int>(R);
+  const int64_t all = (T + R - 1) / R * R;
+  return static_cast<int>(std::min<int64_t>(all, (head_dw_rows + R - 1) / R * R));
+}
+
+WorkLayout work_layout(const Dims& d, int head_chunk_rows, int head_dw_rows) {
   WorkLayout w;
   const size_t T = d.T, e = d.e;
   size_t o = 0;
@@ -135,6 +143,7 @@ WorkLayout work_layout(const Dims& d, int head_chunk_rows) {
     if (d.V > 0) {
       const int R = std::min(Ti, head_chunk_rows > 0 ? head_chunk_rows : 1);
       upd(R, d.V, d.H); upd(R, d.H, d.V); upd(d.V, d.H, R);
+      upd(d.V, d.H, head_dw_rows_eff(d.T, head_chunk_rows, head_dw_rows));
     }
     w.splitk = take(sk);
     w.splitk_bytes = sk;
@@ -151,7 +160,7 @@ WorkLayout work_layout(const Dims& d, int head_chunk_rows) {
     w.rf = take(T * 4);
     w.dhf = take(T * d.H * e);
     w.logits = take(R * d.V * 4);
-    w.dlogits = take(R * d.V * e);
+    w.dlogits = take(static_cast<size_t>(head_dw_rows_eff(d.T, head_chunk_rows, head_dw_rows)) * d.V * e);
     w.loss_rows = take(T * 4);
   } else {
     w.hf = w.rf = w.dhf = w.logits = w.dlogits = w.loss_rows = 0;
@@ -168,12 +177,14 @@ extern "C" {
 
 const char* sf_last_error(void) { return sf::g_last_error.c_str(); }
 
-sf_status sf_layer_layout(const sf_shape* shape, int32_t head_chunk_rows, sf_layout* out) {
+sf_status sf_layer_layout_ex(const sf_shape* shape, int32_t head_chunk_rows, int32_t head_dw_rows,
+                             sf_layout* out) {
   Dims d;
   sf_status st = check_shape(shape, &d);
   if (st) return st;
   if (!out) return fail(SF_ERR_ARG, "out is NULL");
   if (d.V > 0 && head_chunk_rows <= 0) return fail(SF_ERR_ARG, "head_chunk_rows must be >= 1");
+  if (head_dw_rows < 0) return fail(SF_ERR_ARG, "head_dw_rows must be >= 0");
   sf_layout L;
   std::memset(&L, 0, sizeof L);
   param_layout(d, d.e, L.off, L.bytes, &L.param_bytes);
@@ -181,11 +192,15 @@ sf_status sf_layer_layout(const sf_shape* shape, int32_t head_chunk_rows, sf_lay
   L.n_params = static_cast<size_t>(d.Nqkv) * d.H + static_cast<size_t>(d.H) * d.Nq +
                3 * static_cast<size_t>(d.F) * d.H + 2 * static_cast<size_t>(d.H);
   L.saved_bytes = saved_layout(d).total;
-  const WorkLayout w = work_layout(d, head_chunk_rows);
+  const WorkLayout w = work_layout(d, head_chunk_rows, head_dw_rows);
   L.workspace_bytes = w.total;
   L.head_workspace_bytes = w.head_total;
   *out = L;
   return SF_OK;
+}
+
+sf_status sf_layer_layout(const sf_shape* shape, int32_t head_chunk_rows, sf_layout* out) {
+  return sf_layer_layout_ex(shape, head_chunk_rows, 0, out);
 }
 
 }  // extern "C"

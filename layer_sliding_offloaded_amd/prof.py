@@ -413,7 +413,8 @@ def rowops(db_path, workload):
 def head_study(hidden, vocab, batch, seq, chunks, reps=5):
     """Chunk-size sweep of the fused head (final RMSNorm, logits, cross
     entropy, dx, dW_lm) on synthetic inputs: x ~ N(0, 1), W_lm ~ N(0, 0.02^2),
-    g_f = 1, ids ~ U[0, vocab)."""
+    g_f = 1, ids ~ U[0, vocab).  chunks: "R" (one dW_lm product per chunk of
+    R rows) or "R/D" (dlogits of D rows kept, one dW_lm product per D rows)."""
     import statistics
 
     import torch
@@ -439,11 +440,12 @@ def head_study(hidden, vocab, batch, seq, chunks, reps=5):
     s = torch.cuda.current_stream()
     flops = 6.0 * T * vocab * hidden
     rows = []
-    for R in chunks:
+    for spec in chunks:
+        R, D = (int(v) for v in spec.split("/")) if "/" in str(spec) else (int(spec), 0)
         shape = rt.shape_from(w)
-        L = sf.sf_layer_layout(shape, R)
+        L = sf.sf_layer_layout_ex(shape, R, D)
         full = rt.device_bytes(L.workspace_bytes + L.head_workspace_bytes)
-        ctx = sf.sf_ctx_create(shape, R, full.data_ptr(), full.numel())
+        ctx = sf.sf_ctx_create_ex(shape, R, D, full.data_ptr(), full.numel())
 
         def call():
             sf.sf_head_fwd_bwd(ctx, gf.data_ptr(), wlm.data_ptr(), x.data_ptr(), ids.data_ptr(), loss.data_ptr(),
@@ -460,20 +462,21 @@ def head_study(hidden, vocab, batch, seq, chunks, reps=5):
             e1.synchronize()
             times.append(e0.elapsed_time(e1))
         ms = statistics.median(times)
-        rows.append((R, L.head_workspace_bytes, ms, loss.item()))
-        print(f"[head-study] rows {R}: workspace {L.head_workspace_bytes / 2**20:.1f} MiB, {ms:.3f} ms", file=sys.stderr,
-              flush=True)
+        Dn = min(T, -(-max(D, R) // R) * R)
+        rows.append((R, Dn, L.head_workspace_bytes, ms, loss.item()))
+        print(f"[head-study] rows {R} dW rows {Dn}: workspace {L.head_workspace_bytes / 2**20:.1f} MiB, {ms:.3f} ms",
+              file=sys.stderr, flush=True)
         sf.sf_ctx_destroy(ctx)
         del full
         torch.cuda.synchronize()
-    base_ws = max(r[1] for r in rows)
+    base_ws = max(r[2] for r in rows)
     print(f"Head shape: T = {batch} x {seq} = {T} tokens, hidden {hidden}, vocab {vocab} (bf16, fp32 dW_lm); "
           f"fixed head buffers (x, dx, W_lm, dW_lm, g_f, dg_f, ids, loss): {fixed / 2**30:.3f} GiB.\n")
-    print("| chunk rows | head workspace (logits fp32 + dlogits bf16 + norm) | vs all rows at once | "
+    print("| chunk rows | dW_lm rows | head workspace (logits fp32 + dlogits bf16 + norm) | vs all rows at once | "
           "head total (workspace + fixed) | vs all rows at once | ms per call | TFLOP/s | loss |")
-    print("|---:|---:|---:|---:|---:|---:|---:|---:|")
-    for R, wsb, ms, lv in rows:
-        print(f"| {R} | {wsb / 2**30:.3f} GiB | {100.0 * (1 - wsb / base_ws):.1f} % less | "
+    print("|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for R, Dn, wsb, ms, lv in rows:
+        print(f"| {R} | {Dn} | {wsb / 2**30:.3f} GiB | {100.0 * (1 - wsb / base_ws):.1f} % less | "
               f"{(wsb + fixed) / 2**30:.3f} GiB | {100.0 * (1 - (wsb + fixed) / (base_ws + fixed)):.1f} % less | "
               f"{ms:.3f} | {flops / (ms * 1e-3) / 1e12:.0f} | {lv:.5f} |")
 
@@ -504,7 +507,7 @@ def main():
     elif a.mode == "rowops":
         rowops(a.files[0], a.workload)
     elif a.mode == "head-study":
-        head_study(a.hidden, a.vocab, a.batch, a.seq, [int(c) for c in a.chunks.split(",")])
+        head_study(a.hidden, a.vocab, a.batch, a.seq, a.chunks.split(","))
     else:
         kernels(a.files[0], a.top)
 

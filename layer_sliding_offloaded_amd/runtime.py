@@ -93,14 +93,17 @@ def stream_handle(stream=None):
 class Context:
     """An sf_ctx plus the device workspace it borrows."""
 
-    def __init__(self, w, head_chunk_rows=2048, batch=None, seq=None):
+    def __init__(self, w, head_chunk_rows=2048, batch=None, seq=None, head_dw_rows=0):
+        """head_dw_rows: rows of dlogits kept for one LM-head weight-gradient
+        product (sf_ctx_create_ex); 0 = one product per chunk."""
         self.w = w
         self.shape = shape_from(w, batch, seq)
         self.chunk = head_chunk_rows
-        self.layout = sf.sf_layer_layout(self.shape, head_chunk_rows)
+        self.layout = sf.sf_layer_layout_ex(self.shape, head_chunk_rows, head_dw_rows)
         n = self.layout.workspace_bytes + (self.layout.head_workspace_bytes if w.vocab else 0)
         self.ws = device_bytes(n)
-        self.ctx = sf.sf_ctx_create(self.shape, head_chunk_rows, self.ws.data_ptr(), self.ws.numel())
+        self.ctx = sf.sf_ctx_create_ex(self.shape, head_chunk_rows, head_dw_rows, self.ws.data_ptr(),
+                                       self.ws.numel())
 
     def close(self):
         if self.ctx:
@@ -134,11 +137,13 @@ class Engine:
     one step's backward to the next step's forward (h_params unchanged).
     loss_scale, scale_window: fp16 storage's dynamic loss scaling (initial
     scale and growth window; 0 takes the library's defaults).
+    head_dw_rows: rows of dlogits the LM head keeps for one dW_lm product
+    (sf_ctx_create_ex; 0: one product per chunk).
     """
 
     def __init__(self, w, layers, head=None, window=2, n_grad_slots=2, adam=True, chunk=2048,
                  adam_threads=0, adam_hp=None, stream=None, head_adam="device", ckpt=False, pipeline=False,
-                 draw_threads=1, keep_turnaround=False, loss_scale=0.0, scale_window=0):
+                 draw_threads=1, keep_turnaround=False, loss_scale=0.0, scale_window=0, head_dw_rows=0):
         import ctypes
         from concurrent.futures import ThreadPoolExecutor
         hp = adam_hp or dict(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8)
@@ -147,7 +152,7 @@ class Engine:
             layer_fn, self.nl = layers, w.n_layers
         else:
             layer_fn, self.nl = (lambda l: layers[l]), len(layers)
-        self.ctx = Context(w, chunk)
+        self.ctx = Context(w, chunk, head_dw_rows=head_dw_rows)
         L = self.ctx.layout
         self.layout = L
         shape = self.ctx.shape

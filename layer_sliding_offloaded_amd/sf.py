@@ -87,7 +87,7 @@ class SfError(RuntimeError):
 
 
 EXPORTS = (
-    "sf_layer_layout", "sf_ctx_create", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
+    "sf_layer_layout", "sf_layer_layout_ex", "sf_ctx_create", "sf_ctx_create_ex", "sf_ctx_destroy", "sf_layer_fwd", "sf_layer_bwd", "sf_head_fwd_bwd",
     "sf_head_fwd_bwd_scaled", "sf_adam_host_ex", "sf_adam_device_ex",
     "sf_gemm", "sf_gemm_workspace_bytes", "sf_gemm_noalloc", "sf_embed_fwd", "sf_embed_bwd", "sf_adam_host", "sf_adam_device", "sf_engine_act_bytes", "sf_engine_act_bytes_flags", "sf_engine_create", "sf_slide_step",
     "sf_engine_sync", "sf_engine_layer_input", "sf_engine_dx0", "sf_engine_trace", "sf_engine_counters",
@@ -109,6 +109,8 @@ def load():
     sig = {
         "sf_layer_layout": [ctypes.POINTER(SfShape), i32, ctypes.POINTER(SfLayout)],
         "sf_ctx_create": [ctypes.POINTER(SfShape), i32, P, _size_t, ctypes.POINTER(P)],
+        "sf_layer_layout_ex": [ctypes.POINTER(SfShape), i32, i32, ctypes.POINTER(SfLayout)],
+        "sf_ctx_create_ex": [ctypes.POINTER(SfShape), i32, i32, P, _size_t, ctypes.POINTER(P)],
         "sf_ctx_destroy": [P],
         "sf_layer_fwd": [P, P, P, P, P, P],
         "sf_layer_bwd": [P, P, P, P, P, P, P, P],
@@ -171,10 +173,23 @@ def sf_layer_layout(shape, head_chunk_rows=1):
     return out
 
 
+def sf_layer_layout_ex(shape, head_chunk_rows, head_dw_rows):
+    out = SfLayout()
+    _check(load().sf_layer_layout_ex(ctypes.byref(shape), head_chunk_rows, head_dw_rows, ctypes.byref(out)))
+    return out
+
+
 def sf_ctx_create(shape, head_chunk_rows, d_workspace, workspace_bytes):
     ctx = _vp()
     _check(load().sf_ctx_create(ctypes.byref(shape), head_chunk_rows, d_workspace, workspace_bytes,
                                 ctypes.byref(ctx)))
+    return ctx.value
+
+
+def sf_ctx_create_ex(shape, head_chunk_rows, head_dw_rows, d_workspace, workspace_bytes):
+    ctx = _vp()
+    _check(load().sf_ctx_create_ex(ctypes.byref(shape), head_chunk_rows, head_dw_rows, d_workspace,
+                                   workspace_bytes, ctypes.byref(ctx)))
     return ctx.value
 
 

@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 BASE = si.WORKLOADS["layer-h256-fp32"].with_(vocab=1000, batch=2, seq=96)
 
 
-def run_head(w, chunk, gf, Wlm, x, ids, grad_scale=None):
-    c = rt.Context(w, head_chunk_rows=chunk)
+def run_head(w, chunk, gf, Wlm, x, ids, grad_scale=None, dw_rows=0):
+    c = rt.Context(w, head_chunk_rows=chunk, head_dw_rows=dw_rows)
     d_gf = rt.to_storage_tensor(gf, w).cuda()
     d_wlm = rt.to_storage_tensor(Wlm, w).cuda()
     d_x = rt.to_storage_tensor(x, w).cuda()
@@ -54,6 +54,49 @@ def test_head_parity(dtype, tol, chunk):
     errs = {"loss": abs(loss - lo) / abs(lo), "dx": rel(dx, dxo), "dgf": rel(dgf, dgfo), "dWlm": rel(dwlm, dwo)}
     print({k: f"{v:.2e}" for k, v in errs.items()})
     assert all(v <= tol for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-4), ("bf16", 2e-2)])
+@pytest.mark.parametrize("chunk,dw_rows", [(50, 150), (48, 100), (64, 10 ** 6)], ids=["50-150", "48-100", "64-all"])
+def test_head_grouped_dw_parity(dtype, tol, chunk, dw_rows):
+    """dW_lm in one product per group of chunks (sf_ctx_create_ex): 50-row
+    chunks in groups of 150 rows over T = 192 (a ragged last group of 42),
+    48-row chunks with 100 rounded up to 144, and every row in one group.
+    Against the oracle at the dtype's bound; the loss, dx and dg_f do not
+    depend on the grouping (same bits as one product per chunk), dW_lm only
+    through the order of its fp32 sums."""
+    w = BASE.with_(dtype=dtype)
+    say("head-grouped", dtype, chunk, dw_rows, w)
+    gf = si.final_gain(w, gains="random")
+    Wlm = si.lm_head(w)
+    x = si.layer_input(w)
+    ids = si.token_ids(w)
+    loss, dx, dgf, dwlm = run_head(w, chunk, gf, Wlm, x, ids, dw_rows=dw_rows)
+    lo, dxo, dgfo, dwo = oracle.head_fwd_bwd(gf.astype(np.float64), Wlm.astype(np.float64), x.astype(np.float64),
+                                             ids, w.eps)
+    errs = {"loss": abs(loss - lo) / abs(lo), "dx": rel(dx, dxo), "dgf": rel(dgf, dgfo), "dWlm": rel(dwlm, dwo)}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(v <= tol for v in errs.values()), errs
+    l1, dx1, dgf1, dw1 = run_head(w, chunk, gf, Wlm, x, ids)
+    assert loss == l1 and np.array_equal(dx, dx1) and np.array_equal(dgf, dgf1)
+    assert rel(dwlm, dw1) <= 1e-6
+
+
+def test_head_grouped_dw_layout():
+    """The workspace holds dlogits of the group (rounded up to whole chunks,
+    at most every row) instead of one chunk; the logits stay one chunk."""
+    w = BASE.with_(dtype="bf16")
+    shape = rt.shape_from(w)
+    T, V = w.tokens, w.vocab
+    base = sf.sf_layer_layout_ex(shape, 50, 0).head_workspace_bytes
+    assert sf.sf_layer_layout_ex(shape, 50, 50).head_workspace_bytes == base
+    assert sf.sf_layer_layout(shape, 50).head_workspace_bytes == base
+    for want, eff in ((150, 150), (100, 100), (10 ** 6, 200)):
+        got = sf.sf_layer_layout_ex(shape, 50, want).head_workspace_bytes
+        assert base < got <= base + (eff - 50) * V * 2 + 256 * 4, (want, got)
+    assert T == 192
+    with pytest.raises(sf.SfError):
+        sf.sf_layer_layout_ex(shape, 50, -1)
 
 
 @pytest.mark.parametrize("dtype,tol,vocab", [("bf16", 2e-2, 65536), ("f32", 1e-4, 65544), ("bf16", 2e-2, 128256)])

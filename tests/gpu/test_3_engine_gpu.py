@@ -229,6 +229,35 @@ def test_engine_step_matches_oracle():
     eng.close()
 
 
+def test_engine_grouped_head_dw_matches_per_chunk():
+    """The engine's deferred last LM-head weight-gradient product
+    (head_last_dw) with dlogits kept for groups of chunks: 64-row chunks in
+    groups of 192 over T = 256 (the deferred group is the last 64 rows).
+    One step: the loss, every layer's master and the embedding and final
+    gain (none of which reads dW_lm) have the bits of one product per
+    chunk, the LM head's master only differs in the order of its fp32 sums."""
+    w = STACK
+    say("engine-grouped-dw", w)
+    layers, head = make_stack(w, w.n_layers)
+    d_ids = torch.from_numpy(si.token_ids(w).reshape(-1)).cuda()
+    out = []
+    for dw_rows in (0, 192):
+        eng = rt.Engine(w, layers, head, window=2, n_grad_slots=2, adam=True, chunk=64, adam_hp=si.ADAM,
+                        head_dw_rows=dw_rows)
+        loss, _ = eng.step(d_ids)
+        eng.sync()
+        torch.cuda.synchronize()
+        nh = eng.h_head_master.size
+        out.append((loss, [m.copy() for m in eng.h_master], eng.d_head_state[:nh].cpu().numpy()))
+        eng.close()
+    (l0, m0, h0), (l1, m1, h1) = out
+    V, H = w.vocab, w.hidden
+    assert l0 == l1
+    assert all(np.array_equal(a, b) for a, b in zip(m0, m1))
+    assert np.array_equal(h0[:V * H + H], h1[:V * H + H])
+    assert rel(h1[V * H + H:], h0[V * H + H:]) <= 1e-6
+
+
 def test_engine_without_head_or_adam():
     w = STACK.with_(vocab=0, n_layers=3)
     say("engine-no-head", w)
