@@ -1243,7 +1243,10 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
       // the CUs at the 123B-shaped layer, 0-5 % on the input-gradient ones.
       // The weight-gradient kernel (both operands read transposed) already
       // needs 256 VGPRs at four stages and spills in its loop at five
-      // (3.5x slower): four there.
+      // (3.5x slower): four there.  256 x 128 tiles (8 waves of 64 x 64),
+      // which would turn the 3.5 rounds of qkv_fwd's 896 tiles into 7, are
+      // slower on every layer GEMM (0.35-0.44 of the peak against
+      // 0.45-0.58): a 64 x 64 wave tile reads 8 fragments per 16 MFMAs.
       if (cfg == 0) {
         if constexpr (LAY == GemmLayout::TN) return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb);
         return launch<T, 256, 256, 128, 64, LAY, E, 3, 32, 5>(g, s, ws, wsb, ab, bb);
