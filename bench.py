@@ -180,10 +180,10 @@ def main():
                          "fp32 Adam states would need 133 GB of host memory)")
     ap.add_argument("--grad-slots", type=int, default=2,
                     help="pinned fp32 gradient slots shared by all layers (a ring; n_layers = one buffer per layer)")
-    ap.add_argument("--sync-adam", action="store_true",
-                    help="every step waits for its own host Adam and copies before returning (default: Adam, or "
-                         "without Adam the last gradient copies, run on into the next step, whose forward waits per "
-                         "layer for the update it reads)")
+    ap.add_argument("--sync", "--sync-adam", dest="sync", action="store_true",
+                    help="every step waits for its own host Adam and copies before returning (default: pipelined "
+                         "steps: host Adam, or without Adam the last gradient copies, run on into the next step, "
+                         "whose forward waits per layer for what it reads)")
     ap.add_argument("--no-keep", action="store_true",
                     help="without Adam, upload layers 0..window-1 again in every forward (default: they stay in "
                          "their units from the previous backward)")
@@ -236,12 +236,11 @@ def main():
     head = None
     if w.vocab:
         head = dict(E=si.embedding(w), gf=si.final_gain(w), Wlm=si.lm_head(w))
-    # pipelined: host Adam runs on into the next step.  Without Adam the
-    # parameters never change, so the layers that end the backward in their
-    # units open the next forward; those steps stay synchronous (a step's
-    # last gradient copies overlapping the next step's uploads ran at a
-    # quarter of the link rate on this machine)
-    pipeline = adam and not args.sync_adam
+    # pipelined: host Adam, or without Adam a step's last gradient copies,
+    # run on into the next step.  Without Adam the parameters never change,
+    # so the layers that end the backward in their units also open the next
+    # forward (keep-turnaround)
+    pipeline = not args.sync
     keep = not adam and not args.no_keep
     # draws run on a few host threads (each layer has its own seed)
     ncpu = len(os.sched_getaffinity(0))

@@ -884,7 +884,13 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if (sf_status r = await_adam(j)) return r;
     if (!in_gslot(j)) return prefetch(e, j);
     const int u = j % W;
-    SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_grad_free[u], 0));   // last gradients out
+    // The region's last gradients must be out.  The host waits for that
+    // copy rather than the H2D stream: an H2D queue waiting on the D2H
+    // queue's event while later gradient copies are still queued sent those
+    // copies into a ~13 GB/s mode on the MI355X machine (pipelined steps without
+    // Adam, whose last copies run into the next forward).  In synchronous
+    // steps and with Adam the copy is long done here.
+    SF_HIP(hipEventSynchronize(e->ev_grad_free[u]));
     SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_gslot_free[u], 0));  // layer j - 2W's forward
     if (sf_status r = timed_h2d(e, e->ugrad[u], c.h_params[j], e->L.param_bytes, e->s_h2d)) return r;
     SF_HIP(hipEventRecord(e->ev_gslot_ready[u], e->s_h2d));
