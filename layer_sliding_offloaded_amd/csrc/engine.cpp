@@ -939,6 +939,8 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   // later layer's upload as soon as its update finishes, so the copies run
   // meanwhile instead of after it.
   auto advance = [&](int i) -> sf_status {
+    // an upload may be queued once the forward it waits for (the layer 2W
+    // back) has been: its stream wait takes that event's latest record
     const int lim = std::min(nl, i + 2 * W);
     const bool wait_i = adam && e->pipe && e->preloaded && i < W;
     for (;;) {
