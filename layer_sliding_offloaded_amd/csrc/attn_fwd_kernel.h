@@ -15,6 +15,10 @@
 // exponentials and AGPR copies have no second wave to overlap with.  F = 2
 // at two blocks per CU is what runs.
 //
+// Blocks of NW = 8 waves (256 query rows, one block per CU) gave the same
+// bits and times within the launch-to-launch spread of 4-wave blocks at the
+// 1.3B, 6.7B and 123B shapes; 4 waves run.
+//
 // The arithmetic of a query row does not depend on F: the same key tiles in
 // the same order, the same MFMA accumulation orders, the same lazy shift of
 // the exponent, so every F gives the same bits.
@@ -28,10 +32,10 @@ namespace {
 // Grid: (n_heads, query tiles, batch); the query tile index runs backwards
 // so that the blocks with the most key tiles are dispatched first across all
 // heads.
-template <typename T, int D, int F, int MINB>
-__global__ void __launch_bounds__(256, MINB)
+template <typename T, int D, int F, int MINB, int NW = 4>
+__global__ void __launch_bounds__(NW * 64, MINB)
 attn_fwd_kernel(const AttnArgs a, int qkv_bytes) {
-  constexpr int NW = 4, BQ = NW * F * 16, BKV = 64;
+  constexpr int BQ = NW * F * 16, BKV = 64;
   constexpr int DC = D / 32;  // MFMA k-steps along d
   constexpr int FD = D / 16;
   constexpr int TB = BKV * D * 2;
@@ -231,11 +235,11 @@ attn_fwd_kernel(const AttnArgs a, int qkv_bytes) {
   }
 }
 
-template <typename T, int D, int F, int MINB>
+template <typename T, int D, int F, int MINB, int NW = 4>
 hipError_t launch_fwd(const AttnArgs& a, int64_t qkv_bytes, hipStream_t s) {
-  constexpr int BQ = 4 * F * 16;
+  constexpr int BQ = NW * F * 16;
   dim3 grid(a.n_heads, (a.seq + BQ - 1) / BQ, a.batch);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, F, MINB>), grid, dim3(256), 0, s, a, static_cast<int>(qkv_bytes));
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, F, MINB, NW>), grid, dim3(NW * 64), 0, s, a, static_cast<int>(qkv_bytes));
   return hipGetLastError();
 }
 
