@@ -369,7 +369,8 @@ enum {
  *       rows and a row map rather than the dense [V, H] gradient).  With
  *       SF_ENGINE_ADAM the resident tensors are updated in place by default
  *       on the device from d_head_state (device fp32 [master | m | v], each
- *       2 V H + H floats in [E | gf | Wlm] order).  With SF_ENGINE_HEAD_HOST_ADAM instead: h_head_grads (pinned
+ *       2 V H + H floats in [E | gf | Wlm] order; the caller sets the
+ *       masters and zeroes both moments before the first step).  With SF_ENGINE_HEAD_HOST_ADAM instead: h_head_grads (pinned
  *       fp32, 2 V H + H), h_head_params (pinned, storage dtype [E | gf |
  *       Wlm]) and fp32 host h_head_master/m/v; the LM-head gradients leave
  *       after the head, the embedding gradient leaves as its nonzero rows,

@@ -29,13 +29,35 @@ def storage_dtype(w):
     return DTYPES[w.dtype][1]
 
 
+# When true, every buffer this module allocates (and empty() / empty_like())
+# starts as all-ones bytes, which is NaN in fp32, bf16 and fp16: a kernel or
+# copy that reads memory nothing wrote then spreads NaN into its results
+# instead of whatever the allocator last held.  The parity tests turn it on.
+POISON = False
+
+
+def _poison(t):
+    if POISON:
+        t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
 def device_bytes(n, device="cuda"):
     """Uninitialised device buffer of n bytes (torch allocations are >= 256-B aligned)."""
-    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+    return _poison(torch.empty(max(int(n), 256), dtype=torch.uint8, device=device))
 
 
 def pinned_bytes(n):
-    return torch.empty(max(int(n), 256), dtype=torch.uint8, pin_memory=True)
+    return _poison(torch.empty(max(int(n), 256), dtype=torch.uint8, pin_memory=True))
+
+
+def empty(*shape, dtype=torch.float32, device="cuda", pin_memory=False):
+    """torch.empty (poisoned when POISON is set)."""
+    return _poison(torch.empty(*shape, dtype=dtype, device=device, pin_memory=pin_memory))
+
+
+def empty_like(t):
+    return _poison(torch.empty_like(t))
 
 
 def to_storage_tensor(a, w):
@@ -218,8 +240,8 @@ class Engine:
             self.d_E = to_storage_tensor(head["E"], w).cuda()
             self.d_gf = to_storage_tensor(head["gf"], w).cuda()
             self.d_wlm = to_storage_tensor(head["Wlm"], w).cuda()
-            self.d_head_grads = torch.empty(2 * V * H + H, dtype=torch.float32, device="cuda")
-            self.h_head_grads = torch.empty(2 * V * H + H, dtype=torch.float32, pin_memory=True)
+            self.d_head_grads = empty(2 * V * H + H, dtype=torch.float32)
+            self.h_head_grads = empty(2 * V * H + H, dtype=torch.float32, device="cpu", pin_memory=True)
             flat = np.concatenate([head["E"].reshape(-1), head["gf"].reshape(-1), head["Wlm"].reshape(-1)])
             self.h_head_params = torch.empty(flat.size, dtype=dt, pin_memory=True)
             self.h_head_params.copy_(to_storage_tensor(flat, w))

@@ -73,9 +73,15 @@ int g_fail = 0;
     }                                   \
   } while (0)
 
+// "Device" memory starts as all-ones bytes: NaN in fp32, bf16 and fp16, so a
+// stand-in that reads a device buffer before anything wrote it spreads NaN
+// into a result that must equal the sequential model's (FAKE_HIP_POISON=0
+// starts from zeros instead).
 void* dev_alloc(size_t bytes) {
-  void* p = std::aligned_alloc(256, (bytes + 255) / 256 * 256 + 256);
-  std::memset(p, 0, (bytes + 255) / 256 * 256 + 256);
+  const size_t n = (bytes + 255) / 256 * 256 + 256;
+  void* p = std::aligned_alloc(256, n);
+  const char* pz = std::getenv("FAKE_HIP_POISON");
+  std::memset(p, (pz && pz[0] == '0') ? 0 : 0xFF, n);
   return p;
 }
 void* pinned(size_t bytes) {
@@ -362,6 +368,7 @@ struct Run {
       } else if (adam) {
         d_head_state = static_cast<float*>(dev_alloc(3 * NH * 4));
         std::memcpy(d_head_state, st0.head_master.data(), NH * 4);
+        std::memset(d_head_state + NH, 0, 2 * NH * 4);  // moments start at zero
         c.d_head_state = d_head_state;
       }
       d_ids = static_cast<int32_t*>(dev_alloc(T * 4));

@@ -42,10 +42,10 @@ class LayerRun:
         self.dw = rt.pack_params(L, params, w).cuda()
         self.x = rt.to_storage_tensor(x, w).cuda()
         self.dy = rt.to_storage_tensor(dy, w).cuda()
-        self.y = torch.empty_like(self.x)
-        self.dx = torch.empty_like(self.x)
+        self.y = rt.empty_like(self.x)
+        self.dx = rt.empty_like(self.x)
         self.saved = rt.device_bytes(L.saved_bytes)
-        self.grads = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+        self.grads = rt.empty(L.grad_bytes // 4, dtype=torch.float32)
         self.shapes = {k: v.shape for k, v in params.items()}
 
     def fwd(self):

@@ -46,7 +46,7 @@ def test_gemm_parity(layout, dtype, M, N, K):
     ref = (a64.T if layout == 2 else a64) @ (b64.T if layout == 0 else b64)
     dA, dB = A.cuda(), B.cuda()
     wsb = sf.sf_gemm_workspace_bytes(M, N, K)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = rt.empty(max(wsb, 16), dtype=torch.uint8)
     out = {}
     for split in (False, True):
         for out_f32 in (1, 0):

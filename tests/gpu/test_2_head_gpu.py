@@ -22,10 +22,10 @@ def run_head(w, chunk, gf, Wlm, x, ids, grad_scale=None, dw_rows=0):
     d_wlm = rt.to_storage_tensor(Wlm, w).cuda()
     d_x = rt.to_storage_tensor(x, w).cuda()
     d_ids = torch.from_numpy(ids.reshape(-1).astype(np.int32)).cuda()
-    loss = torch.empty(1, dtype=torch.float32, device="cuda")
-    dx = torch.empty_like(d_x)
-    dgf = torch.empty(w.hidden, dtype=torch.float32, device="cuda")
-    dwlm = torch.empty(w.vocab, w.hidden, dtype=torch.float32, device="cuda")
+    loss = rt.empty(1, dtype=torch.float32)
+    dx = rt.empty_like(d_x)
+    dgf = rt.empty(w.hidden, dtype=torch.float32)
+    dwlm = rt.empty(w.vocab, w.hidden, dtype=torch.float32)
     if grad_scale is None:
         sf.sf_head_fwd_bwd(c.ctx, d_gf.data_ptr(), d_wlm.data_ptr(), d_x.data_ptr(), d_ids.data_ptr(),
                            loss.data_ptr(), dx.data_ptr(), dgf.data_ptr(), dwlm.data_ptr(), rt.stream_handle())
@@ -169,12 +169,12 @@ def test_embedding_gather_and_scatter():
     ids = si.token_ids(w)  # 384 ids over 64 rows: many repeats
     d_E = rt.to_storage_tensor(E, w).cuda()
     d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
-    x0 = torch.empty(w.tokens, w.hidden, dtype=torch.bfloat16, device="cuda")
+    x0 = rt.empty(w.tokens, w.hidden, dtype=torch.bfloat16)
     sf.sf_embed_fwd(c.ctx, d_E.data_ptr(), d_ids.data_ptr(), x0.data_ptr(), rt.stream_handle())
     g = si.upstream_grad(w).reshape(w.tokens, w.hidden)
     d_g = rt.to_storage_tensor(g, w).cuda()
-    dE1 = torch.empty(w.vocab, w.hidden, dtype=torch.float32, device="cuda")
-    dE2 = torch.empty_like(dE1)
+    dE1 = rt.empty(w.vocab, w.hidden, dtype=torch.float32)
+    dE2 = rt.empty_like(dE1)
     sf.sf_embed_bwd(c.ctx, d_g.data_ptr(), d_ids.data_ptr(), dE1.data_ptr(), rt.stream_handle())
     sf.sf_embed_bwd(c.ctx, d_g.data_ptr(), d_ids.data_ptr(), dE2.data_ptr(), rt.stream_handle())
     torch.cuda.synchronize()

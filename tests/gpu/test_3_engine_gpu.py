@@ -37,20 +37,20 @@ def manual_step(w, layers, head, ids, chunk, t, hp, masters, moments, head_state
     d_gf = rt.to_storage_tensor(head["gf"], w).cuda()
     d_wlm = rt.to_storage_tensor(head["Wlm"], w).cuda()
     d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
-    xs = [torch.empty(w.tokens, w.hidden, dtype=dt, device="cuda") for _ in range(len(layers) + 1)]
+    xs = [rt.empty(w.tokens, w.hidden, dtype=dt) for _ in range(len(layers) + 1)]
     saved = [rt.device_bytes(L.saved_bytes) for _ in layers]
     sf.sf_embed_fwd(c.ctx, d_E.data_ptr(), d_ids.data_ptr(), xs[0].data_ptr(), s)
     for i in range(len(layers)):
         sf.sf_layer_fwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), xs[i + 1].data_ptr(), saved[i].data_ptr(), s)
     V, H = w.vocab, w.hidden
-    hg = torch.empty(2 * V * H + H, dtype=torch.float32, device="cuda")
-    loss = torch.empty(1, dtype=torch.float32, device="cuda")
-    dbuf = torch.empty_like(xs[0])
+    hg = rt.empty(2 * V * H + H, dtype=torch.float32)
+    loss = rt.empty(1, dtype=torch.float32)
+    dbuf = rt.empty_like(xs[0])
     sf.sf_head_fwd_bwd(c.ctx, d_gf.data_ptr(), d_wlm.data_ptr(), xs[-1].data_ptr(), d_ids.data_ptr(), loss.data_ptr(),
                        dbuf.data_ptr(), hg[V * H:].data_ptr(), hg[V * H + H:].data_ptr(), s)
     grads = []
     for i in reversed(range(len(layers))):
-        g = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+        g = rt.empty(L.grad_bytes // 4, dtype=torch.float32)
         sf.sf_layer_bwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), saved[i].data_ptr(), dbuf.data_ptr(),
                         dbuf.data_ptr(), g.data_ptr(), s)
         grads.insert(0, g)
@@ -147,7 +147,7 @@ def test_device_adam_matches_host_bitwise_and_oracle(dtype):
     dp = torch.from_numpy(p0.copy()).cuda()
     dm = torch.zeros(n, device="cuda")
     dv = torch.zeros(n, device="cuda")
-    out = torch.empty(n, dtype=torch.bfloat16 if dtype == sf.SF_BF16 else torch.float32, device="cuda")
+    out = rt.empty(n, dtype=torch.bfloat16 if dtype == sf.SF_BF16 else torch.float32)
     hb = np.zeros(n, np.uint16)
     p64, m64, v64 = p0.astype(np.float64), np.zeros(n), np.zeros(n)
     for t in (1, 2, 3):
@@ -187,7 +187,7 @@ def test_host_adam_vector_path_bitwise(n, off):
                     hb[off:].ctypes.data, n, 2, hp["lr"], hp["b1"], hp["b2"], hp["eps"], 3)
     dp, dm, dv = (torch.from_numpy(a[off:].copy()).cuda() for a in (p0, m0, v0))
     dg = torch.from_numpy(g[off:].copy()).cuda()
-    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    out = rt.empty(n, dtype=torch.bfloat16)
     sf.sf_adam_device(sf.SF_BF16, dp.data_ptr(), dm.data_ptr(), dv.data_ptr(), dg.data_ptr(), out.data_ptr(), n, 2,
                       hp["lr"], hp["b1"], hp["b2"], hp["eps"], rt.stream_handle())
     torch.cuda.synchronize()
@@ -274,12 +274,12 @@ def test_engine_without_head_or_adam():
     L = c.layout
     s = rt.stream_handle()
     dws = [rt.pack_params(L, p, w).cuda() for p in layers]
-    xs = [d_x] + [torch.empty_like(d_x) for _ in layers]
+    xs = [d_x] + [rt.empty_like(d_x) for _ in layers]
     saved = [rt.device_bytes(L.saved_bytes) for _ in layers]
     for i in range(3):
         sf.sf_layer_fwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), xs[i + 1].data_ptr(), saved[i].data_ptr(), s)
     d = d_dy.clone()
-    g = torch.empty(L.grad_bytes // 4, dtype=torch.float32, device="cuda")
+    g = rt.empty(L.grad_bytes // 4, dtype=torch.float32)
     for i in reversed(range(3)):
         sf.sf_layer_bwd(c.ctx, dws[i].data_ptr(), xs[i].data_ptr(), saved[i].data_ptr(), d.data_ptr(), d.data_ptr(),
                         g.data_ptr(), s)

@@ -56,7 +56,7 @@ def test_adam_f16_host_device_bitwise_and_oracle(scale):
     p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
     hp_, hm, hv = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
     dp, dm, dv = (torch.from_numpy(a.copy()).cuda() for a in (p0, hm, hv))
-    out = torch.empty(n, dtype=torch.float16, device="cuda")
+    out = rt.empty(n, dtype=torch.float16)
     hb = np.zeros(n, np.uint16)
     p64, m64, v64 = p0.astype(np.float64), np.zeros(n), np.zeros(n)
     for t in (1, 2, 3):

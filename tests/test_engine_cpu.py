@@ -9,6 +9,9 @@ pipelined steps, checkpointing, host or device head Adam, windows 2 and 3,
 keep-turnaround without Adam, no head, fp32, fp16 loss scaling with and
 without an injected non-finite layer -- and compares every loss, master,
 moment and parameter bit for bit with a sequential model of the same steps.
+Every "device" buffer (pool, activation region, workspace, head scratch)
+starts as all-ones bytes (NaN in every storage dtype), so a stand-in that
+reads device memory before the engine's data reached it breaks the match.
 
 * ThreadSanitizer build: random delays in every stream (FAKE_HIP_JITTER_US)
   vary the interleavings; any access the engine leaves unordered is
