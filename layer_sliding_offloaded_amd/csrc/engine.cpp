@@ -878,12 +878,27 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
     return SF_OK;
   };
-  auto in_gslot = [&](int i) { return i % (2 * W) >= W; };
+  // Forward buffers.  By default layer i runs from unit i % W: from its
+  // parameter region when i mod 2W < W, from its gradient region otherwise,
+  // so an upload waits for the forward of the layer 2W back.  Without Adam
+  // after a preloaded start (params_first) the previous step's last
+  // gradients are still leaving the gradient regions as the forward begins:
+  // in pages of W layers, pages 0 (the preloaded layers) and 1 then both run
+  // from parameter regions (page 1 behind the forward of the layer W back),
+  // gradient and parameter regions alternate after that, and layer k of a
+  // gradient page takes unit W-1-k, the order in which the previous
+  // backward's gradients leave the regions.
+  const bool params_first = e->preloaded && !adam;
+  auto in_gslot = [&](int i) { return params_first ? (i >= 2 * W && (i / W) % 2 == 0) : (i % (2 * W) >= W); };
+  auto gunit = [&](int i) { return params_first ? W - 1 - i % W : i % W; };
+  // the layer whose forward an upload of layer j waits for (the buffer's
+  // previous user in this step; negative: none)
+  auto dep = [&](int j) { return params_first && j < 2 * W ? j - W : j - 2 * W; };
   auto fetch = [&](int j) -> sf_status {
     if (e->preloaded && j < W) return SF_OK;
     if (sf_status r = await_adam(j)) return r;
     if (!in_gslot(j)) return prefetch(e, j);
-    const int u = j % W;
+    const int u = gunit(j);
     // The region's last gradients must be out.  The host waits for that
     // copy rather than the H2D stream: an H2D queue waiting on the D2H
     // queue's event while later gradient copies are still queued sent those
@@ -891,7 +906,7 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     // Adam, whose last copies run into the next forward).  In synchronous
     // steps and with Adam the copy is long done here.
     SF_HIP(hipEventSynchronize(e->ev_grad_free[u]));
-    SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_gslot_free[u], 0));  // layer j - 2W's forward
+    SF_HIP(hipStreamWaitEvent(e->s_h2d, e->ev_gslot_free[u], 0));  // layer dep(j)'s forward
     if (sf_status r = timed_h2d(e, e->ugrad[u], c.h_params[j], e->L.param_bytes, e->s_h2d)) return r;
     SF_HIP(hipEventRecord(e->ev_gslot_ready[u], e->s_h2d));
     return SF_OK;
@@ -965,21 +980,69 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
       else e->cv.wait(lk, progress);
     }
   };
+  // params_first: uploads are queued in layer order once the forward they
+  // wait for is queued.  While the next one still waits for its region to
+  // drain, a later one that does not is queued whenever the H2D queue has
+  // run dry, and the forward of layer i goes ahead unless it needs that
+  // upload (the host polls the device meanwhile).
+  hipEvent_t last_up = nullptr;
+  auto done = [&](hipEvent_t ev, bool* yes) -> sf_status {
+    const hipError_t q = ev ? hipEventQuery(ev) : hipSuccess;
+    if (q != hipSuccess && q != hipErrorNotReady) return fail(SF_ERR_HIP, "%s", hipGetErrorString(q));
+    *yes = q == hipSuccess;
+    return SF_OK;
+  };
+  auto advance_pf = [&](int i) -> sf_status {
+    const int lim = std::min(nl, i + 2 * W);
+    for (;;) {
+      int j0 = -1;
+      for (int j = W; j < lim && j0 < 0; ++j)
+        if (!fetched[j] && dep(j) < i) j0 = j;
+      if (j0 < 0) return SF_OK;
+      auto ready = [&](int j, bool* yes) -> sf_status {
+        *yes = true;
+        return in_gslot(j) ? done(e->ev_grad_free[gunit(j)], yes) : SF_OK;
+      };
+      int pick = -1;
+      bool yes = false;
+      if (sf_status r = ready(j0, &yes)) return r;
+      if (yes) {
+        pick = j0;
+      } else {
+        bool idle = false;
+        if (sf_status r = done(last_up, &idle)) return r;
+        for (int j = j0 + 1; idle && j < lim && pick < 0; ++j) {
+          if (fetched[j] || dep(j) >= i) continue;
+          if (sf_status r = ready(j, &yes)) return r;
+          if (yes) pick = j;
+        }
+      }
+      if (pick >= 0) {
+        if (sf_status r = fetch(pick)) return r;
+        fetched[pick] = 1;
+        last_up = in_gslot(pick) ? e->ev_gslot_ready[gunit(pick)] : e->ev_param_ready[pick % W];
+        continue;
+      }
+      if (j0 > i) return SF_OK;
+      std::this_thread::sleep_for(std::chrono::microseconds(20));
+    }
+  };
   for (int i = 0; i < nl; ++i) {
     const int u = i % W;
     const bool gs = in_gslot(i);
-    if ((rc = advance(i))) return rc;
+    const int ug = gunit(i);
+    if ((rc = params_first ? advance_pf(i) : advance(i))) return rc;
     if (e->preloaded && i < W && (rc = await_adam(i))) return rc;
-    SF_HIP(hipStreamWaitEvent(e->s_comp, gs ? e->ev_gslot_ready[u] : e->ev_param_ready[u], 0));
+    SF_HIP(hipStreamWaitEvent(e->s_comp, gs ? e->ev_gslot_ready[ug] : e->ev_param_ready[u], 0));
     // the output slot held x_{i-2}: its copy to the host must be done
     if (ck && i >= 2) SF_HIP(hipStreamWaitEvent(e->s_comp, e->ev_xfree[(i + 1) % 3], 0));
     if ((rc = comp_begin(&a))) return rc;
     void* sv = ck ? e->sv[i == nl - 1 ? 1 : 0] : e->saved[i];
-    if ((rc = sf_layer_fwd(ctx, gs ? e->ugrad[u] : e->uparam[u], xin[i], xslot(i + 1), sv, e->s_comp))) return rc;
+    if ((rc = sf_layer_fwd(ctx, gs ? e->ugrad[ug] : e->uparam[u], xin[i], xslot(i + 1), sv, e->s_comp))) return rc;
     if (gs && i >= nl - W)  // stays for the backward: into the parameter region (layer i - W is done with it)
-      SF_HIP(hipMemcpyAsync(e->uparam[u], e->ugrad[u], e->L.param_bytes, hipMemcpyDeviceToDevice, e->s_comp));
+      SF_HIP(hipMemcpyAsync(e->uparam[u], e->ugrad[ug], e->L.param_bytes, hipMemcpyDeviceToDevice, e->s_comp));
     if ((rc = comp_end(a, &b))) return rc;
-    SF_HIP(hipEventRecord(gs ? e->ev_gslot_free[u] : e->ev_param_free[u], e->s_comp));
+    SF_HIP(hipEventRecord(gs ? e->ev_gslot_free[ug] : e->ev_param_free[u], e->s_comp));
     if ((rc = ckpt_out(i + 1, b))) return rc;
   }
   if (ck && nl >= 2) SF_HIP(hipEventRecord(e->ev_ckpt_out, e->s_d2h));

@@ -59,6 +59,12 @@ const Scenario kScenarios[] = {
     {"f16-scale", SF_ENGINE_ADAM | SF_ENGINE_HEAD | SF_ENGINE_PIPELINE, 2, 2, 4, SF_F16, 3, true, -1},
     {"f16-fault", SF_ENGINE_ADAM | SF_ENGINE_HEAD, 2, 2, 4, SF_F16, 3, true, 1},
     {"f16-fault-pipe-nohead", SF_ENGINE_ADAM | SF_ENGINE_PIPELINE, 2, 2, 4, SF_F16, 3, false, 2},
+    // keep-turnaround without Adam past two windows: gradient-region pages in
+    // the forward (a slot per layer, so the last step's gradients all stay)
+    {"noadam-keep-pipe-l8", SF_ENGINE_KEEP_TURNAROUND | SF_ENGINE_PIPELINE, 2, 8, 8, SF_BF16, 4, false, -1},
+    {"noadam-keep-l7", SF_ENGINE_HEAD | SF_ENGINE_KEEP_TURNAROUND, 2, 7, 7, SF_BF16, 3, true, -1},
+    {"noadam-keep-pipe-w3-l10", SF_ENGINE_HEAD | SF_ENGINE_KEEP_TURNAROUND | SF_ENGINE_PIPELINE, 3, 10, 10, SF_BF16, 3,
+     true, -1},
 };
 
 constexpr float kLr = 1e-3f, kB1 = 0.9f, kB2 = 0.999f, kEps = 1e-8f;

@@ -4,9 +4,9 @@ engine.cpp, adam.cpp and layout.cpp are compiled unchanged with g++ against
 a fake HIP runtime (tests/engine_cpu/fake_hip.cpp: one worker thread per
 stream, events with the runtime's ordering rules and nothing more) and
 stand-in kernels that touch the real buffers (fake_kernels.cpp).  The
-driver (engine_check.cpp) runs 13 engine configurations -- synchronous and
+driver (engine_check.cpp) runs 16 engine configurations -- synchronous and
 pipelined steps, checkpointing, host or device head Adam, windows 2 and 3,
-keep-turnaround without Adam, no head, fp32, fp16 loss scaling with and
+keep-turnaround without Adam (also past two windows, windows 2 and 3), no head, fp32, fp16 loss scaling with and
 without an injected non-finite layer -- and compares every loss, master,
 moment and parameter bit for bit with a sequential model of the same steps.
 Every "device" buffer (pool, activation region, workspace, head scratch)
@@ -99,14 +99,14 @@ def test_engine_matches_sequential_model_without_races(builds, jitter, seed):
     p = _run(builds["tsan"], jitter, seed)
     assert "ThreadSanitizer" not in p.stderr, p.stderr[-6000:]
     assert p.returncode == 0, p.stdout[-3000:] + p.stderr[-3000:]
-    assert "13 scenarios, 0 failures" in p.stdout
+    assert "16 scenarios, 0 failures" in p.stdout
 
 
 def test_engine_memory_and_undefined_behaviour(builds):
     p = _run(builds["asan"], 30, 5, san="asan")
     assert "Sanitizer" not in p.stderr and "runtime error" not in p.stderr, p.stderr[-6000:]
     assert p.returncode == 0, p.stdout[-3000:]
-    assert "13 scenarios, 0 failures" in p.stdout
+    assert "16 scenarios, 0 failures" in p.stdout
 
 
 def test_checker_reports_a_missing_wait(tmp_path):
@@ -114,7 +114,7 @@ def test_checker_reports_a_missing_wait(tmp_path):
     waits for a layer's parameters before its forward.  The checker must
     fail the scenario (a race report, a wrong result, or both)."""
     src = open(os.path.join(CSRC, "engine.cpp")).read()
-    line = "    SF_HIP(hipStreamWaitEvent(e->s_comp, gs ? e->ev_gslot_ready[u] : e->ev_param_ready[u], 0));\n"
+    line = "    SF_HIP(hipStreamWaitEvent(e->s_comp, gs ? e->ev_gslot_ready[ug] : e->ev_param_ready[u], 0));\n"
     assert src.count(line) == 1
     mutant = tmp_path / "engine.cpp"
     mutant.write_text(src.replace(line, ""))
