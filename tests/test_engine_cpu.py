@@ -19,8 +19,9 @@ reads device memory before the engine's data reached it breaks the match.
   slow copies expose waits that fast ones hide behind the engine's own
   event polling.
 * AddressSanitizer + UndefinedBehaviorSanitizer build of the same.
-* A mutation check: the forward's wait for its parameters removed from a
-  copy of engine.cpp must be reported.
+* Mutation checks: the forward's wait for its parameters removed from a
+  copy of engine.cpp, or an upload that waits for the wrong forward, must
+  be reported.
 """
 
 import os
@@ -124,3 +125,21 @@ def test_checker_reports_a_missing_wait(tmp_path):
     p = _run(exe, 50, 1, "adam-sync", "adam-pipe")
     assert p.returncode != 0
     assert "ThreadSanitizer: data race" in p.stderr or "FAIL:" in p.stdout
+
+
+def test_checker_reports_a_wrong_upload_dependency(tmp_path):
+    """Plant a bug in a copy of engine.cpp: without Adam after a preloaded
+    start, the second page's uploads wait for the forward 2W layers back (none)
+    instead of W back, so they overwrite parameters a forward still reads.
+    The configurations with gradient-region pages must fail."""
+    src = open(os.path.join(CSRC, "engine.cpp")).read()
+    line = "  auto dep = [&](int j) { return params_first && j < 2 * W ? j - W : j - 2 * W; };\n"
+    assert src.count(line) == 1
+    mutant = tmp_path / "engine.cpp"
+    mutant.write_text(src.replace(line, "  auto dep = [&](int j) { return j - 2 * W; };\n"))
+    sources = [(str(mutant), ["-mf16c"]) if s.endswith("engine.cpp") else (s, f) for s, f in SOURCES]
+    exe = _compile(str(tmp_path), "tsan", sources, [os.path.join(HERE, "tsan_clockwait.cpp")])
+    p = _run(exe, 30, 1, "noadam-keep-pipe-l8", "noadam-keep-l7", "noadam-keep-pipe-w3-l10")
+    assert p.returncode != 0
+    assert "ThreadSanitizer: data race" in p.stderr or "FAIL:" in p.stdout
+
