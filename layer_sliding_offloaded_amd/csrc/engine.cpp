@@ -862,15 +862,6 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
   // after their Adam, when that step ran Adam).  Pipelined, the previous
   // step's Adam of layer j may still be running: wait for it before its
   // parameters are read (host copy) or its upload is waited on (units).
-  // A unit's gradient region is idle in the forward once the previous
-  // backward's gradients have left, and holds a layer's parameters twice
-  // over: layers with i mod 2W >= W run from there, so an upload waits for
-  // the layer 2W back instead of W back.  Of the last W layers, which stay
-  // for the backward, those in a gradient region move to their unit's
-  // parameter region by a device copy after their forward.  Uploads are
-  // queued in layer order as far ahead as the slots allow (2W - 1 layers);
-  // pipelined, one whose update is still running waits for a later turn
-  // unless the next forward needs it.
   auto await_adam = [&](int j) -> sf_status {
     if (!adam || !e->pipe) return SF_OK;
     std::unique_lock<std::mutex> lk(e->mu);
@@ -878,9 +869,14 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     if (!e->job_error.empty()) return fail(SF_ERR_HIP, "%s", e->job_error.c_str());
     return SF_OK;
   };
-  // Forward buffers.  By default layer i runs from unit i % W: from its
+  // Forward buffers.  A unit's gradient region is idle in the forward once
+  // the previous backward's gradients have left, so it holds a layer's
+  // parameters too.  By default layer i runs from unit i % W: from its
   // parameter region when i mod 2W < W, from its gradient region otherwise,
-  // so an upload waits for the forward of the layer 2W back.  Without Adam
+  // so an upload waits for the forward of the layer 2W back instead of W
+  // back.  Of the last W layers, which stay for the backward, those in a
+  // gradient region move to their unit's parameter region by a device copy
+  // after their forward.  Without Adam
   // after a preloaded start (params_first) the previous step's last
   // gradients are still leaving the gradient regions as the forward begins:
   // in pages of W layers, pages 0 (the preloaded layers) and 1 then both run
@@ -916,8 +912,11 @@ sf_status step_impl(sf_engine* e, const void* d_in, const void* d_dy, sf_step_st
     std::lock_guard<std::mutex> lk(e->mu);
     return e->adam_done[j] >= e->step - 1;
   };
-  // Uploads are queued in layer order, except the first window of layers
-  // that run from gradient regions (W .. 2W-1) after a preloaded start: those
+  // Default order: uploads are queued in layer order as far ahead as the
+  // buffers allow (2W - 1 layers); pipelined, one whose update is still
+  // running waits for a later turn unless the next forward needs it.  The
+  // exception is the first window of layers that run from gradient regions
+  // (W .. 2W-1) after a preloaded start (with Adam): those
   // regions are freed by the previous backward from unit W-1 down to unit 0,
   // so each of these layers is queued, highest first, as soon as its update
   // is done rather than behind a lower one still waiting for its region.
