@@ -297,6 +297,46 @@ def test_engine_without_head_or_adam():
     eng.close()
 
 
+@pytest.mark.parametrize("window,n_layers,with_head", [(2, 8, False), (2, 7, True), (3, 10, False)])
+def test_engine_keep_turnaround_pages_match_plain_bitwise(window, n_layers, with_head):
+    """Without Adam after the first step, the forward runs its layers from
+    parameter regions for the first two windows, then alternates gradient
+    and parameter regions (a gradient window's layers in reverse unit
+    order), and queues uploads around the previous step's gradients still
+    leaving.  Every step must give the same loss and gradients, bit for
+    bit, as one plain step."""
+    w = STACK.with_(n_layers=n_layers, vocab=STACK.vocab if with_head else 0)
+    say("engine-keep-pages", window, n_layers, with_head, w)
+    layers, head = make_stack(w, n_layers)
+    if not with_head:
+        head = None
+    if head is not None:
+        d_in = torch.from_numpy(si.token_ids(w).reshape(-1)).cuda()
+        d_dy = None
+    else:
+        d_in = rt.to_storage_tensor(si.layer_input(w), w).cuda()
+        d_dy = rt.to_storage_tensor(si.upstream_grad(w), w).cuda()
+    ref = rt.Engine(w, layers, head, window=window, n_grad_slots=n_layers, adam=False)
+    loss0, st0 = ref.step(d_in, d_dy)
+    ref.sync()
+    ref_slots = [t.numpy().copy() for t in ref.h_slots]
+    ref.close()
+    eng = rt.Engine(w, layers, head, window=window, n_grad_slots=n_layers, adam=False, pipeline=True,
+                    keep_turnaround=True)
+    # three steps in one window: each step's forward overlaps the previous
+    # step's last gradient copies, and every step writes the same slots
+    losses = [eng.step(d_in, d_dy)[0] for _ in range(3)]
+    agg = eng.sync()
+    torch.cuda.synchronize()
+    if head is not None:
+        assert losses == [loss0] * 3
+    for k in range(n_layers):
+        assert np.array_equal(eng.h_slots[k].numpy(), ref_slots[k]), k
+    assert agg["h2d_bytes"] == 3 * st0["h2d_bytes"] - 2 * window * eng.layout.param_bytes
+    assert agg["d2h_bytes"] == 3 * st0["d2h_bytes"]
+    eng.close()
+
+
 def _run_engine(w, layers, head, x, dy, steps, **kw):
     """Steps an engine and returns per-step snapshots of everything it updates."""
     eng = rt.Engine(w, layers, head, n_grad_slots=2, adam=True, chunk=96, adam_hp=si.ADAM, **kw)
