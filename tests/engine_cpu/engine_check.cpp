@@ -64,6 +64,8 @@ const Scenario kScenarios[] = {
     {"noadam-keep-pipe-l8", SF_ENGINE_KEEP_TURNAROUND | SF_ENGINE_PIPELINE, 2, 8, 8, SF_BF16, 4, false, -1},
     {"noadam-keep-l7", SF_ENGINE_HEAD | SF_ENGINE_KEEP_TURNAROUND, 2, 7, 7, SF_BF16, 3, true, -1},
     {"noadam-keep-pipe-l5", SF_ENGINE_KEEP_TURNAROUND | SF_ENGINE_PIPELINE, 2, 5, 5, SF_BF16, 4, false, -1},
+    {"noadam-keep-pipe-ckpt-l8", SF_ENGINE_HEAD | SF_ENGINE_KEEP_TURNAROUND | SF_ENGINE_PIPELINE | SF_ENGINE_CKPT, 2, 8,
+     8, SF_BF16, 3, true, -1},
     {"noadam-keep-pipe-w3-l10", SF_ENGINE_HEAD | SF_ENGINE_KEEP_TURNAROUND | SF_ENGINE_PIPELINE, 3, 10, 10, SF_BF16, 3,
      true, -1},
 };

@@ -4,9 +4,10 @@ engine.cpp, adam.cpp and layout.cpp are compiled unchanged with g++ against
 a fake HIP runtime (tests/engine_cpu/fake_hip.cpp: one worker thread per
 stream, events with the runtime's ordering rules and nothing more) and
 stand-in kernels that touch the real buffers (fake_kernels.cpp).  The
-driver (engine_check.cpp) runs 17 engine configurations -- synchronous and
+driver (engine_check.cpp) runs 18 engine configurations -- synchronous and
 pipelined steps, checkpointing, host or device head Adam, windows 2 and 3,
-keep-turnaround without Adam (also past two windows, windows 2 and 3), no head, fp32, fp16 loss scaling with and
+keep-turnaround without Adam (also past two windows, windows 2 and 3, and
+with checkpointing), no head, fp32, fp16 loss scaling with and
 without an injected non-finite layer -- and compares every loss, master,
 moment and parameter bit for bit with a sequential model of the same steps.
 Every "device" buffer (pool, activation region, workspace, head scratch)
@@ -100,14 +101,14 @@ def test_engine_matches_sequential_model_without_races(builds, jitter, seed):
     p = _run(builds["tsan"], jitter, seed)
     assert "ThreadSanitizer" not in p.stderr, p.stderr[-6000:]
     assert p.returncode == 0, p.stdout[-3000:] + p.stderr[-3000:]
-    assert "17 scenarios, 0 failures" in p.stdout
+    assert "18 scenarios, 0 failures" in p.stdout
 
 
 def test_engine_memory_and_undefined_behaviour(builds):
     p = _run(builds["asan"], 30, 5, san="asan")
     assert "Sanitizer" not in p.stderr and "runtime error" not in p.stderr, p.stderr[-6000:]
     assert p.returncode == 0, p.stdout[-3000:]
-    assert "17 scenarios, 0 failures" in p.stdout
+    assert "18 scenarios, 0 failures" in p.stdout
 
 
 def test_checker_reports_a_missing_wait(tmp_path):
