@@ -338,7 +338,10 @@ enum {
  *   d_pool/pool_bytes : device region (256-B aligned) for min(window,
  *       n_layers) cache units; unit u holds one layer's parameters (storage
  *       dtype, param_bytes rounded up to 256) followed by its fp32 gradients
- *       (grad_bytes rounded up to 256).  Layer l always uses unit l % window.
+ *       (grad_bytes rounded up to 256).  In the backward layer l uses unit
+ *       l % window; in the forward the engine also runs layers from the
+ *       gradient regions, which are idle there once the previous backward's
+ *       gradients have left.
  *   d_act/act_bytes   : device region (256-B aligned) of at least
  *       sf_engine_act_bytes_flags(): the n_layers + 1 layer inputs/outputs
  *       [T, H], the n_layers saved activation sets, one [T, H] gradient
