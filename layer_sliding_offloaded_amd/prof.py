@@ -33,6 +33,11 @@ Modes:
   MFMA busy share (``MfmaUtil``: SQ_VALU_MFMA_BUSY_CYCLES over active cycles
   of all SIMDs) and the bf16 MFMA FLOPs the hardware executed
   (``MfmaFlopsBF16``) against the algorithmic FLOPs.
+* ``timeline``: from the engine timeline ``bench.py --trace`` writes (one
+  row per timed interval: compute, H2D or D2H copy, host Adam), the busy
+  time of each kind over the window, the gaps longer than ``--gap`` ms in
+  which no D2H copy runs (with what the H2D copies and the kernels did
+  meanwhile), and the busy share of each kind per ``--bucket`` ms.
 * ``head-study``: the chunked LM head + cross-entropy (``sf_head_fwd_bwd``)
   at one shape for several chunk sizes, the largest being the whole token
   count (every logit materialised at once): device bytes of the head's
@@ -43,6 +48,7 @@ Modes:
     python -m layer_sliding_offloaded_amd.prof kernels RESULTS_DB [--top N]
     python -m layer_sliding_offloaded_amd.prof gemm-runs RESULTS_DB --workload W
     python -m layer_sliding_offloaded_amd.prof rowops RESULTS_DB --workload W
+    python -m layer_sliding_offloaded_amd.prof timeline TRACE_CSV [--gap 20] [--bucket 50]
     python -m layer_sliding_offloaded_amd.prof head-study --hidden 4096 --vocab 128256 --batch 4 --seq 2048 \
         --chunks 8192,4096,2048,1024,512,256
 """
@@ -481,10 +487,62 @@ def head_study(hidden, vocab, batch, seq, chunks, reps=5):
               f"{ms:.3f} | {flops / (ms * 1e-3) / 1e12:.0f} | {lv:.5f} |")
 
 
+def _union(iv):
+    iv = sorted(iv)
+    out = []
+    for a, b in iv:
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def timeline(path, gap_ms, bucket_ms):
+    rows = [(r["kind"], float(r["start_ms"]), float(r["end_ms"]), float(r["info"]))
+            for r in csv.DictReader(open(path))]
+    kinds = sorted({k for k, _, _, _ in rows})
+    t0 = min(a for _, a, _, _ in rows)
+    t1 = max(b for _, _, b, _ in rows)
+    merged = {k: _union([(a, b) for kk, a, b, _ in rows if kk == k]) for k in kinds}
+
+    def busy(k, lo, hi):
+        return sum(max(0.0, min(b, hi) - max(a, lo)) for a, b in merged.get(k, []))
+
+    print(f"window {t1 - t0:.1f} ms, {len(rows)} intervals")
+    print()
+    print("| kind | busy ms | share of the window | bytes |")
+    print("|---|---:|---:|---:|")
+    for k in kinds:
+        by = sum(x for kk, _, _, x in rows if kk == k and kk in ("h2d", "d2h"))
+        print(f"| {k} | {busy(k, t0, t1):.1f} | {100.0 * busy(k, t0, t1) / (t1 - t0):.1f} % | "
+              f"{by / 1e9:.2f} GB |" if by else f"| {k} | {busy(k, t0, t1):.1f} | "
+              f"{100.0 * busy(k, t0, t1) / (t1 - t0):.1f} % | |")
+    d2h = merged.get("d2h", [])
+    gaps = [(d2h[i][1], d2h[i + 1][0]) for i in range(len(d2h) - 1) if d2h[i + 1][0] - d2h[i][1] > gap_ms]
+    print()
+    print(f"Gaps of more than {gap_ms:g} ms without a D2H copy:")
+    print()
+    print("| from ms | to ms | length ms | H2D busy ms | compute busy ms |")
+    print("|---:|---:|---:|---:|---:|")
+    for a, b in gaps:
+        print(f"| {a - t0:.1f} | {b - t0:.1f} | {b - a:.1f} | {busy('h2d', a, b):.1f} | {busy('compute', a, b):.1f} |")
+    print()
+    print(f"Busy share per {bucket_ms:g} ms:")
+    print()
+    print("| ms | " + " | ".join(kinds) + " |")
+    print("|---:|" + "---:|" * len(kinds))
+    lo = t0
+    while lo < t1:
+        hi = lo + bucket_ms
+        print(f"| {lo - t0:.0f} | " + " | ".join(f"{100.0 * busy(k, lo, hi) / bucket_ms:.0f} %" for k in kinds) + " |")
+        lo = hi
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs", "rowops", "head-study",
-                                     "layer-probe", "mfma"])
+                                     "layer-probe", "mfma", "timeline"])
     ap.add_argument("files", nargs="*")
     ap.add_argument("--workload", default="stack4-h1024-bf16")
     ap.add_argument("--top", type=int, default=30)
@@ -493,6 +551,8 @@ def main():
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--seq", type=int, default=2048)
     ap.add_argument("--chunks", default="8192,4096,2048,1024,512,256")
+    ap.add_argument("--gap", type=float, default=20.0)
+    ap.add_argument("--bucket", type=float, default=50.0)
     a = ap.parse_args()
     if a.mode == "probe":
         probe(a.workload)
@@ -508,6 +568,8 @@ def main():
         rowops(a.files[0], a.workload)
     elif a.mode == "head-study":
         head_study(a.hidden, a.vocab, a.batch, a.seq, a.chunks.split(","))
+    elif a.mode == "timeline":
+        timeline(a.files[0], a.gap, a.bucket)
     else:
         kernels(a.files[0], a.top)
 
