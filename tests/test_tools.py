@@ -1,6 +1,6 @@
-"""Host logic of the measurement tools: kernel-name shortening and the rule
+"""Host logic of the measurement tools: kernel-name shortening, the rule
 that a stored HBM-traffic figure is used only for the GEMM source it was
-measured on."""
+measured on, and the engine-timeline summary."""
 
 import json
 
@@ -28,6 +28,21 @@ def test_stored_traffic_requires_matching_source(tmp_path, monkeypatch):
     path.write_text("gemm_source_sha256: 0000\ntraffic_bytes: " + json.dumps(table) + "\n")
     assert bench.stored_traffic("w", "gu_dw") is None
 
+
+
+def test_timeline_busy_times_and_d2h_gaps(tmp_path, capsys):
+    """Overlapping intervals of one kind count once; a D2H gap is reported
+    with the H2D and compute time inside it."""
+    rows = [("compute", 0, 10), ("compute", 5, 20), ("d2h", 0, 30), ("d2h", 100, 150), ("h2d", 40, 90),
+            ("compute", 60, 70)]
+    path = tmp_path / "t.csv"
+    path.write_text("kind,start_ms,end_ms,info\n" + "".join(f"{k},{a},{b},1000000000\n" for k, a, b in rows))
+    prof.timeline(str(path), 20.0, 50.0)
+    out = capsys.readouterr().out
+    assert "window 150.0 ms" in out
+    assert "| compute | 30.0 | 20.0 % | |" in out
+    assert "| d2h | 80.0 | 53.3 % | 2.00 GB |" in out
+    assert "| 30.0 | 100.0 | 70.0 | 50.0 | 10.0 |" in out
 
 
 def test_layer_gemms_cover_the_projection_flops():
