@@ -337,6 +337,34 @@ def test_engine_keep_turnaround_pages_match_plain_bitwise(window, n_layers, with
     eng.close()
 
 
+def test_engine_window_covering_every_layer():
+    """A window of at least the layer count (the degenerate sliding case):
+    every layer stays in its own unit.  The first step uploads each layer
+    once and nothing moves back in; with the parameters kept at the
+    turnaround the next steps upload nothing.  Gradients equal a window-2
+    step's bit for bit."""
+    w = STACK.with_(vocab=0, n_layers=3)
+    say("engine-window-all", w)
+    layers = [si.layer_params(w, l, gains="random") for l in range(3)]
+    d_x = rt.to_storage_tensor(si.layer_input(w), w).cuda()
+    d_dy = rt.to_storage_tensor(si.upstream_grad(w), w).cuda()
+    ref = rt.Engine(w, layers, None, window=2, n_grad_slots=3, adam=False)
+    ref.step(d_x, d_dy)
+    ref.sync()
+    ref_slots = [t.numpy().copy() for t in ref.h_slots]
+    ref.close()
+    eng = rt.Engine(w, layers, None, window=5, n_grad_slots=3, adam=False, keep_turnaround=True)
+    P = eng.layout.param_bytes
+    for step in range(3):
+        _, st = eng.step(d_x, d_dy)
+        eng.sync()
+        torch.cuda.synchronize()
+        assert st["h2d_bytes"] == (3 * P if step == 0 else 0), step
+        for k in range(3):
+            assert np.array_equal(eng.h_slots[k].numpy(), ref_slots[k]), (step, k)
+    eng.close()
+
+
 def _run_engine(w, layers, head, x, dy, steps, **kw):
     """Steps an engine and returns per-step snapshots of everything it updates."""
     eng = rt.Engine(w, layers, head, n_grad_slots=2, adam=True, chunk=96, adam_hp=si.ADAM, **kw)
