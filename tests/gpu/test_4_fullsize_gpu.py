@@ -1,6 +1,7 @@
 """Parity of one decoder layer at the full sizes of the larger workloads (the
 1.3B- and 6.7B-shaped layers, T = 8192, and the 123B-shaped GQA slice,
-hidden 12288, seq 4096), in the same launch configuration the engine uses.
+hidden 12288, seq 4096; the 6.7B-shaped layer also in fp16 storage), in the
+same launch configuration the engine uses.
 
 The fp64 oracle cannot run a whole layer at these sizes, so two exact
 reductions are used:
@@ -24,17 +25,19 @@ from tests.gpu.helpers import LayerRun, check_errors, f64, oracle_shape, rel, sa
 
 pytestmark = pytest.mark.gpu
 
+# name: (workload, prefix P, tolerance, storage unit roundoff of the deltas' floor)
+F16_TOL = 2.5e-3  # the bf16 bound's multiple of the unit roundoff (5.1 x 2^-11)
 CASES = {
-    "llama1.3b-bf16": 160,
-    "llama6.7b-bf16": 160,
-    "slice123b-gqa-bf16": 96,
+    "llama1.3b-bf16": (si.WORKLOADS["llama1.3b-bf16"], 160, 2e-2, 2.0 ** -8),
+    "llama6.7b-bf16": (si.WORKLOADS["llama6.7b-bf16"], 160, 2e-2, 2.0 ** -8),
+    "slice123b-gqa-bf16": (si.WORKLOADS["slice123b-gqa-bf16"], 96, 2e-2, 2.0 ** -8),
+    "llama6.7b-f16": (si.WORKLOADS["llama6.7b-bf16"].with_(dtype="f16"), 160, F16_TOL, 2.0 ** -11),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_full_size_layer(name):
-    w = si.WORKLOADS[name]
-    P = CASES[name]
+    w, P, tol, u = CASES[name]
     say("full-size layer", name, "prefix", P)
     p = si.layer_params(w, 0, gains="random")
     x = si.layer_input(w)
@@ -60,8 +63,8 @@ def test_full_size_layer(name):
     dxo, go = oracle.layer_bwd(p64, cache, dy_m[0:1, :P].astype(np.float64), sh)
     errs = {"y": rel(y[0:1, :P], yo), "y-x": rel(y[0:1, :P] - x0, yo - x0), "dx": rel(dx[0:1, :P], dxo),
             "dx-dy": rel(dx[0:1, :P] - dy_m[0:1, :P], dxo - dy_m[0:1, :P])}
-    errs["floor:y-x"] = 2.0 ** -8 * np.linalg.norm(yo) / np.linalg.norm(yo - x0)
-    errs["floor:dx-dy"] = 2.0 ** -8 * np.linalg.norm(dxo) / np.linalg.norm(dxo - dy_m[0:1, :P])
+    errs["floor:y-x"] = u * np.linalg.norm(yo) / np.linalg.norm(yo - x0)
+    errs["floor:dx-dy"] = u * np.linalg.norm(dxo) / np.linalg.norm(dxo - dy_m[0:1, :P])
     for k in go:
         errs["d" + k] = rel(g[k], go[k])
     del go, cache
@@ -72,7 +75,7 @@ def test_full_size_layer(name):
     yl = oracle.layer_fwd_rows(p64, xl, rows, oracle_shape(w))
     errs["y_late"] = rel(y[w.batch - 1, rows], yl)
     errs["y-x_late"] = rel(y[w.batch - 1, rows] - xl[rows], yl - xl[rows])
-    errs["floor:y-x_late"] = 2.0 ** -8 * np.linalg.norm(yl) / np.linalg.norm(yl - xl[rows])
+    errs["floor:y-x_late"] = u * np.linalg.norm(yl) / np.linalg.norm(yl - xl[rows])
     print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    bad = check_errors(errs, 2e-2)
+    bad = check_errors(errs, tol)
     assert not bad, bad
