@@ -1,6 +1,7 @@
 """Parity of one decoder layer at the full sizes of the larger workloads (the
 1.3B- and 6.7B-shaped layers, T = 8192, and the 123B-shaped GQA slice,
-hidden 12288, seq 4096; the 6.7B-shaped layer also in fp16 storage), in the
+hidden 12288, seq 4096; the 6.7B- and 123B-shaped layers also in fp16
+storage), in the
 same launch configuration the engine uses.
 
 The fp64 oracle cannot run a whole layer at these sizes, so two exact
@@ -32,6 +33,7 @@ CASES = {
     "llama6.7b-bf16": (si.WORKLOADS["llama6.7b-bf16"], 160, 2e-2, 2.0 ** -8),
     "slice123b-gqa-bf16": (si.WORKLOADS["slice123b-gqa-bf16"], 96, 2e-2, 2.0 ** -8),
     "llama6.7b-f16": (si.WORKLOADS["llama6.7b-bf16"].with_(dtype="f16"), 160, F16_TOL, 2.0 ** -11),
+    "slice123b-gqa-f16": (si.WORKLOADS["slice123b-gqa-bf16"].with_(dtype="f16"), 96, F16_TOL, 2.0 ** -11),
 }
 
 
