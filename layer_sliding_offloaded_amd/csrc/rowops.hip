@@ -57,6 +57,93 @@ rmsnorm_fwd_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restri
   }
 }
 
+// Wide rows, H = NC x 256 x VE (NC = 2 .. 8): a block of four waves owns a
+// row and each thread holds NC 16-byte vectors of it in registers, so the
+// row crosses HBM once (the wave-per-row kernels read it twice: once for the
+// row statistic, once for the output).  The statistic is the sum of the four
+// waves' sums, added in wave order.
+template <typename T, int NC>
+__global__ void __launch_bounds__(256)
+rmsnorm_fwd_rows_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict__ y,
+                        float* __restrict__ r, int H, float eps) {
+  constexpr int VE = 16 / sizeof(T);
+  __shared__ float part[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * H;
+  uint4 xq[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) xq[k] = *reinterpret_cast<const uint4*>(x + base + (k * 256 + tid) * VE);
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    float f[VE];
+    Elem<T>::unpack(xq[k], f);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ss += f[e] * f[e];
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) part[w] = ss;
+  __syncthreads();
+  const float rr = 1.0f / sqrtf((((part[0] + part[1]) + part[2]) + part[3]) / H + eps);
+  if (tid == 0) r[blockIdx.x] = rr;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    float f[VE], gg[VE];
+    Elem<T>::unpack(xq[k], f);
+    load_vec<T>(g + (k * 256 + tid) * VE, gg);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) f[e] = f[e] * rr * gg[e];
+    store_vec<T>(y + base + (k * 256 + tid) * VE, f);
+  }
+}
+
+// RMSNorm backward (input part) for wide rows, one HBM pass: as
+// rmsnorm_bwd_kernel below, with the row in registers (layout as above).
+template <typename T, int NC>
+__global__ void __launch_bounds__(256)
+rmsnorm_bwd_rows_kernel(const T* __restrict__ dout, const T* __restrict__ xin, const float* __restrict__ r,
+                        const T* __restrict__ g, const T* __restrict__ resid, T* __restrict__ dx, int H) {
+  constexpr int VE = 16 / sizeof(T);
+  __shared__ float part[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * H;
+  const float rr = r[blockIdx.x];
+  uint4 dq[NC], xq[NC], gq[NC], rq[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int c = (k * 256 + tid) * VE;
+    dq[k] = *reinterpret_cast<const uint4*>(dout + base + c);
+    xq[k] = *reinterpret_cast<const uint4*>(xin + base + c);
+    gq[k] = *reinterpret_cast<const uint4*>(g + c);
+    rq[k] = resid ? *reinterpret_cast<const uint4*>(resid + base + c) : make_uint4(0, 0, 0, 0);
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    float d[VE], xv[VE], gg[VE];
+    Elem<T>::unpack(dq[k], d);
+    Elem<T>::unpack(xq[k], xv);
+    Elem<T>::unpack(gq[k], gg);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) dot += d[e] * gg[e] * xv[e];
+  }
+  dot = wave_sum(dot);
+  if (lane == 0) part[w] = dot;
+  __syncthreads();
+  const float proj = (((part[0] + part[1]) + part[2]) + part[3]) * rr / H;  // mean(dn * n)
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    float d[VE], xv[VE], gg[VE], o[VE];
+    Elem<T>::unpack(dq[k], d);
+    Elem<T>::unpack(xq[k], xv);
+    Elem<T>::unpack(gq[k], gg);
+    Elem<T>::unpack(rq[k], o);  // zeros (all bits clear) without a residual
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[e] += rr * (d[e] * gg[e] - xv[e] * rr * proj);
+    store_vec<T>(dx + base + (k * 256 + tid) * VE, o);
+  }
+}
+
 // RMSNorm backward (input part): n = xin r, dn = dout g,
 // dx = resid + r (dn - n mean(dn n)).  resid may be null (treated as 0).
 template <typename T>
@@ -763,13 +850,35 @@ loss_reduce_kernel(const float* __restrict__ loss_rows, float* __restrict__ loss
 // Host dispatch: every row kernel exists for fp32, bf16 and fp16 storage.
 #define SF_T typename decltype(tag)::type
 
+// Wide-row kernels' vectors per thread: H / (256 VE) when that is a whole
+// number from 2 to 8 (H = 4096 .. 16384 in steps of 2048 for 16-bit storage),
+// else 0 (the wave-per-row kernels).
+template <typename T>
+int wide_chunks(int H) {
+  constexpr int VE = 16 / sizeof(T);
+  if (H % (256 * VE)) return 0;
+  const int nc = H / (256 * VE);
+  return nc >= 2 && nc <= 8 ? nc : 0;
+}
+
 hipError_t rmsnorm_fwd(int dtype, const void* x, const void* g, void* y, float* r, int rows, int H,
                        float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   return with_storage(dtype, [&](auto tag) {
     using T = SF_T;
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<const T*>(x),
-                       static_cast<const T*>(g), static_cast<T*>(y), r, rows, H, eps);
+    const T* xi = static_cast<const T*>(x);
+    const T* gg = static_cast<const T*>(g);
+    T* yo = static_cast<T*>(y);
+    switch (wide_chunks<T>(H)) {
+#define SF_FWD_ROWS(NC)                                                                                        \
+  case NC:                                                                                                     \
+    hipLaunchKernelGGL((rmsnorm_fwd_rows_kernel<T, NC>), dim3(rows), dim3(256), 0, s, xi, gg, yo, r, H, eps); \
+    break;
+      SF_FWD_ROWS(2) SF_FWD_ROWS(3) SF_FWD_ROWS(4) SF_FWD_ROWS(5) SF_FWD_ROWS(6) SF_FWD_ROWS(7) SF_FWD_ROWS(8)
+#undef SF_FWD_ROWS
+      default:
+        hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, xi, gg, yo, r, rows, H, eps);
+    }
     return hipGetLastError();
   });
 }
@@ -804,7 +913,17 @@ hipError_t rmsnorm_bwd(int dtype, const void* dout, const void* xin, const float
       }
     } else {
       const dim3 pg((H / VE + 63) / 64, nchunks);
-      hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, d, xi, r, gg, rs, o, rows, H);
+      switch (wide_chunks<T>(H)) {
+#define SF_BWD_ROWS(NC)                                                                                          \
+  case NC:                                                                                                       \
+    hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<T, NC>), dim3(rows), dim3(256), 0, s, d, xi, r, gg, rs, o, H); \
+    break;
+        SF_BWD_ROWS(2) SF_BWD_ROWS(3) SF_BWD_ROWS(4) SF_BWD_ROWS(5) SF_BWD_ROWS(6) SF_BWD_ROWS(7) SF_BWD_ROWS(8)
+#undef SF_BWD_ROWS
+        default:
+          hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, d, xi, r, gg, rs, o, rows,
+                             H);
+      }
       hipLaunchKernelGGL(gain_partial_kernel<T>, pg, dim3(64), 0, s, d, xi, r, partial, rows, H, rpc);
     }
     hipLaunchKernelGGL(gain_reduce_kernel, dim3((H + kReduceCols - 1) / kReduceCols),

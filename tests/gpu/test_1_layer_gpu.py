@@ -47,6 +47,14 @@ CASES = {
     "f16-s65-seq-edge": (BASE.with_(dtype="f16", batch=2, seq=65), F16_TOL, 0.05),
     "f16-seq1": (BASE.with_(dtype="f16", batch=3, seq=1), F16_TOL, 0.05),
     "f16-stack4-h1024-full": (W["stack4-h1024-bf16"].with_(dtype="f16"), F16_TOL, 1.0),
+    # wide rows (one block of four waves per row for the RMSNorm forward and
+    # backward): hidden 4096 and 6144 in 16-bit storage, 2048 in fp32
+    "bf16-h4096-wide-rows": (BASE.with_(dtype="bf16", hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128,
+                                        ffn=1024, batch=1, seq=64), 2e-2, 0.05),
+    "f16-h6144-wide-rows": (BASE.with_(dtype="f16", hidden=6144, n_heads=48, n_kv_heads=8, head_dim=128, ffn=512,
+                                       batch=1, seq=40), F16_TOL, 0.05),
+    "fp32-h2048-wide-rows": (BASE.with_(hidden=2048, n_heads=16, n_kv_heads=16, head_dim=128, ffn=1024, batch=2,
+                                        seq=24), 1e-4, 1.0),
 }
 
 
