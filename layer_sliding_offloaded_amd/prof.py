@@ -390,6 +390,9 @@ def rowops(db_path, workload):
     spec = [
         ("rmsnorm_fwd_kernel", None, 2 * T * H * e + T * 4 + H * e, "x in, y out, r out"),
         ("rmsnorm_bwd_kernel", None, 4 * T * H * e + T * 4 + H * e, "dy, x, residual in; dx out"),
+        # wide rows (a block per row, the row in registers)
+        ("rmsnorm_fwd_rows_kernel", None, 2 * T * H * e + T * 4 + H * e, "x in, y out, r out"),
+        ("rmsnorm_bwd_rows_kernel", None, 4 * T * H * e + T * 4 + H * e, "dy, x, residual in; dx out"),
         ("gain_partial_kernel", None, 2 * T * H * e + T * 4 + 512 * H * 4, "dy, x in; 512 partial rows out"),
         # fused RMSNorm backward + gain partial sums (hidden <= 2048): 512 row chunks
         ("rmsnorm_bwd_gain_kernel", None, 4 * T * H * e + T * 4 + H * e + 512 * H * 4,
