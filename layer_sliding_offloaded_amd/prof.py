@@ -38,6 +38,15 @@ Modes:
   time of each kind over the window, the gaps longer than ``--gap`` ms in
   which no D2H copy runs (with what the H2D copies and the kernels did
   meanwhile), and the busy share of each kind per ``--bucket`` ms.
+* ``vendor``: each layer GEMM of a workload (or those named by ``--gemms``)
+  through ``sf_gemm`` and through ``torch.mm`` (hipBLASLt), same operand
+  layouts and output types, ``--reps`` launches of each after two warm-ups,
+  timed with HIP events; prints both durations and TFLOP/s.  Under
+  ``rocprofv3 --kernel-trace`` it also names the library's kernels.
+* ``vendor-counters``: counter CSVs of ``rocprofv3 --pmc ... -- prof vendor``
+  (same ``--workload``, ``--gemms`` and ``--reps``): per GEMM, every counter
+  averaged over the timed launches of this library's kernel and of the
+  library kernel, side by side.
 * ``head-study``: the chunked LM head + cross-entropy (``sf_head_fwd_bwd``)
   at one shape for several chunk sizes, the largest being the whole token
   count (every logit materialised at once): device bytes of the head's
@@ -49,6 +58,8 @@ Modes:
     python -m layer_sliding_offloaded_amd.prof gemm-runs RESULTS_DB --workload W
     python -m layer_sliding_offloaded_amd.prof rowops RESULTS_DB --workload W
     python -m layer_sliding_offloaded_amd.prof timeline TRACE_CSV [--gap 20] [--bucket 50]
+    python -m layer_sliding_offloaded_amd.prof vendor --workload W [--gemms gu_fwd,o_fwd] [--reps 5]
+    python -m layer_sliding_offloaded_amd.prof vendor-counters CSV... --workload W [--gemms ...] [--reps 5]
     python -m layer_sliding_offloaded_amd.prof head-study --hidden 4096 --vocab 128256 --batch 4 --seq 2048 \
         --chunks 8192,4096,2048,1024,512,256
 """
@@ -228,6 +239,100 @@ def mfma(csv_path, workload):
     print(f"Layer total: {tot / 1e12:.3f} TFLOP of bf16 MFMA work executed; algorithmic "
           f"{layer_flops(w) / 1e12:.3f} TFLOP (6 T P_lin + 6 B n_h S^2 d); attention forward alone is "
           f"{attn_fwd / 1e9:.1f} GFLOP algorithmic (causal half).")
+
+
+def _selected(workload, gemms):
+    sel = set(gemms.split(",")) if gemms else None
+    return [g for g in _gemms(workload) if sel is None or g[0] in sel]
+
+
+def vendor(workload, gemms, reps):
+    """This library's GEMMs against torch.mm (hipBLASLt), see the module docstring."""
+    import torch
+
+    from layer_sliding_offloaded_amd import sf
+    sf.load()
+    s = torch.cuda.current_stream()
+
+    def timed(f):
+        for _ in range(2):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            f()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    print("| GEMM | layout | M x N x K | this library us | TFLOP/s | hipBLASLt us | TFLOP/s | library / ours |")
+    print("|---|---|---|---:|---:|---:|---:|---:|")
+    for name, lay, M, N, K in _selected(workload, gemms):
+        a_shape = (K, M) if lay == 2 else (M, K)
+        b_shape = (N, K) if lay == 0 else (K, N)
+        A = torch.randn(a_shape, device="cuda").to(torch.bfloat16)
+        B = torch.randn(b_shape, device="cuda").to(torch.bfloat16)
+        C = torch.empty((M, N), device="cuda", dtype=torch.float32 if lay == 2 else torch.bfloat16)
+        wsb = sf.sf_gemm_workspace_bytes(M, N, K)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        ours = timed(lambda: sf.sf_gemm(sf.SF_BF16, lay, 1 if lay == 2 else 0, M, N, K, A.data_ptr(), a_shape[1],
+                                        B.data_ptr(), b_shape[1], C.data_ptr(), N, s.cuda_stream, ws.data_ptr(),
+                                        wsb))
+        if lay == 0:
+            lib = timed(lambda: torch.mm(A, B.t()))
+        elif lay == 1:
+            lib = timed(lambda: torch.mm(A, B))
+        else:
+            lib = timed(lambda: torch.mm(A.t(), B, out_dtype=torch.float32))
+        fl = 2.0 * M * N * K
+        print(f"| {name} | {['NT', 'NN', 'TN'][lay]} | {M} x {N} x {K} | {ours:.1f} | {fl / ours / 1e6:.0f} | "
+              f"{lib:.1f} | {fl / lib / 1e6:.0f} | {lib / ours:.3f} |", flush=True)
+        del A, B, C, ws
+
+
+def vendor_counters(paths, workload, gemms, reps):
+    """Counters of ``vendor`` launches, this library's kernel beside hipBLASLt's (see the module docstring)."""
+    runs = []  # [(kind, [(name, counters, dur_us)])] over all files, merged per dispatch
+    per = {}
+    for path in paths:
+        for r in _rows(path):
+            n = r["Kernel_Name"]
+            kind = "ours" if "sf::" in n or "_ZN2sf" in n else ("lib" if "Cijk" in n else None)
+            if kind is None or "splitk_reduce" in n:
+                continue
+            k = (path, int(r["Dispatch_Id"]))
+            e = per.setdefault(k, [kind, n, {}, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3])
+            e[2][r["Counter_Name"]] = e[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    sel = _selected(workload, gemms)
+    per_file = {}
+    for (path, d), e in sorted(per.items()):
+        per_file.setdefault(path, []).append(e)
+    counters, rows = [], {}
+    for path, seq in per_file.items():
+        # per GEMM: this library's launches, then the library's, each 2 warm-ups + reps
+        i = 0
+        for name, *_ in sel:
+            for kind in ("ours", "lib"):
+                grp = seq[i:i + 2 + reps]
+                i += 2 + reps
+                if len(grp) < 2 + reps or any(g[0] != kind for g in grp):
+                    raise SystemExit(f"{path}: unexpected launch sequence at {name} {kind}")
+                slot = rows.setdefault((name, kind), {"name": grp[-1][1], "dur": []})
+                for c in grp[-1][2]:
+                    if c not in counters:
+                        counters.append(c)
+                    slot[c] = sum(g[2][c] for g in grp[2:]) / reps
+                slot["dur"] += [g[3] for g in grp[2:]]
+    print("| GEMM | kernel | us (under counters) | " + " | ".join(counters) + " |")
+    print("|---|---|---:|" + "---:|" * len(counters))
+    for name, *_ in sel:
+        for kind in ("ours", "lib"):
+            r = rows[(name, kind)]
+            kn = short_name(r["name"])[:70] if kind == "ours" else r["name"].split("_MT")[0][-40:] + " MT" + \
+                r["name"].split("_MT")[1].split("_")[0] if "_MT" in r["name"] else r["name"][:70]
+            print(f"| {name} | `{kn}` | {sum(r['dur']) / len(r['dur']):.1f} | " +
+                  " | ".join(f"{r.get(c, float('nan')):.4g}" for c in counters) + " |")
 
 
 def _rows(path):
@@ -545,7 +650,7 @@ def timeline(path, gap_ms, bucket_ms):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("mode", choices=["probe", "summarize", "kernels", "gemm-runs", "rowops", "head-study",
-                                     "layer-probe", "mfma", "timeline"])
+                                     "layer-probe", "mfma", "timeline", "vendor", "vendor-counters"])
     ap.add_argument("files", nargs="*")
     ap.add_argument("--workload", default="stack4-h1024-bf16")
     ap.add_argument("--top", type=int, default=30)
@@ -556,6 +661,8 @@ def main():
     ap.add_argument("--chunks", default="8192,4096,2048,1024,512,256")
     ap.add_argument("--gap", type=float, default=20.0)
     ap.add_argument("--bucket", type=float, default=50.0)
+    ap.add_argument("--gemms", default="")
+    ap.add_argument("--reps", type=int, default=5)
     a = ap.parse_args()
     if a.mode == "probe":
         probe(a.workload)
@@ -571,6 +678,10 @@ def main():
         rowops(a.files[0], a.workload)
     elif a.mode == "head-study":
         head_study(a.hidden, a.vocab, a.batch, a.seq, a.chunks.split(","))
+    elif a.mode == "vendor":
+        vendor(a.workload, a.gemms, a.reps)
+    elif a.mode == "vendor-counters":
+        vendor_counters(a.files, a.workload, a.gemms, a.reps)
     elif a.mode == "timeline":
         timeline(a.files[0], a.gap, a.bucket)
     else:

@@ -1,8 +1,11 @@
 """Host logic of the measurement tools: kernel-name shortening, the rule
 that a stored HBM-traffic figure is used only for the GEMM source it was
-measured on, and the engine-timeline summary."""
+measured on, the engine-timeline summary and the pairing of counter rows
+in the comparison with the vendor library."""
 
 import json
+
+import pytest
 
 import bench
 from layer_sliding_offloaded_amd import prof
@@ -43,6 +46,33 @@ def test_timeline_busy_times_and_d2h_gaps(tmp_path, capsys):
     assert "| compute | 30.0 | 20.0 % | |" in out
     assert "| d2h | 80.0 | 53.3 % | 2.00 GB |" in out
     assert "| 30.0 | 100.0 | 70.0 | 50.0 | 10.0 |" in out
+
+
+def test_vendor_counters_pairs_launches_by_order(tmp_path, capsys):
+    """Per GEMM the CSV holds this library's launches, then the library's
+    (two warm-ups + reps each), among unrelated kernels; each side's counters
+    are averaged over its timed launches only, and a launch sequence that does
+    not have that shape is refused."""
+    reps = 2
+    rows, d = [], 0
+    for g in ("o_fwd", "o_dx"):
+        for kind, base in (("_ZN2sf12gemm_pp_kernel", 100.0), ("Cijk_Ailk_Bljk_MT256x256x64_SK3", 10.0)):
+            for i in range(2 + reps):
+                d += 1
+                rows.append((d, "randn_kernel", "X", 1.0))
+                d += 1
+                v = base * (1 if g == "o_fwd" else 2) + (1000.0 if i < 2 else i)
+                rows.append((d, kind, "TCC_MISS_sum", v))
+    path = tmp_path / "c.csv"
+    path.write_text("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n" +
+                    "".join(f"{a},{b},{c},{v},0,1000\n" for a, b, c, v in rows))
+    prof.vendor_counters([str(path)], "slice123b-gqa-bf16", "o_fwd,o_dx", reps)
+    out = capsys.readouterr().out.splitlines()
+    got = {(l.split("|")[1].strip(), "Cijk" in l or "MT256" in l): float(l.split("|")[4]) for l in out[2:]}
+    # timed launches carry base * g + 2 and + 3: mean base * g + 2.5
+    assert got == {("o_fwd", False): 102.5, ("o_fwd", True): 12.5, ("o_dx", False): 202.5, ("o_dx", True): 22.5}
+    with pytest.raises(SystemExit):
+        prof.vendor_counters([str(path)], "slice123b-gqa-bf16", "o_fwd,o_dx", reps + 1)
 
 
 def test_layer_gemms_cover_the_projection_flops():
