@@ -19,7 +19,9 @@
 //  - gemm_pipe_kernel: NS stages of BK k, the loads of stage kt + NS - 1
 //    issued while stage kt is multiplied (small grids);
 //  - gemm_pp_kernel: 256 x 256 tiles whose 8 waves split into two groups
-//    that alternate between a memory phase and an MFMA phase (large grids).
+//    that alternate between a memory phase and an MFMA phase (large grids);
+//  - gemm_pl_kernel: the same for NT with B staged in whole 128-byte lines
+//    (64 k per stage), half the L2 read requests of 32-k stages.
 // The register-staged gemm_kernel (loads through VGPRs, in-register 8x8 /
 // 4x4 transposes of row-contiguous operands, 144-byte padded LDS rows)
 // serves fp32 and operands the direct loads cannot take.
@@ -30,6 +32,7 @@
 // SwiGLU (gate j, up j) need sit in the same lane.
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm.h"
@@ -1124,6 +1127,151 @@ gemm_pp_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
   epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
 }
 
+// Ping-pong variant for NT that reads B in whole lines.  A [row][k] operand
+// staged 32 k at a time contributes 64 bytes per row and stage, half a
+// 128-byte line, so every line reaches L2 as two requests (the transposed
+// operand of NN and TN, 512 bytes per k-row, is read in whole lines anyway).
+// Here B is staged 64 k at a time, one whole line per row, in NL = 3 buffers
+// of 32 KB, and A keeps 32-k stages in NO = 4 buffers of 16 KB (160 KB in
+// all).  Step kt (32 k) multiplies A stage kt with half kt % 2 of B line
+// kt / 2: the same 32-k steps in the same order with the same fragments and
+// MFMAs as gemm_pp_kernel, so the same bits.  Loads run ahead: step kt
+// issues A stage kt + 3 (into the buffer of step kt - 1) and, on even steps,
+// B line kt / 2 + 2 (into the buffer of line kt / 2 - 1, whose second half
+// step kt - 1 read).  What step kt + 1 needs was issued at step kt - 2 or
+// earlier, so after step kt's issues a wave may leave the loads of steps
+// kt - 1 and kt in flight: two A stages and one B line.  The loop body covers
+// 12 steps (the periods 4 and 2 x 3 of the two rings) so that every buffer
+// index is a constant.  (The same ring for NN, with A in lines, needs more
+// than 256 VGPRs and spills in its loop.)
+template <typename T, GemmLayout LAY, Epi E>
+__global__ void __launch_bounds__(512)
+gemm_pl_kernel(const GemmArgs g, int ntm, int ntn, int a_bytes, int b_bytes) {
+  static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
+  static_assert(LAY == GemmLayout::NT, "B read in whole lines: both operands k-contiguous");
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 64, NW = 8;
+  constexpr int FM = WM / 16, FN = WN / 16, WGM = BM / WM;
+  constexpr int NO = 4, NL = 3;
+  constexpr int OSZ = BM * 32 * 2, LSZ = BN * 64 * 2;
+  static_assert(NO * OSZ + NL * LSZ <= 160 * 1024, "stages within the 160 KB of LDS");
+  static_assert(!(E == Epi::Rope || E == Epi::SwigluFwd) || FN % 2 == 0, "pair epilogue needs even FN");
+  struct Smem {
+    __attribute__((aligned(1024))) char a[NO][OSZ];
+    __attribute__((aligned(1024))) char b[NL][LSZ];
+  };
+  __shared__ Smem smem;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WGM, wn = w / WGM;
+  const bool late = w >= 4;  // group 1: one phase behind
+  int tm, tn;
+  tile_coords(ntm, ntn, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), 0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.B), 0, b_bytes, 0x00020000);
+  using LA = direct::DirectK<BM, NW, true, 32>;
+  using LB = direct::DirectK<BN, NW, true, 64>;
+  LA la;
+  LB lb;
+  constexpr int WAITN = 2 * LA::JW + LB::JW;
+  la.init(w, lane, g.lda, m0, g.M, [&](int r) { const int m = m0 + r; return m < g.M ? m : -1; });
+  lb.init(w, lane, g.ldb, n0, g.N, [&](int r) { return ColMap<E, WN>::brow(r, n0, g, BN); });
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kbeg = blockIdx.y * g.kchunk;  // a multiple of 64
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
+  auto issue_a = [&](char* st, int kt) { la.issue(ra, st, w, kbeg + kt * 32, kend, g.lda); };
+  auto issue_b = [&](char* st, int line) { lb.issue(rb, st, w, kbeg + line * 64, kend, g.ldb); };
+  const int lr = lane % 16, lg = lane / 16;
+  uint4 af[FM], bfr[FN];
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    direct::wait_vm<WAITN>();
+    direct::bar();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // memory phase of step kt = kt0 + u (kt0 a multiple of 12): fragments of A
+  // stage u % NO and of half u % 2 of B line (u / 2) % NL, then the loads
+  auto mem = [&](int kt, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const char* as = smem.a[u % NO];
+    const char* bs = smem.b[(u / 2) % NL];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[j] = direct::fragk<BN, true, 64>(bs, wn * WN + j * 16, u % 2, lr, lg);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = direct::fragk<BM, true, 32>(as, wm * WM + i * 16, 0, lr, lg);
+    issue_a(smem.a[(u + 3) % NO], kt + 3);
+    if constexpr (u % 2 == 0) issue_b(smem.b[(u / 2 + 2) % NL], kt / 2 + 2);
+  };
+  auto compute = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) Mfma<T>::run(acc[i][j], bfr[j], af[i]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (nk > 0) {
+    // the issues of steps -4 .. -1
+    issue_b(smem.b[0], 0);
+    issue_a(smem.a[0], 0);
+    issue_a(smem.a[1], 1);
+    issue_b(smem.b[1], 1);
+    issue_a(smem.a[2], 2);
+    sync();
+    if (late) sync();
+    for (int kt = 0; kt < nk; kt += 12) {
+      auto step = [&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (u == 0 || kt + u < nk) {
+          mem(kt + u, uc);
+          sync();
+          compute();
+          sync();
+        }
+      };
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+      step(std::integral_constant<int, 4>{});
+      step(std::integral_constant<int, 5>{});
+      step(std::integral_constant<int, 6>{});
+      step(std::integral_constant<int, 7>{});
+      step(std::integral_constant<int, 8>{});
+      step(std::integral_constant<int, 9>{});
+      step(std::integral_constant<int, 10>{});
+      step(std::integral_constant<int, 11>{});
+    }
+    if (!late) sync();
+    direct::wait_vm<0>();  // no load into LDS outlives the block
+  }
+
+  if constexpr (kRowsEpi<E, WN>) {
+    static_assert(NW * kPatchBytes<WN, E> <= sizeof(Smem), "row epilogue patches");
+    if (g.rows_epi) {
+      __syncthreads();  // every wave is done with the stages
+      epilogue_rows<T, WM, WN, FM, FN, E>(
+          g, acc, m0, n0, wm, wn, lane,
+          reinterpret_cast<float*>(reinterpret_cast<char*>(&smem) + w * kPatchBytes<WN, E>));
+      return;
+    }
+  }
+  epilogue<T, WM, WN, FM, FN, E>(g, acc, m0, n0, wm, wn, lr, lg, BN);
+}
+
 // out[m, n] = sum over s (in order) of partial[s][m][n]; 4 columns per thread.
 template <typename TO>
 __global__ void __launch_bounds__(256)
@@ -1160,7 +1308,8 @@ bool direct_ok(const GemmArgs& g, int64_t* a_bytes, int64_t* b_bytes) {
 }
 
 // KIND 0: register-staged kernel; 1: direct loads, 2 stages of 64 k; 2: direct
-// loads, NS stages of BK k; 3: the same with two wave groups in ping-pong.
+// loads, NS stages of BK k; 3: the same with two wave groups in ping-pong;
+// 4: ping-pong with B in whole-line stages (NT, 256 x 256).
 // S_req > 0: split K into S_req ranges (Store / StoreF32, with enough scratch)
 // instead of the small-grid rule.
 template <typename T, int BM, int BN, int WM, int WN, GemmLayout LAY, Epi E, int KIND = 0, int BK = 64, int NS = 4>
@@ -1197,7 +1346,11 @@ hipError_t launch(const GemmArgs& g_in, hipStream_t s, float* ws, size_t ws_byte
       ok = ok && g.head_dim % 16 == 0 && g.rope_cols % g.head_dim == 0 && a16(g.rope_cos) && a16(g.rope_sin);
     g.rows_epi = ok ? 1 : 0;
   }
-  if constexpr (KIND == 3) {
+  if constexpr (KIND == 4) {
+    static_assert(BM == 256 && BN == 256 && WM == 128 && WN == 64, "whole-line ping-pong tile");
+    hipLaunchKernelGGL((gemm_pl_kernel<T, LAY, E>), dim3(ntm * ntn, S), dim3(NT), 0, s, g, ntm, ntn,
+                       static_cast<int>(a_bytes), static_cast<int>(b_bytes));
+  } else if constexpr (KIND == 3) {
     static_assert(sizeof(T) == 2, "direct loads take 16-bit operands");
     hipLaunchKernelGGL((gemm_pp_kernel<T, BM, BN, WM, WN, BK, LAY, E, NS>), dim3(ntm * ntn, S), dim3(NT), 0, s, g,
                        ntm, ntn, static_cast<int>(a_bytes), static_cast<int>(b_bytes));
@@ -1247,8 +1400,12 @@ hipError_t dispatch_tiles(const GemmArgs& g, hipStream_t s, float* ws, size_t ws
       // which would turn the 3.5 rounds of qkv_fwd's 896 tiles into 7, are
       // slower on every layer GEMM (0.35-0.44 of the peak against
       // 0.45-0.58): a 64 x 64 wave tile reads 8 fragments per 16 MFMAs.
+      // NT takes the whole-line variant: same bits, 5-18 % faster on the
+      // forward products at the 6.7B and 123B shapes (half the L2 read
+      // requests; L2 misses unchanged).
       if (cfg == 0) {
         if constexpr (LAY == GemmLayout::TN) return launch<T, 256, 256, 128, 64, LAY, E, 3, 32>(g, s, ws, wsb, ab, bb);
+        if constexpr (LAY == GemmLayout::NT) return launch<T, 256, 256, 128, 64, LAY, E, 4, 32>(g, s, ws, wsb, ab, bb);
         return launch<T, 256, 256, 128, 64, LAY, E, 3, 32, 5>(g, s, ws, wsb, ab, bb);
       }
       if constexpr (E == Epi::Store || E == Epi::StoreF32) {
