@@ -16,7 +16,10 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(128, 256, 64), (200, 688, 256), (1000, 520, 1376), (37, 8, 8), (4096, 1024, 520), (300, 3072, 2048),
           (512, 1024, 32000), (1024, 1024, 2600),
           # >= 256 tiles of 256 x 256: the large-grid kernels, ragged in M, N and K (K % 32 = 8)
-          (4104, 4112, 1000)]
+          (4104, 4112, 1000),
+          # large grids with fewer k-steps than one pass of the NT kernel's 12-step loop body:
+          # two 32-k steps, the second and the only 64-k B line partly past K; 7 steps, 4 lines
+          (4104, 4104, 40), (2056, 8200, 200)]
 
 
 @pytest.mark.parametrize("layout", [0, 1, 2], ids=["NT", "NN", "TN"])
