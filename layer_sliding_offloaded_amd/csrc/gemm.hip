@@ -13,7 +13,7 @@
 // by the buffer unit itself (buffer_load ... lds, no VGPR round trip) into
 // XOR-swizzled stage buffers: k-contiguous operands as [row][k], the
 // transposed side of NN / TN as [k][row] read back with the LDS transpose
-// load.  Three kernels share those helpers:
+// load.  Four kernels share those helpers:
 //  - gemm_direct_kernel: 2 stages of 64 k (grids that fill the chip with
 //    128 x 128 tiles);
 //  - gemm_pipe_kernel: NS stages of BK k, the loads of stage kt + NS - 1
@@ -21,7 +21,7 @@
 //  - gemm_pp_kernel: 256 x 256 tiles whose 8 waves split into two groups
 //    that alternate between a memory phase and an MFMA phase (large grids);
 //  - gemm_pl_kernel: the same for NT with B staged in whole 128-byte lines
-//    (64 k per stage), half the L2 read requests of 32-k stages.
+//    (64 k per stage): one L2 request per line of B instead of two.
 // The register-staged gemm_kernel (loads through VGPRs, in-register 8x8 /
 // 4x4 transposes of row-contiguous operands, 144-byte padded LDS rows)
 // serves fp32 and operands the direct loads cannot take.
